@@ -1,0 +1,20 @@
+"""MI355X-native 1D deformable convolution forward (DeformConv1d).
+
+The compute lives in ``libdc1d.so`` (HIP kernels for gfx950 behind a C ABI
+declared in ``include/dc1d.h``); ``deformable_convolution_amd.dc1d`` is the
+thin ctypes binding over it.  ``inputs`` holds the seeded synthetic-input
+generator.  The library is loaded on first use, so importing the package
+never requires a GPU.
+"""
+from .dc1d import (  # noqa: F401
+    Dc1dError,
+    debug_positions,
+    forward,
+    library_path,
+    load_library,
+    output_length,
+    plan,
+    resolve_padding,
+    status_string,
+    workspace_bytes,
+)

@@ -1,0 +1,226 @@
+"""ctypes binding over libdc1d (declared in include/dc1d.h).
+
+Argument marshalling only: this module turns torch tensors into
+``dc1d_tensor`` descriptors, passes torch's current HIP stream, and maps
+status codes to exceptions.  Every step of the computation runs in the
+library's HIP kernels; there is no fallback of any kind -- if the library is
+missing or the device is not a gfx950, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libdc1d.so")
+
+DC1D_F32, DC1D_BF16 = 0, 1
+_DTYPES = {torch.float32: DC1D_F32, torch.bfloat16: DC1D_BF16}
+
+OK, ERR_NULL_PTR, ERR_BAD_ARG, ERR_BAD_SHAPE, ERR_BAD_DTYPE, ERR_ALIAS, ERR_WORKSPACE, ERR_DEVICE, ERR_LAUNCH = range(9)
+
+
+class Dc1dError(RuntimeError):
+    """A non-OK status from libdc1d."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, status_string(status), status))
+
+
+class Dc1dValueError(Dc1dError, ValueError):
+    """Argument, shape, dtype, alias or workspace errors."""
+
+
+class _Tensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4)]
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libdc1d.so (built in-tree); raise if it is not there."""
+    global _lib
+    with _lib_lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise ImportError("libdc1d.so is not built (expected at %s); run __graft_entry__.build()"
+                                  % _LIB_PATH)
+            lib = ctypes.CDLL(_LIB_PATH)
+            i64, p, T = ctypes.c_int64, ctypes.c_void_p, ctypes.POINTER(_Tensor)
+            lib.dc1d_output_length.restype = i64
+            lib.dc1d_output_length.argtypes = [i64] * 5
+            lib.dc1d_workspace_bytes.restype = ctypes.c_int
+            lib.dc1d_workspace_bytes.argtypes = [T] * 5 + [i64] * 5 + [ctypes.POINTER(ctypes.c_size_t)]
+            lib.dc1d_forward.restype = ctypes.c_int
+            lib.dc1d_forward.argtypes = [T] * 6 + [i64] * 5 + [p, ctypes.c_size_t, p]
+            lib.dc1d_debug_positions.restype = ctypes.c_int
+            lib.dc1d_debug_positions.argtypes = [T, i64, i64, i64, i64, p, p, p, p]
+            lib.dc1d_plan.restype = ctypes.c_int
+            lib.dc1d_plan.argtypes = [T] * 5 + [i64] * 5 + [ctypes.POINTER(ctypes.c_char_p),
+                                                         ctypes.POINTER(i64),
+                                                         ctypes.POINTER(ctypes.c_int32),
+                                                         ctypes.POINTER(ctypes.c_int32)]
+            lib.dc1d_status_string.restype = ctypes.c_char_p
+            lib.dc1d_status_string.argtypes = [ctypes.c_int]
+            _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load_library().dc1d_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        if status in (ERR_NULL_PTR, ERR_BAD_ARG, ERR_BAD_SHAPE, ERR_BAD_DTYPE, ERR_ALIAS, ERR_WORKSPACE):
+            raise Dc1dValueError(status, where)
+        raise Dc1dError(status, where)
+
+
+def _desc(t):
+    if t is None:
+        return None
+    d = _Tensor()
+    d.data = t.data_ptr() if t.numel() > 0 else None
+    d.dtype = _DTYPES.get(t.dtype, -1)
+    d.ndim = t.dim()
+    for i, s in enumerate(t.shape[:4]):
+        d.shape[i] = s
+    return d
+
+
+def _ref(d):
+    return None if d is None else ctypes.byref(d)
+
+
+def output_length(L_in: int, K: int, stride: int = 1, padding: int = 0, dilation: int = 1) -> int:
+    return int(load_library().dc1d_output_length(L_in, K, stride, padding, dilation))
+
+
+def resolve_padding(padding, K: int, stride: int = 1, dilation: int = 1) -> int:
+    """"valid" -> 0; "same" -> dilation*(K-1)/2 when that keeps the length
+    with stride 1 and is symmetric; an int passes through (dc1d page, Usage:
+    padding may be an int, "valid" or "same")."""
+    if isinstance(padding, str):
+        if padding == "valid":
+            return 0
+        if padding == "same":
+            span = dilation * (K - 1)
+            if stride != 1 or span % 2:
+                raise ValueError('padding="same" needs stride 1 and an even dilation*(K-1)')
+            return span // 2
+        raise ValueError("padding must be an int, 'valid' or 'same'")
+    return int(padding)
+
+
+def _contig(t, name):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _args(x, offsets, weight, bias, mask, stride, padding, dilation, groups):
+    K = weight.shape[-1] if weight.dim() == 3 else 0
+    padding = resolve_padding(padding, K, stride, dilation)
+    G = offsets.shape[1] if offsets.dim() == 4 else 0
+    return padding, G
+
+
+_ws_cache = {}
+
+
+def _workspace(nbytes: int, device):
+    """A zero-initialised workspace per (device, stream), grown as needed.
+    The library leaves its counter region zero after every call, so the
+    buffer is zeroed only when it is (re)allocated."""
+    if nbytes == 0:
+        return None
+    stream = torch.cuda.current_stream(device)
+    key = (device.index, stream.cuda_stream)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+def workspace_bytes(x, offsets, weight, bias=None, mask=None, stride=1, padding=0, dilation=1, groups=1) -> int:
+    padding, G = _args(x, offsets, weight, bias, mask, stride, padding, dilation, groups)
+    n = ctypes.c_size_t(0)
+    dx, do, dm, dw, db = map(_desc, (x, offsets, mask, weight, bias))
+    _check(load_library().dc1d_workspace_bytes(_ref(dx), _ref(do), _ref(dm), _ref(dw), _ref(db),
+                                               stride, padding, dilation, groups, G, ctypes.byref(n)),
+           "dc1d_workspace_bytes")
+    return int(n.value)
+
+
+def plan(x, offsets, weight, bias=None, mask=None, stride=1, padding=0, dilation=1, groups=1) -> dict:
+    padding, G = _args(x, offsets, weight, bias, mask, stride, padding, dilation, groups)
+    name = ctypes.c_char_p()
+    grid = ctypes.c_int64()
+    block = ctypes.c_int32()
+    splits = ctypes.c_int32()
+    dx, do, dm, dw, db = map(_desc, (x, offsets, mask, weight, bias))
+    _check(load_library().dc1d_plan(_ref(dx), _ref(do), _ref(dm), _ref(dw), _ref(db), stride, padding,
+                                    dilation, groups, G, ctypes.byref(name), ctypes.byref(grid),
+                                    ctypes.byref(block), ctypes.byref(splits)), "dc1d_plan")
+    return {"kernel": name.value.decode(), "grid": grid.value, "block": block.value, "splits": splits.value}
+
+
+def forward(x, offsets, weight, bias=None, mask=None, stride=1, padding=0, dilation=1, groups=1,
+            out=None, workspace=None):
+    """DeformConv1d forward on the GPU.  Tensors must be contiguous device
+    tensors of one dtype (float32 or bfloat16); returns out [B, C_out, L_out]
+    (allocated unless given).  Enqueued on torch's current stream."""
+    lib = load_library()
+    x, offsets, weight, bias, mask = (_contig(t, n) for t, n in ((x, "x"), (offsets, "offsets"),
+                                                                   (weight, "weight"), (bias, "bias"),
+                                                                   (mask, "mask")))
+    padding, G = _args(x, offsets, weight, bias, mask, stride, padding, dilation, groups)
+    if out is None:
+        L_out = output_length(x.shape[-1], weight.shape[-1], stride, padding, dilation)
+        if L_out < 1 or x.dim() != 3 or weight.dim() != 3:
+            raise Dc1dValueError(ERR_BAD_SHAPE, "dc1d_forward")
+        out = torch.empty((x.shape[0], weight.shape[0], L_out), dtype=x.dtype, device=x.device)
+    dx, do, dm, dw, db, dout = map(_desc, (x, offsets, mask, weight, bias, out))
+    if workspace is None:
+        n = ctypes.c_size_t(0)
+        with torch.cuda.device(x.device):
+            _check(lib.dc1d_workspace_bytes(_ref(dx), _ref(do), _ref(dm), _ref(dw), _ref(db), stride, padding,
+                                            dilation, groups, G, ctypes.byref(n)), "dc1d_workspace_bytes")
+            workspace = _workspace(int(n.value), x.device)
+    ws_ptr = None if workspace is None else workspace.data_ptr()
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        _check(lib.dc1d_forward(_ref(dx), _ref(do), _ref(dm), _ref(dw), _ref(db), _ref(dout), stride, padding,
+                                dilation, groups, G, ws_ptr, ws_len, stream), "dc1d_forward")
+    return out
+
+
+def debug_positions(offsets, L_in, stride=1, padding=0, dilation=1):
+    """(i0 int32, frac float32, valid uint8) device tensors shaped like offsets."""
+    lib = load_library()
+    _contig(offsets, "offsets")
+    i0 = torch.empty(offsets.shape, dtype=torch.int32, device=offsets.device)
+    fr = torch.empty(offsets.shape, dtype=torch.float32, device=offsets.device)
+    va = torch.empty(offsets.shape, dtype=torch.uint8, device=offsets.device)
+    d = _desc(offsets)
+    with torch.cuda.device(offsets.device):
+        stream = torch.cuda.current_stream(offsets.device).cuda_stream
+        _check(lib.dc1d_debug_positions(ctypes.byref(d), L_in, stride, padding, dilation, i0.data_ptr(),
+                                        fr.data_ptr(), va.data_ptr(), stream), "dc1d_debug_positions")
+    return i0, fr, va

@@ -1,0 +1,187 @@
+/*
+ * dc1d.h -- C ABI of libdc1d, the MI355X (gfx950) forward pass of 1D
+ * deformable convolution with an optional modulation mask.
+ *
+ * The operation (restated from the pages; each part cited by page and
+ * section):
+ *
+ *   out[b, co, l] = bias[co]
+ *       + sum_{ci in co's group} sum_{k < K} weight[co, ci_local, k] * S[b, ci, k, l]
+ *
+ *   S[b, ci, k, l] = m * ( (1 - f) * x~(i0) + f * x~(i0 + 1) )
+ *       i0 = l*stride - padding + k*dilation + floor(o),   f = o - floor(o)
+ *       o  = offsets[b, g, l, k],   g = ci / (C_in / offset_groups)
+ *       m  = mask[b, g, l, k], or 1 when no mask is given
+ *       x~(i) = x[b, ci, i] for 0 <= i < L_in, else 0
+ *
+ *   - The sum and its grid position l*stride - padding + k*dilation are the
+ *     conv1d cross-correlation (conv1d operator page, section Description);
+ *     the offset moves each tap's sampling point (dilated/deformable
+ *     convolution article, section Deformable Convolution, the y(p0)
+ *     formula, and its Step 2 / Step 3 workflow: sample, then weigh).
+ *   - Sampling between integer positions is linear (dc1d page, section Demo
+ *     notebook: integer offsets shift exactly, fractional ones interpolate
+ *     linearly); samples off either end read zero (torchvision issue on the
+ *     deform_conv2d offset layout, its printed demo output).
+ *   - Offsets are [B, offset_groups, L_out, K] with offset_groups dividing
+ *     C_in (dc1d page, section Usage / DeformConv1d); the mask has the same
+ *     shape and is applied as given, no sigmoid inside (dc1d page, section
+ *     Modulation (DCNv2)).
+ *   - groups split channels into contiguous independent blocks, weight is
+ *     [C_out, C_in/groups, K], bias [C_out] (conv1d operator page, sections
+ *     Arguments and Axis convention).
+ *   - L_out = floor((L_in + 2*padding - dilation*(K-1) - 1)/stride + 1)
+ *     (conv1d operator page, section Shape).
+ *
+ * Layout: every tensor is dense, contiguous, row-major, channels-first
+ * ([B, C, L], conv1d operator page, section Axis convention).  All tensors of
+ * one call share one dtype; the output has the input's dtype (conv1d page:
+ * the computation stays in the input dtype).  Arithmetic is fp32 inside the
+ * kernels (bf16 values are widened exactly; a bf16 output is rounded once,
+ * to nearest even).
+ *
+ * Ownership: the caller owns every buffer (device memory for tensors and the
+ * workspace).  The library allocates nothing, keeps no pointer after a call
+ * returns, and has no mutable global state other than a per-device
+ * capability cache filled once.  Work is enqueued on the given HIP stream and
+ * the call returns without synchronising; buffers must stay alive until that
+ * stream's work is done.  Calls are re-entrant; calls that share a workspace
+ * must be ordered on one stream.
+ *
+ * Errors: every entry returns a dc1d_status.  Errors detected on the host
+ * return before any device work and write nothing.  Faults inside a kernel
+ * surface at the caller's next synchronisation.  No C++ exception crosses
+ * this boundary.
+ */
+#ifndef DC1D_H
+#define DC1D_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage dtypes. */
+typedef enum dc1d_dtype {
+    DC1D_F32 = 0,  /* IEEE binary32 */
+    DC1D_BF16 = 1  /* bfloat16 (upper half of a binary32) */
+} dc1d_dtype;
+
+typedef enum dc1d_status {
+    DC1D_OK = 0,
+    DC1D_ERR_NULL_PTR = 1,  /* a required descriptor or data pointer is NULL */
+    DC1D_ERR_BAD_ARG = 2,   /* stride/padding/dilation/groups/offset_groups/K out of range,
+                               groups or offset_groups not dividing the channels,
+                               offset_groups disagreeing with offsets->shape[1] */
+    DC1D_ERR_BAD_SHAPE = 3, /* a tensor's rank or shape disagrees, L_out <= 0, or a size
+                               beyond the supported limits (see dc1d_forward) */
+    DC1D_ERR_BAD_DTYPE = 4, /* unsupported dtype, or dtypes mixed within a call */
+    DC1D_ERR_ALIAS = 5,     /* out overlaps an input */
+    DC1D_ERR_WORKSPACE = 6, /* workspace NULL or smaller than dc1d_workspace_bytes() */
+    DC1D_ERR_DEVICE = 7,    /* no current HIP device, or it is not a gfx950 */
+    DC1D_ERR_LAUNCH = 8     /* the kernel launch reported an error */
+} dc1d_status;
+
+/* A dense, contiguous tensor in device memory.  shape[i] for i >= ndim is
+ * ignored.  data may be NULL only when the tensor has no elements. */
+typedef struct dc1d_tensor {
+    void *data;
+    int32_t dtype; /* a dc1d_dtype */
+    int32_t ndim;
+    int64_t shape[4];
+} dc1d_tensor;
+
+/*
+ * conv1d output length (conv1d operator page, section Shape):
+ *   floor((L_in + 2*padding - dilation*(K-1) - 1)/stride + 1).
+ * Returns -1 when an argument is out of range (L_in < 0, K < 1, stride < 1,
+ * padding < 0, dilation < 1) or the result is not positive.  Host only.
+ */
+int64_t dc1d_output_length(int64_t L_in, int64_t K, int64_t stride, int64_t padding,
+                           int64_t dilation);
+
+/*
+ * Bytes of device workspace that dc1d_forward needs for these arguments on
+ * the current device (0 when the chosen kernels need none).  Only the
+ * descriptors' dtype, ndim and shape are read; data pointers may be NULL.
+ * The same validation as dc1d_forward applies (except pointers and
+ * aliasing).  The workspace holds split-reduction partial sums and a
+ * per-tile arrival counter region; see dc1d_forward for its contract.
+ */
+int dc1d_workspace_bytes(const dc1d_tensor *x, const dc1d_tensor *offsets,
+                         const dc1d_tensor *mask_or_null, const dc1d_tensor *weight,
+                         const dc1d_tensor *bias_or_null, int64_t stride, int64_t padding,
+                         int64_t dilation, int64_t groups, int64_t offset_groups,
+                         size_t *bytes_out);
+
+/*
+ * Forward pass.  Overwrites all of out; never accumulates into it.
+ *
+ *   x       [B, C_in, L_in]
+ *   offsets [B, offset_groups, L_out, K]     (K fastest)
+ *   mask    [B, offset_groups, L_out, K] or NULL (NULL means a mask of ones;
+ *           an all-ones mask gives bit-identical results)
+ *   weight  [C_out, C_in/groups, K]
+ *   bias    [C_out] or NULL (NULL means zero)
+ *   out     [B, C_out, L_out]
+ *
+ * offset_groups must equal offsets->shape[1] (a double entry, checked).
+ * stream is a hipStream_t (NULL: the null stream).
+ *
+ * workspace: device memory of at least dc1d_workspace_bytes() bytes, or NULL
+ * with workspace_bytes 0 when that is 0.  Its counter region (the first
+ * 256-byte-aligned part; all of it when in doubt) must be zero the first time
+ * a workspace is used; every call that runs to completion leaves it zero
+ * again, so a workspace zeroed once at allocation can be reused by any
+ * number of calls ordered on one stream.  Calls in flight at the same time
+ * must not share a workspace.
+ *
+ * Limits (DC1D_ERR_BAD_SHAPE beyond them): L_in + padding <= 2^29,
+ * dilation*(K-1) <= 2^29, L_out*stride <= 2^30, C_in*K <= 2^30,
+ * C_out <= 2^30.  Offsets whose magnitude exceeds 2^29 are clamped to
+ * +-2^29, which under these limits only moves a sample that already reads
+ * zero.  Non-finite offsets or masks are outside the contract: the kernels
+ * stay memory-safe but the values are unspecified.
+ *
+ * B == 0 is a valid no-op.  The call is asynchronous.
+ */
+int dc1d_forward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_tensor *mask_or_null,
+                 const dc1d_tensor *weight, const dc1d_tensor *bias_or_null, const dc1d_tensor *out,
+                 int64_t stride, int64_t padding, int64_t dilation, int64_t groups,
+                 int64_t offset_groups, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Test aid: the sampling positions the forward kernels use, from the same
+ * device function.  For every (b, g, l, k) of offsets [B, G, L_out, K]
+ * (K = offsets->shape[3]; L_out must equal dc1d_output_length(L_in, K, ...)):
+ *   i0[idx]    = l*stride - padding + k*dilation + floor(o)   (int32, exact)
+ *   frac[idx]  = o - floor(o)                                 (fp32)
+ *   valid[idx] = (0 <= i0 < L_in) | (0 <= i0+1 < L_in) << 1
+ * i0, frac and valid are device buffers of B*G*L_out*K elements each.
+ */
+int dc1d_debug_positions(const dc1d_tensor *offsets, int64_t L_in, int64_t stride,
+                         int64_t padding, int64_t dilation, int32_t *i0, float *frac,
+                         uint8_t *valid, void *stream);
+
+/*
+ * Which kernel dc1d_forward would launch for these arguments on the
+ * current device, as a short static string ("mfma_f32", "mfma_bf16",
+ * "depthwise", "direct", ...), and its launch shape.  Same validation as
+ * dc1d_workspace_bytes.  For logging, tests and profiling.
+ */
+int dc1d_plan(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_tensor *mask_or_null,
+              const dc1d_tensor *weight, const dc1d_tensor *bias_or_null, int64_t stride,
+              int64_t padding, int64_t dilation, int64_t groups, int64_t offset_groups,
+              const char **kernel_name, int64_t *grid_blocks, int32_t *block_threads,
+              int32_t *splits);
+
+/* A static, NUL-terminated description of a status code. */
+const char *dc1d_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DC1D_H */

@@ -1,0 +1,164 @@
+"""CPU oracle for the 1D deformable convolution forward (double precision).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import this package.  The product
+path (``deformable_convolution_amd``) never imports it, and this package
+imports nothing from the product.
+
+Two independent formulations live here:
+
+* ``forward`` / ``forward_points`` / ``positions`` -- ctypes front end of
+  ``dc1d_oracle.c``: the two-stage definition (sample, then contract) in
+  plain C loops over doubles.
+* ``hat.forward`` -- a NumPy brute force that never splits a position into
+  integer and fractional parts; it is the pin for the C oracle's
+  floor/fraction logic and its zero-fill boundary.
+
+Inputs may be NumPy arrays or CPU torch tensors of any floating dtype; they
+are converted exactly to float64 before the call (bf16 and fp32 values are
+representable in double).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dc1d_oracle.c")
+_LIB = os.path.join(_HERE, "libdc1d_oracle.so")
+
+# gcc flags: no contraction into FMA, no fast-math, so the C arithmetic is
+# exactly the double-precision expression as written.
+CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared", "-std=c11"]
+
+
+def build(force: bool = False) -> str:
+    """Compile ``dc1d_oracle.c`` into ``libdc1d_oracle.so`` next to it."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Lib:
+    """ctypes handle on one build of ``dc1d_oracle.c`` (the default build, or a
+    test's deliberately altered copy)."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        i64, p = ctypes.c_int64, ctypes.c_void_p
+        lib.oracle_output_length.restype = i64
+        lib.oracle_output_length.argtypes = [i64] * 5
+        lib.oracle_positions.restype = ctypes.c_int
+        lib.oracle_positions.argtypes = [p, i64, i64, i64, i64, i64, i64, i64, p, p, p]
+        lib.oracle_forward.restype = ctypes.c_int
+        lib.oracle_forward.argtypes = [p] * 5 + [i64] * 10 + [p]
+        lib.oracle_forward_points.restype = ctypes.c_int
+        lib.oracle_forward_points.argtypes = [p] * 5 + [i64] * 10 + [p, i64, p]
+        self.lib = lib
+
+
+_default = None
+
+
+def _load(lib=None):
+    """The ctypes library to call: ``lib`` if given, else the default build."""
+    global _default
+    if lib is not None:
+        return lib.lib
+    if _default is None:
+        _default = _Lib(build())
+    return _default.lib
+
+
+def load_variant(path: str) -> "_Lib":
+    """Bind another build of the oracle source (used by the tests that check
+    that the pins catch deliberately planted mistakes)."""
+    return _Lib(path)
+
+
+def _f64(a):
+    if a is None:
+        return None
+    if hasattr(a, "detach"):  # torch tensor: exact widening to double on the CPU
+        a = a.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+_ERR = {1: "bad argument or shape", 2: "non-finite input", 3: "out of memory"}
+
+
+def output_length(L_in: int, K: int, stride: int = 1, padding: int = 0, dilation: int = 1, lib=None) -> int:
+    """conv1d closed form; -1 when out of range or not positive."""
+    return int(_load(lib).oracle_output_length(L_in, K, stride, padding, dilation))
+
+
+def _shapes(x, offsets, weight, groups):
+    B, C_in, L_in = x.shape
+    C_out, cpg, K = weight.shape
+    G = offsets.shape[1]
+    if cpg * groups != C_in:
+        raise ValueError("weight shape does not match C_in / groups")
+    return B, C_in, L_in, C_out, K, G
+
+
+def forward(x, offsets, weight, bias=None, mask=None, stride=1, padding=0, dilation=1, groups=1, lib=None):
+    """Deformable conv1d forward in float64; returns out [B, C_out, L_out]."""
+    x, offsets, weight, bias, mask = map(_f64, (x, offsets, weight, bias, mask))
+    B, C_in, L_in, C_out, K, G = _shapes(x, offsets, weight, groups)
+    L_out = output_length(L_in, K, stride, padding, dilation, lib)
+    if L_out < 1 or offsets.shape != (B, G, L_out, K):
+        raise ValueError("offsets must be [B, G, L_out, K] with L_out=%d" % L_out)
+    if mask is not None and mask.shape != offsets.shape:
+        raise ValueError("mask must have the offsets' shape")
+    if bias is not None and bias.shape != (C_out,):
+        raise ValueError("bias must be [C_out]")
+    out = np.empty((B, C_out, L_out), dtype=np.float64)
+    st = _load(lib).oracle_forward(_ptr(x), _ptr(offsets), _ptr(mask), _ptr(weight), _ptr(bias),
+                                B, C_in, L_in, C_out, K, stride, padding, dilation, groups, G,
+                                _ptr(out))
+    if st:
+        raise ValueError("oracle_forward: " + _ERR.get(st, str(st)))
+    return out
+
+
+def forward_points(x, offsets, weight, points, bias=None, mask=None, stride=1, padding=0,
+                   dilation=1, groups=1, lib=None):
+    """Oracle outputs at the given (b, co, l) triples only (array [n, 3])."""
+    x, offsets, weight, bias, mask = map(_f64, (x, offsets, weight, bias, mask))
+    B, C_in, L_in, C_out, K, G = _shapes(x, offsets, weight, groups)
+    L_out = output_length(L_in, K, stride, padding, dilation, lib)
+    if L_out < 1 or offsets.shape != (B, G, L_out, K):
+        raise ValueError("offsets must be [B, G, L_out, K] with L_out=%d" % L_out)
+    pts = np.ascontiguousarray(np.asarray(points, dtype=np.int64).reshape(-1, 3))
+    out = np.empty(len(pts), dtype=np.float64)
+    st = _load(lib).oracle_forward_points(_ptr(x), _ptr(offsets), _ptr(mask), _ptr(weight),
+                                       _ptr(bias), B, C_in, L_in, C_out, K, stride, padding,
+                                       dilation, groups, G, _ptr(pts), len(pts), _ptr(out))
+    if st:
+        raise ValueError("oracle_forward_points: " + _ERR.get(st, str(st)))
+    return out
+
+
+def positions(offsets, L_in, K, stride=1, padding=0, dilation=1, lib=None):
+    """(i0 int64, frac float64, valid uint8) for offsets [B, G, L_out, K]."""
+    offsets = _f64(offsets)
+    B, G, L_out, Ko = offsets.shape
+    if Ko != K or L_out != output_length(L_in, K, stride, padding, dilation, lib):
+        raise ValueError("offsets shape disagrees with L_out")
+    i0 = np.empty(offsets.shape, dtype=np.int64)
+    fr = np.empty(offsets.shape, dtype=np.float64)
+    va = np.empty(offsets.shape, dtype=np.uint8)
+    st = _load(lib).oracle_positions(_ptr(offsets), B, G, L_in, K, stride, padding, dilation,
+                                  _ptr(i0), _ptr(fr), _ptr(va))
+    if st:
+        raise ValueError("oracle_positions: " + _ERR.get(st, str(st)))
+    return i0, fr, va

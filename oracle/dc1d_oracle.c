@@ -1,0 +1,262 @@
+/*
+ * dc1d_oracle.c -- plain, slow CPU oracle for the 1D deformable convolution
+ * forward, in double precision.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: it exists so that tests, the smoke check and the bench's
+ * CPU-baseline leg have an independent answer to compare the GPU kernels
+ * against.  It shares no header, helper, table or constant with the HIP
+ * library, and includes nothing from it.
+ *
+ * What it computes (restated from the pages, cited by page and section):
+ *
+ *  - Output length, from the conv1d operator page ("conv1d", section
+ *    Shape and the closing paragraph of Axis convention):
+ *        L_out = floor((L_in + 2p - d(K-1) - 1) / s + 1).
+ *  - Plain conv1d, same page, section Description: a cross-correlation,
+ *        out[b,co,l] = bias[co] + sum_{ci,k} w[co,ci,k] * x[b,ci, l*s - p + k*d].
+ *  - The deformable form, from the dilated/deformable convolution article
+ *    (section Deformable Convolution, the y(p0) formula): each tap samples
+ *    the input at its regular grid position plus a learned offset, and the
+ *    two-stage workflow of that article (Step 2 deformable sampling, then
+ *    Step 3 weighted summation) is followed literally: stage 1 builds the
+ *    sampled tensor, stage 2 contracts it with the weight.
+ *  - 1D sampling is linear interpolation between the two neighbouring
+ *    integer positions (dc1d page, section Demo notebook: a fractional
+ *    offset interpolates linearly; an integer offset is an exact shift).
+ *    The weights are the 1D analogue of the article's bilinear weights:
+ *    the integer part picks the left neighbour, the fractional part f
+ *    weighs the right one by f and the left one by 1 - f.
+ *  - Positions outside [0, L_in) read zero (the torchvision issue page's
+ *    printed demo: samples shifted off the edge come back as 0).
+ *  - Offsets have shape [B, G, L_out, K] with G (offset groups) dividing
+ *    C_in (dc1d page, section Usage / DeformConv1d); channel ci uses
+ *    offset group ci / (C_in / G) (reading: contiguous channel blocks, as
+ *    the torchvision demo divides its input channels into groups).
+ *  - The optional modulation mask has the offsets' shape and multiplies
+ *    each sampled value as given (dc1d page, section Modulation (DCNv2)).
+ *  - groups split C_in and C_out into contiguous independent blocks; the
+ *    weight is [C_out, C_in/groups, K] (conv1d page, Arguments and Axis
+ *    convention).
+ *
+ * Arithmetic: every input value arrives already converted exactly to
+ * double; all arithmetic is double; the contraction sums over
+ * (ci_local, k) in ascending order and then adds the bias.  Build with
+ * -O2 -ffp-contract=off and without fast-math so the compiler neither
+ * fuses nor reassociates.
+ *
+ * Non-finite inputs are outside the contract; the entry points reject them.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Status codes of this file (independent of the GPU library's codes). */
+#define OR_OK 0
+#define OR_BAD_ARG 1
+#define OR_NONFINITE 2
+#define OR_NOMEM 3
+
+/* conv1d output length; -1 when the arguments are out of range or the
+ * result would not be positive. */
+int64_t oracle_output_length(int64_t L_in, int64_t K, int64_t s, int64_t p, int64_t d)
+{
+    if (L_in < 0 || K < 1 || s < 1 || p < 0 || d < 1)
+        return -1;
+    int64_t num = L_in + 2 * p - d * (K - 1) - 1;
+    if (num < 0)
+        return -1; /* floor(num/s) + 1 <= 0 */
+    return num / s + 1;
+}
+
+/* Zero-extended input: x~(i) = x[i] inside [0, L), 0 outside. */
+static double x_ext(const double *row, int64_t L, int64_t i)
+{
+    return (i >= 0 && i < L) ? row[i] : 0.0;
+}
+
+/* Split a sampling position base + o into its integer left neighbour i0 and
+ * fractional weight f in [0, 1).  The integer part of the grid term is
+ * exact, so only the offset is floored. */
+static void split_position(int64_t base, double o, int64_t *i0, double *f)
+{
+    double fl = floor(o);
+    *i0 = base + (int64_t)fl;
+    *f = o - fl;
+}
+
+/* One linearly interpolated, optionally modulated sample. */
+static double sample(const double *row, int64_t L_in, int64_t base, double o, const double *m)
+{
+    int64_t i0;
+    double f;
+    split_position(base, o, &i0, &f);
+    double v = (1.0 - f) * x_ext(row, L_in, i0) + f * x_ext(row, L_in, i0 + 1);
+    return m ? v * (*m) : v;
+}
+
+static int all_finite(const double *a, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        if (!isfinite(a[i]))
+            return 0;
+    return 1;
+}
+
+typedef struct {
+    int64_t B, C_in, L_in, C_out, K, s, p, d, groups, G, L_out;
+} shape_t;
+
+static int check_shape(shape_t *sh)
+{
+    if (sh->B < 0 || sh->C_in < 1 || sh->C_out < 1 || sh->groups < 1 || sh->G < 1)
+        return OR_BAD_ARG;
+    if (sh->C_in % sh->groups || sh->C_out % sh->groups || sh->C_in % sh->G)
+        return OR_BAD_ARG;
+    sh->L_out = oracle_output_length(sh->L_in, sh->K, sh->s, sh->p, sh->d);
+    if (sh->L_out < 1)
+        return OR_BAD_ARG;
+    return OR_OK;
+}
+
+/*
+ * Sampling positions only: for every (b, g, l, k) the left neighbour i0,
+ * the fraction f and the two validity bits (bit0: 0 <= i0 < L_in,
+ * bit1: 0 <= i0 + 1 < L_in).  offsets is [B, G, L_out, K].
+ */
+int oracle_positions(const double *offsets, int64_t B, int64_t G, int64_t L_in, int64_t K,
+                     int64_t s, int64_t p, int64_t d, int64_t *i0_out, double *f_out,
+                     uint8_t *valid_out)
+{
+    int64_t L_out = oracle_output_length(L_in, K, s, p, d);
+    if (L_out < 1 || B < 0 || G < 1)
+        return OR_BAD_ARG;
+    int64_t n = B * G * L_out * K;
+    if (!all_finite(offsets, n))
+        return OR_NONFINITE;
+    for (int64_t bg = 0; bg < B * G; ++bg)
+        for (int64_t l = 0; l < L_out; ++l)
+            for (int64_t k = 0; k < K; ++k) {
+                int64_t idx = (bg * L_out + l) * K + k;
+                int64_t base = l * s - p + k * d;
+                int64_t i0;
+                double f;
+                split_position(base, offsets[idx], &i0, &f);
+                i0_out[idx] = i0;
+                f_out[idx] = f;
+                valid_out[idx] = (uint8_t)((i0 >= 0 && i0 < L_in ? 1 : 0) |
+                                           (i0 + 1 >= 0 && i0 + 1 < L_in ? 2 : 0));
+            }
+    return OR_OK;
+}
+
+/*
+ * Full forward, two stages.
+ *   x       [B, C_in, L_in]
+ *   offsets [B, G, L_out, K]
+ *   mask    [B, G, L_out, K] or NULL
+ *   weight  [C_out, C_in/groups, K]
+ *   bias    [C_out] or NULL
+ *   out     [B, C_out, L_out]
+ */
+int oracle_forward(const double *x, const double *offsets, const double *mask,
+                   const double *weight, const double *bias, int64_t B, int64_t C_in,
+                   int64_t L_in, int64_t C_out, int64_t K, int64_t s, int64_t p, int64_t d,
+                   int64_t groups, int64_t G, double *out)
+{
+    shape_t sh = {B, C_in, L_in, C_out, K, s, p, d, groups, G, 0};
+    int st = check_shape(&sh);
+    if (st)
+        return st;
+    const int64_t L_out = sh.L_out;
+    const int64_t cpg = C_in / groups, opg = C_out / groups, cpo = C_in / G;
+    const int64_t n_off = B * G * L_out * K;
+    if (!all_finite(x, B * C_in * L_in) || !all_finite(offsets, n_off) ||
+        (mask && !all_finite(mask, n_off)) || !all_finite(weight, C_out * cpg * K) ||
+        (bias && !all_finite(bias, C_out)))
+        return OR_NONFINITE;
+    if (B == 0)
+        return OR_OK;
+
+    /* Stage 1: the sampled tensor S[b, ci, k, l]. */
+    double *S = (double *)malloc(sizeof(double) * (size_t)(B * C_in * K * L_out));
+    if (!S)
+        return OR_NOMEM;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t ci = 0; ci < C_in; ++ci) {
+            const int64_t g = ci / cpo;
+            const double *row = x + (b * C_in + ci) * L_in;
+            for (int64_t k = 0; k < K; ++k)
+                for (int64_t l = 0; l < L_out; ++l) {
+                    const int64_t oi = ((b * G + g) * L_out + l) * K + k;
+                    S[((b * C_in + ci) * K + k) * L_out + l] =
+                        sample(row, L_in, l * s - p + k * d, offsets[oi], mask ? mask + oi : NULL);
+                }
+        }
+
+    /* Stage 2: weighted sum over the group's input channels and taps. */
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t co = 0; co < C_out; ++co) {
+            const int64_t grp = co / opg;
+            for (int64_t l = 0; l < L_out; ++l) {
+                double acc = 0.0;
+                for (int64_t cl = 0; cl < cpg; ++cl)
+                    for (int64_t k = 0; k < K; ++k)
+                        acc += weight[(co * cpg + cl) * K + k] *
+                               S[((b * C_in + grp * cpg + cl) * K + k) * L_out + l];
+                out[(b * C_out + co) * L_out + l] = acc + (bias ? bias[co] : 0.0);
+            }
+        }
+    free(S);
+    return OR_OK;
+}
+
+/*
+ * The same forward evaluated only at selected outputs, for shapes too big
+ * to evaluate whole.  points holds npts triples (b, co, l); the arithmetic
+ * per output is exactly that of oracle_forward (same sample(), same
+ * ascending (ci_local, k) order, bias last), so each value equals the full
+ * oracle's at that index.
+ */
+int oracle_forward_points(const double *x, const double *offsets, const double *mask,
+                          const double *weight, const double *bias, int64_t B, int64_t C_in,
+                          int64_t L_in, int64_t C_out, int64_t K, int64_t s, int64_t p,
+                          int64_t d, int64_t groups, int64_t G, const int64_t *points,
+                          int64_t npts, double *out)
+{
+    shape_t sh = {B, C_in, L_in, C_out, K, s, p, d, groups, G, 0};
+    int st = check_shape(&sh);
+    if (st)
+        return st;
+    const int64_t L_out = sh.L_out;
+    const int64_t cpg = C_in / groups, opg = C_out / groups, cpo = C_in / G;
+    for (int64_t q = 0; q < npts; ++q) {
+        const int64_t b = points[3 * q], co = points[3 * q + 1], l = points[3 * q + 2];
+        if (b < 0 || b >= B || co < 0 || co >= C_out || l < 0 || l >= L_out)
+            return OR_BAD_ARG;
+    }
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 16) reduction(| : bad)
+    for (int64_t q = 0; q < npts; ++q) {
+        const int64_t b = points[3 * q], co = points[3 * q + 1], l = points[3 * q + 2];
+        const int64_t grp = co / opg;
+        double acc = 0.0;
+        for (int64_t cl = 0; cl < cpg; ++cl) {
+            const int64_t ci = grp * cpg + cl;
+            const int64_t g = ci / cpo;
+            const double *row = x + (b * C_in + ci) * L_in;
+            for (int64_t k = 0; k < K; ++k) {
+                const int64_t oi = ((b * G + g) * L_out + l) * K + k;
+                if (!isfinite(offsets[oi]) || (mask && !isfinite(mask[oi])))
+                    bad = 1;
+                double v = sample(row, L_in, l * s - p + k * d, offsets[oi], mask ? mask + oi : NULL);
+                acc += weight[(co * cpg + cl) * K + k] * v;
+            }
+        }
+        out[q] = acc + (bias ? bias[co] : 0.0);
+    }
+    return bad ? OR_NONFINITE : OR_OK;
+}
