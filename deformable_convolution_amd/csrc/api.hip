@@ -1,0 +1,296 @@
+// api.hip -- the C ABI of libdc1d (include/dc1d.h): argument validation,
+// kernel choice, and launch.  No allocation, no synchronisation, no
+// exceptions across the boundary.
+#include <mutex>
+#include <string.h>
+
+#include "../../include/dc1d.h"
+#include "dc1d_internal.h"
+
+using namespace dc1d;
+
+namespace {
+
+constexpr int64_t kMaxPos = (int64_t)1 << 29;  // position-range limit (see dc1d.h)
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+    bool gfx950;
+    int num_cus;
+};
+
+std::once_flag g_dev_once[kMaxDevices];
+DeviceInfo g_dev[kMaxDevices];
+
+// The current device's capability, probed once per device.
+int current_device(DeviceInfo *info) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return DC1D_ERR_DEVICE;
+    }
+    std::call_once(g_dev_once[dev], [dev]() {
+        hipDeviceProp_t prop;
+        DeviceInfo di = {false, 0};
+        if (hipGetDeviceProperties(&prop, dev) == hipSuccess) {
+            di.gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+            di.num_cus = prop.multiProcessorCount;
+        } else {
+            (void)hipGetLastError();
+        }
+        g_dev[dev] = di;
+    });
+    *info = g_dev[dev];
+    return info->gfx950 ? DC1D_OK : DC1D_ERR_DEVICE;
+}
+
+int64_t numel(const dc1d_tensor *t) {
+    int64_t n = 1;
+    for (int i = 0; i < t->ndim; ++i) n *= t->shape[i];
+    return n;
+}
+
+size_t elem_size(int dtype) { return dtype == DC1D_F32 ? 4 : 2; }
+
+bool shape_is(const dc1d_tensor *t, int ndim, const int64_t *s) {
+    if (t->ndim != ndim) return false;
+    for (int i = 0; i < ndim; ++i)
+        if (t->shape[i] != s[i]) return false;
+    return true;
+}
+
+// Validate shapes and arguments and fill p (pointers included).
+int validate(const dc1d_tensor *x, const dc1d_tensor *off, const dc1d_tensor *mask,
+             const dc1d_tensor *w, const dc1d_tensor *bias, const dc1d_tensor *out, int64_t stride,
+             int64_t padding, int64_t dilation, int64_t groups, int64_t offset_groups, Params *p) {
+    if (!x || !off || !w) return DC1D_ERR_NULL_PTR;
+    if (stride < 1 || padding < 0 || dilation < 1 || groups < 1 || offset_groups < 1)
+        return DC1D_ERR_BAD_ARG;
+    if (x->ndim != 3 || w->ndim != 3 || off->ndim != 4) return DC1D_ERR_BAD_SHAPE;
+    const int dt = x->dtype;
+    if (dt != DC1D_F32 && dt != DC1D_BF16) return DC1D_ERR_BAD_DTYPE;
+    if (off->dtype != dt || w->dtype != dt || (mask && mask->dtype != dt) ||
+        (bias && bias->dtype != dt) || (out && out->dtype != dt))
+        return DC1D_ERR_BAD_DTYPE;
+    const int64_t B = x->shape[0], C_in = x->shape[1], L_in = x->shape[2];
+    const int64_t C_out = w->shape[0], K = w->shape[2];
+    if (B < 0 || C_in < 1 || L_in < 0 || C_out < 1 || K < 1) return DC1D_ERR_BAD_SHAPE;
+    if (C_in % groups || C_out % groups || C_in % offset_groups) return DC1D_ERR_BAD_ARG;
+    if (off->shape[1] != offset_groups) return DC1D_ERR_BAD_ARG;
+    if (w->shape[1] != C_in / groups) return DC1D_ERR_BAD_SHAPE;
+    // size limits that keep all position arithmetic inside int32
+    if (L_in + padding > kMaxPos || dilation * (K - 1) > kMaxPos || C_in * K > ((int64_t)1 << 30) ||
+        C_out > ((int64_t)1 << 30) || B > ((int64_t)1 << 30) || offset_groups * K > ((int64_t)1 << 30))
+        return DC1D_ERR_BAD_SHAPE;
+    const int64_t L_out = dc1d_output_length(L_in, K, stride, padding, dilation);
+    if (L_out < 1 || L_out * stride > ((int64_t)1 << 30)) return DC1D_ERR_BAD_SHAPE;
+    const int64_t so[4] = {B, offset_groups, L_out, K};
+    if (!shape_is(off, 4, so)) return DC1D_ERR_BAD_SHAPE;
+    if (mask && !shape_is(mask, 4, so)) return DC1D_ERR_BAD_SHAPE;
+    const int64_t sb[1] = {C_out};
+    if (bias && !shape_is(bias, 1, sb)) return DC1D_ERR_BAD_SHAPE;
+    const int64_t sout[3] = {B, C_out, L_out};
+    if (out && !shape_is(out, 3, sout)) return DC1D_ERR_BAD_SHAPE;
+
+    memset(p, 0, sizeof(*p));
+    p->x = x->data;
+    p->off = off->data;
+    p->mask = mask ? mask->data : nullptr;
+    p->w = w->data;
+    p->bias = bias ? bias->data : nullptr;
+    p->out = out ? out->data : nullptr;
+    p->dtype = dt;
+    p->B = (int)B;
+    p->C_in = (int)C_in;
+    p->C_out = (int)C_out;
+    p->L_in = (int)L_in;
+    p->L_out = (int)L_out;
+    p->K = (int)K;
+    p->stride = (int)stride;
+    p->padding = (int)padding;
+    p->dilation = (int)dilation;
+    p->groups = (int)groups;
+    p->G = (int)offset_groups;
+    p->cpg = (int)(C_in / groups);
+    p->opg = (int)(C_out / groups);
+    p->cpo = (int)(C_in / offset_groups);
+    p->Kred = (int)(C_in / groups * K);
+    return DC1D_OK;
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+enum Kernel { kDirect, kDepthwise, kMfma };
+
+struct Plan {
+    Kernel kernel;
+    MfmaPlan mfma;
+    DepthwisePlan dw;
+    size_t ws_bytes;
+    const char *name;
+    int64_t grid;
+    int block;
+    int splits;
+};
+
+Plan make_plan(const Params &p, const DeviceInfo &dev) {
+    Plan pl = {};
+    pl.mfma = plan_mfma(p, dev.num_cus);
+    if (pl.mfma.ok) {
+        pl.kernel = kMfma;
+        pl.ws_bytes = pl.mfma.ws_bytes;
+        pl.name = pl.mfma.name;
+        pl.grid = pl.mfma.blocks;
+        pl.block = pl.mfma.threads;
+        pl.splits = pl.mfma.splits;
+        return pl;
+    }
+    if (p.cpg == 1) {
+        pl.kernel = kDepthwise;
+        pl.dw = plan_depthwise(p);
+        pl.name = "depthwise";
+        pl.grid = pl.dw.blocks;
+        pl.block = 256;
+        pl.splits = 1;
+        return pl;
+    }
+    pl.kernel = kDirect;
+    pl.name = "direct";
+    const int64_t total = (int64_t)p.B * p.C_out * p.L_out;
+    pl.grid = (total + 255) / 256;
+    pl.block = 256;
+    pl.splits = 1;
+    return pl;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t dc1d_output_length(int64_t L_in, int64_t K, int64_t stride, int64_t padding, int64_t dilation) {
+    if (L_in < 0 || K < 1 || stride < 1 || padding < 0 || dilation < 1) return -1;
+    if (L_in > ((int64_t)1 << 40) || padding > ((int64_t)1 << 40) || K > ((int64_t)1 << 40) ||
+        dilation > ((int64_t)1 << 20))
+        return -1;  // keeps the arithmetic below exact in int64
+    const int64_t num = L_in + 2 * padding - dilation * (K - 1) - 1;
+    if (num < 0) return -1;
+    return num / stride + 1;
+}
+
+int dc1d_workspace_bytes(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_tensor *mask_or_null,
+                         const dc1d_tensor *weight, const dc1d_tensor *bias_or_null, int64_t stride,
+                         int64_t padding, int64_t dilation, int64_t groups, int64_t offset_groups,
+                         size_t *bytes_out) {
+    if (!bytes_out) return DC1D_ERR_NULL_PTR;
+    Params p;
+    int st = validate(x, offsets, mask_or_null, weight, bias_or_null, nullptr, stride, padding, dilation,
+                      groups, offset_groups, &p);
+    if (st) return st;
+    DeviceInfo dev;
+    if ((st = current_device(&dev))) return st;
+    *bytes_out = make_plan(p, dev).ws_bytes;
+    return DC1D_OK;
+}
+
+int dc1d_plan(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_tensor *mask_or_null,
+              const dc1d_tensor *weight, const dc1d_tensor *bias_or_null, int64_t stride, int64_t padding,
+              int64_t dilation, int64_t groups, int64_t offset_groups, const char **kernel_name,
+              int64_t *grid_blocks, int32_t *block_threads, int32_t *splits) {
+    Params p;
+    int st = validate(x, offsets, mask_or_null, weight, bias_or_null, nullptr, stride, padding, dilation,
+                      groups, offset_groups, &p);
+    if (st) return st;
+    DeviceInfo dev;
+    if ((st = current_device(&dev))) return st;
+    const Plan pl = make_plan(p, dev);
+    if (kernel_name) *kernel_name = pl.name;
+    if (grid_blocks) *grid_blocks = pl.grid;
+    if (block_threads) *block_threads = pl.block;
+    if (splits) *splits = pl.splits;
+    return DC1D_OK;
+}
+
+int dc1d_forward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_tensor *mask_or_null,
+                 const dc1d_tensor *weight, const dc1d_tensor *bias_or_null, const dc1d_tensor *out,
+                 int64_t stride, int64_t padding, int64_t dilation, int64_t groups, int64_t offset_groups,
+                 void *workspace, size_t workspace_bytes, void *stream) {
+    if (!out) return DC1D_ERR_NULL_PTR;
+    Params p;
+    int st = validate(x, offsets, mask_or_null, weight, bias_or_null, out, stride, padding, dilation, groups,
+                      offset_groups, &p);
+    if (st) return st;
+    // data pointers: required for every tensor with elements
+    const dc1d_tensor *all[6] = {x, offsets, mask_or_null, weight, bias_or_null, out};
+    for (const dc1d_tensor *t : all)
+        if (t && numel(t) > 0 && !t->data) return DC1D_ERR_NULL_PTR;
+    // out must not overlap any input
+    const size_t es = elem_size(p.dtype);
+    const size_t out_bytes = (size_t)numel(out) * es;
+    for (int i = 0; i < 5; ++i)
+        if (all[i] && overlaps(out->data, out_bytes, all[i]->data, (size_t)numel(all[i]) * es))
+            return DC1D_ERR_ALIAS;
+    DeviceInfo dev;
+    if ((st = current_device(&dev))) return st;
+    const Plan pl = make_plan(p, dev);
+    if (pl.ws_bytes > 0) {
+        if (!workspace || workspace_bytes < pl.ws_bytes) return DC1D_ERR_WORKSPACE;
+        if (overlaps(workspace, pl.ws_bytes, out->data, out_bytes)) return DC1D_ERR_ALIAS;
+        for (int i = 0; i < 5; ++i)
+            if (all[i] && overlaps(workspace, pl.ws_bytes, all[i]->data, (size_t)numel(all[i]) * es))
+                return DC1D_ERR_ALIAS;
+    }
+    if (p.B == 0) return DC1D_OK;
+    p.ws = workspace;
+    p.ws_bytes = workspace_bytes;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    switch (pl.kernel) {
+    case kMfma: e = launch_mfma(p, pl.mfma, s); break;
+    case kDepthwise: e = launch_depthwise(p, pl.dw, s); break;
+    default: e = launch_direct(p, s); break;
+    }
+    return e == hipSuccess ? DC1D_OK : DC1D_ERR_LAUNCH;
+}
+
+int dc1d_debug_positions(const dc1d_tensor *offsets, int64_t L_in, int64_t stride, int64_t padding,
+                         int64_t dilation, int32_t *i0, float *frac, uint8_t *valid, void *stream) {
+    if (!offsets) return DC1D_ERR_NULL_PTR;
+    if (stride < 1 || padding < 0 || dilation < 1 || L_in < 0) return DC1D_ERR_BAD_ARG;
+    if (offsets->ndim != 4) return DC1D_ERR_BAD_SHAPE;
+    if (offsets->dtype != DC1D_F32 && offsets->dtype != DC1D_BF16) return DC1D_ERR_BAD_DTYPE;
+    const int64_t K = offsets->shape[3];
+    if (K < 1 || L_in + padding > kMaxPos || dilation * (K - 1) > kMaxPos) return DC1D_ERR_BAD_SHAPE;
+    const int64_t L_out = dc1d_output_length(L_in, K, stride, padding, dilation);
+    if (L_out < 1 || offsets->shape[2] != L_out || offsets->shape[0] < 0 || offsets->shape[1] < 1)
+        return DC1D_ERR_BAD_SHAPE;
+    const int64_t n = numel(offsets);
+    if (n > 0 && (!offsets->data || !i0 || !frac || !valid)) return DC1D_ERR_NULL_PTR;
+    DeviceInfo dev;
+    int st = current_device(&dev);
+    if (st) return st;
+    hipError_t e = launch_positions(offsets->data, offsets->dtype, n, (int)L_out, (int)K, (int)stride,
+                                    (int)padding, (int)dilation, (int)L_in, i0, frac, valid,
+                                    (hipStream_t)stream);
+    return e == hipSuccess ? DC1D_OK : DC1D_ERR_LAUNCH;
+}
+
+const char *dc1d_status_string(int status) {
+    switch (status) {
+    case DC1D_OK: return "ok";
+    case DC1D_ERR_NULL_PTR: return "a required pointer is NULL";
+    case DC1D_ERR_BAD_ARG: return "argument out of range or inconsistent (stride, padding, dilation, groups, offset_groups, K)";
+    case DC1D_ERR_BAD_SHAPE: return "tensor rank or shape disagrees, L_out <= 0, or size beyond the supported limits";
+    case DC1D_ERR_BAD_DTYPE: return "unsupported or mixed dtypes";
+    case DC1D_ERR_ALIAS: return "output or workspace overlaps another buffer";
+    case DC1D_ERR_WORKSPACE: return "workspace missing or too small";
+    case DC1D_ERR_DEVICE: return "no current HIP device, or it is not a gfx950";
+    case DC1D_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,127 @@
+// dc1d_internal.h -- private declarations shared by the libdc1d sources:
+// the launch parameter block, device helpers (dtype access, position split),
+// and the kernel launchers each translation unit provides.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace dc1d {
+
+// Offsets are clamped to +-2^29 before they are floored.  Under the size
+// limits the library enforces (L_in + padding <= 2^29) every position whose
+// offset reaches the clamp already reads zero, and the integer arithmetic
+// on positions stays far inside int32.
+constexpr float kOffsetClamp = 536870912.0f;  // 2^29
+
+enum Dtype : int { kF32 = 0, kBF16 = 1 };
+
+// Everything a launcher needs; filled and validated by the C ABI layer.
+struct Params {
+    const void *x, *off, *mask, *w, *bias;
+    void *out;
+    int dtype;
+    int B, C_in, C_out, L_in, L_out, K, stride, padding, dilation, groups, G;
+    int cpg;   // input channels per conv group  (C_in / groups)
+    int opg;   // output channels per conv group (C_out / groups)
+    int cpo;   // input channels per offset group (C_in / G)
+    int Kred;  // reduction length of one output: cpg * K
+    void *ws;
+    size_t ws_bytes;
+};
+
+// Division by a run-time invariant d >= 1 for numerators n < 2^31:
+// q = (umulhi(n, mul) + n) >> shift, with 2^shift >= d and
+// mul = floor(2^32 (2^shift - d) / d) + 1.
+struct FastDiv {
+    uint32_t d, mul, shift;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+    FastDiv f;
+    f.d = d;
+    uint32_t s = 0;
+    while ((1ull << s) < d) ++s;
+    f.shift = s;
+    f.mul = (uint32_t)((((1ull << s) - d) << 32) / d + 1);
+    return f;
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f) {
+    return (__umulhi(n, f.mul) + n) >> f.shift;
+}
+
+// ---- storage dtypes ------------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// float -> bfloat16, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+struct F32 {
+    using T = float;
+    static __device__ __forceinline__ float ld(const T *p, int64_t i) { return p[i]; }
+    static __device__ __forceinline__ void st(T *p, int64_t i, float v) { p[i] = v; }
+};
+
+struct BF16 {
+    using T = uint16_t;
+    static __device__ __forceinline__ float ld(const T *p, int64_t i) { return bf16_bits_to_f32(p[i]); }
+    static __device__ __forceinline__ void st(T *p, int64_t i, float v) { p[i] = f32_to_bf16_rne(v); }
+};
+
+// ---- the sampling position ------------------------------------------------
+//
+// A tap at grid position base = l*stride - padding + k*dilation moved by the
+// offset o samples between the integer neighbours i0 = base + floor(o) and
+// i0 + 1 with weights 1 - f and f, f = o - floor(o).  Only the offset is
+// floored; the grid term is an exact integer, so i0 is exact for any
+// sequence length (no rounding of base + o in floating point).
+__device__ __forceinline__ void split_position(float o, int base, int &i0, float &f) {
+    o = fminf(fmaxf(o, -kOffsetClamp), kOffsetClamp);  // a NaN becomes -2^29
+    const float fl = floorf(o);
+    i0 = base + (int)fl;
+    f = o - fl;
+}
+
+// ---- launchers ------------------------------------------------------------
+
+hipError_t launch_positions(const void *off, int dtype, int64_t n, int L_out, int K, int stride,
+                            int padding, int dilation, int L_in, int32_t *i0, float *frac,
+                            uint8_t *valid, hipStream_t stream);
+
+// Generic one-thread-per-output kernel: any groups / offset groups / mask.
+hipError_t launch_direct(const Params &p, hipStream_t stream);
+
+// One input channel per output (C_in / groups == 1): depthwise and
+// depthwise-multiplier shapes.  Streams each row's offsets once through LDS.
+struct DepthwisePlan {
+    int outputs_per_block;  // LT
+    int window;             // x window capacity in elements
+    size_t lds_bytes;
+    int64_t blocks;
+};
+DepthwisePlan plan_depthwise(const Params &p);
+hipError_t launch_depthwise(const Params &p, const DepthwisePlan &pl, hipStream_t stream);
+
+// Fused deformable im2col + MFMA GEMM (groups == 1).
+struct MfmaPlan {
+    bool ok;          // shape supported by this kernel
+    int bm, bn, bk;   // block tile
+    int tiles_m, tiles_n, splits, chunks;
+    int64_t blocks;
+    int threads;
+    size_t lds_bytes;
+    size_t ws_bytes;  // counters + partials (0 when splits == 1)
+    const char *name;
+};
+MfmaPlan plan_mfma(const Params &p, int num_cus);
+hipError_t launch_mfma(const Params &p, const MfmaPlan &pl, hipStream_t stream);
+
+}  // namespace dc1d

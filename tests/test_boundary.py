@@ -1,0 +1,185 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every entry point include/dc1d.h declares,
+compute the conv1d output length, and reject every malformed call with the
+documented status before touching a device.  Fake non-NULL data pointers
+are used: host validation never dereferences them.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from deformable_convolution_amd import dc1d
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dc1d.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dc1d.library_path()):
+        from deformable_convolution_amd.csrc import build
+        build.build()
+    return dc1d.load_library()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dc1d_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert {"dc1d_forward", "dc1d_output_length", "dc1d_workspace_bytes", "dc1d_debug_positions",
+            "dc1d_status_string", "dc1d_plan"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), "libdc1d.so does not export %s" % n
+
+
+def test_output_length_matches_oracle(lib):
+    for L_in in range(0, 30):
+        for K in range(1, 5):
+            for s in range(1, 4):
+                for p in range(0, 3):
+                    for d in range(1, 3):
+                        assert dc1d.output_length(L_in, K, s, p, d) == oracle.output_length(L_in, K, s, p, d)
+    assert dc1d.output_length(128, 16, 1, 0, 3) == 83
+    assert dc1d.output_length(-1, 3, 1, 0, 1) == -1
+    assert dc1d.output_length(10, 0, 1, 0, 1) == -1
+    assert dc1d.output_length(10, 3, 0, 0, 1) == -1
+    assert dc1d.output_length(10, 3, 1, -1, 1) == -1
+    assert dc1d.output_length(10, 3, 1, 0, 0) == -1
+
+
+def test_status_strings(lib):
+    for st in range(9):
+        assert dc1d.status_string(st)
+    assert dc1d.status_string(0) == "ok"
+    assert dc1d.status_string(99) == "unknown status"
+
+
+def test_resolve_padding():
+    assert dc1d.resolve_padding("valid", 16, 1, 3) == 0
+    assert dc1d.resolve_padding("same", 3, 1, 4) == 4
+    assert dc1d.resolve_padding(2, 3) == 2
+    with pytest.raises(ValueError):
+        dc1d.resolve_padding("same", 4, 1, 1)  # asymmetric
+    with pytest.raises(ValueError):
+        dc1d.resolve_padding("same", 3, 2, 1)
+    with pytest.raises(ValueError):
+        dc1d.resolve_padding("full", 3)
+
+
+# ---- error codes ------------------------------------------------------------
+
+FAKE = 0x10000000  # a non-NULL address that host validation never dereferences
+
+
+def T(shape, dtype=0, addr=FAKE):
+    d = dc1d._Tensor()
+    d.data = addr
+    d.dtype = dtype
+    d.ndim = len(shape)
+    for i, s in enumerate(shape):
+        d.shape[i] = s
+    return d
+
+
+def call(lib, x, off, mask, w, bias, out, s=1, p=0, d=1, groups=1, G=None, ws=None, ws_n=0):
+    if G is None:
+        G = off.shape[1]
+    r = lambda t: None if t is None else ctypes.byref(t)
+    return lib.dc1d_forward(r(x), r(off), r(mask), r(w), r(bias), r(out), s, p, d, groups, G, ws, ws_n, None)
+
+
+def good(B=2, C=8, L=20, K=3, G=2, C_out=6, groups=1, addr0=FAKE):
+    L_out = L - K + 1
+    step = 1 << 24
+    x = T([B, C, L], addr=addr0)
+    off = T([B, G, L_out, K], addr=addr0 + step)
+    mask = T([B, G, L_out, K], addr=addr0 + 2 * step)
+    w = T([C_out, C // groups, K], addr=addr0 + 3 * step)
+    bias = T([C_out], addr=addr0 + 4 * step)
+    out = T([B, C_out, L_out], addr=addr0 + 5 * step)
+    return x, off, mask, w, bias, out
+
+
+def test_valid_call_reaches_device_check(lib):
+    # everything host-checkable is fine, so the only failure left is the
+    # missing gfx950 device in this container (or OK/other on a GPU machine)
+    st = call(lib, *good())
+    assert st in (dc1d.ERR_DEVICE, dc1d.ERR_WORKSPACE, dc1d.OK)
+
+
+def test_null_pointers(lib):
+    x, off, mask, w, bias, out = good()
+    assert call(lib, None, off, mask, w, bias, out, G=2) == dc1d.ERR_NULL_PTR
+    assert call(lib, x, None, mask, w, bias, out, G=2) == dc1d.ERR_NULL_PTR
+    assert call(lib, x, off, mask, None, bias, out) == dc1d.ERR_NULL_PTR
+    assert call(lib, x, off, mask, w, bias, None) == dc1d.ERR_NULL_PTR
+    x.data = None
+    assert call(lib, x, off, mask, w, bias, out) == dc1d.ERR_NULL_PTR
+
+
+def test_bad_args(lib):
+    x, off, mask, w, bias, out = good()
+    assert call(lib, x, off, mask, w, bias, out, s=0) == dc1d.ERR_BAD_ARG
+    assert call(lib, x, off, mask, w, bias, out, p=-1) == dc1d.ERR_BAD_ARG
+    assert call(lib, x, off, mask, w, bias, out, d=0) == dc1d.ERR_BAD_ARG
+    assert call(lib, x, off, mask, w, bias, out, groups=0) == dc1d.ERR_BAD_ARG
+    assert call(lib, x, off, mask, w, bias, out, G=0) == dc1d.ERR_BAD_ARG
+    # offset_groups disagreeing with offsets.shape[1] (the double entry)
+    assert call(lib, x, off, mask, w, bias, out, G=4) == dc1d.ERR_BAD_ARG
+    # offset groups not dividing C_in
+    x3, off3, mask3, w3, b3, out3 = good(G=3)
+    assert call(lib, x3, off3, mask3, w3, b3, out3) == dc1d.ERR_BAD_ARG
+    # groups not dividing C_in / C_out
+    xg, offg, maskg, wg, bg, outg = good(C=8, C_out=6, groups=4)
+    assert call(lib, xg, offg, maskg, wg, bg, outg, groups=4) == dc1d.ERR_BAD_ARG
+
+
+def test_bad_shapes(lib):
+    x, off, mask, w, bias, out = good()
+    # offsets length disagreeing with the closed form
+    off_bad = T([2, 2, 17, 3], addr=off.data)
+    assert call(lib, x, off_bad, mask, w, bias, out) == dc1d.ERR_BAD_SHAPE
+    assert call(lib, x, off, T([2, 2, 18, 2], addr=mask.data), w, bias, out) == dc1d.ERR_BAD_SHAPE
+    assert call(lib, x, off, mask, w, T([5], addr=bias.data), out) == dc1d.ERR_BAD_SHAPE
+    assert call(lib, x, off, mask, w, bias, T([2, 6, 17], addr=out.data)) == dc1d.ERR_BAD_SHAPE
+    assert call(lib, x, off, mask, T([6, 4, 3], addr=w.data), bias, out) == dc1d.ERR_BAD_SHAPE
+    assert call(lib, T([2, 8]), off, mask, w, bias, out) == dc1d.ERR_BAD_SHAPE
+    # L_out <= 0: kernel longer than the padded input
+    xs = T([2, 8, 2])
+    assert call(lib, xs, T([2, 2, 1, 3]), None, w, bias, T([2, 6, 1])) == dc1d.ERR_BAD_SHAPE
+    # beyond the position-range limit
+    xb = T([1, 8, (1 << 29) + 1])
+    Lb = (1 << 29) - 1
+    assert call(lib, xb, T([1, 2, Lb, 3]), None, w, None, T([1, 6, Lb])) == dc1d.ERR_BAD_SHAPE
+
+
+def test_bad_dtypes(lib):
+    x, off, mask, w, bias, out = good()
+    assert call(lib, T([2, 8, 20], dtype=7), off, mask, w, bias, out) == dc1d.ERR_BAD_DTYPE
+    assert call(lib, x, T([2, 2, 18, 3], dtype=1, addr=off.data), mask, w, bias, out) == dc1d.ERR_BAD_DTYPE
+    assert call(lib, x, off, mask, w, bias, T([2, 6, 18], dtype=1, addr=out.data)) == dc1d.ERR_BAD_DTYPE
+
+
+def test_alias(lib):
+    x, off, mask, w, bias, out = good()
+    out_on_x = T([2, 6, 18], addr=x.data + 64)
+    assert call(lib, x, off, mask, w, bias, out_on_x) == dc1d.ERR_ALIAS
+    out_on_bias = T([2, 6, 18], addr=bias.data - 8)
+    assert call(lib, x, off, mask, w, bias, out_on_bias) == dc1d.ERR_ALIAS
+
+
+def test_positions_entry_validation(lib):
+    off = T([1, 1, 18, 3])
+    i0 = ctypes.c_void_p(FAKE)
+    assert lib.dc1d_debug_positions(None, 20, 1, 0, 1, i0, i0, i0, None) == dc1d.ERR_NULL_PTR
+    assert lib.dc1d_debug_positions(ctypes.byref(off), 20, 0, 0, 1, i0, i0, i0, None) == dc1d.ERR_BAD_ARG
+    assert lib.dc1d_debug_positions(ctypes.byref(off), 21, 1, 0, 1, i0, i0, i0, None) == dc1d.ERR_BAD_SHAPE
+    assert lib.dc1d_debug_positions(ctypes.byref(off), 20, 1, 0, 1, None, i0, i0, None) == dc1d.ERR_NULL_PTR
