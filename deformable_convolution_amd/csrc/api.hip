@@ -4,7 +4,7 @@
 #include <mutex>
 #include <string.h>
 
-#include "../../include/dc1d.h"
+#include "dc1d.h"
 #include "dc1d_internal.h"
 
 using namespace dc1d;

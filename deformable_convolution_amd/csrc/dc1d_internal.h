@@ -120,6 +120,9 @@ struct MfmaPlan {
     size_t lds_bytes;
     size_t ws_bytes;  // counters + partials (0 when splits == 1)
     const char *name;
+    int variant;      // window staging variant
+    int nch, wt_max;  // channel rows per chunk, window capacity per row
+    int off_mask, off_row, off_w, off_x;  // LDS layout (bytes)
 };
 MfmaPlan plan_mfma(const Params &p, int num_cus);
 hipError_t launch_mfma(const Params &p, const MfmaPlan &pl, hipStream_t stream);

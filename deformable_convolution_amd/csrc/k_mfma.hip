@@ -1,38 +1,59 @@
-// k_mfma.hip -- fused deformable im2col + MFMA GEMM for groups == 1.
+// k_mfma.hip -- fused deformable sampling + MFMA GEMM for groups == 1.
 //
 // The contraction out[b, co, l] = bias[co] + sum_r W[co, r] S[r, (b, l)] is a
 // GEMM with M = C_out, N = B*L_out and reduction r = ci*K + k over the
 // weight viewed as [C_out, C_in*K] (conv1d operator page, Description; the
 // article's Step 3 weighted summation).  S is the deformable sample matrix
-// (the article's Step 2); it never touches HBM.  Each workgroup owns a
-// BM x BN output tile and a contiguous range of reduction chunks of 32 rows.
-// Per chunk it
-//   1. gathers x at the two neighbours of each (row, column) sample -- the
-//      positions (left index, right index, and the two interpolation weights
-//      with the mask folded in) were computed once per workgroup into an LDS
-//      table indexed by (offset group, tap, column);
-//   2. runs the MFMAs of the previous chunk while those loads are in flight;
-//   3. interpolates and writes the chunk's samples into an LDS tile in the
-//      MFMA's B-operand order.
-// The weight operand goes straight from global memory (L2) into the MFMA A
-// registers: each wave owns distinct output rows, so no weight value is
-// loaded twice by one workgroup.
+// (the article's Step 2).  It is never stored anywhere: every MFMA lane
+// computes the samples of its own B-operand fragment in registers.
 //
-// Two instantiations share the structure: fp32 storage on
-// v_mfma_f32_32x32x2_f32, and bf16 storage on v_mfma_f32_32x32x16_bf16 (fp32
-// accumulation, one round-to-nearest-even of the output).  In both, lane
-// (i = lane % 32, h = lane / 32) of a wave holds, per chunk and 32-row
-// block, the 16 weights W[m0 + i][r0 + 16h .. r0 + 16h + 15] and, per 32-column
-// block, the 16 samples S[r0 + 16h .. + 15][n0 + i]; the MFMA sequence pairs
-// them element by element, so every reduction row meets its own sample.
+// Workgroup: 4 waves; tile BM x BN with BN = 4 * 32 * NB columns.  Each wave
+// owns 32*NB distinct columns and all BM rows, so every sample is computed
+// exactly once per workgroup and feeds BM/32 MFMAs.  The reduction runs in
+// chunks of BK = 32 rows through a three-stage pipeline, one barrier per
+// chunk:
+//   * global -> registers for chunk c+2: the weight tile [BM x BK], the
+//     zero-padded x windows of the chunk's input channels, and the chunk's
+//     row descriptors (position-table row and window row of each reduction
+//     row);
+//   * chunk c+1: the B fragments (samples) from the LDS windows and the
+//     position table;
+//   * chunk c: MFMAs on the weight tile (LDS) and the B fragments computed
+//     in the previous iteration;
+//   * registers -> LDS for chunk c+2 (weight tiles are triple-buffered,
+//     windows and row descriptors double-buffered).
+//
+// Position table (built once per workgroup): for each (offset group, tap,
+// column) the left neighbour i0 and the fraction f of the sample position
+// (dc1d page, Demo notebook: linear interpolation between neighbours), and
+// the mask value when there is one (dc1d page, Modulation; applied as a
+// plain multiply, so an all-ones mask gives the no-mask bits).
+//
+// Windows: the columns of a tile fall into at most NSEG batch segments; for
+// each segment the smallest and largest left neighbour over the tile give a
+// window [lo, hi + 1] of the input row, staged per channel with zeros
+// outside [0, L_in) (torchvision issue demo: samples off the ends read
+// zero).  Interpolation is then one paired LDS read and two FMAs, with no
+// bounds checks.  When the offsets spread wider than the window capacity, or
+// the tile crosses too many batches, the workgroup gathers x from global
+// memory instead (same arithmetic, bounds-checked loads).
+//
+// Columns past the end of N and reduction rows past Kred are computed on
+// clamped, finite inputs and never stored (an MFMA output column depends
+// only on its own B column, and the weight rows past Kred are zero).
 //
 // Split reduction: when there are too few output tiles to fill the GPU, the
 // reduction range is split over several workgroups.  Each writes its fp32
-// partial tile into the workspace and bumps the tile's arrival counter; the
-// last to arrive adds the partials in split order (so the result does not
-// depend on arrival order), adds the bias, stores the output, and resets the
-// counter to zero for the next call.
+// partial tile into the workspace; a second, small kernel on the same stream
+// adds the partials in split order (so the result is deterministic), adds
+// the bias and stores the output.  Kernel order on the stream is the only
+// synchronisation, so the workspace needs no initialisation.
 #include "dc1d_internal.h"
+
+#include <limits.h>
+
+#include <algorithm>
+#include <type_traits>
 
 namespace dc1d {
 
@@ -40,15 +61,18 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f16v __attribute__((ext_vector_type(16)));
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef int i4 __attribute__((ext_vector_type(4)));
 
 namespace {
 
-constexpr int BK = 32;      // reduction rows per chunk
-constexpr int GK_MAX = 24;  // offset groups x taps covered by the position table (LDS)
+constexpr int NT = 256;   // threads per workgroup (4 waves)
+constexpr int BK = 32;    // reduction rows per chunk
+constexpr int NSEG = 4;   // batch segments a windowed tile may span
+constexpr int NWBUF = 3;  // weight tile buffers
 
-struct TabEntry {
-    int idx0, idx1;  // clamped in-row indices of the two neighbours
-    float w0, w1;    // (1 - f) * m and f * m, or 0 for a neighbour outside [0, L_in)
+struct Pos {
+    int j;    // windowed: index into the tile's window row; global: left neighbour clamped to [-2, L_in]
+    float f;  // interpolation fraction
 };
 
 struct MfmaArgs {
@@ -56,8 +80,10 @@ struct MfmaArgs {
     FastDiv fd_K, fd_cpo;
     int tiles_m, tiles_n, splits, chunks;
     int64_t N;
-    int *counters;
-    float *partials;
+    float *partials;  // split partial tiles [splits][tiles][BM*BN], or null
+    int nch;     // input channels a chunk can touch
+    int wt_max;  // window capacity per channel row (elements); 0: always gather
+    int off_mask, off_row, off_w, off_x;  // byte offsets of the LDS regions
 };
 
 __device__ __forceinline__ int remap_xcd(int u, int U) {
@@ -68,151 +94,96 @@ __device__ __forceinline__ int remap_xcd(int u, int U) {
     return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + loc;
 }
 
-// ---- per-dtype MFMA traits --------------------------------------------------
-
-struct TrF32 {
-    using D = F32;
-    using T = float;
-    static constexpr int BM = 128, BN = 64, NT = 256;
-    static constexpr int WM = 4, WN = 1;   // wave grid
-    static constexpr int SLD = BK + 4;     // padded LDS row (elements) of the sample tile [BN][SLD]
-    struct AFrag { float v[16]; };
-    struct BFrag { float v[16]; };
-    static __device__ __forceinline__ void load_a(const float *row, int rb, int Kred, bool vec, bool live,
-                                                  AFrag &a) {
-        if (vec && rb + 16 <= Kred) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f4 t = *(const f4 *)(row + rb + 4 * q);
-                a.v[4 * q] = t[0]; a.v[4 * q + 1] = t[1]; a.v[4 * q + 2] = t[2]; a.v[4 * q + 3] = t[3];
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < 16; ++j) a.v[j] = (rb + j < Kred) ? row[rb + j] : 0.0f;
-        }
-        if (!live) {
-#pragma unroll
-            for (int j = 0; j < 16; ++j) a.v[j] = 0.0f;
-        }
-    }
-    static __device__ __forceinline__ void load_b(const float *src, BFrag &b) {
-        const f4 *p = (const f4 *)src;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const f4 t = p[q];
-            b.v[4 * q] = t[0]; b.v[4 * q + 1] = t[1]; b.v[4 * q + 2] = t[2]; b.v[4 * q + 3] = t[3];
-        }
-    }
-    static __device__ __forceinline__ void mma(const AFrag &a, const BFrag &b, f16v &acc) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[j], b.v[j], acc, 0, 0, 0);
-    }
-    // 8 samples -> LDS (two 16-byte stores)
-    static __device__ __forceinline__ void store_samples(float *dst, const float (&v)[8]) {
-        f4 lo = {v[0], v[1], v[2], v[3]}, hi = {v[4], v[5], v[6], v[7]};
-        ((f4 *)dst)[0] = lo;
-        ((f4 *)dst)[1] = hi;
-    }
-    static __device__ __forceinline__ float to_out(float v) { return v; }
-};
-
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
 }
 
+// ---- per-dtype traits ---------------------------------------------------------
+//
+// Lane (i = lane % 32, h = lane / 32) holds, per chunk, the 16 weights
+// W[m0 + 32*mb + i][r0 + 16h .. r0 + 16h + 15] of each 32-row block and the 16
+// samples S[r0 + 16h .. + 15][column] of each 32-column block.  fp32 pairs
+// them in 16 v_mfma_f32_32x32x2_f32 (element j of both halves per
+// instruction); bf16 in 2 v_mfma_f32_32x32x16_bf16 (elements 8s .. 8s+7).
+//
+// The weight tile in LDS is [BM][BK] without padding; its 16-byte words are
+// XOR-swizzled by row so that lanes reading one word each of consecutive
+// rows hit distinct banks.
+
+struct TrF32 {
+    using D = F32;
+    using T = float;
+    static constexpr int MB = 4, NB = 1;  // 32x32 blocks per wave: BM = 128, BN = 128
+    static constexpr int WPR = BK / 4;    // 16-byte words per weight-tile row (8)
+    struct Frag { float v[16]; };
+    static __device__ __forceinline__ int swz(int row, int word) { return word ^ (row & 7); }
+    static __device__ __forceinline__ void lds_a(const float *tile, int row, int h, Frag &a) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f4 t = *(const f4 *)(tile + row * BK + 4 * swz(row, 4 * h + q));
+            a.v[4 * q] = t[0]; a.v[4 * q + 1] = t[1]; a.v[4 * q + 2] = t[2]; a.v[4 * q + 3] = t[3];
+        }
+    }
+    static __device__ __forceinline__ void make_b(const float (&v)[16], Frag &b) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) b.v[j] = v[j];
+    }
+    static __device__ __forceinline__ void mma(const Frag &a, const Frag &b, f16v &acc) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[j], b.v[j], acc, 0, 0, 0);
+    }
+};
+
 struct TrBF16 {
     using D = BF16;
     using T = uint16_t;
-    static constexpr int BM = 128, BN = 128, NT = 256;
-    static constexpr int WM = 2, WN = 2;
-    static constexpr int SLD = BK + 8;
-    struct AFrag { u4 v[2]; };  // 16 bf16
-    struct BFrag { u4 v[2]; };
-    static __device__ __forceinline__ void load_a(const uint16_t *row, int rb, int Kred, bool vec, bool live,
-                                                  AFrag &a) {
-        if (vec && rb + 16 <= Kred) {
-            a.v[0] = *(const u4 *)(row + rb);
-            a.v[1] = *(const u4 *)(row + rb + 8);
-        } else {
-            uint32_t w[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t lo = (rb + 2 * j < Kred) ? row[rb + 2 * j] : 0u;
-                const uint32_t hi = (rb + 2 * j + 1 < Kred) ? row[rb + 2 * j + 1] : 0u;
-                w[j] = lo | (hi << 16);
-            }
-            a.v[0] = u4{w[0], w[1], w[2], w[3]};
-            a.v[1] = u4{w[4], w[5], w[6], w[7]};
-        }
-        if (!live) {
-            a.v[0] = u4{0, 0, 0, 0};
-            a.v[1] = u4{0, 0, 0, 0};
-        }
+    static constexpr int MB = 8, NB = 1;  // BM = 256, BN = 128
+    static constexpr int WPR = BK / 8;    // 4
+    struct Frag { u4 v[2]; };
+    static __device__ __forceinline__ int swz(int row, int word) { return word ^ ((row >> 1) & 3); }
+    static __device__ __forceinline__ void lds_a(const uint16_t *tile, int row, int h, Frag &a) {
+        a.v[0] = *(const u4 *)(tile + row * BK + 8 * swz(row, 2 * h));
+        a.v[1] = *(const u4 *)(tile + row * BK + 8 * swz(row, 2 * h + 1));
     }
-    static __device__ __forceinline__ void load_b(const uint16_t *src, BFrag &b) {
-        b.v[0] = ((const u4 *)src)[0];
-        b.v[1] = ((const u4 *)src)[1];
+    static __device__ __forceinline__ void make_b(const float (&v)[16], Frag &b) {
+        b.v[0] = u4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                    pack_bf16x2(v[6], v[7])};
+        b.v[1] = u4{pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]), pack_bf16x2(v[12], v[13]),
+                    pack_bf16x2(v[14], v[15])};
     }
-    static __device__ __forceinline__ void mma(const AFrag &a, const BFrag &b, f16v &acc) {
+    static __device__ __forceinline__ void mma(const Frag &a, const Frag &b, f16v &acc) {
 #pragma unroll
         for (int s = 0; s < 2; ++s)
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf8, a.v[s]),
                                                           __builtin_bit_cast(bf8, b.v[s]), acc, 0, 0, 0);
     }
-    static __device__ __forceinline__ void store_samples(uint16_t *dst, const float (&v)[8]) {
-        u4 q = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                pack_bf16x2(v[6], v[7])};
-        *(u4 *)dst = q;
-    }
 };
 
-// Build the per-workgroup position table: entry [g*K + k][n] for the tile's
-// columns n0 .. n0 + BN - 1.
 template <class Tr>
-__device__ __forceinline__ void build_table(const MfmaArgs &a, int64_t n0, TabEntry *s_tab) {
+struct Geo {
+    static constexpr int BM = 32 * Tr::MB;
+    static constexpr int BN = 4 * 32 * Tr::NB;
+    static constexpr int WV = BM * Tr::WPR / NT;  // 16-byte weight words per thread per chunk
+};
+
+template <class Tr, bool VEC_W, bool MASK, int NCHM, int SLOTM>
+__global__ void __launch_bounds__(NT) k_mfma(MfmaArgs a) {
     using D = typename Tr::D;
     using T = typename Tr::T;
-    const Params &p = a.p;
-    const T *__restrict__ off = (const T *)p.off;
-    const T *__restrict__ mask = (const T *)p.mask;
-    const int GK = p.G * p.K;
-    for (int e = threadIdx.x; e < GK * Tr::BN; e += Tr::NT) {
-        const int n = e % Tr::BN;
-        const int gk = e / Tr::BN;
-        const int g = gk / p.K, k = gk - g * p.K;
-        const int64_t col = n0 + n;
-        TabEntry te = {0, 0, 0.0f, 0.0f};
-        if (col < a.N) {
-            const int b = (int)(col / p.L_out), l = (int)(col - (int64_t)b * p.L_out);
-            const int64_t oi = (((int64_t)b * p.G + g) * p.L_out + l) * p.K + k;
-            const float m = mask ? D::ld(mask, oi) : 1.0f;
-            int i0;
-            float f;
-            split_position(D::ld(off, oi), l * p.stride - p.padding + k * p.dilation, i0, f);
-            const bool v0 = i0 >= 0 && i0 < p.L_in;
-            const bool v1 = i0 + 1 >= 0 && i0 + 1 < p.L_in;
-            te.idx0 = v0 ? i0 : 0;
-            te.idx1 = v1 ? i0 + 1 : 0;
-            te.w0 = v0 ? (1.0f - f) * m : 0.0f;
-            te.w1 = v1 ? f * m : 0.0f;
-        }
-        s_tab[e] = te;
-    }
-}
+    using Frag = typename Tr::Frag;
+    constexpr int MB = Tr::MB, NB = Tr::NB, BM = Geo<Tr>::BM, BN = Geo<Tr>::BN;
+    constexpr int WPR = Tr::WPR, WV = Geo<Tr>::WV;
+    constexpr int EPW = 16 / sizeof(T);  // elements per 16-byte word
+    static_assert(WV * NT == BM * WPR, "weight tile split");
 
-template <class Tr, bool VEC_W>
-__global__ void __launch_bounds__(Tr::NT, 2) k_mfma(MfmaArgs a) {
-    using D = typename Tr::D;
-    using T = typename Tr::T;
-    constexpr int BM = Tr::BM, BN = Tr::BN, NT = Tr::NT, SLD = Tr::SLD;
-    constexpr int TM = BM / Tr::WM, TN = BN / Tr::WN;  // per-wave tile
-    constexpr int MB = TM / 32, NB = TN / 32;          // 32x32 blocks per wave
-    constexpr int SPT = BN * 4 / NT;                   // sampled columns per thread (8 rows each)
-    static_assert(Tr::WM * Tr::WN * 64 == NT, "wave grid");
-
-    extern __shared__ TabEntry s_tab[];  // [G*K][BN], sized at launch
-    __shared__ __attribute__((aligned(16))) T s_S[2][BN * SLD];
-    __shared__ int s_last;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    Pos *s_tab = (Pos *)smem;                   // [G*K][BN]
+    float *s_m = (float *)(smem + a.off_mask);  // [G*K][BN] if MASK
+    int *s_row = (int *)(smem + a.off_row);     // [2][BK][2]: table row offset, window row offset / channel
+    T *s_w = (T *)(smem + a.off_w);             // [NWBUF][BM][BK], swizzled
+    float *s_x = (float *)(smem + a.off_x);     // [2][nch][wt_max]
+    __shared__ int s_lo[NSEG], s_hi[NSEG], s_base[NSEG + 1];
+    __shared__ int s_win;
 
     const Params &p = a.p;
     const int t = threadIdx.x;
@@ -226,34 +197,144 @@ __global__ void __launch_bounds__(Tr::NT, 2) k_mfma(MfmaArgs a) {
     const int64_t n0 = (int64_t)tn * BN;
     const int c_begin = (int)((int64_t)sp * a.chunks / a.splits);
     const int c_end = (int)((int64_t)(sp + 1) * a.chunks / a.splits);
-    const int M = p.C_out, Kred = p.Kred, K = p.K, L_in = p.L_in;
+    const int M = p.C_out, Kred = p.Kred, K = p.K, L_in = p.L_in, L_out = p.L_out;
+    const int GK = p.G * K;
+    const T *__restrict__ x = (const T *)p.x;
+    const T *__restrict__ off = (const T *)p.off;
+    const T *__restrict__ mask = (const T *)p.mask;
+    const T *__restrict__ w = (const T *)p.w;
 
-    build_table<Tr>(a, n0, s_tab);
+    // ---- column tile geometry
+    const int64_t n_end = (n0 + BN < a.N) ? n0 + BN : a.N;
+    const int b_first = (int)(n0 / L_out);
+    const int nseg = (int)((n_end - 1) / L_out) - b_first + 1;
+    bool win = (a.wt_max > 0) && (nseg <= NSEG);
+    if (t < NSEG) {
+        s_lo[t] = INT_MAX;
+        s_hi[t] = INT_MIN;
+    }
+    __syncthreads();
 
-    // sampler role: columns sn + BN/SPT*q (q < SPT), rows 8*srg .. 8*srg + 7 of each chunk
-    const int sn = t % (BN / SPT), srg = t / (BN / SPT);
-    const T *__restrict__ xs[SPT];
-    bool sok[SPT];
+    // ---- position table, pass 1: left neighbours, fractions, mask; per-segment extent
+    {
+        int lo[NSEG], hi[NSEG];
 #pragma unroll
-    for (int q = 0; q < SPT; ++q) {
-        const int64_t col = n0 + sn + (BN / SPT) * q;
-        sok[q] = col < a.N;
-        xs[q] = (const T *)p.x + (sok[q] ? (col / p.L_out) * (int64_t)p.C_in * L_in : 0);
+        for (int q = 0; q < NSEG; ++q) {
+            lo[q] = INT_MAX;
+            hi[q] = INT_MIN;
+        }
+        constexpr int TB = 4;  // entries per thread per batch of loads
+        for (int e0 = 0; e0 < GK * BN; e0 += NT * TB) {
+            float ov[TB], mv[TB];
+            int64_t oi[TB];
+            bool ok[TB];
+#pragma unroll
+            for (int q = 0; q < TB; ++q) {
+                const int e = e0 + t + NT * q;
+                const int n = e % BN, gk = e / BN;
+                const int g = gk / K, k = gk - g * K;
+                const int64_t col = n0 + n;
+                ok[q] = e < GK * BN && col < a.N;
+                const int b = (int)(col / L_out), l = (int)(col - (int64_t)b * L_out);
+                oi[q] = ok[q] ? (((int64_t)b * p.G + g) * L_out + l) * K + k : 0;
+            }
+#pragma unroll
+            for (int q = 0; q < TB; ++q) {
+                ov[q] = D::ld(off, oi[q]);
+                mv[q] = MASK ? D::ld(mask, oi[q]) : 1.0f;
+            }
+#pragma unroll
+            for (int q = 0; q < TB; ++q) {
+                const int e = e0 + t + NT * q;
+                if (e >= GK * BN) continue;
+                const int n = e % BN, gk = e / BN;
+                const int k = gk % K;
+                const int64_t col = n0 + n;
+                Pos ps = {0, 0.0f};
+                if (ok[q]) {
+                    const int b = (int)(col / L_out), l = (int)(col - (int64_t)b * L_out);
+                    int i0;
+                    split_position(ov[q], l * p.stride - p.padding + k * p.dilation, i0, ps.f);
+                    ps.j = min(max(i0, -2), L_in);  // x~ reads zero at both neighbours beyond these bounds
+                    const int sg = b - b_first;
+#pragma unroll
+                    for (int z = 0; z < NSEG; ++z) {
+                        lo[z] = (z == sg) ? min(lo[z], ps.j) : lo[z];
+                        hi[z] = (z == sg) ? max(hi[z], ps.j) : hi[z];
+                    }
+                }
+                s_tab[e] = ps;
+                if (MASK) s_m[e] = ok[q] ? mv[q] : 0.0f;
+            }
+        }
+        if (win) {
+#pragma unroll
+            for (int z = 0; z < NSEG; ++z) {
+                for (int o = 32; o > 0; o >>= 1) {
+                    lo[z] = min(lo[z], __shfl_xor(lo[z], o));
+                    hi[z] = max(hi[z], __shfl_xor(hi[z], o));
+                }
+                if ((t & 63) == 0 && z < nseg) {
+                    atomicMin(&s_lo[z], lo[z]);
+                    atomicMax(&s_hi[z], hi[z]);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (t == 0) {
+        int base = 0;
+        for (int s = 0; s < (win ? nseg : 0); ++s) {
+            s_base[s] = base;
+            base += s_hi[s] + 2 - s_lo[s];
+        }
+        s_base[win ? nseg : 0] = base;
+        s_win = win && base <= a.wt_max;
+    }
+    __syncthreads();
+    win = s_win;
+    const int WT = win ? s_base[nseg] : 0;
+    // ---- pass 2 (windowed): left neighbour -> index into the tile's window row
+    if (win) {
+        for (int e = t; e < GK * BN; e += NT) {
+            const int64_t col = n0 + e % BN;
+            if (col < a.N) {
+                const int s = (int)(col / L_out) - b_first;
+                s_tab[e].j += s_base[s] - s_lo[s];
+            }
+        }
     }
 
-    // MFMA role
+    // ---- staging roles
+    // window slots of this thread: positions jj = t + NT*q of the window row
+    const int nslot = win ? (WT + NT - 1) / NT : 0;  // <= SLOTM by the plan
+    int64_t xoff[SLOTM];  // per slot: element offset of x~ at channel 0, or -1 for a zero
+#pragma unroll
+    for (int q = 0; q < SLOTM; ++q) {
+        const int jj = t + NT * q;
+        int64_t o = -1;
+        if (q < nslot && jj < WT) {
+            int s = 0;
+            while (s + 1 < nseg && s_base[s + 1] <= jj) ++s;
+            const int pos = s_lo[s] + (jj - s_base[s]);
+            if (pos >= 0 && pos < L_in) o = (int64_t)(b_first + s) * p.C_in * L_in + pos;
+        }
+        xoff[q] = o;
+    }
+    const int nch = a.nch;  // <= NCHM by the plan
+    const int wt_max = a.wt_max;
+
+    // MFMA / sampling role
     const int wv = t / 64, lane = t % 64, li = lane % 32, lh = lane / 32;
-    const int wm = wv % Tr::WM, wn = wv / Tr::WM;
-    const T *__restrict__ wrow[MB];
-    bool alive[MB];
+    int colL[NB];
+    const T *xcol[NB];  // global mode: x block of the column's batch
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        const int am = m0 + wm * TM + 32 * mb + li;
-        alive[mb] = am < M;
-        wrow[mb] = (const T *)p.w + (int64_t)(alive[mb] ? am : M - 1) * Kred;
+    for (int nb = 0; nb < NB; ++nb) {
+        colL[nb] = 32 * (NB * wv + nb) + li;
+        const int64_t col = n0 + colL[nb];
+        xcol[nb] = x + (col < a.N ? (col / L_out) * (int64_t)p.C_in * L_in : 0);
     }
 
-    typename Tr::AFrag acur[MB], anext[MB];
     f16v acc[MB][NB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -262,87 +343,167 @@ __global__ void __launch_bounds__(Tr::NT, 2) k_mfma(MfmaArgs a) {
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[mb][nb][q] = 0.0f;
 
-    float xv0[SPT][8], xv1[SPT][8], ww0[SPT][8], ww1[SPT][8];
+    u4 wreg[WV];
+    float xreg[NCHM][SLOTM];
+    int rrow0 = 0, rrow1 = 0;
 
-    auto load_a = [&](int c, typename Tr::AFrag (&af)[MB]) {
-        const int rb = c * BK + 16 * lh;
+    // global -> registers for chunk c (weights, windows) and the row descriptors
+    auto fetch = [&](int c) {
+        const int r0 = c * BK;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) Tr::load_a(wrow[mb], rb, Kred, VEC_W, alive[mb], af[mb]);
-    };
-
-    // issue the x gathers of chunk c into registers
-    auto gather = [&](int c) {
-        const int r_first = c * BK + 8 * srg;
-        const int ci0 = (int)fdiv((uint32_t)r_first, a.fd_K);
-        const int k0 = r_first - ci0 * K;
+        for (int v = 0; v < WV; ++v) {
+            const int e = t + NT * v;
+            const int row = e / WPR, part = e % WPR;
+            const int m = m0 + row, rb = r0 + part * EPW;
+            const T *src = w + (int64_t)(m < M ? m : M - 1) * Kred + rb;
+            u4 q = {0, 0, 0, 0};
+            if (VEC_W) {
+                // Kred is a multiple of the word size: a word is wholly inside or outside
+                if (m < M && rb < Kred) q = *(const u4 *)src;
+            } else {
+                T tmp[EPW];
 #pragma unroll
-        for (int q = 0; q < SPT; ++q) {
-            int ci = ci0, k = k0;
+                for (int z = 0; z < EPW; ++z) tmp[z] = (m < M && rb + z < Kred) ? src[z] : (T)0;
+                q = __builtin_bit_cast(u4, tmp);
+            }
+            wreg[v] = q;
+        }
+        const int ci_lo = (int)fdiv((uint32_t)r0, a.fd_K);
+        if (win) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int r = r_first + e;
-                xv0[q][e] = 0.0f;
-                xv1[q][e] = 0.0f;
-                ww0[q][e] = 0.0f;
-                ww1[q][e] = 0.0f;
-                if (sok[q] && r < Kred) {
-                    const int g = (p.G == 1) ? 0 : (int)fdiv((uint32_t)ci, a.fd_cpo);
-                    const TabEntry te = s_tab[(g * K + k) * BN + sn + (BN / SPT) * q];
-                    const T *xr = xs[q] + (int64_t)ci * L_in;
-                    xv0[q][e] = D::ld(xr, te.idx0);
-                    xv1[q][e] = D::ld(xr, te.idx1);
-                    ww0[q][e] = te.w0;
-                    ww1[q][e] = te.w1;
-                }
-                if (++k == K) {
-                    k = 0;
-                    ++ci;
+            for (int cr = 0; cr < NCHM; ++cr) {
+                const int ci = ci_lo + cr;
+#pragma unroll
+                for (int q = 0; q < SLOTM; ++q) {
+                    const int64_t o = xoff[q];
+                    xreg[cr][q] = (cr < nch && ci < p.C_in && o >= 0) ? D::ld(x, o + (int64_t)ci * L_in) : 0.0f;
                 }
             }
         }
+        if (t < BK) {
+            const int r = min(r0 + t, Kred - 1);
+            const int ci = (int)fdiv((uint32_t)r, a.fd_K);
+            const int k = r - ci * K;
+            const int g = (int)fdiv((uint32_t)ci, a.fd_cpo);
+            rrow0 = (g * K + k) * BN;
+            rrow1 = win ? (ci - ci_lo) * wt_max : ci;
+        }
     };
-
-    // interpolate the gathered values and store them in the sample tile
-    auto finish = [&](T *dst) {
+    // registers -> LDS for chunk c
+    auto commit = [&](int c) {
+        T *dw = s_w + (c % NWBUF) * BM * BK;
 #pragma unroll
-        for (int q = 0; q < SPT; ++q) {
-            float v[8];
+        for (int v = 0; v < WV; ++v) {
+            const int e = t + NT * v;
+            const int row = e / WPR, part = e % WPR;
+            *(u4 *)(dw + row * BK + EPW * Tr::swz(row, part)) = wreg[v];
+        }
+        if (win) {
+            float *dx = s_x + (c & 1) * nch * wt_max;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = fmaf(ww1[q][e], xv1[q][e], ww0[q][e] * xv0[q][e]);
-            Tr::store_samples(dst + (sn + (BN / SPT) * q) * SLD + 8 * srg, v);
+            for (int cr = 0; cr < NCHM; ++cr)
+#pragma unroll
+                for (int q = 0; q < SLOTM; ++q)
+                    if (cr < nch && q < nslot && t + NT * q < WT) dx[cr * wt_max + t + NT * q] = xreg[cr][q];
+        }
+        if (t < BK) {
+            int *dr = s_row + (c & 1) * 2 * BK;
+            dr[2 * t] = rrow0;
+            dr[2 * t + 1] = rrow1;
         }
     };
 
-    auto mfma_chunk = [&](const T *src, const typename Tr::AFrag (&af)[MB]) {
+    // The 16 samples of this lane's B fragments for chunk c: rows
+    // r0 + 16*lh + s, s = 0..15, of column colL[nb].  Straight-line phases
+    // (row descriptors, table reads, x reads, arithmetic) so the LDS reads
+    // of all samples are in flight together.
+    auto sample = [&](auto win_tag, int c, Frag(&bf)[NB]) {
+        constexpr bool WIN = decltype(win_tag)::value;
+        const int *dr = s_row + (c & 1) * 2 * BK + 2 * 16 * lh;
+        int toff[16], xo[16];
+#pragma unroll
+        for (int s = 0; s < 16; s += 2) {
+            const i4 q = *(const i4 *)(dr + 2 * s);
+            toff[s] = q[0];
+            xo[s] = q[1];
+            toff[s + 1] = q[2];
+            xo[s + 1] = q[3];
+        }
+        const float *xw = s_x + (c & 1) * nch * wt_max;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            typename Tr::BFrag bf;
-            Tr::load_b(src + (wn * TN + 32 * nb + li) * SLD + 16 * lh, bf);
+            Pos ps[16];
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) Tr::mma(af[mb], bf, acc[mb][nb]);
+            for (int s = 0; s < 16; ++s) ps[s] = s_tab[toff[s] + colL[nb]];
+            float x0[16], x1[16];
+            if (WIN) {
+#pragma unroll
+                for (int s = 0; s < 16; ++s) {
+                    const float *rw = xw + xo[s] + ps[s].j;
+                    x0[s] = rw[0];
+                    x1[s] = rw[1];
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < 16; ++s) {
+                    const T *rw = xcol[nb] + (int64_t)xo[s] * L_in;
+                    const int i0 = ps[s].j;
+                    const float a0 = D::ld(rw, min(max(i0, 0), L_in - 1));
+                    const float a1 = D::ld(rw, min(max(i0 + 1, 0), L_in - 1));
+                    x0[s] = (i0 >= 0 && i0 < L_in) ? a0 : 0.0f;
+                    x1[s] = (i0 + 1 >= 0 && i0 + 1 < L_in) ? a1 : 0.0f;
+                }
+            }
+            float v[16];
+#pragma unroll
+            for (int s = 0; s < 16; ++s) v[s] = fmaf(ps[s].f, x1[s] - x0[s], x0[s]);
+            if (MASK) {
+#pragma unroll
+                for (int s = 0; s < 16; ++s) v[s] *= s_m[toff[s] + colL[nb]];
+            }
+            Tr::make_b(v, bf[nb]);
         }
     };
 
-    __syncthreads();  // position table ready
-    int buf = 0;
-    if (c_begin < c_end) {
-        load_a(c_begin, acur);
-        gather(c_begin);
-        finish(s_S[0]);
-    }
-    __syncthreads();
-    for (int c = c_begin; c < c_end; ++c) {
-        const bool more = c + 1 < c_end;
-        if (more) {
-            load_a(c + 1, anext);
-            gather(c + 1);
-        }
-        mfma_chunk(s_S[buf], acur);
-        if (more) finish(s_S[buf ^ 1]);
-        __syncthreads();
-        buf ^= 1;
+    auto mfma_chunk = [&](int c, const Frag(&bf)[NB]) {
+        const T *tile = s_w + (c % NWBUF) * BM * BK;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acur[mb] = anext[mb];
+        for (int mb = 0; mb < MB; ++mb) {
+            Frag af;
+            Tr::lds_a(tile, 32 * mb + li, lh, af);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) Tr::mma(af, bf[nb], acc[mb][nb]);
+        }
+    };
+
+    __syncthreads();  // position table complete
+    Frag bcur[NB], bnext[NB];
+    if (c_begin < c_end) {
+        fetch(c_begin);
+        commit(c_begin);
+        if (c_begin + 1 < c_end) {
+            fetch(c_begin + 1);
+            commit(c_begin + 1);
+        }
+        __syncthreads();
+        if (win)
+            sample(std::true_type{}, c_begin, bcur);
+        else
+            sample(std::false_type{}, c_begin, bcur);
+    }
+    for (int c = c_begin; c < c_end; ++c) {
+        if (c + 2 < c_end) fetch(c + 2);
+        if (c + 1 < c_end) {
+            if (win)
+                sample(std::true_type{}, c + 1, bnext);
+            else
+                sample(std::false_type{}, c + 1, bnext);
+        }
+        mfma_chunk(c, bcur);
+        if (c + 2 < c_end) commit(c + 2);
+        __syncthreads();
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) bcur[nb] = bnext[nb];
     }
 
     // ---- epilogue
@@ -350,65 +511,141 @@ __global__ void __launch_bounds__(Tr::NT, 2) k_mfma(MfmaArgs a) {
     T *__restrict__ out = (T *)p.out;
     constexpr int NQ = MB * NB * 4;  // f4 groups per thread
     if (a.splits > 1) {
+        // fp32 partial tile, in this thread's register order; summed over the
+        // splits in split order by k_split_reduce
         const int tile = tm * a.tiles_n + tn;
-        f4 *part = (f4 *)(a.partials + ((int64_t)tile * a.splits + sp) * (BM * BN));
+        f4 *part = (f4 *)(a.partials + ((int64_t)sp * a.tiles_m * a.tiles_n + tile) * (BM * BN));
 #pragma unroll
         for (int q4 = 0; q4 < NQ; ++q4) {
             const int mb = q4 / (NB * 4), nb = (q4 / 4) % NB, qq = (q4 & 3) * 4;
             f4 v = {acc[mb][nb][qq], acc[mb][nb][qq + 1], acc[mb][nb][qq + 2], acc[mb][nb][qq + 3]};
             part[q4 * NT + t] = v;
         }
-        __threadfence();
-        __syncthreads();
-        if (t == 0) s_last = (atomicAdd(&a.counters[tile], 1) == a.splits - 1);
-        __syncthreads();
-        if (!s_last) return;
-        __threadfence();
-        const f4 *part0 = (const f4 *)(a.partials + (int64_t)tile * a.splits * (BM * BN));
-#pragma unroll
-        for (int q4 = 0; q4 < NQ; ++q4) {
-            f4 tot = part0[q4 * NT + t];
-            for (int s2 = 1; s2 < a.splits; ++s2) tot += part0[(int64_t)s2 * (BM * BN / 4) + q4 * NT + t];
-            const int mb = q4 / (NB * 4), nb = (q4 / 4) % NB, qq = (q4 & 3) * 4;
-            acc[mb][nb][qq] = tot[0];
-            acc[mb][nb][qq + 1] = tot[1];
-            acc[mb][nb][qq + 2] = tot[2];
-            acc[mb][nb][qq + 3] = tot[3];
-        }
-        if (t == 0) a.counters[tile] = 0;
+        return;
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-        const int64_t col = n0 + wn * TN + 32 * nb + li;
+        const int64_t col = n0 + colL[nb];
         if (col >= a.N) continue;
-        const int b = (int)(col / p.L_out);
-        const int l = (int)(col - (int64_t)b * p.L_out);
-        T *ob = out + (int64_t)b * M * p.L_out + l;
+        const int b = (int)(col / L_out);
+        const int l = (int)(col - (int64_t)b * L_out);
+        T *ob = out + (int64_t)b * M * L_out + l;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
-                const int row = m0 + wm * TM + 32 * mb + 8 * (q >> 2) + 4 * lh + (q & 3);
-                if (row < M) D::st(ob, (int64_t)row * p.L_out, acc[mb][nb][q] + (bias ? D::ld(bias, row) : 0.0f));
+                const int row = m0 + 32 * mb + 8 * (q >> 2) + 4 * lh + (q & 3);
+                if (row < M) D::st(ob, (int64_t)row * L_out, acc[mb][nb][q] + (bias ? D::ld(bias, row) : 0.0f));
             }
+    }
+}
+
+// Sum of the split partial tiles (in split order), plus bias, into out.
+// Thread (tile, t) handles the values thread t of every split's workgroup
+// held, so the register-order layout maps back to (row, column) exactly as
+// in the direct epilogue.
+template <class Tr>
+__global__ void __launch_bounds__(NT) k_split_reduce(MfmaArgs a) {
+    using D = typename Tr::D;
+    using T = typename Tr::T;
+    constexpr int MB = Tr::MB, NB = Tr::NB, BM = Geo<Tr>::BM, BN = Geo<Tr>::BN;
+    constexpr int NQ = MB * NB * 4;
+    const Params &p = a.p;
+    const int t = threadIdx.x;
+    const int tile = blockIdx.x;
+    const int tm = tile / a.tiles_n, tn = tile % a.tiles_n;
+    const int m0 = tm * BM;
+    const int64_t n0 = (int64_t)tn * BN;
+    const int wv = t / 64, lane = t % 64, li = lane % 32, lh = lane / 32;
+    const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
+    const f4 *part = (const f4 *)a.partials + (int64_t)tile * (BM * BN / 4);
+    const T *__restrict__ bias = (const T *)p.bias;
+    T *__restrict__ out = (T *)p.out;
+    const int M = p.C_out, L_out = p.L_out;
+#pragma unroll
+    for (int q4 = 0; q4 < NQ; ++q4) {
+        f4 tot = part[q4 * NT + t];
+        for (int s2 = 1; s2 < a.splits; ++s2) tot += part[(int64_t)s2 * tiles * (BM * BN / 4) + q4 * NT + t];
+        const int mb = q4 / (NB * 4), nb = (q4 / 4) % NB, qq = (q4 & 3) * 4;
+        const int64_t col = n0 + 32 * (NB * wv + nb) + li;
+        if (col >= a.N) continue;
+        const int b = (int)(col / L_out);
+        const int l = (int)(col - (int64_t)b * L_out);
+        T *ob = out + (int64_t)b * M * L_out + l;
+#pragma unroll
+        for (int z = 0; z < 4; ++z) {
+            const int q = qq + z;
+            const int row = m0 + 32 * mb + 8 * (q >> 2) + 4 * lh + (q & 3);
+            if (row < M) D::st(ob, (int64_t)row * L_out, tot[z] + (bias ? D::ld(bias, row) : 0.0f));
+        }
     }
 }
 
 template <class Tr>
 void plan_for(const Params &p, int num_cus, MfmaPlan &pl) {
-    pl.bm = Tr::BM;
-    pl.bn = Tr::BN;
+    using T = typename Tr::T;
+    constexpr int BM = Geo<Tr>::BM, BN = Geo<Tr>::BN;
+    pl.bm = BM;
+    pl.bn = BN;
     pl.bk = BK;
-    pl.threads = Tr::NT;
+    pl.threads = NT;
     const int64_t N = (int64_t)p.B * p.L_out;
-    pl.tiles_m = (p.C_out + Tr::BM - 1) / Tr::BM;
-    pl.tiles_n = (int)((N + Tr::BN - 1) / Tr::BN);
+    pl.tiles_m = (p.C_out + BM - 1) / BM;
+    pl.tiles_n = (int)((N + BN - 1) / BN);
     pl.chunks = (p.Kred + BK - 1) / BK;
+
+    // LDS: position table (+ mask), row descriptors, weight tiles, x windows
+    const size_t tab = (size_t)p.G * p.K * BN * sizeof(Pos);
+    const size_t msk = p.mask ? (size_t)p.G * p.K * BN * 4 : 0;
+    const size_t rows = 2 * BK * 2 * 4;
+    const size_t wtile = (size_t)NWBUF * BM * BK * sizeof(T);
+    const int nch = (BK - 1) / p.K + 2;
+    // window staging variant (compile-time register budget): K >= 8 -> at
+    // most 5 channel rows x 4 slots; 3 <= K < 8 -> 12 rows x 2 slots; K < 3 ->
+    // no window (gather from global memory).
+    int slotm = 0;
+    if (p.K >= 8) {
+        pl.variant = 0;
+        slotm = 4;
+    } else if (p.K >= 3) {
+        pl.variant = 1;
+        slotm = 2;
+    } else {
+        pl.variant = 2;
+        slotm = 0;
+    }
+    // window capacity: the tile's grid span per batch segment plus a margin
+    // for the offsets' spread, within the staging slots
+    const int seg_possible = (int)std::min<int64_t>(NSEG, (BN - 1) / p.L_out + 2);
+    const int64_t span = (int64_t)(std::min<int64_t>(BN, p.L_out) - 1) * p.stride +
+                         (int64_t)(p.K - 1) * p.dilation + 2 + 64;
+    int64_t wt = span * seg_possible;
+    if (wt > (int64_t)slotm * NT) wt = (int64_t)slotm * NT;
+    if (wt < 64) wt = 0;  // too little room for a window: gather from global memory
+    const size_t lds_cap = 160 * 1024 - 1024;
+    size_t xwin = 2 * (size_t)nch * wt * 4;
+    if (tab + msk + rows + wtile + xwin > lds_cap) {
+        wt = 0;
+        xwin = 0;
+    }
+    pl.nch = nch;
+    pl.wt_max = (int)wt;
+    pl.off_mask = (int)tab;
+    pl.off_row = (int)((tab + msk + 15) & ~(size_t)15);
+    pl.off_w = (int)(pl.off_row + rows);
+    pl.off_x = (int)(pl.off_w + wtile);
+    pl.lds_bytes = pl.off_x + xwin;
+    if (pl.lds_bytes > lds_cap) {
+        pl.ok = false;
+        return;
+    }
+
     const int64_t tiles = (int64_t)pl.tiles_m * pl.tiles_n;
+    const int per_cu = std::max<int>(1, (int)(lds_cap / pl.lds_bytes));
+    const int64_t slots = (int64_t)num_cus * std::min(per_cu, 2);
     // Split the reduction when the tiles alone leave the GPU's workgroup
-    // slots (2 per CU) badly filled: pick the split count minimising
-    // (waves of workgroups) x (chunks per workgroup).
-    const int64_t slots = 2 * (int64_t)num_cus;
+    // slots badly filled: pick the split count minimising (waves of
+    // workgroups) x (chunks per workgroup + pipeline fill).
     int best_s = 1;
     double best = 1e300;
     const int s_max = pl.chunks < 16 ? pl.chunks : 16;
@@ -416,7 +653,7 @@ void plan_for(const Params &p, int num_cus, MfmaPlan &pl) {
         const int64_t units = tiles * s;
         if (units > ((int64_t)1 << 30)) break;
         const int64_t waves = (units + slots - 1) / slots;
-        const double cost = (double)waves * ((pl.chunks + s - 1) / s) * (s > 1 ? 1.03 : 1.0);
+        const double cost = (double)waves * ((pl.chunks + s - 1) / s + 2) * (s > 1 ? 1.03 : 1.0);
         if (cost < best - 1e-9) {
             best = cost;
             best_s = s;
@@ -424,13 +661,7 @@ void plan_for(const Params &p, int num_cus, MfmaPlan &pl) {
     }
     pl.splits = best_s;
     pl.blocks = tiles * best_s;
-    pl.lds_bytes = (size_t)p.G * p.K * Tr::BN * sizeof(TabEntry);
-    if (best_s > 1) {
-        const size_t cnt = ((size_t)tiles * 4 + 255) & ~(size_t)255;
-        pl.ws_bytes = cnt + (size_t)tiles * best_s * Tr::BM * Tr::BN * 4;
-    } else {
-        pl.ws_bytes = 0;
-    }
+    pl.ws_bytes = best_s > 1 ? (size_t)tiles * best_s * BM * BN * 4 : 0;
 }
 
 template <class Tr>
@@ -444,21 +675,46 @@ hipError_t launch_for(const Params &p, const MfmaPlan &pl, hipStream_t stream) {
     a.splits = pl.splits;
     a.chunks = pl.chunks;
     a.N = (int64_t)p.B * p.L_out;
+    a.nch = pl.nch;
+    a.wt_max = pl.wt_max;
+    a.off_mask = pl.off_mask;
+    a.off_row = pl.off_row;
+    a.off_w = pl.off_w;
+    a.off_x = pl.off_x;
     const int64_t tiles = (int64_t)pl.tiles_m * pl.tiles_n;
-    if (pl.splits > 1) {
-        const size_t cnt = ((size_t)tiles * 4 + 255) & ~(size_t)255;
-        a.counters = (int *)p.ws;
-        a.partials = (float *)((char *)p.ws + cnt);
-    } else {
-        a.counters = nullptr;
-        a.partials = nullptr;
-    }
+    a.partials = pl.splits > 1 ? (float *)p.ws : nullptr;
     const int vec_elems = 16 / (int)sizeof(typename Tr::T);
     const bool vec = (p.Kred % vec_elems == 0) && (((uintptr_t)p.w & 15) == 0);
-    if (vec)
-        hipLaunchKernelGGL((k_mfma<Tr, true>), dim3((unsigned)pl.blocks), dim3(Tr::NT), pl.lds_bytes, stream, a);
+    const dim3 grid((unsigned)pl.blocks), block(NT);
+#define DC1D_LAUNCH(V, MK, A, B) hipLaunchKernelGGL((k_mfma<Tr, V, MK, A, B>), grid, block, pl.lds_bytes, stream, a)
+#define DC1D_LAUNCH_V(MK, A, B)           \
+    do {                                  \
+        if (vec)                          \
+            DC1D_LAUNCH(true, MK, A, B);  \
+        else                              \
+            DC1D_LAUNCH(false, MK, A, B); \
+    } while (0)
+#define DC1D_LAUNCH_M(A, B)            \
+    do {                               \
+        if (p.mask)                    \
+            DC1D_LAUNCH_V(true, A, B); \
+        else                           \
+            DC1D_LAUNCH_V(false, A, B);\
+    } while (0)
+    if (pl.variant == 0)
+        DC1D_LAUNCH_M(5, 4);
+    else if (pl.variant == 1)
+        DC1D_LAUNCH_M(12, 2);
     else
-        hipLaunchKernelGGL((k_mfma<Tr, false>), dim3((unsigned)pl.blocks), dim3(Tr::NT), pl.lds_bytes, stream, a);
+        DC1D_LAUNCH_M(1, 1);
+#undef DC1D_LAUNCH_M
+#undef DC1D_LAUNCH_V
+#undef DC1D_LAUNCH
+    if (pl.splits > 1) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((k_split_reduce<Tr>), dim3((unsigned)tiles), dim3(NT), 0, stream, a);
+    }
     return hipGetLastError();
 }
 
@@ -468,7 +724,7 @@ MfmaPlan plan_mfma(const Params &p, int num_cus) {
     MfmaPlan pl = {};
     pl.ok = false;
     pl.name = "none";
-    if (p.groups != 1 || p.G * p.K > GK_MAX) return pl;
+    if (p.groups != 1) return pl;
     if (p.C_out < 32 || p.Kred < 16) return pl;  // too small to fill a tile: the direct kernel serves
     pl.ok = true;
     if (p.dtype == kF32) {

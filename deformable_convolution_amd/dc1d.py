@@ -143,16 +143,16 @@ _ws_cache = {}
 
 
 def _workspace(nbytes: int, device):
-    """A zero-initialised workspace per (device, stream), grown as needed.
-    The library leaves its counter region zero after every call, so the
-    buffer is zeroed only when it is (re)allocated."""
+    """A cached workspace per (device, stream), grown as needed (the library
+    needs no initialisation of it; calls on one stream are ordered, so they
+    can share it)."""
     if nbytes == 0:
         return None
     stream = torch.cuda.current_stream(device)
     key = (device.index, stream.cuda_stream)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _ws_cache[key] = buf
     return buf
 

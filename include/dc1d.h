@@ -107,8 +107,8 @@ int64_t dc1d_output_length(int64_t L_in, int64_t K, int64_t stride, int64_t padd
  * the current device (0 when the chosen kernels need none).  Only the
  * descriptors' dtype, ndim and shape are read; data pointers may be NULL.
  * The same validation as dc1d_forward applies (except pointers and
- * aliasing).  The workspace holds split-reduction partial sums and a
- * per-tile arrival counter region; see dc1d_forward for its contract.
+ * aliasing).  The workspace holds split-reduction partial sums; see
+ * dc1d_forward.
  */
 int dc1d_workspace_bytes(const dc1d_tensor *x, const dc1d_tensor *offsets,
                          const dc1d_tensor *mask_or_null, const dc1d_tensor *weight,
@@ -131,12 +131,11 @@ int dc1d_workspace_bytes(const dc1d_tensor *x, const dc1d_tensor *offsets,
  * stream is a hipStream_t (NULL: the null stream).
  *
  * workspace: device memory of at least dc1d_workspace_bytes() bytes, or NULL
- * with workspace_bytes 0 when that is 0.  Its counter region (the first
- * 256-byte-aligned part; all of it when in doubt) must be zero the first time
- * a workspace is used; every call that runs to completion leaves it zero
- * again, so a workspace zeroed once at allocation can be reused by any
- * number of calls ordered on one stream.  Calls in flight at the same time
- * must not share a workspace.
+ * with workspace_bytes 0 when that is 0.  It carries the fp32 partial sums of
+ * a split reduction from the main kernel to a second kernel enqueued right
+ * after it on the same stream; it needs no initialisation and holds nothing
+ * between calls.  Calls in flight at the same time must not share a
+ * workspace.
  *
  * Limits (DC1D_ERR_BAD_SHAPE beyond them): L_in + padding <= 2^29,
  * dilation*(K-1) <= 2^29, L_out*stride <= 2^30, C_in*K <= 2^30,
