@@ -122,7 +122,7 @@ struct MfmaPlan {
     const char *name;
     int variant;      // window staging variant
     int nch, wt_max;  // channel rows per chunk, window capacity per row
-    int off_mask, off_row, off_w, off_x;  // LDS layout (bytes)
+    int off_mask, off_row, off_w, off_s, off_x;  // LDS layout (bytes)
 };
 MfmaPlan plan_mfma(const Params &p, int num_cus);
 hipError_t launch_mfma(const Params &p, const MfmaPlan &pl, hipStream_t stream);
