@@ -45,8 +45,9 @@ PEAK = {  # MI355X published peaks
     "mfma_bf16_TFLOPs": 2516.6,
     "valu_f32_TFLOPs": 157.3,
 }
-KERNEL_SOURCES = ["deformable_convolution_amd/csrc/k_mfma.hip", "deformable_convolution_amd/csrc/k_direct.hip",
-                  "deformable_convolution_amd/csrc/dc1d_internal.h"]
+CSRC = "deformable_convolution_amd/csrc"
+KERNEL_SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(os.path.join(ROOT, CSRC))
+                        if f.endswith((".hip", ".h")))
 
 
 def work(w):

@@ -237,7 +237,8 @@ int dc1d_forward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_te
     if ((st = current_device(&dev))) return st;
     const Plan pl = make_plan(p, dev);
     if (pl.ws_bytes > 0) {
-        if (!workspace || workspace_bytes < pl.ws_bytes) return DC1D_ERR_WORKSPACE;
+        if (!workspace || workspace_bytes < pl.ws_bytes || ((uintptr_t)workspace & 255))
+            return DC1D_ERR_WORKSPACE;
         if (overlaps(workspace, pl.ws_bytes, out->data, out_bytes)) return DC1D_ERR_ALIAS;
         for (int i = 0; i < 5; ++i)
             if (all[i] && overlaps(workspace, pl.ws_bytes, all[i]->data, (size_t)numel(all[i]) * es))

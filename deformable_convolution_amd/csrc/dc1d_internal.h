@@ -120,11 +120,22 @@ struct MfmaPlan {
     size_t lds_bytes;
     size_t ws_bytes;  // counters + partials (0 when splits == 1)
     const char *name;
-    int variant;      // window staging variant
-    int nch, wt_max;  // channel rows per chunk, window capacity per row
-    int off_mask, off_row, off_w, off_s, off_x;  // LDS layout (bytes)
+    int variant;      // compiled window staging shape (index into its table)
+    int nch, wt_max;  // channel rows per chunk, window capacity per row (0: gather)
+    int off_mask, off_w, off_s, off_x;  // LDS layout (bytes)
+    // channel-block reduction order (blocked != 0): CB channels per block,
+    // ncb blocks, nkb tap groups, staging shape; the rearranged weights take
+    // the first wb_bytes of the workspace, split partials follow
+    int blocked, cb, slot, lpp, ncb, nkb;
+    int variant_dw;  // the same shape reading the weights directly when they are 16-byte aligned (-1: none)
+    size_t wb_bytes;
 };
 MfmaPlan plan_mfma(const Params &p, int num_cus);
 hipError_t launch_mfma(const Params &p, const MfmaPlan &pl, hipStream_t stream);
+// one per storage dtype and mask presence (k_mfma_*.hip)
+hipError_t launch_mfma_f32(const Params &p, const MfmaPlan &pl, hipStream_t stream);
+hipError_t launch_mfma_f32_mask(const Params &p, const MfmaPlan &pl, hipStream_t stream);
+hipError_t launch_mfma_bf16(const Params &p, const MfmaPlan &pl, hipStream_t stream);
+hipError_t launch_mfma_bf16_mask(const Params &p, const MfmaPlan &pl, hipStream_t stream);
 
 }  // namespace dc1d

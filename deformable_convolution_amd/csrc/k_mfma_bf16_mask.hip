@@ -1,0 +1,11 @@
+// k_mfma_bf16_mask.hip -- instantiates the fused MFMA kernels (mfma_kernel.h) for
+// bfloat16 storage with a modulation mask.
+#include "mfma_kernel.h"
+
+namespace dc1d {
+
+hipError_t launch_mfma_bf16_mask(const Params &p, const MfmaPlan &pl, hipStream_t stream) {
+    return launch_for<TrBF16, true>(p, pl, stream);
+}
+
+}  // namespace dc1d

@@ -1,0 +1,1062 @@
+// mfma_kernel.h -- fused deformable sampling + MFMA GEMM for groups == 1:
+// the kernel templates, included by the translation units that instantiate
+// them (k_mfma_*.hip) and by the planner (k_mfma.hip).
+//
+// The contraction out[b, co, l] = bias[co] + sum_r W[co, r] S[r, (b, l)] is a
+// GEMM with M = C_out, N = B*L_out and reduction r = ci*K + k over the
+// weight viewed as [C_out, C_in*K] (conv1d operator page, Description; the
+// article's Step 3 weighted summation).  S is the deformable sample matrix
+// (the article's Step 2); it lives only as a small double-buffered tile in
+// LDS, never in HBM.
+//
+// Workgroup: 8 waves in two roles (warp specialisation), one per SIMD each:
+//   * 4 MFMA waves.  MFMA wave w owns the 32*NB columns [32*NB*w, ...) of
+//     the BM x BN output tile and all its BM rows; it reads operand
+//     fragments from LDS and issues MFMAs, and stages the next chunk's
+//     weight tile, whose load latency hides under its MFMAs.
+//   * 4 sampler waves.  They stage the zero-padded x windows from HBM into
+//     LDS and compute the sample tile of the next reduction chunk.
+// The hardware interleaves the two roles on every SIMD: MFMAs of one wave
+// run while the other wave's VALU, LDS and memory instructions issue.  The
+// reduction runs in chunks of BK = 32 rows; in iteration c the MFMA waves
+// consume chunk c and stage chunk c+1's weight tile while the sampler waves
+// produce chunk c+1's sample tile and stage windows two chunks ahead; one
+// barrier per chunk.  Sample tiles, weight tiles and windows are all
+// double-buffered.
+//
+// Position table (built once per workgroup): for each (offset group, tap,
+// column) the left neighbour i0 and the fraction f of the sample position
+// (dc1d page, Demo notebook: linear interpolation between neighbours), and
+// the mask value when there is one (dc1d page, Modulation; applied as a
+// plain multiply, so an all-ones mask gives the no-mask bits).
+//
+// Windows: the columns of a tile fall into at most NSEG batch segments; for
+// each segment the smallest and largest left neighbour over the tile give a
+// window [lo, hi + 1] of the input row, staged per channel with zeros
+// outside [0, L_in) (torchvision issue demo: samples off the ends read
+// zero).  Interpolation is then one paired LDS read and two FMAs, with no
+// bounds checks.  When the offsets spread wider than the window capacity, or
+// the tile crosses too many batches, the workgroup gathers x from global
+// memory instead (same arithmetic, bounds-checked loads).
+//
+// Columns past the end of N and reduction rows past Kred are computed on
+// clamped, finite inputs and never stored (an MFMA output column depends
+// only on its own B column, and the weight rows past Kred are zero).
+//
+// Split reduction: when there are too few output tiles to fill the GPU, the
+// reduction range is split over several workgroups.  Each writes its fp32
+// partial tile into the workspace; a second, small kernel on the same stream
+// adds the partials in split order (so the result is deterministic), adds
+// the bias and stores the output.  Kernel order on the stream is the only
+// synchronisation, so the workspace needs no initialisation.
+#pragma once
+
+#include "dc1d_internal.h"
+
+#include <limits.h>
+
+#include <algorithm>
+#include <type_traits>
+
+namespace dc1d {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef int i4 __attribute__((ext_vector_type(4)));
+
+namespace {
+
+constexpr int NWM = 4;          // MFMA waves
+constexpr int NTM = 64 * NWM;   // MFMA threads
+constexpr int NTS = 256;        // sampler threads (4 waves)
+constexpr int NTT = NTM + NTS;  // threads per workgroup
+constexpr int BK = 32;          // reduction rows per chunk
+constexpr int NSEG = 4;         // batch segments a windowed tile may span
+
+struct Pos {
+    int j;    // windowed: index into the tile's window row; global: left neighbour clamped to [-2, L_in]
+    float f;  // interpolation fraction
+};
+
+struct MfmaArgs {
+    Params p;
+    FastDiv fd_K, fd_cpo, fd_Lout;
+    int tiles_m, tiles_n, splits, chunks;
+    int64_t N;
+    float *partials;  // split partial tiles [splits][tiles][BM*BN], or null
+    int wt_max;       // window capacity per channel row (elements); 0: always gather
+    int vec_w;        // weight rows can be read in aligned 16-byte words
+    int off_mask, off_w, off_s, off_x;  // byte offsets of the LDS regions
+    // channel-block order only: the reduction runs over ncb blocks of CB
+    // input channels (outer) and nkb groups of 32/CB taps (inner); wb holds
+    // the weights rearranged into [nkb][C_out][ncb][32] chunk rows
+    const void *wb;
+    int ncb, nkb;
+    FastDiv fd_nkb;
+};
+
+__device__ __forceinline__ int remap_xcd(int u, int U) {
+    // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so
+    // that consecutive unit ids (which share a weight slice) run on one XCD
+    // and hit its L2.
+    const int q = U >> 3, r = U & 7, xcd = u & 7, loc = u >> 3;
+    return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + loc;
+}
+
+// ---- per-dtype traits ---------------------------------------------------------
+//
+// MFMA lane (i = lane % 32, h = lane / 32) holds, per chunk, the 16 weights
+// W[m0 + 32*mb + i][r0 + 16h .. r0 + 16h + 15] of each 32-row block and the 16
+// samples S[r0 + 16h .. + 15][column] of each 32-column block.  fp32 pairs
+// them in 16 v_mfma_f32_32x32x2_f32 (element j of both halves per
+// instruction); bf16 in 2 v_mfma_f32_32x32x16_bf16 (elements 8s .. 8s+7).
+//
+// The weight tile in LDS is [BM][BK] without padding; its 16-byte words are
+// XOR-swizzled by row so that lanes reading one word each of consecutive
+// rows hit distinct banks.  The sample tile is [BN][BK + pad]: a lane's 16
+// samples are contiguous, and the pad spreads consecutive columns over the
+// banks.
+
+struct TrF32 {
+    using D = F32;
+    using T = float;
+    static constexpr int MB = 8, NB = 1;  // BM = 256, BN = 128
+    static constexpr int WPR = BK / 4;    // 16-byte words per weight-tile row (8)
+    static constexpr int SLD = BK + 4;    // sample-tile row (elements)
+    struct Frag { float v[16]; };
+    static __device__ __forceinline__ int swz(int row, int word) { return word ^ (row & 7); }
+    static __device__ __forceinline__ void lds_a(const float *tile, int row, int h, Frag &a) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f4 t = *(const f4 *)(tile + row * BK + 4 * swz(row, 4 * h + q));
+            a.v[4 * q] = t[0]; a.v[4 * q + 1] = t[1]; a.v[4 * q + 2] = t[2]; a.v[4 * q + 3] = t[3];
+        }
+    }
+    static __device__ __forceinline__ void lds_b(const float *src, Frag &b) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f4 t = ((const f4 *)src)[q];
+            b.v[4 * q] = t[0]; b.v[4 * q + 1] = t[1]; b.v[4 * q + 2] = t[2]; b.v[4 * q + 3] = t[3];
+        }
+    }
+    static __device__ __forceinline__ void store_b(float *dst, const float (&v)[16]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ((f4 *)dst)[q] = f4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+    }
+    static __device__ __forceinline__ void mma(const Frag &a, const Frag &b, f16v &acc) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[j], b.v[j], acc, 0, 0, 0);
+    }
+};
+
+// Two floats -> two bfloat16 (round to nearest even), packed low/high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const bf2 r = __builtin_convertvector(f2{lo, hi}, bf2);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+struct TrBF16 {
+    using D = BF16;
+    using T = uint16_t;
+    static constexpr int MB = 8, NB = 1;  // BM = 256, BN = 128
+    static constexpr int WPR = BK / 8;    // 4
+    static constexpr int SLD = BK + 8;
+    struct Frag { u4 v[2]; };
+    static __device__ __forceinline__ int swz(int row, int word) { return word ^ ((row >> 1) & 3); }
+    static __device__ __forceinline__ void lds_a(const uint16_t *tile, int row, int h, Frag &a) {
+        a.v[0] = *(const u4 *)(tile + row * BK + 8 * swz(row, 2 * h));
+        a.v[1] = *(const u4 *)(tile + row * BK + 8 * swz(row, 2 * h + 1));
+    }
+    static __device__ __forceinline__ void lds_b(const uint16_t *src, Frag &b) {
+        b.v[0] = ((const u4 *)src)[0];
+        b.v[1] = ((const u4 *)src)[1];
+    }
+    static __device__ __forceinline__ void store_b(uint16_t *dst, const float (&v)[16]) {
+        ((u4 *)dst)[0] = u4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                            pack_bf16x2(v[6], v[7])};
+        ((u4 *)dst)[1] = u4{pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]), pack_bf16x2(v[12], v[13]),
+                            pack_bf16x2(v[14], v[15])};
+    }
+    static __device__ __forceinline__ void mma(const Frag &a, const Frag &b, f16v &acc) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf8, a.v[s]),
+                                                          __builtin_bit_cast(bf8, b.v[s]), acc, 0, 0, 0);
+    }
+};
+
+template <class Tr>
+struct Geo {
+    static constexpr int BM = 32 * Tr::MB;
+    static constexpr int BN = NWM * 32 * Tr::NB;
+    static constexpr int WV = BM * Tr::WPR / NTM;  // 16-byte weight words per MFMA thread per chunk
+};
+
+// Shared per-workgroup state the two roles read.
+struct Tile {
+    int m0, tm, tn, sp, c_begin, c_end;
+    int64_t n0;
+    bool win;
+    int WT, nseg, b_first;
+};
+
+// ---- the MFMA role -------------------------------------------------------------
+//
+// Weight layout WL: 0: the weight viewed as [C_out][Kred], chunk c at
+// reduction rows 32c .. 32c+31; 1: the rearranged copy a.wb (channel-block
+// order, rows of 32 contiguous elements, always in bounds); 2: channel-block
+// order read straight from the weight when a chunk row's four taps of one
+// channel are one aligned 16-byte word (fp32, 32/CB == 4, K % 4 == 0).
+template <class Tr, int WL>
+__device__ __forceinline__ void mfma_role(const MfmaArgs &a, const Tile &tl, typename Tr::T *s_w,
+                                          const typename Tr::T *s_S) {
+    using D = typename Tr::D;
+    using T = typename Tr::T;
+    using Frag = typename Tr::Frag;
+    constexpr int MB = Tr::MB, NB = Tr::NB, BM = Geo<Tr>::BM, BN = Geo<Tr>::BN, SLD = Tr::SLD;
+    constexpr int WPR = Tr::WPR, WV = Geo<Tr>::WV;
+    constexpr int EPW = 16 / sizeof(T);  // elements per 16-byte word
+    static_assert(WV * NTM == BM * WPR, "weight tile split");
+    static_assert(WL != 2 || EPW == 4, "direct channel-block weights are fp32 words of four taps");
+    const Params &p = a.p;
+    const int t = threadIdx.x;
+    const int wv = t / 64, lane = t % 64, li = lane % 32, lh = lane / 32;
+    const int M = p.C_out, Kred = p.Kred, C_in = p.C_in;
+    const T *__restrict__ w = (const T *)p.w;
+    const bool m_full = tl.m0 + BM <= M;  // no rows past C_out in this tile
+
+    // The weight tile of chunk c+1 is loaded into registers at the start of
+    // iteration c and written to LDS after chunk c's MFMAs, so its load
+    // latency hides under them.  Loads never wait on a bounds test: words
+    // outside the matrix load a clamped address and are zeroed in commit_w.
+    u4 wreg[WV];
+    auto fetch_w = [&](int cw) {
+        const int r0 = cw * BK;
+        if (WL == 1) {
+            const int cb = (int)fdiv((uint32_t)cw, a.fd_nkb), kb = cw - cb * a.nkb;
+            const T *wb = (const T *)a.wb + ((int64_t)kb * M * a.ncb + cb) * BK;
+#pragma unroll
+            for (int v = 0; v < WV; ++v) {
+                const int e = t + NTM * v;
+                const int row = e / WPR, part = e % WPR;
+                const int m = min(tl.m0 + row, M - 1);
+                wreg[v] = *(const u4 *)(wb + (int64_t)m * a.ncb * BK + part * EPW);
+            }
+        } else if (WL == 2) {
+            const int cb = (int)fdiv((uint32_t)cw, a.fd_nkb), kb = cw - cb * a.nkb;
+            // word `part` of a row: channel CB*cb + part, taps 4kb .. 4kb+3
+            const T *wk = w + 4 * kb;
+#pragma unroll
+            for (int v = 0; v < WV; ++v) {
+                const int e = t + NTM * v;
+                const int row = e / WPR, part = e % WPR;
+                const int m = min(tl.m0 + row, M - 1);
+                const int ci = min(cb * (BK / 4) + part, C_in - 1);
+                wreg[v] = *(const u4 *)(wk + ((int64_t)m * C_in + ci) * p.K);
+            }
+        } else if (a.vec_w) {
+            // Kred is a multiple of the word size: a word is wholly inside or outside
+#pragma unroll
+            for (int v = 0; v < WV; ++v) {
+                const int e = t + NTM * v;
+                const int row = e / WPR, part = e % WPR;
+                const int m = tl.m0 + row, rb = r0 + part * EPW;
+                const bool ok = m < M && rb < Kred;
+                wreg[v] = *(const u4 *)(w + (ok ? (int64_t)m * Kred + rb : 0));
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < WV; ++v) {
+                const int e = t + NTM * v;
+                const int row = e / WPR, part = e % WPR;
+                const int m = tl.m0 + row, rb = r0 + part * EPW;
+                const T *src = w + (int64_t)(m < M ? m : M - 1) * Kred;
+                T tmp[EPW];
+#pragma unroll
+                for (int z = 0; z < EPW; ++z) tmp[z] = (m < M && rb + z < Kred) ? src[min(rb + z, Kred - 1)] : (T)0;
+                wreg[v] = __builtin_bit_cast(u4, tmp);
+            }
+        }
+    };
+    // registers -> LDS (swizzled words).  Tiles wholly inside the matrix
+    // store without tests.
+    auto commit_w = [&](int cw) {
+        T *dw = s_w + (cw & 1) * BM * BK;
+        const int r0 = cw * BK;
+        const int cb = WL == 2 ? (int)fdiv((uint32_t)cw, a.fd_nkb) : 0;
+        const bool full = m_full && (WL == 1 || (WL == 2 ? (cb + 1) * (BK / 4) <= C_in : r0 + BK <= Kred));
+        if (full) {
+#pragma unroll
+            for (int v = 0; v < WV; ++v) {
+                const int e = t + NTM * v;
+                const int row = e / WPR, part = e % WPR;
+                *(u4 *)(dw + row * BK + EPW * Tr::swz(row, part)) = wreg[v];
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < WV; ++v) {
+                const int e = t + NTM * v;
+                const int row = e / WPR, part = e % WPR;
+                const bool ok = tl.m0 + row < M && (WL == 1 || (WL == 2 ? cb * (BK / 4) + part < C_in
+                                                                         : r0 + part * EPW < Kred));
+                *(u4 *)(dw + row * BK + EPW * Tr::swz(row, part)) = ok ? wreg[v] : u4{0, 0, 0, 0};
+            }
+        }
+    };
+
+    f16v acc[MB][NB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[mb][nb][q] = 0.0f;
+
+    if (tl.c_begin < tl.c_end) {
+        fetch_w(tl.c_begin);
+        commit_w(tl.c_begin);
+    }
+    // prologue barriers shared with the sampler role: staging done, first sample tile done
+    __syncthreads();
+    __syncthreads();
+    for (int c = tl.c_begin; c < tl.c_end; ++c) {
+        const bool more = c + 1 < tl.c_end;
+        if (more) fetch_w(c + 1);
+        const T *tile = s_w + (c & 1) * BM * BK;
+        const T *st = s_S + (c & 1) * BN * SLD;
+        Frag bf[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) Tr::lds_b(st + (32 * (NB * wv + nb) + li) * SLD + 16 * lh, bf[nb]);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            Frag af;
+            Tr::lds_a(tile, 32 * mb + li, lh, af);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) Tr::mma(af, bf[nb], acc[mb][nb]);
+        }
+        if (more) commit_w(c + 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue
+    const T *__restrict__ bias = (const T *)p.bias;
+    T *__restrict__ out = (T *)p.out;
+    const int L_out = p.L_out;
+    constexpr int NQ = MB * NB * 4;  // f4 groups per thread
+    if (a.splits > 1) {
+        // fp32 partial tile, in this thread's register order; summed over the
+        // splits in split order by k_split_reduce
+        const int tile = tl.tm * a.tiles_n + tl.tn;
+        f4 *part = (f4 *)(a.partials + ((int64_t)tl.sp * a.tiles_m * a.tiles_n + tile) * (BM * BN));
+#pragma unroll
+        for (int q4 = 0; q4 < NQ; ++q4) {
+            const int mb = q4 / (NB * 4), nb = (q4 / 4) % NB, qq = (q4 & 3) * 4;
+            part[q4 * NTM + t] = f4{acc[mb][nb][qq], acc[mb][nb][qq + 1], acc[mb][nb][qq + 2], acc[mb][nb][qq + 3]};
+        }
+        return;
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int col = (int)tl.n0 + 32 * (NB * wv + nb) + li;
+        if (col >= a.N) continue;
+        const int b = (int)fdiv((uint32_t)col, a.fd_Lout);
+        const int l = col - b * L_out;
+        T *ob = out + (int64_t)b * M * L_out + l;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int row = tl.m0 + 32 * mb + 8 * (q >> 2) + 4 * lh + (q & 3);
+                if (row < M) D::st(ob, (int64_t)row * L_out, acc[mb][nb][q] + (bias ? D::ld(bias, row) : 0.0f));
+            }
+    }
+}
+
+// ---- the sampler role ------------------------------------------------------------
+//
+// Sampler wave sw computes the samples of reduction rows r0 + 16*h .. + 15
+// (h = sw & 1) for 64 columns (64*(sw >> 1) + lane), so that a row's
+// position-table row and window row are the same for the whole wave and are
+// computed in scalar registers.  Windows are double-buffered and staged
+// through registers: the loads of chunk c+3 are issued in iteration c and
+// written to LDS at the start of iteration c+1, a full iteration later.
+//
+// NCH channel rows of WTM = SLOT * NTS elements each are staged per chunk
+// (compile-time counts, so the staging code is straight-line): thread ts
+// owns positions ts + NTS*q (q < SLOT) of every row.
+template <class Tr, bool MASK, bool WIN, int NCH, int SLOT>
+__device__ __forceinline__ void sampler_role(const MfmaArgs &a, const Tile &tl, const Pos *s_tab,
+                                             const float *s_m, typename Tr::T *s_S, float *s_x,
+                                             const int *s_lo, const int *s_base) {
+    using D = typename Tr::D;
+    using T = typename Tr::T;
+    constexpr int BN = Geo<Tr>::BN, SLD = Tr::SLD;
+    constexpr int WTM = SLOT * NTS;   // window row length (elements)
+    constexpr int XBUF = NCH * WTM;  // floats per window buffer
+    static_assert(BN == 128, "two sampler waves per 64 columns");
+    const Params &p = a.p;
+    const int ts = threadIdx.x - NTM;  // 0 .. NTS-1
+    const int lane = ts % 64;
+    const int sw = __builtin_amdgcn_readfirstlane(ts / 64);
+    const int h = sw & 1;
+    const int col = 64 * (sw >> 1) + lane;
+    const int Kred = p.Kred, K = p.K, L_in = p.L_in, L_out = p.L_out, C_in = p.C_in, cpo = p.cpo;
+    const T *__restrict__ x = (const T *)p.x;
+    const int WT = tl.WT;
+
+    // Per slot: the x offset of its window position in channel 0 (clamped to
+    // a real element) and whether the position lies inside [0, L_in).  Loads
+    // are unconditional; positions outside are zeroed when committed.
+    int64_t xoff[SLOT];
+    bool xval[SLOT];
+#pragma unroll
+    for (int q = 0; q < SLOT; ++q) {
+        const int jj = ts + NTS * q;
+        int64_t o = 0;
+        bool ok = false;
+        if (WIN && jj < WT) {
+            int sg = 0;
+            while (sg + 1 < tl.nseg && s_base[sg + 1] <= jj) ++sg;
+            const int pos = s_lo[sg] + (jj - s_base[sg]);
+            ok = pos >= 0 && pos < L_in;
+            o = (int64_t)(tl.b_first + sg) * C_in * L_in + (ok ? pos : 0);
+        }
+        xoff[q] = o;
+        xval[q] = ok;
+    }
+    const int64_t colg = tl.n0 + col;
+    const T *xcol = x + (colg < a.N ? (colg / L_out) * (int64_t)C_in * L_in : 0);
+
+    float xreg[NCH][SLOT];
+    int xci = 0;  // first channel of the rows held in xreg
+    auto fetch_x = [&](int cx) {
+        xci = (int)fdiv((uint32_t)(cx * BK), a.fd_K);
+#pragma unroll
+        for (int cr = 0; cr < NCH; ++cr) {
+            const int64_t rowo = (int64_t)min(xci + cr, C_in - 1) * L_in;
+#pragma unroll
+            for (int q = 0; q < SLOT; ++q) xreg[cr][q] = D::ld(x, xoff[q] + rowo);
+        }
+    };
+    auto commit_x = [&](int cx) {
+        float *dx = s_x + (cx & 1) * XBUF + ts;
+#pragma unroll
+        for (int cr = 0; cr < NCH; ++cr) {
+            const bool cok = xci + cr < C_in;
+#pragma unroll
+            for (int q = 0; q < SLOT; ++q) dx[cr * WTM + NTS * q] = (cok && xval[q]) ? xreg[cr][q] : 0.0f;
+        }
+    };
+
+    // The 16 samples (rows r0 + 16h + s) of this lane's column for chunk c,
+    // into the sample tile.  Row descriptors are wave-uniform (scalar).
+    auto sample = [&](int c) {
+        const int r0 = c * BK;
+        const int ci_lo = (int)fdiv((uint32_t)r0, a.fd_K);
+        // Row descriptors, wave-uniform: walk rows rs, rs+1, ... as (ci, k)
+        // and ci's offset group g, in scalar registers.  Rows past Kred
+        // repeat the last row (their weights are zero).
+        int toff[16], xo[16];
+        {
+            const int rs = __builtin_amdgcn_readfirstlane(min(r0 + 16 * h, Kred - 1));
+            const int adv = Kred - 1 - rs;  // steps that stay inside the reduction
+            int ci = __builtin_amdgcn_readfirstlane((int)fdiv((uint32_t)rs, a.fd_K));
+            int k = rs - ci * K;
+            int g = __builtin_amdgcn_readfirstlane((int)fdiv((uint32_t)ci, a.fd_cpo));
+            int cg = ci - g * cpo;  // channel within its offset group
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                toff[s] = (g * K + k) * BN;
+                xo[s] = WIN ? (c & 1) * XBUF + (ci - ci_lo) * WTM : ci;
+                // branch-free advance (selects, not jumps)
+                k += (s < adv) ? 1 : 0;
+                const int wk = (k == K) ? 1 : 0;
+                k = wk ? 0 : k;
+                ci += wk;
+                cg += wk;
+                const int wg = (cg == cpo) ? 1 : 0;
+                cg = wg ? 0 : cg;
+                g += wg;
+            }
+        }
+        Pos ps[16];
+#pragma unroll
+        for (int s = 0; s < 16; ++s) ps[s] = s_tab[toff[s] + col];
+        float x0[16], x1[16];
+        if (WIN) {
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                const float *rw = s_x + xo[s] + ps[s].j;
+                x0[s] = rw[0];
+                x1[s] = rw[1];
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                const T *rw = xcol + (int64_t)xo[s] * L_in;
+                const int i0 = ps[s].j;
+                const float a0 = D::ld(rw, min(max(i0, 0), L_in - 1));
+                const float a1 = D::ld(rw, min(max(i0 + 1, 0), L_in - 1));
+                x0[s] = (i0 >= 0 && i0 < L_in) ? a0 : 0.0f;
+                x1[s] = (i0 + 1 >= 0 && i0 + 1 < L_in) ? a1 : 0.0f;
+            }
+        }
+        float v[16];
+#pragma unroll
+        for (int s = 0; s < 16; ++s) v[s] = fmaf(ps[s].f, x1[s] - x0[s], x0[s]);
+        if (MASK) {
+#pragma unroll
+            for (int s = 0; s < 16; ++s) v[s] *= s_m[toff[s] + col];
+        }
+        Tr::store_b(s_S + (c & 1) * BN * SLD + col * SLD + 16 * h, v);
+    };
+
+    const int c0 = tl.c_begin, c1 = tl.c_end;
+    // prologue: windows of c0 and c0+1 in LDS, the loads of c0+2 in registers
+    if (WIN) {
+        if (c0 < c1) {
+            fetch_x(c0);
+            commit_x(c0);
+        }
+        if (c0 + 1 < c1) {
+            fetch_x(c0 + 1);
+            commit_x(c0 + 1);
+        }
+        if (c0 + 2 < c1) fetch_x(c0 + 2);
+    }
+    __syncthreads();
+    if (c0 < c1) sample(c0);
+    __syncthreads();
+    for (int c = c0; c < c1; ++c) {
+        if (WIN && c + 2 < c1) commit_x(c + 2);  // loaded during the previous iteration
+        if (c + 1 < c1) sample(c + 1);
+        // issued after the samples so that nothing in them waits for these loads
+        if (WIN && c + 3 < c1) fetch_x(c + 3);
+        __syncthreads();
+    }
+}
+
+// ---- per-workgroup set-up ----------------------------------------------------------
+//
+// The tile a workgroup owns (output rows, columns, reduction range) and its
+// position table: for each (offset group, tap, column) the left neighbour
+// and fraction of the sample position (dc1d page, Demo notebook: linear
+// interpolation between neighbours) and the mask value (dc1d page,
+// Modulation; applied as a plain multiply).  When the tile's positions fit
+// the window capacity a.wt_max, the left neighbours become indices into the
+// tile's window row: batch segment s occupies [s_base[s], s_base[s+1]) and
+// holds input positions s_lo[s] .. s_hi[s] + 1.
+template <class Tr, bool MASK>
+__device__ __forceinline__ void setup_tile(const MfmaArgs &a, Tile &tl, Pos *s_tab, float *s_m, int *s_lo,
+                                           int *s_hi, int *s_base, int *s_win) {
+    using D = typename Tr::D;
+    using T = typename Tr::T;
+    constexpr int BM = Geo<Tr>::BM, BN = Geo<Tr>::BN;
+    const Params &p = a.p;
+    const int t = threadIdx.x;
+    const int U = a.tiles_m * a.tiles_n * a.splits;
+    const int u = remap_xcd(blockIdx.x, U);
+    tl.tn = u % a.tiles_n;
+    const int rest = u / a.tiles_n;
+    tl.sp = rest % a.splits;
+    tl.tm = rest / a.splits;
+    tl.m0 = tl.tm * BM;
+    tl.n0 = (int64_t)tl.tn * BN;
+    tl.c_begin = (int)((int64_t)tl.sp * a.chunks / a.splits);
+    tl.c_end = (int)((int64_t)(tl.sp + 1) * a.chunks / a.splits);
+    const int K = p.K, L_in = p.L_in, L_out = p.L_out;
+    const int GK = p.G * K;
+    const T *__restrict__ off = (const T *)p.off;
+    const T *__restrict__ mask = (const T *)p.mask;
+
+    // ---- column tile geometry (N < 2^31: 32-bit column arithmetic)
+    const int n_end = (int)((tl.n0 + BN < a.N) ? tl.n0 + BN : a.N);
+    tl.b_first = (int)fdiv((uint32_t)tl.n0, a.fd_Lout);
+    tl.nseg = (int)fdiv((uint32_t)(n_end - 1), a.fd_Lout) - tl.b_first + 1;
+    const bool win = (a.wt_max > 0) && (tl.nseg <= NSEG);
+    if (t < NSEG) {
+        s_lo[t] = INT_MAX;
+        s_hi[t] = INT_MIN;
+    }
+
+    // ---- position table, pass 1: left neighbours, fractions, mask; per-segment extent.
+    // Thread t serves column n = t % BN (its batch b and position l computed
+    // once) and every (NTT/BN)-th entry (g, k) of it.
+    constexpr int TPCOL = NTT / BN;  // threads per column
+    static_assert(NTT % BN == 0, "whole columns per thread");
+    const int n = t % BN;
+    const int col = (int)tl.n0 + n;
+    const bool cok = col < n_end;
+    const int cb_ = cok ? (int)fdiv((uint32_t)col, a.fd_Lout) : tl.b_first;
+    const int cl = cok ? col - cb_ * L_out : 0;
+    const int sg = cb_ - tl.b_first;  // batch segment of the column
+    const int64_t obase = ((int64_t)cb_ * p.G * L_out + cl) * K;
+    const int64_t gstride = (int64_t)L_out * K;
+    const int grid0 = cl * p.stride - p.padding;
+    int lo = INT_MAX, hi = INT_MIN;
+    {
+        constexpr int TB = 4;  // entries per thread per batch of loads
+        for (int gk0 = t / BN; gk0 < GK; gk0 += TPCOL * TB) {
+            float ov[TB], mv[TB];
+#pragma unroll
+            for (int q = 0; q < TB; ++q) {
+                const int gk = gk0 + TPCOL * q;
+                const int g = (int)fdiv((uint32_t)gk, a.fd_K), k = gk - g * K;
+                const bool ok = cok && gk < GK;
+                const int64_t oi = ok ? obase + g * gstride + k : 0;
+                ov[q] = D::ld(off, oi);
+                mv[q] = MASK ? D::ld(mask, oi) : 1.0f;
+            }
+#pragma unroll
+            for (int q = 0; q < TB; ++q) {
+                const int gk = gk0 + TPCOL * q;
+                if (gk >= GK) break;
+                const int k = gk - (int)fdiv((uint32_t)gk, a.fd_K) * K;
+                Pos ps = {0, 0.0f};
+                if (cok) {
+                    int i0;
+                    split_position(ov[q], grid0 + k * p.dilation, i0, ps.f);
+                    ps.j = min(max(i0, -2), L_in);  // x~ reads zero at both neighbours beyond these bounds
+                    lo = min(lo, ps.j);
+                    hi = max(hi, ps.j);
+                }
+                s_tab[gk * BN + n] = ps;
+                if (MASK) s_m[gk * BN + n] = cok ? mv[q] : 0.0f;
+            }
+        }
+    }
+    __syncthreads();  // s_lo / s_hi initialised
+    if (win) {
+#pragma unroll
+        for (int z = 0; z < NSEG; ++z) {
+            int zl = (z == sg) ? lo : INT_MAX, zh = (z == sg) ? hi : INT_MIN;
+            for (int o = 32; o > 0; o >>= 1) {
+                zl = min(zl, __shfl_xor(zl, o));
+                zh = max(zh, __shfl_xor(zh, o));
+            }
+            if ((t & 63) == 0 && z < tl.nseg && zl <= zh) {
+                atomicMin(&s_lo[z], zl);
+                atomicMax(&s_hi[z], zh);
+            }
+        }
+    }
+    __syncthreads();
+    if (t == 0) {
+        int base = 0;
+        for (int z = 0; z < (win ? tl.nseg : 0); ++z) {
+            s_base[z] = base;
+            base += s_hi[z] + 2 - s_lo[z];
+        }
+        s_base[win ? tl.nseg : 0] = base;
+        // two elements of slack past the last window position (paired reads)
+        *s_win = win && base + 2 <= a.wt_max;
+    }
+    __syncthreads();
+    tl.win = *s_win;
+    tl.WT = tl.win ? s_base[tl.nseg] : 0;
+    // ---- pass 2 (windowed): left neighbour -> index into the tile's window row
+    if (tl.win && cok) {
+        const int shift = s_base[sg] - s_lo[sg];
+        for (int gk = t / BN; gk < GK; gk += TPCOL) s_tab[gk * BN + n].j += shift;
+    }
+    __syncthreads();  // position table complete
+
+}
+
+template <class Tr, bool MASK, int NCH, int SLOT>
+__global__ void __launch_bounds__(NTT) k_mfma(MfmaArgs a) {
+    using T = typename Tr::T;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    Pos *s_tab = (Pos *)smem;                   // [G*K][BN]
+    float *s_m = (float *)(smem + a.off_mask);  // [G*K][BN] if MASK
+    T *s_w = (T *)(smem + a.off_w);             // [2][BM][BK], swizzled
+    T *s_S = (T *)(smem + a.off_s);             // [2][BN][SLD]
+    float *s_x = (float *)(smem + a.off_x);     // [2][NCH][SLOT * NTS]
+    __shared__ int s_lo[NSEG], s_hi[NSEG], s_base[NSEG + 1];
+    __shared__ int s_win;
+    Tile tl;
+    setup_tile<Tr, MASK>(a, tl, s_tab, s_m, s_lo, s_hi, s_base, &s_win);
+    if (threadIdx.x < NTM) {
+        mfma_role<Tr, 0>(a, tl, s_w, s_S);
+    } else if (tl.win) {
+        sampler_role<Tr, MASK, true, NCH, SLOT>(a, tl, s_tab, s_m, s_S, s_x, s_lo, s_base);
+    } else {
+        sampler_role<Tr, MASK, false, 1, 1>(a, tl, s_tab, s_m, s_S, s_x, s_lo, s_base);
+    }
+}
+
+// ---- channel-block order ------------------------------------------------------------
+//
+// The reduction over r = (ci, k) may run in any order as long as the weight
+// tile and the sample tile agree.  In channel-block order a chunk of 32
+// reduction rows is CB consecutive input channels (ci = CB*cb + i) at
+// TPC = 32/CB consecutive taps (k = TPC*kb + t), row i*TPC + t; the chunks
+// run over taps (kb, inner) within channel blocks (cb, outer).  Then:
+//   * a sampler thread's 16 rows are 16/TPC channels at all TPC taps of the
+//     chunk and lie in one offset group, so it reads TPC (j, f) pairs (and
+//     mask values) per chunk from the position table and reuses each over
+//     its channels;
+//   * the x window of a channel block (CB rows covering every tap's reach)
+//     is staged once and serves all nkb chunks of the block.
+// The weights are read in the same order: straight from [C_out][C_in][K]
+// when a chunk row's taps are one aligned 16-byte word (DW), else from a copy
+// rearranged into [nkb][C_out][ncb][32] by k_weight_blocks.  Taps past K and
+// channels past C_in get zero weights.
+//
+// Window staging: a block's window is NL = CB*SLOT lines of NTS positions
+// (thread ts owns position ts of each line; a row holds WTM = SLOT*NTS
+// positions).  While the sampler works on block B it stages block B+1 in nkb
+// parts of LPP lines, one part per chunk: the loads of a part are issued in
+// one iteration and written to LDS at the start of the next, so their
+// latency hides behind the barrier.  Windows are double-buffered by block
+// parity.
+template <class Tr, bool MASK, bool WIN, int CB, int SLOT, int LPP>
+__device__ __forceinline__ void sampler_cb(const MfmaArgs &a, const Tile &tl, const Pos *s_tab,
+                                           const float *s_m, typename Tr::T *s_S, typename Tr::T *s_x,
+                                           const int *s_lo, const int *s_base) {
+    using D = typename Tr::D;
+    using T = typename Tr::T;
+    constexpr int BN = Geo<Tr>::BN, SLD = Tr::SLD;
+    constexpr int TPC = BK / CB;    // taps per chunk
+    constexpr int CPT = 16 / TPC;   // channels per sampler thread
+    constexpr int NL = CB * SLOT;   // staging lines per block
+    constexpr int WTM = SLOT * NTS;  // window row (elements)
+    constexpr int XBUF = CB * WTM;   // window buffer (elements)
+    constexpr bool BF = sizeof(T) == 2;
+    static_assert(BN == 128, "two sampler waves per 64 columns");
+    static_assert(LPP % SLOT == 0, "a part holds whole window rows");
+    const Params &p = a.p;
+    const int ts = threadIdx.x - NTM;  // 0 .. NTS-1
+    const int lane = ts % 64;
+    const int sw = __builtin_amdgcn_readfirstlane(ts / 64);
+    const int h = sw & 1;
+    const int col = 64 * (sw >> 1) + lane;
+    const int K = p.K, L_in = p.L_in, L_out = p.L_out, C_in = p.C_in;
+    const int nkb = a.nkb;
+    const T *__restrict__ x = (const T *)p.x;
+    const int i0 = 16 * h / TPC;  // this thread's first channel in a block
+
+    // Per slot: the x offset of its window position in channel 0 (clamped to
+    // a real element) and whether the position lies inside [0, L_in).
+    int64_t xoff[SLOT];
+    bool xval[SLOT];
+#pragma unroll
+    for (int q = 0; q < SLOT; ++q) {
+        const int jj = ts + NTS * q;
+        int64_t o = 0;
+        bool ok = false;
+        if (WIN && jj < tl.WT) {
+            int sg = 0;
+            while (sg + 1 < tl.nseg && s_base[sg + 1] <= jj) ++sg;
+            const int pos = s_lo[sg] + (jj - s_base[sg]);
+            ok = pos >= 0 && pos < L_in;
+            o = (int64_t)(tl.b_first + sg) * C_in * L_in + (ok ? pos : 0);
+        }
+        xoff[q] = o;
+        xval[q] = ok;
+    }
+    const int colg = (int)tl.n0 + col;
+    const T *xcol = x + (colg < a.N ? (int64_t)fdiv((uint32_t)colg, a.fd_Lout) * C_in * L_in : 0);
+
+    // ---- window staging
+    T xreg[LPP];
+    int pend_blk = 0, pend_l0 = NL;  // pending part: lines pend_l0 .. +LPP of block pend_blk
+    auto load_part = [&](int blk, int part) {
+        pend_blk = blk;
+        pend_l0 = part * LPP;
+        if (pend_l0 < NL) {  // uniform
+            const int ib = pend_l0 / SLOT;
+#pragma unroll
+            for (int n = 0; n < LPP; ++n) {
+                const int ci = min(blk * CB + ib + n / SLOT, C_in - 1);
+                xreg[n] = x[xoff[n % SLOT] + (int64_t)ci * L_in];
+            }
+        }
+    };
+    auto commit_part = [&]() {
+        if (pend_l0 < NL) {  // uniform
+            T *dx = s_x + (pend_blk & 1) * XBUF + (pend_l0 / SLOT) * WTM + ts;
+            const int cib = pend_blk * CB + pend_l0 / SLOT;
+#pragma unroll
+            for (int n = 0; n < LPP; ++n) {
+                const int q = n % SLOT;
+                if (pend_l0 + n < NL)  // uniform
+                    dx[(n / SLOT) * WTM + NTS * q] = (xval[q] && cib + n / SLOT < C_in) ? xreg[n] : (T)0;
+            }
+        }
+        pend_l0 = NL;
+    };
+    auto stage_block = [&](int blk) {
+        for (int part = 0; part * LPP < NL; ++part) {
+            load_part(blk, part);
+            commit_part();
+        }
+    };
+
+    // ---- the 16 samples (rows 16h .. 16h+15) of this lane's column for chunk u
+    auto sample = [&](int u) {
+        const int cb = (int)fdiv((uint32_t)u, a.fd_nkb), kb = u - cb * nkb;
+        const int g = (int)fdiv((uint32_t)min(cb * CB + i0, C_in - 1), a.fd_cpo);
+        const T *xw = s_x + (cb & 1) * XBUF + i0 * WTM;
+        float v[16];
+#pragma unroll
+        for (int tt = 0; tt < TPC; ++tt) {
+            const int k = min(kb * TPC + tt, K - 1);  // taps past K have zero weights
+            const int te = (g * K + k) * BN + col;
+            const Pos ps = s_tab[te];
+            const float mk = MASK ? s_m[te] : 1.0f;
+#pragma unroll
+            for (int ii = 0; ii < CPT; ++ii) {
+                float x0, x1;
+                if (WIN) {
+                    if constexpr (BF) {
+                        // the two neighbours from the aligned dword pair holding them
+                        const uint32_t *w32 = (const uint32_t *)(xw + ii * WTM) + (ps.j >> 1);
+                        const uint32_t pr = __builtin_amdgcn_alignbit(w32[1], w32[0], (ps.j & 1) * 16);
+                        x0 = __uint_as_float(pr << 16);
+                        x1 = __uint_as_float(pr & 0xffff0000u);
+                    } else {
+                        const float *rw = xw + ii * WTM + ps.j;
+                        x0 = rw[0];
+                        x1 = rw[1];
+                    }
+                } else {
+                    const T *rw = xcol + (int64_t)min(cb * CB + i0 + ii, C_in - 1) * L_in;
+                    const int j = ps.j;
+                    const float a0 = D::ld(rw, min(max(j, 0), L_in - 1));
+                    const float a1 = D::ld(rw, min(max(j + 1, 0), L_in - 1));
+                    x0 = (j >= 0 && j < L_in) ? a0 : 0.0f;
+                    x1 = (j + 1 >= 0 && j + 1 < L_in) ? a1 : 0.0f;
+                }
+                float val = fmaf(ps.f, x1 - x0, x0);
+                if (MASK) val *= mk;
+                v[ii * TPC + tt] = val;
+            }
+        }
+        Tr::store_b(s_S + (u & 1) * BN * SLD + col * SLD + 16 * h, v);
+    };
+
+    const int c0 = tl.c_begin, c1 = tl.c_end;
+    // Prologue: the windows of the blocks of chunks c0 and c0+1 in LDS; the
+    // parts of the following block that the steady state would already have
+    // staged, in LDS, and its next part loaded into registers.
+    if (WIN && c0 < c1) {
+        const int b0 = (int)fdiv((uint32_t)c0, a.fd_nkb);
+        stage_block(b0);
+        if (c0 + 1 < c1) {
+            const int b1 = (int)fdiv((uint32_t)(c0 + 1), a.fd_nkb), k1 = c0 + 1 - b1 * nkb;
+            if (b1 != b0) stage_block(b1);
+            if ((b1 + 1) * nkb < c1) {
+                for (int part = 0; part < k1; ++part) {
+                    load_part(b1 + 1, part);
+                    commit_part();
+                }
+                load_part(b1 + 1, k1);
+            }
+        }
+    }
+    __syncthreads();
+    if (c0 < c1) sample(c0);
+    __syncthreads();
+    for (int c = c0; c < c1; ++c) {
+        if (WIN) commit_part();  // loaded during the previous iteration
+        if (c + 1 < c1) sample(c + 1);
+        if (WIN && c + 2 < c1) {
+            // part kb(c+2) of the block after chunk c+2's, if this workgroup uses it
+            const int b2 = (int)fdiv((uint32_t)(c + 2), a.fd_nkb);
+            if ((b2 + 1) * nkb < c1) load_part(b2 + 1, c + 2 - b2 * nkb);
+        }
+        __syncthreads();
+    }
+}
+
+template <class Tr, bool MASK, int CB, int SLOT, int LPP, bool DW>
+__global__ void __launch_bounds__(NTT) k_mfma_cb(MfmaArgs a) {
+    using T = typename Tr::T;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    Pos *s_tab = (Pos *)smem;                   // [G*K][BN]
+    float *s_m = (float *)(smem + a.off_mask);  // [G*K][BN] if MASK
+    T *s_w = (T *)(smem + a.off_w);             // [2][BM][BK], swizzled
+    T *s_S = (T *)(smem + a.off_s);             // [2][BN][SLD]
+    T *s_x = (T *)(smem + a.off_x);             // [2][CB][SLOT * NTS]
+    __shared__ int s_lo[NSEG], s_hi[NSEG], s_base[NSEG + 1];
+    __shared__ int s_win;
+    Tile tl;
+    setup_tile<Tr, MASK>(a, tl, s_tab, s_m, s_lo, s_hi, s_base, &s_win);
+    if (threadIdx.x < NTM) {
+        mfma_role<Tr, DW ? 2 : 1>(a, tl, s_w, s_S);
+    } else if (tl.win) {
+        sampler_cb<Tr, MASK, true, CB, SLOT, LPP>(a, tl, s_tab, s_m, s_S, s_x, s_lo, s_base);
+    } else {
+        sampler_cb<Tr, MASK, false, CB, 1, 4>(a, tl, s_tab, s_m, s_S, s_x, s_lo, s_base);
+    }
+}
+
+// Weights [C_out][C_in][K] -> chunk rows [nkb][C_out][ncb][32]: element
+// (kb, m, cb, i*TPC + t) = W[m][CB*cb + i][TPC*kb + t], zero past C_in or K.
+// A plain copy of the stored bits; one workgroup per destination row.
+template <class T>
+__global__ void __launch_bounds__(256) k_weight_blocks(const T *__restrict__ w, T *__restrict__ wb, int C_out,
+                                                       int C_in, int K, int tpc_log2, int ncb) {
+    const int row = blockIdx.x;  // kb * C_out + m
+    const int kb = row / C_out, m = row - kb * C_out;
+    const int len = ncb * BK, cbs = BK >> tpc_log2, tmask = (1 << tpc_log2) - 1;
+    const T *__restrict__ wm = w + (int64_t)m * C_in * K;
+    T *__restrict__ dst = wb + (int64_t)row * len;
+    for (int j = threadIdx.x; j < len; j += 256) {
+        const int r = j & (BK - 1);
+        const int ci = (j >> 5) * cbs + (r >> tpc_log2), k = (kb << tpc_log2) + (r & tmask);
+        dst[j] = (ci < C_in && k < K) ? wm[ci * K + k] : (T)0;
+    }
+}
+
+// Sum of the split partial tiles (in split order), plus bias, into out.
+// One thread per 4-float vector of a partial tile: vector (q4, t) holds what
+// MFMA thread t of every split's workgroup kept in its register group q4, so
+// the register-order layout maps back to (row, column) exactly as in the
+// direct epilogue.
+template <class Tr>
+__global__ void __launch_bounds__(256) k_split_reduce(MfmaArgs a) {
+    using D = typename Tr::D;
+    using T = typename Tr::T;
+    constexpr int MB = Tr::MB, NB = Tr::NB, BM = Geo<Tr>::BM, BN = Geo<Tr>::BN;
+    constexpr int VPT = BM * BN / 4;  // vectors per tile
+    const Params &p = a.p;
+    const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
+    const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (v >= tiles * VPT) return;
+    const int tile = (int)(v / VPT);
+    const int rem = (int)(v - (int64_t)tile * VPT);
+    const int q4 = rem / NTM, t = rem % NTM;
+    const int tm = tile / a.tiles_n, tn = tile % a.tiles_n;
+    const int wv = t / 64, lane = t % 64, li = lane % 32, lh = lane / 32;
+    const f4 *part = (const f4 *)a.partials + v;
+    f4 tot = part[0];
+    for (int s2 = 1; s2 < a.splits; ++s2) tot += part[(int64_t)s2 * tiles * VPT];
+    const int mb = q4 / (NB * 4), nb = (q4 / 4) % NB, qq = (q4 & 3) * 4;
+    const int col = tn * BN + 32 * (NB * wv + nb) + li;
+    if (col >= a.N) return;
+    const int L_out = p.L_out, M = p.C_out;
+    const int b = (int)fdiv((uint32_t)col, a.fd_Lout);
+    const int l = col - b * L_out;
+    const T *__restrict__ bias = (const T *)p.bias;
+    T *ob = (T *)p.out + (int64_t)b * M * L_out + l;
+#pragma unroll
+    for (int z = 0; z < 4; ++z) {
+        const int q = qq + z;
+        const int row = tm * BM + 32 * mb + 8 * (q >> 2) + 4 * lh + (q & 3);
+        if (row < M) D::st(ob, (int64_t)row * L_out, tot[z] + (bias ? D::ld(bias, row) : 0.0f));
+    }
+}
+
+
+// ---- launch ----------------------------------------------------------------------
+
+// Window staging shapes the sampler role is compiled for: (channel rows per
+// chunk, 256-element slots per row).  The plan picks the smallest that holds a
+// chunk's channel rows and the tiles' expected window extent.
+struct Combo {
+    int nch, slot;
+};
+constexpr Combo kCombos[] = {{2, 1}, {2, 2}, {3, 2}, {5, 2}, {8, 2}, {12, 1}, {12, 2}, {16, 1}};
+constexpr int kNumCombos = sizeof(kCombos) / sizeof(kCombos[0]);
+
+template <class Tr, bool MASK, int I>
+void launch_combo(int idx, const MfmaArgs &a, dim3 grid, size_t lds, hipStream_t stream) {
+    if constexpr (I < kNumCombos) {
+        if (idx == I)
+            hipLaunchKernelGGL((k_mfma<Tr, MASK, kCombos[I].nch, kCombos[I].slot>), grid, dim3(NTT), lds, stream, a);
+        else
+            launch_combo<Tr, MASK, I + 1>(idx, a, grid, lds, stream);
+    }
+}
+
+// Staging shapes of the channel-block kernel: (channels per block, window
+// slots of NTS positions, lines staged per chunk, weights read directly).
+struct CbCombo {
+    int cb, slot, lpp;
+    bool dw;
+};
+constexpr CbCombo kCbCombos[] = {
+    {8, 1, 4, false},   {8, 1, 8, false},   {8, 2, 4, false},   {8, 2, 8, false},   {8, 2, 16, false},
+    {16, 1, 4, false},  {16, 1, 8, false},  {16, 1, 16, false}, {16, 2, 4, false},  {16, 2, 8, false},
+    {16, 2, 16, false}, {16, 2, 32, false}, {32, 1, 4, false},  {32, 1, 8, false},  {32, 1, 16, false},
+    {32, 1, 32, false}, {32, 2, 4, false},  {32, 2, 8, false},  {32, 2, 16, false}, {32, 2, 32, false},
+    {8, 1, 4, true},    {8, 1, 8, true},    {8, 2, 4, true},    {8, 2, 8, true},    {8, 2, 16, true}};
+constexpr int kNumCbCombos = sizeof(kCbCombos) / sizeof(kCbCombos[0]);
+
+template <class Tr, bool MASK, int I>
+void launch_cb_combo(int idx, const MfmaArgs &a, dim3 grid, size_t lds, hipStream_t stream) {
+    if constexpr (I < kNumCbCombos) {
+        constexpr CbCombo c = kCbCombos[I];
+        if constexpr (!c.dw || sizeof(typename Tr::T) == 4) {  // direct weights: fp32 only
+            if (idx == I) {
+                hipLaunchKernelGGL((k_mfma_cb<Tr, MASK, c.cb, c.slot, c.lpp, c.dw>), grid, dim3(NTT), lds, stream, a);
+                return;
+            }
+        }
+        launch_cb_combo<Tr, MASK, I + 1>(idx, a, grid, lds, stream);
+    }
+}
+
+template <class Tr, bool MASK>
+hipError_t launch_for(const Params &p, const MfmaPlan &pl, hipStream_t stream) {
+    using T = typename Tr::T;
+    MfmaArgs a;
+    a.p = p;
+    a.fd_K = make_fastdiv((uint32_t)p.K);
+    a.fd_cpo = make_fastdiv((uint32_t)p.cpo);
+    a.fd_Lout = make_fastdiv((uint32_t)p.L_out);
+    a.tiles_m = pl.tiles_m;
+    a.tiles_n = pl.tiles_n;
+    a.splits = pl.splits;
+    a.chunks = pl.chunks;
+    a.N = (int64_t)p.B * p.L_out;
+    a.wt_max = pl.wt_max;
+    a.off_mask = pl.off_mask;
+    a.off_w = pl.off_w;
+    a.off_s = pl.off_s;
+    a.off_x = pl.off_x;
+    const int vec_elems = 16 / (int)sizeof(T);
+    a.vec_w = (p.Kred % vec_elems == 0) && (((uintptr_t)p.w & 15) == 0);
+    a.wb = nullptr;
+    a.ncb = pl.ncb;
+    a.nkb = pl.nkb;
+    a.fd_nkb = make_fastdiv((uint32_t)(pl.nkb > 0 ? pl.nkb : 1));
+    a.partials = pl.splits > 1 ? (float *)((char *)p.ws + pl.wb_bytes) : nullptr;
+    const dim3 grid((unsigned)pl.blocks);
+    if (pl.blocked) {
+        int variant = pl.variant;
+        if (pl.variant_dw >= 0 && ((uintptr_t)p.w & 15) == 0) variant = pl.variant_dw;
+        if (variant < 0 || variant >= kNumCbCombos) return hipErrorInvalidValue;
+        if (!kCbCombos[variant].dw) {
+            T *wb = (T *)p.ws;
+            a.wb = wb;
+            int tpc_log2 = 0;
+            while ((BK >> tpc_log2) > pl.cb) ++tpc_log2;
+            hipLaunchKernelGGL((k_weight_blocks<T>), dim3((unsigned)(pl.nkb * p.C_out)), dim3(256), 0, stream,
+                               (const T *)p.w, wb, p.C_out, p.C_in, p.K, tpc_log2, pl.ncb);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        launch_cb_combo<Tr, MASK, 0>(variant, a, grid, pl.lds_bytes, stream);
+    } else {
+        if (pl.variant < 0 || pl.variant >= kNumCombos) return hipErrorInvalidValue;
+        launch_combo<Tr, MASK, 0>(pl.variant, a, grid, pl.lds_bytes, stream);
+    }
+    if (pl.splits > 1) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t tiles = (int64_t)pl.tiles_m * pl.tiles_n;
+        const int64_t vecs = tiles * (Geo<Tr>::BM * Geo<Tr>::BN / 4);
+        hipLaunchKernelGGL((k_split_reduce<Tr>), dim3((unsigned)((vecs + 255) / 256)), dim3(256), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace dc1d

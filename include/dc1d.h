@@ -79,7 +79,8 @@ typedef enum dc1d_status {
                                beyond the supported limits (see dc1d_forward) */
     DC1D_ERR_BAD_DTYPE = 4, /* unsupported dtype, or dtypes mixed within a call */
     DC1D_ERR_ALIAS = 5,     /* out overlaps an input */
-    DC1D_ERR_WORKSPACE = 6, /* workspace NULL or smaller than dc1d_workspace_bytes() */
+    DC1D_ERR_WORKSPACE = 6, /* workspace NULL, smaller than dc1d_workspace_bytes(), or not
+                               256-byte aligned */
     DC1D_ERR_DEVICE = 7,    /* no current HIP device, or it is not a gfx950 */
     DC1D_ERR_LAUNCH = 8     /* the kernel launch reported an error */
 } dc1d_status;
@@ -107,8 +108,7 @@ int64_t dc1d_output_length(int64_t L_in, int64_t K, int64_t stride, int64_t padd
  * the current device (0 when the chosen kernels need none).  Only the
  * descriptors' dtype, ndim and shape are read; data pointers may be NULL.
  * The same validation as dc1d_forward applies (except pointers and
- * aliasing).  The workspace holds split-reduction partial sums; see
- * dc1d_forward.
+ * aliasing).  What the workspace holds is described at dc1d_forward.
  */
 int dc1d_workspace_bytes(const dc1d_tensor *x, const dc1d_tensor *offsets,
                          const dc1d_tensor *mask_or_null, const dc1d_tensor *weight,
@@ -130,12 +130,13 @@ int dc1d_workspace_bytes(const dc1d_tensor *x, const dc1d_tensor *offsets,
  * offset_groups must equal offsets->shape[1] (a double entry, checked).
  * stream is a hipStream_t (NULL: the null stream).
  *
- * workspace: device memory of at least dc1d_workspace_bytes() bytes, or NULL
- * with workspace_bytes 0 when that is 0.  It carries the fp32 partial sums of
- * a split reduction from the main kernel to a second kernel enqueued right
- * after it on the same stream; it needs no initialisation and holds nothing
- * between calls.  Calls in flight at the same time must not share a
- * workspace.
+ * workspace: device memory of at least dc1d_workspace_bytes() bytes, aligned
+ * to 256 bytes, or NULL with workspace_bytes 0 when that is 0.  It holds the
+ * weights rearranged into the kernel's reduction order (written by a first
+ * kernel of the call) and the fp32 partial sums of a split reduction, passed
+ * from the main kernel to a last one on the same stream; it needs no
+ * initialisation and holds nothing between calls.  Calls in flight at the
+ * same time must not share a workspace.
  *
  * Limits (DC1D_ERR_BAD_SHAPE beyond them): L_in + padding <= 2^29,
  * dilation*(K-1) <= 2^29, L_out*stride <= 2^30, C_in*K <= 2^30,

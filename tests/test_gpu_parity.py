@@ -108,6 +108,12 @@ def _shape_cases():
         (1, 6, 6, 5000, 3, 1, 1, 1, 6, 6, "f32", False, 2000.0),    # depthwise, offsets too wide for a window
         (2, 64, 96, 77, 3, 1, 1, 1, 1, 2, "bf16", True, 3.0),       # bf16 dense
         (2, 32, 32, 300, 5, 1, 2, 2, 32, 32, "bf16", False, 4.0),   # bf16 depthwise
+        (1, 64, 80, 400, 6, 1, 0, 8, 1, 1, "f32", False, 5.0),      # channel blocks of 16 (wide window)
+        (2, 30, 64, 90, 3, 1, 1, 1, 1, 3, "bf16", True, 2.0),       # bf16, ci-major order (10 ch / group)
+        (2, 36, 64, 90, 3, 1, 1, 1, 1, 3, "bf16", True, 2.0),       # bf16 channel blocks of 8 (12 ch / group)
+        (1, 48, 40, 700, 5, 1, 2, 1, 1, 6, "bf16", False, 3.0),     # bf16 channel blocks of 16
+        (3, 100, 72, 150, 3, 2, 1, 1, 1, 1, "f32", True, 2.5),      # C_in not a multiple of the block
+        (1, 64, 64, 600, 3, 1, 1, 1, 1, 1, "f32", False, 2.0),      # f32 K=3, long rows
     ]
     for i, (B, C_in, C_out, L_in, K, s, p, d, groups, G, dt, mask, sc) in enumerate(spec):
         L_out = oracle.output_length(L_in, K, s, p, d)
@@ -121,6 +127,38 @@ def _shape_cases():
 @pytest.mark.parametrize("w", _shape_cases(), ids=lambda w: w.name)
 def test_ragged_shapes(w):
     run_case(w, seed=3)
+
+
+def test_ragged_shapes_reach_every_kernel():
+    """The shapes above run every kernel family and staging order."""
+    names = set()
+    for w in _shape_cases():
+        g = to_dev(inputs.make_inputs(w, seed=3))
+        pl = dc1d.plan(g["x"], g["offsets"], g["weight"], g["bias"], g["mask"], stride=w.stride,
+                       padding=w.padding, dilation=w.dilation, groups=w.groups)
+        names.add(pl["kernel"])
+    # (fp32 blocks of 32 channels need more LDS than a workgroup has next to
+    # the fp32 weight and sample tiles, so the planner never picks them)
+    want = {"direct", "depthwise", "mfma_f32", "mfma_bf16", "mfma_f32_cb8", "mfma_f32_cb16", "mfma_bf16_cb8",
+            "mfma_bf16_cb16", "mfma_bf16_cb32"}
+    assert want <= names, sorted(want - names)
+
+
+def test_weights_read_in_place_or_rearranged():
+    """fp32 blocks of 8 channels x 4 taps read the weights in place when they
+    are 16-byte aligned and from a rearranged copy otherwise; same results."""
+    w = inputs.custom("cb8", B=2, C_in=64, C_out=96, L_in=128, K=16, dilation=3, L_out=83,
+                      off_dist=("normal", 0.0, 1.0))
+    t = inputs.make_inputs(w, seed=5)
+    g = to_dev(t)
+    assert dc1d.plan(g["x"], g["offsets"], g["weight"], g["bias"], None, dilation=3)["kernel"] == "mfma_f32_cb8"
+    ref = oracle_forward(w, t)
+    check(w, gpu_forward(w, g), ref, "aligned weights")
+    buf = torch.empty(g["weight"].numel() + 1, dtype=torch.float32, device=DEV)
+    wv = buf[1:].view(g["weight"].shape)
+    wv.copy_(g["weight"])
+    assert wv.data_ptr() % 16 != 0
+    check(w, gpu_forward(w, dict(g, weight=wv)), ref, "misaligned weights")
 
 
 # ---- positions: bit-exact ---------------------------------------------------
@@ -234,6 +272,13 @@ def test_workspace_too_small_is_rejected():
     small = torch.zeros(need - 256, dtype=torch.uint8, device=DEV)
     with pytest.raises(ValueError):
         gpu_forward(w, t, workspace=small)
+    # big enough but not 256-byte aligned
+    big = torch.zeros(need + 512, dtype=torch.uint8, device=DEV)
+    with pytest.raises(ValueError):
+        gpu_forward(w, t, workspace=big[16:])
+    out = gpu_forward(w, t, workspace=big[256:])
+    torch.cuda.synchronize()
+    check(w, out, oracle_forward(w, inputs.make_inputs(w)))
 
 
 # ---- full sizes, sampled outputs -------------------------------------------
