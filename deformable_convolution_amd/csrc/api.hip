@@ -149,7 +149,7 @@ Plan make_plan(const Params &p, const DeviceInfo &dev) {
         pl.splits = pl.mfma.splits;
         return pl;
     }
-    if (p.cpg == 1) {
+    if (p.cpg == 1 && plan_depthwise(p).blocks < ((int64_t)1 << 31)) {
         pl.kernel = kDepthwise;
         pl.dw = plan_depthwise(p);
         pl.name = "depthwise";

@@ -108,153 +108,193 @@ hipError_t launch_direct(const Params &p, hipStream_t stream) {
 // ---------------------------------------------------------------------------
 // depthwise: C_in / groups == 1.
 //
-// One block computes LT consecutive outputs l of one (b, co).  Its offsets
-// (and mask) for those outputs are one contiguous run of LT*K values in HBM
-// ([B, G, L_out, K] with K fastest); the block streams that run into LDS
-// with coalesced loads, bounds the x window the positions can touch from the
-// run's smallest and largest offset, stages that window of the input row in
-// LDS with zero fill outside [0, L_in), and then interpolates from LDS.  When
-// the offsets spread wider than the window capacity, the block gathers x from
-// global memory instead (same arithmetic, bounds-checked loads).
+// A streaming kernel: the bytes are the offsets (K per output), the output
+// and one read of x; every output costs K interpolations.  A block computes
+// LT = 256*OPT consecutive outputs l of one (b, co); thread t owns outputs
+// l0 + OPT*t .. +OPT-1, whose OPT*K offsets (and mask values) are one
+// contiguous run that it loads straight into registers with 4-element vector
+// loads.  The input row is staged in LDS over a fixed window: the tile's
+// grid span plus kDwMargin positions on each side, zero outside [0, L_in).
+// Samples whose offset moves them outside the window read x from global
+// memory (bounds-checked), so any offset is served and the window needs no
+// pass over the offsets first.
 
 constexpr int kDwThreads = 256;
+constexpr int kDwOpt = 4;      // outputs per thread
+constexpr int kDwMargin = 64;  // window margin per side (input positions)
 
+// Four consecutive elements as floats (16-byte fp32 or 8-byte bf16 load).
 template <class D>
-__global__ void __launch_bounds__(kDwThreads) k_depthwise(Params p, int LT, int WCAP, int tiles_l,
-                                                          int64_t n_blocks) {
-    using T = typename D::T;
-    extern __shared__ float smem[];
-    const int K = p.K;
-    float *s_w = smem;                           // K
-    float *s_off = s_w + ((K + 3) & ~3);         // LT*K
-    float *s_mask = s_off + LT * K;              // LT*K (if mask)
-    float *s_x = s_mask + (p.mask ? LT * K : 0); // WCAP
-    __shared__ float s_red[2][kDwThreads / 64];
+__device__ __forceinline__ void ld4(const typename D::T *p, float (&v)[4]);
+template <>
+__device__ __forceinline__ void ld4<F32>(const float *p, float (&v)[4]) {
+    const float4 q = *(const float4 *)p;
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+}
+template <>
+__device__ __forceinline__ void ld4<BF16>(const uint16_t *p, float (&v)[4]) {
+    const uint2 q = *(const uint2 *)p;
+    v[0] = __uint_as_float(q.x << 16); v[1] = __uint_as_float(q.x & 0xffff0000u);
+    v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xffff0000u);
+}
+template <class D>
+__device__ __forceinline__ void st4(typename D::T *p, const float (&v)[4]);
+template <>
+__device__ __forceinline__ void st4<F32>(float *p, const float (&v)[4]) {
+    *(float4 *)p = float4{v[0], v[1], v[2], v[3]};
+}
+template <>
+__device__ __forceinline__ void st4<BF16>(uint16_t *p, const float (&v)[4]) {
+    *(uint2 *)p = uint2{(uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16),
+                        (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16)};
+}
 
+// KT: compile-time K (0: any K, read per tap).
+template <class D, int KT>
+__global__ void __launch_bounds__(kDwThreads) k_depthwise(Params p, int WIN, int tiles_l) {
+    using T = typename D::T;
+    constexpr int OPT = kDwOpt;
+    constexpr int NV = KT > 0 ? OPT * KT : 1;  // offsets held per thread
+    extern __shared__ float s_x[];               // WIN input positions from lo
+    const int K = KT > 0 ? KT : p.K;
+    const int t = threadIdx.x;
+    const int tile = blockIdx.x % tiles_l;
+    const int row = blockIdx.x / tiles_l;  // b * C_out + co
+    const int co = row % p.C_out, b = row / p.C_out;
+    const int ci = co / p.opg;  // cpg == 1: the conv group index is the input channel
+    const int g = ci / p.cpo;
+    const int l0 = tile * (kDwThreads * OPT);
+    const T *__restrict__ xrow = (const T *)p.x + ((int64_t)b * p.C_in + ci) * p.L_in;
     const T *__restrict__ off = (const T *)p.off;
     const T *__restrict__ mask = (const T *)p.mask;
-    const int t = threadIdx.x;
+    const int L_in = p.L_in;
+    const int lo = l0 * p.stride - p.padding - kDwMargin;
 
-    for (int64_t blk = blockIdx.x; blk < n_blocks; blk += gridDim.x) {
-        int64_t rest = blk;
-        const int tile = (int)(rest % tiles_l);
-        rest /= tiles_l;
-        const int co = (int)(rest % p.C_out);
-        const int b = (int)(rest / p.C_out);
-        const int ci = co / p.opg;  // cpg == 1: the conv group index is the input channel
-        const int g = ci / p.cpo;
-        const int l0 = tile * LT;
-        const int nl = min(LT, p.L_out - l0);
-        const T *__restrict__ xrow = (const T *)p.x + ((int64_t)b * p.C_in + ci) * p.L_in;
-        const int64_t e0 = (((int64_t)b * p.G + g) * p.L_out + l0) * K;
-
-        __syncthreads();  // LDS reuse across loop iterations
-        float vmin = kOffsetClamp, vmax = -kOffsetClamp;
-        for (int j = t; j < nl * K; j += kDwThreads) {
-            float v = D::ld(off, e0 + j);
-            v = fminf(fmaxf(v, -kOffsetClamp), kOffsetClamp);
-            s_off[j] = v;
-            vmin = fminf(vmin, v);
-            vmax = fmaxf(vmax, v);
-        }
-        if (mask)
-            for (int j = t; j < nl * K; j += kDwThreads) s_mask[j] = D::ld(mask, e0 + j);
-        for (int j = t; j < K; j += kDwThreads) s_w[j] = D::ld((const T *)p.w, (int64_t)co * K + j);
-
-        // block min / max of the offsets
-        for (int o = 32; o > 0; o >>= 1) {
-            vmin = fminf(vmin, __shfl_xor(vmin, o));
-            vmax = fmaxf(vmax, __shfl_xor(vmax, o));
-        }
-        if ((t & 63) == 0) {
-            s_red[0][t >> 6] = vmin;
-            s_red[1][t >> 6] = vmax;
-        }
-        __syncthreads();
-        vmin = s_red[0][0];
-        vmax = s_red[1][0];
+    // x window (WIN == 0: every sample reads global memory)
+    for (int j = t; j < WIN; j += kDwThreads) {
+        const int i = lo + j;
+        s_x[j] = (i >= 0 && i < L_in) ? D::ld(xrow, i) : 0.0f;
+    }
+    // this thread's offsets and mask values
+    const int lt = l0 + OPT * t;
+    const int nvalid = min(OPT, p.L_out - lt);  // may be <= 0
+    const int64_t e0 = (((int64_t)b * p.G + g) * p.L_out + lt) * K;
+    float ov[NV], mv[NV];
+    if (KT > 0) {
+        const bool vec = nvalid == OPT && (((uintptr_t)(off + e0) & (4 * sizeof(T) - 1)) == 0) &&
+                         (!mask || (((uintptr_t)(mask + e0) & (4 * sizeof(T) - 1)) == 0));
+        if (vec) {
 #pragma unroll
-        for (int q = 1; q < kDwThreads / 64; ++q) {
-            vmin = fminf(vmin, s_red[0][q]);
-            vmax = fmaxf(vmax, s_red[1][q]);
-        }
-        // Every left neighbour i0 of this block lies in [lo_b, hi_b]; clamped
-        // to [-2, L_in] (where both neighbours read zero outside the
-        // sequence) it lies in [lo, hi].
-        const int lo_b = l0 * p.stride - p.padding + (int)floorf(vmin);
-        const int hi_b = (l0 + nl - 1) * p.stride - p.padding + (K - 1) * p.dilation + (int)floorf(vmax);
-        const int lo = min(max(lo_b, -2), p.L_in);
-        const int hi = min(max(hi_b, -2), p.L_in);
-        const int W = hi - lo + 2;  // window elements x~(lo .. hi + 1)
-        const bool windowed = (W <= WCAP);
-        if (windowed) {
-            for (int j = t; j < W; j += kDwThreads) {
-                const int i = lo + j;
-                s_x[j] = (i >= 0 && i < p.L_in) ? D::ld(xrow, i) : 0.0f;
-            }
-        }
-        __syncthreads();
-
-        T *__restrict__ out = (T *)p.out + ((int64_t)b * p.C_out + co) * p.L_out;
-        const float bias = p.bias ? D::ld((const T *)p.bias, co) : 0.0f;
-        for (int ll = t; ll < nl; ll += kDwThreads) {
-            const int l = l0 + ll;
-            const int base0 = l * p.stride - p.padding;
-            float acc = 0.0f;
-            for (int k = 0; k < K; ++k) {
-                int i0;
-                float f;
-                split_position(s_off[ll * K + k], base0 + k * p.dilation, i0, f);
-                float x0, x1;
-                if (windowed) {
-                    int j = min(max(i0, -2), p.L_in) - lo;
-                    j = min(max(j, 0), W - 2);
-                    x0 = s_x[j];
-                    x1 = s_x[j + 1];
-                } else {
-                    x0 = (i0 >= 0 && i0 < p.L_in) ? D::ld(xrow, i0) : 0.0f;
-                    x1 = (i0 + 1 >= 0 && i0 + 1 < p.L_in) ? D::ld(xrow, i0 + 1) : 0.0f;
+            for (int c = 0; c < NV / 4; ++c) {
+                float q[4];
+                ld4<D>(off + e0 + 4 * c, q);
+#pragma unroll
+                for (int z = 0; z < 4; ++z) ov[4 * c + z] = q[z];
+                if (mask) {
+                    ld4<D>(mask + e0 + 4 * c, q);
+#pragma unroll
+                    for (int z = 0; z < 4; ++z) mv[4 * c + z] = q[z];
                 }
-                float v = fmaf(f, x1 - x0, x0);
-                if (mask) v *= s_mask[ll * K + k];
-                acc = fmaf(s_w[k], v, acc);
             }
-            D::st(out, l, acc + bias);
+        } else {
+#pragma unroll
+            for (int q = 0; q < NV; ++q) {
+                const bool ok = q < nvalid * K;
+                ov[q] = ok ? D::ld(off, e0 + q) : 0.0f;
+                mv[q] = (ok && mask) ? D::ld(mask, e0 + q) : 1.0f;
+            }
         }
+    }
+    __syncthreads();
+    if (nvalid <= 0) return;
+
+    const T *__restrict__ wrow = (const T *)p.w + (int64_t)co * K;
+    const float bias = p.bias ? D::ld((const T *)p.bias, co) : 0.0f;
+    float res[OPT];
+#pragma unroll
+    for (int o = 0; o < OPT; ++o) {
+        const int l = lt + o;
+        const int base0 = l * p.stride - p.padding;
+        float acc = 0.0f;
+        for (int k = 0; k < K; ++k) {  // unrolled when K is a constant
+            float ofs, m = 1.0f;
+            if (KT > 0) {
+                ofs = ov[o * KT + k];
+                if (mask) m = mv[o * KT + k];
+            } else {
+                const bool ok = o < nvalid;
+                ofs = ok ? D::ld(off, e0 + o * K + k) : 0.0f;
+                if (mask) m = ok ? D::ld(mask, e0 + o * K + k) : 0.0f;
+            }
+            int i0;
+            float f;
+            split_position(ofs, base0 + k * p.dilation, i0, f);
+            const int j = i0 - lo;
+            float x0, x1;
+            if ((unsigned)j < (unsigned)(WIN - 1)) {
+                x0 = s_x[j];
+                x1 = s_x[j + 1];
+            } else {
+                x0 = (i0 >= 0 && i0 < L_in) ? D::ld(xrow, i0) : 0.0f;
+                x1 = (i0 + 1 >= 0 && i0 + 1 < L_in) ? D::ld(xrow, i0 + 1) : 0.0f;
+            }
+            float v = fmaf(f, x1 - x0, x0);
+            if (mask) v *= m;
+            acc = fmaf(D::ld(wrow, k), v, acc);
+        }
+        res[o] = acc + bias;
+    }
+    T *__restrict__ out = (T *)p.out + (int64_t)row * p.L_out + lt;
+    if (nvalid == OPT && ((uintptr_t)out & (4 * sizeof(T) - 1)) == 0) {
+        st4<D>(out, res);
+    } else {
+#pragma unroll
+        for (int o = 0; o < OPT; ++o)
+            if (o < nvalid) D::st(out, o, res[o]);
     }
 }
 
 DepthwisePlan plan_depthwise(const Params &p) {
     DepthwisePlan pl;
-    // outputs per block: as many as keep the offsets (+ mask) run and the x
-    // window within ~48 KB of LDS, a multiple of the block size, at most 1024.
-    const int per_out = p.K * (p.mask ? 2 : 1) * 4;
-    int LT = 1024;
-    while (LT > kDwThreads && (size_t)LT * per_out > 32768) LT -= kDwThreads;
-    if (LT > p.L_out) LT = ((p.L_out + kDwThreads - 1) / kDwThreads) * kDwThreads;
-    // window: the taps' grid span plus a margin of 512 for the offsets' spread
-    int64_t span = (int64_t)(LT - 1) * p.stride + (int64_t)(p.K - 1) * p.dilation + 2;
-    int64_t wcap = span + 512;
-    if (wcap > 8192) wcap = 8192;
+    const int LT = kDwThreads * kDwOpt;
+    // window: the tile's grid span, both neighbours and the margins, in
+    // whole 64-element lines, at most 12 K positions (48 KB); wider spans
+    // gather from global memory
+    int64_t win = (int64_t)(LT - 1) * p.stride + (int64_t)(p.K - 1) * p.dilation + 2 + 2 * kDwMargin;
+    win = (win + 63) / 64 * 64;
+    if (win > 12288) win = 0;
     pl.outputs_per_block = LT;
-    pl.window = (int)wcap;
-    pl.lds_bytes = (size_t)(((p.K + 3) & ~3) * 4) + (size_t)LT * per_out + (size_t)wcap * 4;
-    const int tiles_l = (p.L_out + LT - 1) / LT;
-    pl.blocks = (int64_t)tiles_l * p.C_out * p.B;
+    pl.window = (int)win;
+    pl.lds_bytes = (size_t)win * 4;
+    const int64_t tiles_l = (p.L_out + LT - 1) / LT;
+    pl.blocks = tiles_l * p.C_out * p.B;
     return pl;
+}
+
+template <class D>
+static hipError_t launch_dw(const Params &p, const DepthwisePlan &pl, hipStream_t stream) {
+    const int tiles_l = (p.L_out + pl.outputs_per_block - 1) / pl.outputs_per_block;
+    const dim3 grid((unsigned)pl.blocks), block(kDwThreads);
+    switch (p.K) {
+#define DC1D_DW(KK) \
+    case KK: hipLaunchKernelGGL((k_depthwise<D, KK>), grid, block, pl.lds_bytes, stream, p, pl.window, tiles_l); break;
+        DC1D_DW(1)
+        DC1D_DW(2)
+        DC1D_DW(3)
+        DC1D_DW(4)
+        DC1D_DW(5)
+        DC1D_DW(7)
+        DC1D_DW(9)
+#undef DC1D_DW
+        default:
+            hipLaunchKernelGGL((k_depthwise<D, 0>), grid, block, pl.lds_bytes, stream, p, pl.window, tiles_l);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_depthwise(const Params &p, const DepthwisePlan &pl, hipStream_t stream) {
     if (pl.blocks == 0) return hipSuccess;
-    const int tiles_l = (p.L_out + pl.outputs_per_block - 1) / pl.outputs_per_block;
-    const unsigned grid = (unsigned)(pl.blocks < (1 << 30) ? pl.blocks : (1 << 30));
-    if (p.dtype == kF32)
-        hipLaunchKernelGGL(k_depthwise<F32>, dim3(grid), dim3(kDwThreads), pl.lds_bytes, stream, p,
-                           pl.outputs_per_block, pl.window, tiles_l, pl.blocks);
-    else
-        hipLaunchKernelGGL(k_depthwise<BF16>, dim3(grid), dim3(kDwThreads), pl.lds_bytes, stream, p,
-                           pl.outputs_per_block, pl.window, tiles_l, pl.blocks);
-    return hipGetLastError();
+    return p.dtype == kF32 ? launch_dw<F32>(p, pl, stream) : launch_dw<BF16>(p, pl, stream);
 }
 
 }  // namespace dc1d
