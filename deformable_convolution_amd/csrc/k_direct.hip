@@ -112,7 +112,7 @@ hipError_t launch_direct(const Params &p, hipStream_t stream) {
 // and one read of x; every output costs K interpolations.  A block computes
 // LT = 256*OPT consecutive outputs l of one (b, co); thread t owns outputs
 // l0 + OPT*t .. +OPT-1, whose OPT*K offsets (and mask values) are one
-// contiguous run that it loads straight into registers with 4-element vector
+// contiguous run that it loads straight into registers with 2- or 4-element vector
 // loads.  The input row is staged in LDS over a fixed window: the tile's
 // grid span plus kDwMargin positions on each side, zero outside [0, L_in).
 // Samples whose offset moves them outside the window read x from global
@@ -120,41 +120,55 @@ hipError_t launch_direct(const Params &p, hipStream_t stream) {
 // pass over the offsets first.
 
 constexpr int kDwThreads = 256;
-constexpr int kDwOpt = 4;      // outputs per thread
+constexpr int kDwOpt = 2;      // outputs per thread (few registers: high occupancy)
 constexpr int kDwMargin = 64;  // window margin per side (input positions)
 
-// Four consecutive elements as floats (16-byte fp32 or 8-byte bf16 load).
-template <class D>
-__device__ __forceinline__ void ld4(const typename D::T *p, float (&v)[4]);
-template <>
-__device__ __forceinline__ void ld4<F32>(const float *p, float (&v)[4]) {
-    const float4 q = *(const float4 *)p;
-    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+// VW consecutive elements (VW = 2 or 4) as floats, in one load.
+template <class D, int VW>
+__device__ __forceinline__ void ldv(const typename D::T *p, float *v) {
+    if constexpr (sizeof(typename D::T) == 4) {
+        if constexpr (VW == 4) {
+            const float4 q = *(const float4 *)p;
+            v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+        } else {
+            const float2 q = *(const float2 *)p;
+            v[0] = q.x; v[1] = q.y;
+        }
+    } else {
+        if constexpr (VW == 4) {
+            const uint2 q = *(const uint2 *)p;
+            v[0] = __uint_as_float(q.x << 16); v[1] = __uint_as_float(q.x & 0xffff0000u);
+            v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xffff0000u);
+        } else {
+            const uint32_t q = *(const uint32_t *)p;
+            v[0] = __uint_as_float(q << 16); v[1] = __uint_as_float(q & 0xffff0000u);
+        }
+    }
 }
-template <>
-__device__ __forceinline__ void ld4<BF16>(const uint16_t *p, float (&v)[4]) {
-    const uint2 q = *(const uint2 *)p;
-    v[0] = __uint_as_float(q.x << 16); v[1] = __uint_as_float(q.x & 0xffff0000u);
-    v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xffff0000u);
-}
-template <class D>
-__device__ __forceinline__ void st4(typename D::T *p, const float (&v)[4]);
-template <>
-__device__ __forceinline__ void st4<F32>(float *p, const float (&v)[4]) {
-    *(float4 *)p = float4{v[0], v[1], v[2], v[3]};
-}
-template <>
-__device__ __forceinline__ void st4<BF16>(uint16_t *p, const float (&v)[4]) {
-    *(uint2 *)p = uint2{(uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16),
-                        (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16)};
+template <class D, int VW>
+__device__ __forceinline__ void stv(typename D::T *p, const float *v) {
+    if constexpr (sizeof(typename D::T) == 4) {
+        if constexpr (VW == 4)
+            *(float4 *)p = float4{v[0], v[1], v[2], v[3]};
+        else
+            *(float2 *)p = float2{v[0], v[1]};
+    } else {
+        const uint32_t a = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+        if constexpr (VW == 4)
+            *(uint2 *)p = uint2{a, (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16)};
+        else
+            *(uint32_t *)p = a;
+    }
 }
 
-// KT: compile-time K (0: any K, read per tap).
-template <class D, int KT>
+// KT: compile-time K (0: any K, read per tap); MASK: a mask is given.
+template <class D, int KT, bool MASK>
 __global__ void __launch_bounds__(kDwThreads) k_depthwise(Params p, int WIN, int tiles_l) {
     using T = typename D::T;
     constexpr int OPT = kDwOpt;
     constexpr int NV = KT > 0 ? OPT * KT : 1;  // offsets held per thread
+    constexpr int VW = OPT % 4 == 0 ? 4 : 2;    // vector width of loads and stores
+    static_assert(OPT % VW == 0, "whole vectors per thread");
     extern __shared__ float s_x[];               // WIN input positions from lo
     const int K = KT > 0 ? KT : p.K;
     const int t = threadIdx.x;
@@ -166,7 +180,7 @@ __global__ void __launch_bounds__(kDwThreads) k_depthwise(Params p, int WIN, int
     const int l0 = tile * (kDwThreads * OPT);
     const T *__restrict__ xrow = (const T *)p.x + ((int64_t)b * p.C_in + ci) * p.L_in;
     const T *__restrict__ off = (const T *)p.off;
-    const T *__restrict__ mask = (const T *)p.mask;
+    const T *__restrict__ mask = MASK ? (const T *)p.mask : nullptr;
     const int L_in = p.L_in;
     const int lo = l0 * p.stride - p.padding - kDwMargin;
 
@@ -179,29 +193,22 @@ __global__ void __launch_bounds__(kDwThreads) k_depthwise(Params p, int WIN, int
     const int lt = l0 + OPT * t;
     const int nvalid = min(OPT, p.L_out - lt);  // may be <= 0
     const int64_t e0 = (((int64_t)b * p.G + g) * p.L_out + lt) * K;
-    float ov[NV], mv[NV];
+    float ov[NV], mv[MASK ? NV : 1];
     if (KT > 0) {
-        const bool vec = nvalid == OPT && (((uintptr_t)(off + e0) & (4 * sizeof(T) - 1)) == 0) &&
-                         (!mask || (((uintptr_t)(mask + e0) & (4 * sizeof(T) - 1)) == 0));
+        const bool vec = nvalid == OPT && (((uintptr_t)(off + e0) & (VW * sizeof(T) - 1)) == 0) &&
+                         (!MASK || (((uintptr_t)(mask + e0) & (VW * sizeof(T) - 1)) == 0));
         if (vec) {
 #pragma unroll
-            for (int c = 0; c < NV / 4; ++c) {
-                float q[4];
-                ld4<D>(off + e0 + 4 * c, q);
-#pragma unroll
-                for (int z = 0; z < 4; ++z) ov[4 * c + z] = q[z];
-                if (mask) {
-                    ld4<D>(mask + e0 + 4 * c, q);
-#pragma unroll
-                    for (int z = 0; z < 4; ++z) mv[4 * c + z] = q[z];
-                }
+            for (int c = 0; c < NV / VW; ++c) {
+                ldv<D, VW>(off + e0 + VW * c, ov + VW * c);
+                if (MASK) ldv<D, VW>(mask + e0 + VW * c, mv + VW * c);
             }
         } else {
 #pragma unroll
             for (int q = 0; q < NV; ++q) {
                 const bool ok = q < nvalid * K;
                 ov[q] = ok ? D::ld(off, e0 + q) : 0.0f;
-                mv[q] = (ok && mask) ? D::ld(mask, e0 + q) : 1.0f;
+                if (MASK) mv[q] = ok ? D::ld(mask, e0 + q) : 0.0f;
             }
         }
     }
@@ -220,11 +227,11 @@ __global__ void __launch_bounds__(kDwThreads) k_depthwise(Params p, int WIN, int
             float ofs, m = 1.0f;
             if (KT > 0) {
                 ofs = ov[o * KT + k];
-                if (mask) m = mv[o * KT + k];
+                if (MASK) m = mv[o * KT + k];
             } else {
                 const bool ok = o < nvalid;
                 ofs = ok ? D::ld(off, e0 + o * K + k) : 0.0f;
-                if (mask) m = ok ? D::ld(mask, e0 + o * K + k) : 0.0f;
+                if (MASK) m = ok ? D::ld(mask, e0 + o * K + k) : 0.0f;
             }
             int i0;
             float f;
@@ -239,14 +246,15 @@ __global__ void __launch_bounds__(kDwThreads) k_depthwise(Params p, int WIN, int
                 x1 = (i0 + 1 >= 0 && i0 + 1 < L_in) ? D::ld(xrow, i0 + 1) : 0.0f;
             }
             float v = fmaf(f, x1 - x0, x0);
-            if (mask) v *= m;
+            if (MASK) v *= m;
             acc = fmaf(D::ld(wrow, k), v, acc);
         }
         res[o] = acc + bias;
     }
     T *__restrict__ out = (T *)p.out + (int64_t)row * p.L_out + lt;
-    if (nvalid == OPT && ((uintptr_t)out & (4 * sizeof(T) - 1)) == 0) {
-        st4<D>(out, res);
+    if (nvalid == OPT && ((uintptr_t)out & (VW * sizeof(T) - 1)) == 0) {
+#pragma unroll
+        for (int c = 0; c < OPT / VW; ++c) stv<D, VW>(out + VW * c, res + VW * c);
     } else {
 #pragma unroll
         for (int o = 0; o < OPT; ++o)
@@ -271,13 +279,13 @@ DepthwisePlan plan_depthwise(const Params &p) {
     return pl;
 }
 
-template <class D>
+template <class D, bool MASK>
 static hipError_t launch_dw(const Params &p, const DepthwisePlan &pl, hipStream_t stream) {
     const int tiles_l = (p.L_out + pl.outputs_per_block - 1) / pl.outputs_per_block;
     const dim3 grid((unsigned)pl.blocks), block(kDwThreads);
     switch (p.K) {
 #define DC1D_DW(KK) \
-    case KK: hipLaunchKernelGGL((k_depthwise<D, KK>), grid, block, pl.lds_bytes, stream, p, pl.window, tiles_l); break;
+    case KK: hipLaunchKernelGGL((k_depthwise<D, KK, MASK>), grid, block, pl.lds_bytes, stream, p, pl.window, tiles_l); break;
         DC1D_DW(1)
         DC1D_DW(2)
         DC1D_DW(3)
@@ -287,14 +295,15 @@ static hipError_t launch_dw(const Params &p, const DepthwisePlan &pl, hipStream_
         DC1D_DW(9)
 #undef DC1D_DW
         default:
-            hipLaunchKernelGGL((k_depthwise<D, 0>), grid, block, pl.lds_bytes, stream, p, pl.window, tiles_l);
+            hipLaunchKernelGGL((k_depthwise<D, 0, MASK>), grid, block, pl.lds_bytes, stream, p, pl.window, tiles_l);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_depthwise(const Params &p, const DepthwisePlan &pl, hipStream_t stream) {
     if (pl.blocks == 0) return hipSuccess;
-    return p.dtype == kF32 ? launch_dw<F32>(p, pl, stream) : launch_dw<BF16>(p, pl, stream);
+    if (p.dtype == kF32) return p.mask ? launch_dw<F32, true>(p, pl, stream) : launch_dw<F32, false>(p, pl, stream);
+    return p.mask ? launch_dw<BF16, true>(p, pl, stream) : launch_dw<BF16, false>(p, pl, stream);
 }
 
 }  // namespace dc1d
