@@ -9,8 +9,10 @@ dc1d page's layer shape (B16, C512 -> 512, K16, dilation 3, "valid", L128,
 fp32).  Prints ONE JSON line (rank 0, one GPU):
 
   value      contraction + sampling GFLOP per step / seconds per step
-  roofline   the dominant kernel's achieved rate against its roofline peak,
-             from HIP events around every timed launch on the launch stream
+  roofline   the achieved rate of one launch (one forward call: its
+             dominant kernel and any small kernels it enqueues, back to
+             back) against the dominant kernel's roofline peak, from HIP
+             events between consecutive forwards on the launch stream
   cpu_baseline  the CPU oracle timed on the host cores (reported baseline)
 
 Parity is checked in the same run (sampled outputs against the oracle)
@@ -20,8 +22,11 @@ before timing; a mismatch aborts the bench.
 --profile-run runs only the warmup + timed launches (no oracle, no JSON),
 for rocprofv3; --copy-calibration MB runs one device-to-device copy of that
 size (the reference kernel for scaling the HBM byte counters).
---summarize-counters DIR folds rocprofv3 counter CSVs into the markdown
-summary kept under profiles/.
+--summarize-profile DIR --kernel NAME folds the rocprofv3 output of the
+commands listed in PROFILE_COMMANDS (kernel trace, FETCH_SIZE / WRITE_SIZE
+passes, copy calibration) into profiles/<workload>__<kernel>.md; the bench
+reads the HBM traffic per launch from there while the kernel sources are
+unchanged.
 """
 from __future__ import annotations
 
@@ -78,7 +83,7 @@ def workload_label(w):
 def read_traffic(name, kernel, khash):
     """HBM bytes per launch of `kernel` on workload `name` from the committed
     counter summary, or None if absent or taken on other kernel sources."""
-    path = os.path.join(ROOT, "profiles", "counters_%s.md" % name)
+    path = os.path.join(ROOT, "profiles", "%s__%s.md" % (name, kernel))
     if not os.path.exists(path):
         return None
     meta = {}
@@ -133,23 +138,21 @@ def run_gpu(w, steps, warmup, check=True, quiet=False):
         if not ok:
             raise SystemExit("bench parity check failed: %r" % parity)
 
+    # Timed region: one HIP event on the launch stream before each forward and
+    # one after the last; forward i lasts ev[i] -> ev[i+1] (its kernels run
+    # back to back on that stream), the region ev[0] -> ev[steps].
     stream = torch.cuda.current_stream(dev)
     for _ in range(warmup):
         step()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    region0 = torch.cuda.Event(enable_timing=True)
-    region1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    region0.record(stream)
     for i in range(steps):
-        ev[i][0].record(stream)
+        ev[i].record(stream)
         step()
-        ev[i][1].record(stream)
-    region1.record(stream)
+    ev[steps].record(stream)
     torch.cuda.synchronize()
-    region_ms = region0.elapsed_time(region1)
-    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    launch_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    region_ms = ev[0].elapsed_time(ev[steps])
     return {"plan": plan, "region_ms": region_ms, "launch_ms": launch_ms, "parity": parity}
 
 
@@ -189,15 +192,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB")
-    ap.add_argument("--summarize-counters", default=None, metavar="DIR")
+    ap.add_argument("--summarize-profile", default=None, metavar="DIR")
+    ap.add_argument("--kernel", default=None, help="the plan's kernel name, for --summarize-profile")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; the forward shards by batch or output channel "
               "with no exchange (see DESIGN.md), and no multi-GPU figure is produced.", file=sys.stderr)
         raise SystemExit(2)
-    if args.summarize_counters:
-        summarize_counters(args.summarize_counters, args.workload)
+    if args.summarize_profile:
+        if not args.kernel:
+            raise SystemExit("--summarize-profile needs --kernel (the plan's kernel name)")
+        write_profile_md(args.summarize_profile, args.workload, args.kernel)
         return
 
     import torch
@@ -274,34 +280,137 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def summarize_counters(d, workload):
-    """Fold rocprofv3 --pmc output (FETCH_SIZE and WRITE_SIZE passes of the
-    bench profile run and of the copy calibration) into a markdown summary
-    with the per-launch HBM bytes of the dominant kernel."""
+PROFILE_COMMANDS = """\
+cd /tmp && export TMPDIR=/tmp; R=<repo root>; P=$R/gpurun_out/prof/{wl}
+rocprofv3 --kernel-trace --stats --output-format csv -d $P/trace -o run -- \\
+    python3 $R/bench.py --workload {wl} --profile-run --steps 20 --warmup 3
+rocprofv3 --pmc FETCH_SIZE --output-format csv -d $P/fetch -o run -- \\
+    python3 $R/bench.py --workload {wl} --profile-run --steps 5 --warmup 1
+rocprofv3 --pmc WRITE_SIZE --output-format csv -d $P/write -o run -- \\
+    python3 $R/bench.py --workload {wl} --profile-run --steps 5 --warmup 1
+rocprofv3 --pmc FETCH_SIZE --output-format csv -d $P/copy_fetch -o run -- \\
+    python3 $R/bench.py --copy-calibration 512
+rocprofv3 --pmc WRITE_SIZE --output-format csv -d $P/copy_write -o run -- \\
+    python3 $R/bench.py --copy-calibration 512
+python3 $R/bench.py --workload {wl} --summarize-profile $P --kernel {kernel}
+"""
+
+
+def short(name):
+    """A kernel's name without namespaces and arguments."""
+    name = name.replace("(anonymous namespace)::", "").replace("dc1d::", "").replace("void ", "")
+    return name.split("(")[0][:100]
+
+
+def summarize_profile(d, workload):
+    """Fold the rocprofv3 output of PROFILE_COMMANDS (kernel-trace stats, then
+    FETCH_SIZE and WRITE_SIZE passes of the profile run and of a 512 MiB
+    device copy) into profiles/<workload>__<kernel>.md.  The copy fixes the
+    scale of the counters: bytes a copy of N bytes must read and write over
+    what the counters report for it."""
     import csv
     import glob
 
-    def rows(sub):
+    from deformable_convolution_amd import inputs
+
+    w = inputs.WORKLOADS[workload]
+
+    def csvs(sub, pattern):
         out = []
-        for f in glob.glob(os.path.join(d, sub, "**", "*counter_collection.csv"), recursive=True):
+        for f in sorted(glob.glob(os.path.join(d, sub, "**", pattern), recursive=True)):
             out += list(csv.DictReader(open(f)))
         return out
 
-    def per_kernel(rs, counter):
+
+    def ours(name):
+        return "dc1d::" in name
+
+    stats = [r for r in csvs("trace", "*kernel_stats.csv") if ours(r["Name"])]
+
+    def counter(sub, cname):
         acc = {}
-        for r in rs:
-            if r.get("Counter_Name") != counter:
-                continue
-            name = r.get("Kernel_Name", "")
-            acc.setdefault(name, []).append(float(r["Counter_Value"]))
+        for r in csvs(sub, "*counter_collection.csv"):
+            if r.get("Counter_Name") == cname:
+                acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         return acc
 
-    res = {}
-    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
-        res[counter] = {"bench": per_kernel(rows("bench_" + counter), counter),
-                        "copy": per_kernel(rows("copy_" + counter), counter)}
-    print(json.dumps({c: {k: {n: (len(v), float(np.mean(v))) for n, v in kk.items()} for k, kk in r.items()}
-                      for c, r in res.items()}, indent=1))
+    fetch, write = counter("fetch", "FETCH_SIZE"), counter("write", "WRITE_SIZE")
+    cf, cw = counter("copy_fetch", "FETCH_SIZE"), counter("copy_write", "WRITE_SIZE")
+    copy_bytes = 512 << 20
+    # the copy's dispatch is the one that moved the most
+    cf_v = max((max(v) for v in cf.values()), default=0.0)
+    cw_v = max((max(v) for v in cw.values()), default=0.0)
+    f_scale = copy_bytes / cf_v if cf_v > 0 else None
+    w_scale = copy_bytes / cw_v if cw_v > 0 else None
+
+    rows_k = []
+    total_bytes = 0.0
+    for name in sorted(set(fetch) | set(write)):
+        if not ours(name):
+            continue
+        fv = float(np.mean(fetch.get(name, [0.0])))
+        wv = float(np.mean(write.get(name, [0.0])))
+        fb = fv * f_scale if f_scale else None
+        wb = wv * w_scale if w_scale else None
+        if fb is not None and wb is not None:
+            total_bytes += fb + wb
+        rows_k.append((short(name), fv, wv, fb, wb))
+    return stats, rows_k, total_bytes, (cf_v, cw_v, f_scale, w_scale), w
+
+
+def write_profile_md(d, workload, kernel):
+    stats, rows_k, total_bytes, (cf_v, cw_v, f_scale, w_scale), w = summarize_profile(d, workload)
+    _, _, alg_bytes = work(w)
+    contraction, sampling, _ = work(w)
+    fwd_ns = sum(float(r["AverageNs"]) for r in stats)
+    out = []
+    out.append("# %s -- %s" % (workload_label(w), kernel))
+    out.append("")
+    out.append("<!-- kernel=%s -->" % kernel)
+    out.append("<!-- kernel_sources=%s -->" % kernel_hash())
+    if rows_k and f_scale and w_scale:
+        out.append("<!-- hbm_bytes_per_launch=%.0f -->" % total_bytes)
+    out.append("")
+    out.append("One launch = one forward call (every kernel it enqueues, back to back on one stream).")
+    out.append("")
+    out.append("Commands (rocprofv3, ROCm 7.2, one MI355X):")
+    out.append("")
+    out.append("```")
+    out.append(PROFILE_COMMANDS.format(wl=workload, kernel=kernel).rstrip())
+    out.append("```")
+    out.append("")
+    out.append("## Kernel trace (--kernel-trace --stats)")
+    out.append("")
+    out.append("| kernel | calls | average (us) | total (us) |")
+    out.append("|---|---|---|---|")
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        out.append("| %s | %s | %.2f | %.1f |" % (short(r["Name"]), r["Calls"],
+                                               float(r["AverageNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e3))
+    out.append("")
+    out.append("Sum of the averages of one forward's kernels: %.2f us; contraction %.3f GFLOP -> %.1f TFLOP/s "
+               "over that time." % (fwd_ns / 1e3, contraction / 1e9, contraction / (fwd_ns * 1e-9) / 1e12
+                                    if fwd_ns else 0.0))
+    out.append("")
+    out.append("## HBM traffic (--pmc FETCH_SIZE, --pmc WRITE_SIZE; KiB per dispatch)")
+    out.append("")
+    if f_scale and w_scale:
+        out.append("Copy calibration: a 512 MiB device-to-device copy reads as FETCH_SIZE %.0f and WRITE_SIZE %.0f; "
+                   "scale factors %.4f and %.4f bytes per counter unit." % (cf_v, cw_v, f_scale, w_scale))
+    else:
+        out.append("Copy calibration missing: traffic not scaled.")
+    out.append("")
+    out.append("| kernel | FETCH_SIZE | WRITE_SIZE | fetched (MB) | written (MB) |")
+    out.append("|---|---|---|---|---|")
+    for name, fv, wv, fb, wb in rows_k:
+        out.append("| %s | %.0f | %.0f | %s | %s |" % (name, fv, wv, "%.2f" % (fb / 1e6) if fb else "-",
+                                                   "%.2f" % (wb / 1e6) if wb else "-"))
+    out.append("")
+    out.append("Per forward: %.2f MB of HBM traffic against %.2f MB of algorithmic bytes (each tensor moved once)."
+               % (total_bytes / 1e6, alg_bytes / 1e6))
+    path = os.path.join(ROOT, "profiles", "%s__%s.md" % (workload, kernel))
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    open(path, "w").write("\n".join(out) + "\n")
+    print("wrote", path)
 
 
 if __name__ == "__main__":
