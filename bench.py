@@ -198,7 +198,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; the forward shards by batch or output channel "
-              "with no exchange (see DESIGN.md), and no multi-GPU figure is produced.", file=sys.stderr)
+              "with no exchange, and no multi-GPU figure is produced.", file=sys.stderr)
         raise SystemExit(2)
     if args.summarize_profile:
         if not args.kernel:
@@ -256,7 +256,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32" if w.dtype == "f32" else "bf16",
-        "data": "synthetic (seeded; see DESIGN.md input recipe)",
+        "data": "synthetic, seeded (deformable_convolution_amd/inputs.py; no dataset)",
         "config": {"workload": workload_label(w), "plan": r["plan"],
                    "gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "parity": r["parity"]},
         "roofline": roof,
