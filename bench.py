@@ -99,7 +99,7 @@ def read_traffic(name, kernel, khash):
         return None
 
 
-def run_gpu(w, steps, warmup, check=True, quiet=False):
+def run_gpu(w, steps, warmup, check=True, cold_reps=0):
     import torch
     from deformable_convolution_amd import dc1d, inputs
 
@@ -153,10 +153,43 @@ def run_gpu(w, steps, warmup, check=True, quiet=False):
     torch.cuda.synchronize()
     launch_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
     region_ms = ev[0].elapsed_time(ev[steps])
-    return {"plan": plan, "region_ms": region_ms, "launch_ms": launch_ms, "parity": parity}
+    cold_ms = []
+    if cold_reps:
+        # cold: a 512 MiB write (twice the last-level cache) before each
+        # forward, outside its events
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(cold_reps):
+            flush.fill_(1)
+            a.record(stream)
+            step()
+            b.record(stream)
+            torch.cuda.synchronize()
+            cold_ms.append(a.elapsed_time(b))
+        del flush
+    return {"plan": plan, "region_ms": region_ms, "launch_ms": launch_ms, "cold_ms": cold_ms, "parity": parity}
 
 
-def cpu_baseline(w, budget_s=12.0, max_reps=20):
+def pct(v):
+    """median, p10, p90 of a list of times (ms)."""
+    if not v:
+        return None
+    q = np.percentile(np.asarray(v), [50, 10, 90])
+    return {"median": round(float(q[0]), 5), "p10": round(float(q[1]), 5), "p90": round(float(q[2]), 5),
+            "n": len(v)}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, budget_s=12.0, max_reps=200):
     """The oracle, untouched, on this host's cores: full forwards of the same
     workload repeated until about budget_s seconds have passed."""
     import oracle
@@ -178,8 +211,8 @@ def cpu_baseline(w, budget_s=12.0, max_reps=20):
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
     return {"value": (contraction + sampling) * reps / el / 1e9, "unit": "GFLOP/s", "cores": min(threads, cores),
             "kind": "oracle",
-            "sample": "%d full forward(s) of the same workload (all %d outputs each), %.1f s" % (
-                reps, w.B * w.C_out * w.L_out, el)}
+            "sample": "%d full forward(s) of the same workload (all %d outputs each), %.1f s, on %s" % (
+                reps, w.B * w.C_out * w.L_out, el, cpu_model())}
 
 
 def main():
@@ -226,7 +259,7 @@ def main():
             w.name, r["plan"]["kernel"], args.steps, float(np.mean(r["launch_ms"]))), flush=True)
         return
 
-    r = run_gpu(w, args.steps, args.warmup)
+    r = run_gpu(w, args.steps, args.warmup, cold_reps=20)
     contraction, sampling, nbytes = work(w)
     ms = r["region_ms"] / args.steps
     kern_ms = float(np.mean(r["launch_ms"]))
@@ -258,7 +291,8 @@ def main():
         "dtype": "f32" if w.dtype == "f32" else "bf16",
         "data": "synthetic, seeded (deformable_convolution_amd/inputs.py; no dataset)",
         "config": {"workload": workload_label(w), "plan": r["plan"],
-                   "gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "parity": r["parity"]},
+                   "gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "parity": r["parity"],
+                   "forward_ms": {"warm": pct(r["launch_ms"]), "cold": pct(r["cold_ms"])}},
         "roofline": roof,
     }
     if args.all:
