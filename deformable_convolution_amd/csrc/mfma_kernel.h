@@ -10,10 +10,10 @@
 // LDS, never in HBM.
 //
 // Workgroup: 8 waves in two roles (warp specialisation), one per SIMD each:
-//   * 4 MFMA waves.  MFMA wave w owns the 32*NB columns [32*NB*w, ...) of
-//     the BM x BN output tile and all its BM rows; it reads operand
-//     fragments from LDS and issues MFMAs, and stages the next chunk's
-//     weight tile, whose load latency hides under its MFMAs.
+//   * 4 MFMA waves in a 2 x 2 grid over the BM x BN = 256 x 128 output
+//     tile, each owning 128 rows x 64 columns; they read operand fragments
+//     from LDS and issue MFMAs, and stage the next chunk's weight tile,
+//     whose load latency hides under their MFMAs.
 //   * 4 sampler waves.  They stage the zero-padded x windows from HBM into
 //     LDS and compute the sample tile of the next reduction chunk.
 // The hardware interleaves the two roles on every SIMD: MFMAs of one wave
@@ -124,7 +124,7 @@ __device__ __forceinline__ int remap_xcd(int u, int U) {
 struct TrF32 {
     using D = F32;
     using T = float;
-    static constexpr int MB = 8, NB = 1;  // BM = 256, BN = 128
+    static constexpr int MB = 4, NB = 2;  // per MFMA wave: 128 rows x 64 columns
     static constexpr int WPR = BK / 4;    // 16-byte words per weight-tile row (8)
     static constexpr int SLD = BK + 4;    // sample-tile row (elements)
     struct Frag { float v[16]; };
@@ -162,7 +162,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 struct TrBF16 {
     using D = BF16;
     using T = uint16_t;
-    static constexpr int MB = 8, NB = 1;  // BM = 256, BN = 128
+    static constexpr int MB = 4, NB = 2;  // per MFMA wave: 128 rows x 64 columns
     static constexpr int WPR = BK / 8;    // 4
     static constexpr int SLD = BK + 8;
     struct Frag { u4 v[2]; };
@@ -191,8 +191,14 @@ struct TrBF16 {
 
 template <class Tr>
 struct Geo {
-    static constexpr int BM = 32 * Tr::MB;
-    static constexpr int BN = NWM * 32 * Tr::NB;
+    // the MFMA waves form a WM x WN grid over the BM x BN tile (BM = 256,
+    // BN = 128); each owns 32*MB rows and 32*NB columns, which balances the
+    // weight and sample fragments it reads from LDS per chunk
+    static constexpr int WM = 2, WN = NWM / WM;
+    static constexpr int BM = 32 * Tr::MB * WM;
+    static constexpr int BN = 32 * Tr::NB * WN;
+    static __device__ __forceinline__ int row0(int wv) { return 32 * Tr::MB * (wv / WN); }
+    static __device__ __forceinline__ int col0(int wv) { return 32 * Tr::NB * (wv % WN); }
     static constexpr int WV = BM * Tr::WPR / NTM;  // 16-byte weight words per MFMA thread per chunk
 };
 
@@ -225,6 +231,7 @@ __device__ __forceinline__ void mfma_role(const MfmaArgs &a, const Tile &tl, typ
     const Params &p = a.p;
     const int t = threadIdx.x;
     const int wv = t / 64, lane = t % 64, li = lane % 32, lh = lane / 32;
+    const int row0 = Geo<Tr>::row0(wv), col0 = Geo<Tr>::col0(wv);
     const int M = p.C_out, Kred = p.Kred, C_in = p.C_in;
     const T *__restrict__ w = (const T *)p.w;
     const bool m_full = tl.m0 + BM <= M;  // no rows past C_out in this tile
@@ -330,11 +337,11 @@ __device__ __forceinline__ void mfma_role(const MfmaArgs &a, const Tile &tl, typ
         const T *st = s_S + (c & 1) * BN * SLD;
         Frag bf[NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) Tr::lds_b(st + (32 * (NB * wv + nb) + li) * SLD + 16 * lh, bf[nb]);
+        for (int nb = 0; nb < NB; ++nb) Tr::lds_b(st + (col0 + 32 * nb + li) * SLD + 16 * lh, bf[nb]);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             Frag af;
-            Tr::lds_a(tile, 32 * mb + li, lh, af);
+            Tr::lds_a(tile, row0 + 32 * mb + li, lh, af);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) Tr::mma(af, bf[nb], acc[mb][nb]);
         }
@@ -361,7 +368,7 @@ __device__ __forceinline__ void mfma_role(const MfmaArgs &a, const Tile &tl, typ
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-        const int col = (int)tl.n0 + 32 * (NB * wv + nb) + li;
+        const int col = (int)tl.n0 + col0 + 32 * nb + li;
         if (col >= a.N) continue;
         const int b = (int)fdiv((uint32_t)col, a.fd_Lout);
         const int l = col - b * L_out;
@@ -370,7 +377,7 @@ __device__ __forceinline__ void mfma_role(const MfmaArgs &a, const Tile &tl, typ
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
-                const int row = tl.m0 + 32 * mb + 8 * (q >> 2) + 4 * lh + (q & 3);
+                const int row = tl.m0 + row0 + 32 * mb + 8 * (q >> 2) + 4 * lh + (q & 3);
                 if (row < M) D::st(ob, (int64_t)row * L_out, acc[mb][nb][q] + (bias ? D::ld(bias, row) : 0.0f));
             }
     }
@@ -710,10 +717,10 @@ __global__ void __launch_bounds__(NTT) k_mfma(MfmaArgs a) {
 // Window staging: a block's window is NL = CB*SLOT lines of NTS positions
 // (thread ts owns position ts of each line; a row holds WTM = SLOT*NTS
 // positions).  While the sampler works on block B it stages block B+1 in nkb
-// parts of LPP lines, one part per chunk: the loads of a part are issued in
-// one iteration and written to LDS at the start of the next, so their
-// latency hides behind the barrier.  Windows are double-buffered by block
-// parity.
+// parts of LPP lines, one part per chunk: the loads of a part are issued at
+// the end of one iteration and written to LDS at the end of the next, after
+// its samples, so their latency hides behind a barrier and a sampling pass.
+// Windows are double-buffered by block parity.
 template <class Tr, bool MASK, bool WIN, int CB, int SLOT, int LPP>
 __device__ __forceinline__ void sampler_cb(const MfmaArgs &a, const Tile &tl, const Pos *s_tab,
                                            const float *s_m, typename Tr::T *s_S, typename Tr::T *s_x,
@@ -729,6 +736,7 @@ __device__ __forceinline__ void sampler_cb(const MfmaArgs &a, const Tile &tl, co
     constexpr bool BF = sizeof(T) == 2;
     static_assert(BN == 128, "two sampler waves per 64 columns");
     static_assert(LPP % SLOT == 0, "a part holds whole window rows");
+    static_assert(NL % LPP == 0, "a non-empty part is a full part");
     const Params &p = a.p;
     const int ts = threadIdx.x - NTM;  // 0 .. NTS-1
     const int lane = ts % 64;
@@ -784,8 +792,7 @@ __device__ __forceinline__ void sampler_cb(const MfmaArgs &a, const Tile &tl, co
 #pragma unroll
             for (int n = 0; n < LPP; ++n) {
                 const int q = n % SLOT;
-                if (pend_l0 + n < NL)  // uniform
-                    dx[(n / SLOT) * WTM + NTS * q] = (xval[q] && cib + n / SLOT < C_in) ? xreg[n] : (T)0;
+                dx[(n / SLOT) * WTM + NTS * q] = (xval[q] && cib + n / SLOT < C_in) ? xreg[n] : (T)0;
             }
         }
         pend_l0 = NL;
@@ -863,12 +870,18 @@ __device__ __forceinline__ void sampler_cb(const MfmaArgs &a, const Tile &tl, co
     if (c0 < c1) sample(c0);
     __syncthreads();
     for (int c = c0; c < c1; ++c) {
-        if (WIN) commit_part();  // loaded during the previous iteration
         if (c + 1 < c1) sample(c + 1);
-        if (WIN && c + 2 < c1) {
-            // part kb(c+2) of the block after chunk c+2's, if this workgroup uses it
-            const int b2 = (int)fdiv((uint32_t)(c + 2), a.fd_nkb);
-            if ((b2 + 1) * nkb < c1) load_part(b2 + 1, c + 2 - b2 * nkb);
+        if (WIN) {
+            // The part loaded in the previous iteration (for the block after
+            // chunk c+1's) goes to LDS only now, after this iteration's
+            // samples, so its loads had a whole iteration to arrive.  Then
+            // part kb(c+2) of the block after chunk c+2's, if this workgroup
+            // uses it.
+            commit_part();
+            if (c + 2 < c1) {
+                const int b2 = (int)fdiv((uint32_t)(c + 2), a.fd_nkb);
+                if ((b2 + 1) * nkb < c1) load_part(b2 + 1, c + 2 - b2 * nkb);
+            }
         }
         __syncthreads();
     }
@@ -938,7 +951,7 @@ __global__ void __launch_bounds__(256) k_split_reduce(MfmaArgs a) {
     f4 tot = part[0];
     for (int s2 = 1; s2 < a.splits; ++s2) tot += part[(int64_t)s2 * tiles * VPT];
     const int mb = q4 / (NB * 4), nb = (q4 / 4) % NB, qq = (q4 & 3) * 4;
-    const int col = tn * BN + 32 * (NB * wv + nb) + li;
+    const int col = tn * BN + Geo<Tr>::col0(wv) + 32 * nb + li;
     if (col >= a.N) return;
     const int L_out = p.L_out, M = p.C_out;
     const int b = (int)fdiv((uint32_t)col, a.fd_Lout);
@@ -948,7 +961,7 @@ __global__ void __launch_bounds__(256) k_split_reduce(MfmaArgs a) {
 #pragma unroll
     for (int z = 0; z < 4; ++z) {
         const int q = qq + z;
-        const int row = tm * BM + 32 * mb + 8 * (q >> 2) + 4 * lh + (q & 3);
+        const int row = tm * BM + Geo<Tr>::row0(wv) + 32 * mb + 8 * (q >> 2) + 4 * lh + (q & 3);
         if (row < M) D::st(ob, (int64_t)row * L_out, tot[z] + (bias ? D::ld(bias, row) : 0.0f));
     }
 }
