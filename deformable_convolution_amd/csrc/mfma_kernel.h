@@ -809,41 +809,72 @@ __device__ __forceinline__ void sampler_cb(const MfmaArgs &a, const Tile &tl, co
         const int cb = (int)fdiv((uint32_t)u, a.fd_nkb), kb = u - cb * nkb;
         const int g = (int)fdiv((uint32_t)min(cb * CB + i0, C_in - 1), a.fd_cpo);
         const T *xw = s_x + (cb & 1) * XBUF + i0 * WTM;
-        float v[16];
+        // all reads first (the position pairs, then every neighbour pair),
+        // then the arithmetic, so that the LDS latency is paid once
+        Pos ps[TPC];
+        float mk[TPC];
 #pragma unroll
         for (int tt = 0; tt < TPC; ++tt) {
             const int k = min(kb * TPC + tt, K - 1);  // taps past K have zero weights
             const int te = (g * K + k) * BN + col;
-            const Pos ps = s_tab[te];
-            const float mk = MASK ? s_m[te] : 1.0f;
+            ps[tt] = s_tab[te];
+            mk[tt] = MASK ? s_m[te] : 1.0f;
+        }
+        float x0[16], x1[16];
+        if (WIN) {
+            if constexpr (BF) {
+                // the two neighbours from the aligned dword pair holding them
+                uint32_t d0[16], d1[16];
 #pragma unroll
-            for (int ii = 0; ii < CPT; ++ii) {
-                float x0, x1;
-                if (WIN) {
-                    if constexpr (BF) {
-                        // the two neighbours from the aligned dword pair holding them
-                        const uint32_t *w32 = (const uint32_t *)(xw + ii * WTM) + (ps.j >> 1);
-                        const uint32_t pr = __builtin_amdgcn_alignbit(w32[1], w32[0], (ps.j & 1) * 16);
-                        x0 = __uint_as_float(pr << 16);
-                        x1 = __uint_as_float(pr & 0xffff0000u);
-                    } else {
-                        const float *rw = xw + ii * WTM + ps.j;
-                        x0 = rw[0];
-                        x1 = rw[1];
+                for (int tt = 0; tt < TPC; ++tt)
+#pragma unroll
+                    for (int ii = 0; ii < CPT; ++ii) {
+                        const uint32_t *w32 = (const uint32_t *)(xw + ii * WTM) + (ps[tt].j >> 1);
+                        d0[ii * TPC + tt] = w32[0];
+                        d1[ii * TPC + tt] = w32[1];
                     }
-                } else {
+#pragma unroll
+                for (int tt = 0; tt < TPC; ++tt)
+#pragma unroll
+                    for (int ii = 0; ii < CPT; ++ii) {
+                        const int s = ii * TPC + tt;
+                        const uint32_t pr = __builtin_amdgcn_alignbit(d1[s], d0[s], (ps[tt].j & 1) * 16);
+                        x0[s] = __uint_as_float(pr << 16);
+                        x1[s] = __uint_as_float(pr & 0xffff0000u);
+                    }
+            } else {
+#pragma unroll
+                for (int tt = 0; tt < TPC; ++tt)
+#pragma unroll
+                    for (int ii = 0; ii < CPT; ++ii) {
+                        const float *rw = xw + ii * WTM + ps[tt].j;
+                        x0[ii * TPC + tt] = rw[0];
+                        x1[ii * TPC + tt] = rw[1];
+                    }
+            }
+        } else {
+#pragma unroll
+            for (int tt = 0; tt < TPC; ++tt)
+#pragma unroll
+                for (int ii = 0; ii < CPT; ++ii) {
                     const T *rw = xcol + (int64_t)min(cb * CB + i0 + ii, C_in - 1) * L_in;
-                    const int j = ps.j;
+                    const int j = ps[tt].j;
                     const float a0 = D::ld(rw, min(max(j, 0), L_in - 1));
                     const float a1 = D::ld(rw, min(max(j + 1, 0), L_in - 1));
-                    x0 = (j >= 0 && j < L_in) ? a0 : 0.0f;
-                    x1 = (j + 1 >= 0 && j + 1 < L_in) ? a1 : 0.0f;
+                    x0[ii * TPC + tt] = (j >= 0 && j < L_in) ? a0 : 0.0f;
+                    x1[ii * TPC + tt] = (j + 1 >= 0 && j + 1 < L_in) ? a1 : 0.0f;
                 }
-                float val = fmaf(ps.f, x1 - x0, x0);
-                if (MASK) val *= mk;
-                v[ii * TPC + tt] = val;
-            }
         }
+        float v[16];
+#pragma unroll
+        for (int tt = 0; tt < TPC; ++tt)
+#pragma unroll
+            for (int ii = 0; ii < CPT; ++ii) {
+                const int s = ii * TPC + tt;
+                float val = fmaf(ps[tt].f, x1[s] - x0[s], x0[s]);
+                if (MASK) val *= mk[tt];
+                v[s] = val;
+            }
         Tr::store_b(s_S + (u & 1) * BN * SLD + col * SLD + 16 * h, v);
     };
 
