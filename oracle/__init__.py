@@ -7,9 +7,9 @@ imports nothing from the product.
 
 Two independent formulations live here:
 
-* ``forward`` / ``forward_points`` / ``positions`` -- ctypes front end of
-  ``dc1d_oracle.c``: the two-stage definition (sample, then contract) in
-  plain C loops over doubles.
+* ``forward`` / ``forward_points`` / ``positions`` / ``backward`` -- ctypes
+  front end of ``dc1d_oracle.c``: the two-stage definition (sample, then
+  contract) in plain C loops over doubles, and its term-by-term derivative.
 * ``hat.forward`` -- a NumPy brute force that never splits a position into
   integer and fractional parts; it is the pin for the C oracle's
   floor/fraction logic and its zero-fill boundary.
@@ -59,6 +59,8 @@ class _Lib:
         lib.oracle_forward.argtypes = [p] * 5 + [i64] * 10 + [p]
         lib.oracle_forward_points.restype = ctypes.c_int
         lib.oracle_forward_points.argtypes = [p] * 5 + [i64] * 10 + [p, i64, p]
+        lib.oracle_backward.restype = ctypes.c_int
+        lib.oracle_backward.argtypes = [p] * 5 + [i64] * 10 + [p] * 5
         self.lib = lib
 
 
@@ -162,3 +164,28 @@ def positions(offsets, L_in, K, stride=1, padding=0, dilation=1, lib=None):
     if st:
         raise ValueError("oracle_positions: " + _ERR.get(st, str(st)))
     return i0, fr, va
+
+
+def backward(x, offsets, weight, dout, mask=None, stride=1, padding=0, dilation=1, groups=1, lib=None):
+    """Gradients of sum(dout * forward(...)) in float64, as a dict with keys
+    x, offsets, mask (None without a mask), weight, bias."""
+    x, offsets, weight, dout, mask = map(_f64, (x, offsets, weight, dout, mask))
+    B, C_in, L_in, C_out, K, G = _shapes(x, offsets, weight, groups)
+    L_out = output_length(L_in, K, stride, padding, dilation, lib)
+    if L_out < 1 or offsets.shape != (B, G, L_out, K):
+        raise ValueError("offsets must be [B, G, L_out, K] with L_out=%d" % L_out)
+    if mask is not None and mask.shape != offsets.shape:
+        raise ValueError("mask must have the offsets' shape")
+    if dout.shape != (B, C_out, L_out):
+        raise ValueError("dout must be [B, C_out, L_out]")
+    gx = np.empty_like(x)
+    goff = np.empty_like(offsets)
+    gmask = np.empty_like(offsets) if mask is not None else None
+    gw = np.empty_like(weight)
+    gb = np.empty(C_out, dtype=np.float64)
+    st = _load(lib).oracle_backward(_ptr(x), _ptr(offsets), _ptr(mask), _ptr(weight), _ptr(dout),
+                                 B, C_in, L_in, C_out, K, stride, padding, dilation, groups, G,
+                                 _ptr(gx), _ptr(goff), _ptr(gmask), _ptr(gw), _ptr(gb))
+    if st:
+        raise ValueError("oracle_backward: " + _ERR.get(st, str(st)))
+    return {"x": gx, "offsets": goff, "mask": gmask, "weight": gw, "bias": gb}

@@ -260,3 +260,150 @@ int oracle_forward_points(const double *x, const double *offsets, const double *
     }
     return bad ? OR_NONFINITE : OR_OK;
 }
+
+/*
+ * Backward of oracle_forward: the gradients of the scalar
+ * sum_{b,co,l} dout[b,co,l] * out[b,co,l] with respect to every input, for
+ * a given dout [B, C_out, L_out].  The dc1d page trains the offsets and
+ * checks the offset gradient against a finite difference (section Demo
+ * notebook) and discusses what the backward keeps alive (section Going
+ * faster); the formulas below are the derivatives of the forward as written
+ * above, taken term by term:
+ *
+ *   dS[b,ci,k,l] = sum over the group's output channels co of
+ *                  w[co, ci_local, k] * dout[b, co, l]
+ *   gx[b,ci,i0]   += dS * m * (1 - f)     (only for 0 <= i0 < L_in)
+ *   gx[b,ci,i0+1] += dS * m * f           (only for 0 <= i0+1 < L_in)
+ *   goff[b,g,l,k]  = sum over ci in g of dS * m * (x~(i0+1) - x~(i0))
+ *   gmask[b,g,l,k] = sum over ci in g of dS * ((1-f) x~(i0) + f x~(i0+1))
+ *   gw[co,cl,k]    = sum over (b, l) of dout[b,co,l] * S[b, grp*cpg+cl, k, l]
+ *   gb[co]         = sum over (b, l) of dout[b,co,l]
+ *
+ * The offset derivative is that of the interpolation formula with i0 held
+ * fixed, i.e. the right derivative where the offset is an integer (the
+ * forward is continuous there but not differentiable).  Any gradient
+ * pointer may be NULL.  Sums run in ascending index order.
+ */
+int oracle_backward(const double *x, const double *offsets, const double *mask,
+                    const double *weight, const double *dout, int64_t B, int64_t C_in,
+                    int64_t L_in, int64_t C_out, int64_t K, int64_t s, int64_t p, int64_t d,
+                    int64_t groups, int64_t G, double *gx, double *goff, double *gmask,
+                    double *gw, double *gb)
+{
+    shape_t sh = {B, C_in, L_in, C_out, K, s, p, d, groups, G, 0};
+    int st = check_shape(&sh);
+    if (st)
+        return st;
+    const int64_t L_out = sh.L_out;
+    const int64_t cpg = C_in / groups, opg = C_out / groups, cpo = C_in / G;
+    const int64_t n_off = B * G * L_out * K;
+    if (!all_finite(x, B * C_in * L_in) || !all_finite(offsets, n_off) ||
+        (mask && !all_finite(mask, n_off)) || !all_finite(weight, C_out * cpg * K) ||
+        !all_finite(dout, B * C_out * L_out))
+        return OR_NONFINITE;
+
+    /* dS for every (b, ci, k, l) */
+    double *dS = (double *)malloc(sizeof(double) * (size_t)(B * C_in * K * L_out + 1));
+    if (!dS)
+        return OR_NOMEM;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t ci = 0; ci < C_in; ++ci) {
+            const int64_t grp = ci / cpg, cl = ci - grp * cpg;
+            for (int64_t k = 0; k < K; ++k)
+                for (int64_t l = 0; l < L_out; ++l) {
+                    double acc = 0.0;
+                    for (int64_t oc = 0; oc < opg; ++oc) {
+                        const int64_t co = grp * opg + oc;
+                        acc += weight[(co * cpg + cl) * K + k] * dout[(b * C_out + co) * L_out + l];
+                    }
+                    dS[((b * C_in + ci) * K + k) * L_out + l] = acc;
+                }
+        }
+
+    /* gx: each (b, ci) row receives only its own samples' contributions */
+    if (gx) {
+#pragma omp parallel for collapse(2) schedule(static)
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t ci = 0; ci < C_in; ++ci) {
+                const int64_t g = ci / cpo;
+                double *grow = gx + (b * C_in + ci) * L_in;
+                for (int64_t i = 0; i < L_in; ++i)
+                    grow[i] = 0.0;
+                for (int64_t k = 0; k < K; ++k)
+                    for (int64_t l = 0; l < L_out; ++l) {
+                        const int64_t oi = ((b * G + g) * L_out + l) * K + k;
+                        int64_t i0;
+                        double f;
+                        split_position(l * s - p + k * d, offsets[oi], &i0, &f);
+                        const double m = mask ? mask[oi] : 1.0;
+                        const double ds = dS[((b * C_in + ci) * K + k) * L_out + l];
+                        if (i0 >= 0 && i0 < L_in)
+                            grow[i0] += ds * m * (1.0 - f);
+                        if (i0 + 1 >= 0 && i0 + 1 < L_in)
+                            grow[i0 + 1] += ds * m * f;
+                    }
+            }
+    }
+
+    /* goff, gmask: sums over the offset group's channels */
+    if (goff || gmask) {
+#pragma omp parallel for collapse(2) schedule(static)
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t g = 0; g < G; ++g)
+                for (int64_t l = 0; l < L_out; ++l)
+                    for (int64_t k = 0; k < K; ++k) {
+                        const int64_t oi = ((b * G + g) * L_out + l) * K + k;
+                        int64_t i0;
+                        double f;
+                        split_position(l * s - p + k * d, offsets[oi], &i0, &f);
+                        const double m = mask ? mask[oi] : 1.0;
+                        double ao = 0.0, am = 0.0;
+                        for (int64_t ci = g * cpo; ci < (g + 1) * cpo; ++ci) {
+                            const double *row = x + (b * C_in + ci) * L_in;
+                            const double x0 = x_ext(row, L_in, i0), x1 = x_ext(row, L_in, i0 + 1);
+                            const double ds = dS[((b * C_in + ci) * K + k) * L_out + l];
+                            ao += ds * m * (x1 - x0);
+                            am += ds * ((1.0 - f) * x0 + f * x1);
+                        }
+                        if (goff)
+                            goff[oi] = ao;
+                        if (gmask)
+                            gmask[oi] = am;
+                    }
+    }
+    free(dS);
+
+    /* gw: dout against the sampled tensor, recomputed per term */
+    if (gw) {
+#pragma omp parallel for schedule(static)
+        for (int64_t co = 0; co < C_out; ++co) {
+            const int64_t grp = co / opg;
+            for (int64_t cl = 0; cl < cpg; ++cl) {
+                const int64_t ci = grp * cpg + cl, g = ci / cpo;
+                for (int64_t k = 0; k < K; ++k) {
+                    double acc = 0.0;
+                    for (int64_t b = 0; b < B; ++b) {
+                        const double *row = x + (b * C_in + ci) * L_in;
+                        for (int64_t l = 0; l < L_out; ++l) {
+                            const int64_t oi = ((b * G + g) * L_out + l) * K + k;
+                            acc += dout[(b * C_out + co) * L_out + l] *
+                                   sample(row, L_in, l * s - p + k * d, offsets[oi], mask ? mask + oi : NULL);
+                        }
+                    }
+                    gw[(co * cpg + cl) * K + k] = acc;
+                }
+            }
+        }
+    }
+    if (gb) {
+        for (int64_t co = 0; co < C_out; ++co) {
+            double acc = 0.0;
+            for (int64_t b = 0; b < B; ++b)
+                for (int64_t l = 0; l < L_out; ++l)
+                    acc += dout[(b * C_out + co) * L_out + l];
+            gb[co] = acc;
+        }
+    }
+    return OR_OK;
+}

@@ -14,6 +14,7 @@ import tempfile
 import pytest
 
 import oracle
+import test_oracle_backward as bwd
 import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "dc1d_oracle.c")
@@ -44,6 +45,20 @@ MUTANTS = {
     "tap order reversed": ("acc += weight[(co * cpg + cl) * K + k] *\n",
                            "acc += weight[(co * cpg + cl) * K + (K - 1 - k)] *\n"),
     "output length off by one": ("return num / s + 1;", "return (num + 1) / s + 1;"),
+    # the backward
+    "bwd left weight dropped": ("grow[i0] += ds * m * (1.0 - f);", "grow[i0] += ds * m;"),
+    "bwd mask missing in gx": ("grow[i0 + 1] += ds * m * f;", "grow[i0 + 1] += ds * f;"),
+    "bwd offset derivative sign": ("ao += ds * m * (x1 - x0);", "ao += ds * m * (x0 - x1);"),
+    "bwd mask gradient scaled by mask": ("am += ds * ((1.0 - f) * x0 + f * x1);",
+                                         "am += ds * m * ((1.0 - f) * x0 + f * x1);"),
+    "bwd conv group ignored in dS": ("const int64_t co = grp * opg + oc;", "const int64_t co = oc;"),
+    "bwd weight gradient without mask": (
+        "acc += dout[(b * C_out + co) * L_out + l] *\n"
+        "                                   sample(row, L_in, l * s - p + k * d, offsets[oi], mask ? mask + oi : NULL);",
+        "acc += dout[(b * C_out + co) * L_out + l] *\n"
+        "                                   sample(row, L_in, l * s - p + k * d, offsets[oi], NULL);"),
+    "bwd bias over the first batch only": ("            for (int64_t b = 0; b < B; ++b)\n                for (int64_t l = 0; l < L_out; ++l)\n                    acc += dout",
+                                           "            for (int64_t b = 0; b < 1; ++b)\n                for (int64_t l = 0; l < L_out; ++l)\n                    acc += dout"),
 }
 
 PIN_CALLS = [
@@ -61,6 +76,9 @@ PIN_CALLS = [
     ("positions edges", pins.test_positions_edges),
     ("output length", pins.test_output_length_closed_form_vs_count),
     ("operator examples", pins.test_conv1d_operator_examples_shapes_and_params),
+    ("backward = finite differences", lambda: bwd.test_backward_equals_finite_differences(bwd.SHAPES[1])),
+    ("backward = hat-form autograd", lambda: bwd.test_backward_matches_hat_form_autograd(bwd.SHAPES[3])),
+    ("backward = conv1d autograd", lambda: bwd.test_zero_offsets_match_conv1d_autograd(bwd.SHAPES[1])),
 ]
 
 
