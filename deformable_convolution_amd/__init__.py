@@ -1,4 +1,4 @@
-"""MI355X-native 1D deformable convolution forward (DeformConv1d).
+"""MI355X-native 1D deformable convolution (DeformConv1d): forward and backward.
 
 The compute lives in ``libdc1d.so`` (HIP kernels for gfx950 behind a C ABI
 declared in ``include/dc1d.h``); ``deformable_convolution_amd.dc1d`` is the
@@ -8,6 +8,7 @@ never requires a GPU.
 """
 from .dc1d import (  # noqa: F401
     Dc1dError,
+    backward,
     debug_positions,
     forward,
     library_path,

@@ -257,6 +257,109 @@ int dc1d_forward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_te
     return e == hipSuccess ? DC1D_OK : DC1D_ERR_LAUNCH;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Backward arguments: the forward's (without bias and out) plus grad_out and
+// the optional gradients, each shaped like its input.
+int validate_backward(const dc1d_tensor *x, const dc1d_tensor *off, const dc1d_tensor *mask,
+                      const dc1d_tensor *w, const dc1d_tensor *gout, const dc1d_tensor *gx,
+                      const dc1d_tensor *goff, const dc1d_tensor *gmask, const dc1d_tensor *gw,
+                      const dc1d_tensor *gb, int64_t stride, int64_t padding, int64_t dilation,
+                      int64_t groups, int64_t offset_groups, Params *p) {
+    if (!gout) return DC1D_ERR_NULL_PTR;
+    int st = validate(x, off, mask, w, nullptr, gout, stride, padding, dilation, groups, offset_groups, p);
+    if (st) return st;
+    if (p->dtype != DC1D_F32) return DC1D_ERR_BAD_DTYPE;
+    if (gmask && !mask) return DC1D_ERR_BAD_ARG;
+    const dc1d_tensor *pairs[4][2] = {{gx, x}, {goff, off}, {gmask, mask}, {gw, w}};
+    for (auto &pr : pairs) {
+        if (!pr[0]) continue;
+        if (pr[0]->dtype != DC1D_F32) return DC1D_ERR_BAD_DTYPE;
+        if (!shape_is(pr[0], pr[1]->ndim, pr[1]->shape)) return DC1D_ERR_BAD_SHAPE;
+    }
+    if (gb) {
+        const int64_t sb[1] = {p->C_out};
+        if (gb->dtype != DC1D_F32) return DC1D_ERR_BAD_DTYPE;
+        if (!shape_is(gb, 1, sb)) return DC1D_ERR_BAD_SHAPE;
+    }
+    return DC1D_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dc1d_backward_workspace_bytes(const dc1d_tensor *x, const dc1d_tensor *offsets,
+                                  const dc1d_tensor *mask_or_null, const dc1d_tensor *weight,
+                                  const dc1d_tensor *grad_out, int want_grad_weight, int64_t stride,
+                                  int64_t padding, int64_t dilation, int64_t groups, int64_t offset_groups,
+                                  size_t *bytes_out) {
+    if (!bytes_out) return DC1D_ERR_NULL_PTR;
+    Params p;
+    int st = validate_backward(x, offsets, mask_or_null, weight, grad_out, nullptr, nullptr, nullptr, nullptr,
+                               nullptr, stride, padding, dilation, groups, offset_groups, &p);
+    if (st) return st;
+    DeviceInfo dev;
+    if ((st = current_device(&dev))) return st;
+    *bytes_out = backward_workspace_bytes(p, want_grad_weight != 0);
+    return DC1D_OK;
+}
+
+int dc1d_backward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_tensor *mask_or_null,
+                  const dc1d_tensor *weight, const dc1d_tensor *grad_out, const dc1d_tensor *grad_x_or_null,
+                  const dc1d_tensor *grad_offsets_or_null, const dc1d_tensor *grad_mask_or_null,
+                  const dc1d_tensor *grad_weight_or_null, const dc1d_tensor *grad_bias_or_null, int64_t stride,
+                  int64_t padding, int64_t dilation, int64_t groups, int64_t offset_groups, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+    Params p;
+    int st = validate_backward(x, offsets, mask_or_null, weight, grad_out, grad_x_or_null, grad_offsets_or_null,
+                               grad_mask_or_null, grad_weight_or_null, grad_bias_or_null, stride, padding,
+                               dilation, groups, offset_groups, &p);
+    if (st) return st;
+    const dc1d_tensor *ins[5] = {x, offsets, mask_or_null, weight, grad_out};
+    const dc1d_tensor *outs[5] = {grad_x_or_null, grad_offsets_or_null, grad_mask_or_null, grad_weight_or_null,
+                                  grad_bias_or_null};
+    for (const dc1d_tensor *t : ins)
+        if (t && numel(t) > 0 && !t->data) return DC1D_ERR_NULL_PTR;
+    for (const dc1d_tensor *t : outs)
+        if (t && numel(t) > 0 && !t->data) return DC1D_ERR_NULL_PTR;
+    // no gradient may overlap an input, another gradient or the workspace
+    const size_t need = backward_workspace_bytes(p, grad_weight_or_null != nullptr);
+    for (int i = 0; i < 5; ++i) {
+        const dc1d_tensor *o = outs[i];
+        if (!o) continue;
+        const size_t ob = (size_t)numel(o) * 4;
+        for (const dc1d_tensor *t : ins)
+            if (t && overlaps(o->data, ob, t->data, (size_t)numel(t) * 4)) return DC1D_ERR_ALIAS;
+        for (int j = i + 1; j < 5; ++j)
+            if (outs[j] && overlaps(o->data, ob, outs[j]->data, (size_t)numel(outs[j]) * 4)) return DC1D_ERR_ALIAS;
+        if (workspace && overlaps(o->data, ob, workspace, need)) return DC1D_ERR_ALIAS;
+    }
+    DeviceInfo dev;
+    if ((st = current_device(&dev))) return st;
+    const bool want_ds = grad_x_or_null || grad_offsets_or_null || grad_mask_or_null || grad_weight_or_null;
+    if (want_ds && (int64_t)p.B * p.C_in * p.K * p.L_out > 0) {
+        if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255)) return DC1D_ERR_WORKSPACE;
+        for (const dc1d_tensor *t : ins)
+            if (t && overlaps(workspace, need, t->data, (size_t)numel(t) * 4)) return DC1D_ERR_ALIAS;
+    }
+    BwdParams a;
+    a.p = p;
+    a.dout = (const float *)grad_out->data;
+    a.gx = grad_x_or_null ? (float *)grad_x_or_null->data : nullptr;
+    a.goff = grad_offsets_or_null ? (float *)grad_offsets_or_null->data : nullptr;
+    a.gmask = grad_mask_or_null ? (float *)grad_mask_or_null->data : nullptr;
+    a.gw = grad_weight_or_null ? (float *)grad_weight_or_null->data : nullptr;
+    a.gb = grad_bias_or_null ? (float *)grad_bias_or_null->data : nullptr;
+    const size_t half = backward_workspace_bytes(p, false);
+    a.dS = (float *)workspace;
+    a.S = grad_weight_or_null ? (float *)((char *)workspace + half) : nullptr;
+    const hipError_t e = launch_backward(a, (hipStream_t)stream);
+    return e == hipSuccess ? DC1D_OK : DC1D_ERR_LAUNCH;
+}
+
 int dc1d_debug_positions(const dc1d_tensor *offsets, int64_t L_in, int64_t stride, int64_t padding,
                          int64_t dilation, int32_t *i0, float *frac, uint8_t *valid, void *stream) {
     if (!offsets) return DC1D_ERR_NULL_PTR;

@@ -138,4 +138,16 @@ hipError_t launch_mfma_f32_mask(const Params &p, const MfmaPlan &pl, hipStream_t
 hipError_t launch_mfma_bf16(const Params &p, const MfmaPlan &pl, hipStream_t stream);
 hipError_t launch_mfma_bf16_mask(const Params &p, const MfmaPlan &pl, hipStream_t stream);
 
+// Backward (fp32): gradients of sum(dout * out).  Any gradient pointer may
+// be null (not computed); dS and S point into the workspace (S only when the
+// weight gradient is wanted).
+struct BwdParams {
+    Params p;  // forward arguments; p.out unused
+    const float *dout;
+    float *gx, *goff, *gmask, *gw, *gb;
+    float *dS, *S;
+};
+size_t backward_workspace_bytes(const Params &p, bool want_weight);
+hipError_t launch_backward(BwdParams a, hipStream_t stream);
+
 }  // namespace dc1d

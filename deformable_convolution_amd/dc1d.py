@@ -71,6 +71,11 @@ def load_library():
                                                          ctypes.POINTER(i64),
                                                          ctypes.POINTER(ctypes.c_int32),
                                                          ctypes.POINTER(ctypes.c_int32)]
+            lib.dc1d_backward_workspace_bytes.restype = ctypes.c_int
+            lib.dc1d_backward_workspace_bytes.argtypes = [T] * 5 + [ctypes.c_int] + [i64] * 5 + [
+                ctypes.POINTER(ctypes.c_size_t)]
+            lib.dc1d_backward.restype = ctypes.c_int
+            lib.dc1d_backward.argtypes = [T] * 10 + [i64] * 5 + [p, ctypes.c_size_t, p]
             lib.dc1d_status_string.restype = ctypes.c_char_p
             lib.dc1d_status_string.argtypes = [ctypes.c_int]
             _lib = lib
@@ -209,6 +214,48 @@ def forward(x, offsets, weight, bias=None, mask=None, stride=1, padding=0, dilat
         _check(lib.dc1d_forward(_ref(dx), _ref(do), _ref(dm), _ref(dw), _ref(db), _ref(dout), stride, padding,
                                 dilation, groups, G, ws_ptr, ws_len, stream), "dc1d_forward")
     return out
+
+
+def backward(x, offsets, weight, grad_out, mask=None, stride=1, padding=0, dilation=1, groups=1,
+             need=("x", "offsets", "mask", "weight", "bias"), workspace=None):
+    """Gradients of sum(grad_out * forward(...)) on the GPU (fp32 tensors).
+    Returns a dict with the requested keys among x, offsets, mask (only with
+    a mask), weight, bias; tensors are allocated here, the arithmetic runs in
+    the library's kernels on torch's current stream."""
+    lib = load_library()
+    x, offsets, weight, grad_out, mask = (_contig(t, n) for t, n in ((x, "x"), (offsets, "offsets"),
+                                                                      (weight, "weight"),
+                                                                      (grad_out, "grad_out"),
+                                                                      (mask, "mask")))
+    padding, G = _args(x, offsets, weight, None, mask, stride, padding, dilation, groups)
+    like = {"x": x, "offsets": offsets, "mask": mask, "weight": weight}
+    grads = {}
+    for k in need:
+        if k == "mask" and mask is None:
+            continue
+        if k == "bias":
+            grads[k] = torch.empty(weight.shape[0], dtype=weight.dtype, device=weight.device)
+        else:
+            grads[k] = torch.empty_like(like[k])
+    dx, do, dm, dw, dg = map(_desc, (x, offsets, mask, weight, grad_out))
+    gd = {k: _desc(v) for k, v in grads.items()}
+    if workspace is None:
+        n = ctypes.c_size_t(0)
+        with torch.cuda.device(x.device):
+            _check(lib.dc1d_backward_workspace_bytes(_ref(dx), _ref(do), _ref(dm), _ref(dw), _ref(dg),
+                                                     int("weight" in grads), stride, padding, dilation,
+                                                     groups, G, ctypes.byref(n)),
+                   "dc1d_backward_workspace_bytes")
+            workspace = _workspace(int(n.value), x.device)
+    ws_ptr = None if workspace is None else workspace.data_ptr()
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        _check(lib.dc1d_backward(_ref(dx), _ref(do), _ref(dm), _ref(dw), _ref(dg),
+                                 _ref(gd.get("x")), _ref(gd.get("offsets")), _ref(gd.get("mask")),
+                                 _ref(gd.get("weight")), _ref(gd.get("bias")), stride, padding, dilation,
+                                 groups, G, ws_ptr, ws_len, stream), "dc1d_backward")
+    return grads
 
 
 def debug_positions(offsets, L_in, stride=1, padding=0, dilation=1):

@@ -153,6 +153,48 @@ int dc1d_forward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_te
                  int64_t offset_groups, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Backward (fp32 storage only; DC1D_ERR_BAD_DTYPE otherwise).  For
+ * grad_out = dL/d(out) [B, C_out, L_out], writes the gradients of
+ * L = sum(grad_out * out) with respect to the inputs of dc1d_forward, each
+ * into a caller buffer shaped like that input (NULL: not computed):
+ *
+ *   dS[b,ci,k,l]    = sum over co's group of weight[co,ci_local,k] * grad_out[b,co,l]
+ *   grad_x[b,ci,i0] += dS*m*(1-f);  grad_x[b,ci,i0+1] += dS*m*f  (indices inside [0, L_in))
+ *   grad_offsets[b,g,l,k] = sum over ci in g of dS*m*(x~(i0+1) - x~(i0))
+ *   grad_mask[b,g,l,k]    = sum over ci in g of dS*((1-f)*x~(i0) + f*x~(i0+1))
+ *   grad_weight[co,cl,k]  = sum over (b,l) of grad_out[b,co,l] * S[b,ci,k,l]
+ *   grad_bias[co]         = sum over (b,l) of grad_out[b,co,l]
+ *
+ * with i0, f, m, x~ and S as in dc1d_forward: the derivatives of the
+ * forward's definition term by term (the dc1d page trains the offsets and
+ * checks their gradient against a finite difference, section Demo
+ * notebook).  The offset gradient is that of the interpolation formula with
+ * i0 held fixed, i.e. the right derivative at integer offsets.  Every
+ * requested gradient is overwritten (grad_x is cleared, then accumulated
+ * with atomics, so its last bits may differ between runs).  grad_mask needs
+ * a mask.  Gradients must not overlap the inputs, each other or the
+ * workspace.
+ *
+ * workspace: at least dc1d_backward_workspace_bytes() bytes, 256-byte
+ * aligned, when any of grad_x, grad_offsets, grad_mask, grad_weight is
+ * requested and B*C_in*K*L_out > 0 (it holds dS, and the samples S when
+ * grad_weight is requested); no initialisation; nothing kept.
+ */
+int dc1d_backward_workspace_bytes(const dc1d_tensor *x, const dc1d_tensor *offsets,
+                                  const dc1d_tensor *mask_or_null, const dc1d_tensor *weight,
+                                  const dc1d_tensor *grad_out, int want_grad_weight, int64_t stride,
+                                  int64_t padding, int64_t dilation, int64_t groups,
+                                  int64_t offset_groups, size_t *bytes_out);
+
+int dc1d_backward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_tensor *mask_or_null,
+                  const dc1d_tensor *weight, const dc1d_tensor *grad_out,
+                  const dc1d_tensor *grad_x_or_null, const dc1d_tensor *grad_offsets_or_null,
+                  const dc1d_tensor *grad_mask_or_null, const dc1d_tensor *grad_weight_or_null,
+                  const dc1d_tensor *grad_bias_or_null, int64_t stride, int64_t padding,
+                  int64_t dilation, int64_t groups, int64_t offset_groups, void *workspace,
+                  size_t workspace_bytes, void *stream);
+
+/*
  * Test aid: the sampling positions the forward kernels use, from the same
  * device function.  For every (b, g, l, k) of offsets [B, G, L_out, K]
  * (K = offsets->shape[3]; L_out must equal dc1d_output_length(L_in, K, ...)):

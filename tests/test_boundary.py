@@ -183,3 +183,45 @@ def test_positions_entry_validation(lib):
     assert lib.dc1d_debug_positions(ctypes.byref(off), 20, 0, 0, 1, i0, i0, i0, None) == dc1d.ERR_BAD_ARG
     assert lib.dc1d_debug_positions(ctypes.byref(off), 21, 1, 0, 1, i0, i0, i0, None) == dc1d.ERR_BAD_SHAPE
     assert lib.dc1d_debug_positions(ctypes.byref(off), 20, 1, 0, 1, None, i0, i0, None) == dc1d.ERR_NULL_PTR
+
+
+# ---- backward entry ------------------------------------------------------------
+
+def bcall(lib, x, off, mask, w, gout, gx=None, goff=None, gmask=None, gw=None, gb=None, G=None, ws=None, ws_n=0):
+    if G is None:
+        G = off.shape[1]
+    r = lambda t: None if t is None else ctypes.byref(t)
+    return lib.dc1d_backward(r(x), r(off), r(mask), r(w), r(gout), r(gx), r(goff), r(gmask), r(gw), r(gb),
+                             1, 0, 1, 1, G, ws, ws_n, None)
+
+
+def grads_like(x, off, mask, w, base=FAKE + (8 << 24)):
+    step = 1 << 24
+    return (T(list(x.shape[:3]), addr=base), T(list(off.shape[:4]), addr=base + step),
+            T(list(mask.shape[:4]), addr=base + 2 * step), T(list(w.shape[:3]), addr=base + 3 * step),
+            T([w.shape[0]], addr=base + 4 * step))
+
+
+def test_backward_validation(lib):
+    x, off, mask, w, bias, out = good()
+    gout = out  # grad_out has the output's shape
+    gx, goff, gmask, gw, gb = grads_like(x, off, mask, w)
+    # everything host-checkable is fine
+    assert bcall(lib, x, off, mask, w, gout, gx, goff, gmask, gw, gb) in (dc1d.ERR_DEVICE, dc1d.ERR_WORKSPACE,
+                                                                         dc1d.OK)
+    assert bcall(lib, x, off, mask, w, None, gx) == dc1d.ERR_NULL_PTR
+    # fp32 only
+    xb = T([2, 8, 20], dtype=1, addr=x.data)
+    ob = T([2, 2, 18, 3], dtype=1, addr=off.data)
+    wb = T([6, 8, 3], dtype=1, addr=w.data)
+    gb16 = T([2, 6, 18], dtype=1, addr=gout.data)
+    assert bcall(lib, xb, ob, None, wb, gb16) == dc1d.ERR_BAD_DTYPE
+    # a mask gradient needs a mask
+    assert bcall(lib, x, off, None, w, gout, gmask=gmask) == dc1d.ERR_BAD_ARG
+    # gradient shapes follow their inputs
+    assert bcall(lib, x, off, mask, w, gout, gx=T([2, 8, 19], addr=gx.data)) == dc1d.ERR_BAD_SHAPE
+    assert bcall(lib, x, off, mask, w, gout, gb=T([5], addr=gb.data)) == dc1d.ERR_BAD_SHAPE
+    assert bcall(lib, x, off, mask, w, T([2, 6, 17], addr=gout.data)) == dc1d.ERR_BAD_SHAPE
+    # no gradient on an input or on another gradient
+    assert bcall(lib, x, off, mask, w, gout, gx=T([2, 8, 20], addr=x.data)) == dc1d.ERR_ALIAS
+    assert bcall(lib, x, off, mask, w, gout, gx=gx, gw=T([6, 8, 3], addr=gx.data + 16)) == dc1d.ERR_ALIAS
