@@ -22,6 +22,8 @@ before timing; a mismatch aborts the bench.
 --profile-run runs only the warmup + timed launches (no oracle, no JSON),
 for rocprofv3; --copy-calibration MB runs one device-to-device copy of that
 size (the reference kernel for scaling the HBM byte counters).
+--backward times the backward (all five gradients, fp32 workloads) the
+same way, with the oracle's backward as parity check and CPU baseline.
 --summarize-profile DIR --kernel NAME folds the rocprofv3 output of the
 commands listed in PROFILE_COMMANDS (kernel trace, FETCH_SIZE / WRITE_SIZE
 passes, copy calibration) into profiles/<workload>__<kernel>.md; the bench
@@ -170,6 +172,114 @@ def run_gpu(w, steps, warmup, check=True, cold_reps=0):
     return {"plan": plan, "region_ms": region_ms, "launch_ms": launch_ms, "cold_ms": cold_ms, "parity": parity}
 
 
+def work_backward(w):
+    """Algorithmic work of one backward (all five gradients): the two
+    contractions (dS = W^T dout and grad_W = dout S^T, each as many flops as
+    the forward's), sampling and scattering (7 flops per sample: the sample,
+    dS times the two lerp weights and the two offset/mask terms), and the
+    bytes of every input read once and every gradient written once."""
+    contraction, _, _ = work(w)
+    samples = w.B * w.C_in * w.L_out * w.K
+    n_off = w.B * w.G * w.L_out * w.K
+    elems_in = (w.B * w.C_in * w.L_in + n_off * (2 if w.mask_dist else 1) + w.C_out * (w.C_in // w.groups) * w.K
+                + w.B * w.C_out * w.L_out)
+    elems_out = (w.B * w.C_in * w.L_in + n_off * (2 if w.mask_dist else 1) + w.C_out * (w.C_in // w.groups) * w.K
+                 + w.C_out)
+    return 2 * contraction, 7 * samples, 4 * (elems_in + elems_out)
+
+
+def run_backward(w, steps, warmup, check=True, baseline=True):
+    """Time the backward (every gradient) on the GPU; check it against the
+    oracle's backward, whose run is also the CPU baseline."""
+    import torch
+    from deformable_convolution_amd import dc1d, inputs
+
+    dev = torch.device("cuda:0")
+    t = inputs.make_inputs(w, seed=0)
+    gen = torch.Generator().manual_seed(1000)
+    dout = torch.randn((w.B, w.C_out, w.L_out), generator=gen, dtype=torch.float32)
+    g = {k: (v.to(dev) if v is not None else None) for k, v in t.items()}
+    gd = dout.to(dev)
+    kw = dict(stride=w.stride, padding=w.padding, dilation=w.dilation, groups=w.groups)
+
+    def step():
+        return dc1d.backward(g["x"], g["offsets"], g["weight"], gd, g["mask"], **kw)
+
+    got = step()
+    torch.cuda.synchronize()
+    parity, cpu = None, None
+    if check or baseline:
+        import oracle
+        cores = len(os.sched_getaffinity(0))
+        os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+        t0 = time.perf_counter()
+        ref = oracle.backward(t["x"], t["offsets"], t["weight"], dout, t["mask"], **kw)
+        el = time.perf_counter() - t0
+        c2, s2, _ = work_backward(w)
+        cpu = {"value": (c2 + s2) / el / 1e9, "unit": "GFLOP/s", "cores": min(int(os.environ["OMP_NUM_THREADS"]),
+                                                                             cores),
+               "kind": "oracle", "sample": "1 full backward (all five gradients) of the same workload, %.1f s, on %s"
+               % (el, cpu_model())}
+        opg, cpo = w.C_out // w.groups, w.C_in // w.G
+        n = {"x": opg * w.K * 2, "offsets": cpo * opg, "mask": cpo * opg, "weight": w.B * w.L_out,
+             "bias": w.B * w.L_out}
+        worst = 0.0
+        for k, r in ref.items():
+            if r is None:
+                continue
+            a = got[k].double().cpu().numpy()
+            rms = math.sqrt(float(np.mean(r ** 2))) if r.size else 0.0
+            tol = 1e-5 * math.sqrt(n[k]) * rms + 1e-6
+            e = float(np.abs(a - r).max()) if r.size else 0.0
+            worst = max(worst, e / tol)
+        parity = {"gradients": sorted(k for k, r in ref.items() if r is not None), "max_err_over_tol": worst,
+                  "ok": bool(worst <= 1.0)}
+        if not parity["ok"]:
+            raise SystemExit("backward parity check failed: %r" % parity)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        step()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i].record(stream)
+        step()
+    ev[steps].record(stream)
+    torch.cuda.synchronize()
+    launch_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return {"region_ms": ev[0].elapsed_time(ev[steps]), "launch_ms": launch_ms, "parity": parity, "cpu": cpu}
+
+
+def main_backward(args, w):
+    r = run_backward(w, args.steps, args.warmup, baseline=not args.no_cpu_baseline)
+    contraction, sampling, nbytes = work_backward(w)
+    ms = r["region_ms"] / args.steps
+    if w.groups == 1:
+        achieved = contraction / (ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK["mfma_f32_TFLOPs"], "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK["mfma_f32_TFLOPs"], 4)}
+    else:
+        achieved = nbytes / (ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm_GBps"], "unit": "GB/s",
+                "frac": round(achieved / PEAK["hbm_GBps"], 4)}
+    roof["traffic"] = None
+    roof["kernel"] = "backward"
+    roof["kernel_ms"] = round(ms, 5)
+    line = {
+        "metric": "DeformConv1d bwd GFLOP/s (all five gradients)",
+        "value": round((contraction + sampling) / (ms * 1e-3) / 1e9, 1),
+        "unit": "GFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic, seeded (deformable_convolution_amd/inputs.py; no dataset)",
+        "config": {"workload": workload_label(w), "pass": "backward", "gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                   "parity": r["parity"], "forward_ms": {"warm": pct(r["launch_ms"])}},
+        "roofline": roof,
+    }
+    if r["cpu"] is not None:
+        line["cpu_baseline"] = r["cpu"]
+    print(json.dumps(line), flush=True)
+
+
 def pct(v):
     """median, p10, p90 of a list of times (ms)."""
     if not v:
@@ -224,6 +334,7 @@ def main():
     ap.add_argument("--all", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true")
+    ap.add_argument("--backward", action="store_true", help="time the backward (fp32 workloads) instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB")
     ap.add_argument("--summarize-profile", default=None, metavar="DIR")
     ap.add_argument("--kernel", default=None, help="the plan's kernel name, for --summarize-profile")
@@ -253,6 +364,15 @@ def main():
         return
 
     w = inputs.WORKLOADS[args.workload]
+    if args.backward:
+        if w.dtype != "f32":
+            raise SystemExit("the backward runs on fp32 workloads")
+        if args.profile_run:
+            run_backward(w, args.steps, args.warmup, check=False, baseline=False)
+            print("profile run: %s backward, %d timed launches" % (w.name, args.steps), flush=True)
+            return
+        main_backward(args, w)
+        return
     if args.profile_run:
         r = run_gpu(w, args.steps, args.warmup, check=False)
         print("profile run: %s %s, %d timed launches, %.4f ms/launch" % (

@@ -303,7 +303,7 @@ int dc1d_backward_workspace_bytes(const dc1d_tensor *x, const dc1d_tensor *offse
     if (st) return st;
     DeviceInfo dev;
     if ((st = current_device(&dev))) return st;
-    *bytes_out = backward_workspace_bytes(p, want_grad_weight != 0);
+    *bytes_out = backward_workspace_bytes(p, want_grad_weight != 0, dev.num_cus);
     return DC1D_OK;
 }
 
@@ -325,8 +325,7 @@ int dc1d_backward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_t
         if (t && numel(t) > 0 && !t->data) return DC1D_ERR_NULL_PTR;
     for (const dc1d_tensor *t : outs)
         if (t && numel(t) > 0 && !t->data) return DC1D_ERR_NULL_PTR;
-    // no gradient may overlap an input, another gradient or the workspace
-    const size_t need = backward_workspace_bytes(p, grad_weight_or_null != nullptr);
+    // no gradient may overlap an input or another gradient
     for (int i = 0; i < 5; ++i) {
         const dc1d_tensor *o = outs[i];
         if (!o) continue;
@@ -335,10 +334,13 @@ int dc1d_backward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_t
             if (t && overlaps(o->data, ob, t->data, (size_t)numel(t) * 4)) return DC1D_ERR_ALIAS;
         for (int j = i + 1; j < 5; ++j)
             if (outs[j] && overlaps(o->data, ob, outs[j]->data, (size_t)numel(outs[j]) * 4)) return DC1D_ERR_ALIAS;
-        if (workspace && overlaps(o->data, ob, workspace, need)) return DC1D_ERR_ALIAS;
     }
     DeviceInfo dev;
     if ((st = current_device(&dev))) return st;
+    // ... nor the workspace
+    const size_t need = backward_workspace_bytes(p, grad_weight_or_null != nullptr, dev.num_cus);
+    for (const dc1d_tensor *o : outs)
+        if (o && workspace && overlaps(o->data, (size_t)numel(o) * 4, workspace, need)) return DC1D_ERR_ALIAS;
     const bool want_ds = grad_x_or_null || grad_offsets_or_null || grad_mask_or_null || grad_weight_or_null;
     if (want_ds && (int64_t)p.B * p.C_in * p.K * p.L_out > 0) {
         if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255)) return DC1D_ERR_WORKSPACE;
@@ -353,10 +355,9 @@ int dc1d_backward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_t
     a.gmask = grad_mask_or_null ? (float *)grad_mask_or_null->data : nullptr;
     a.gw = grad_weight_or_null ? (float *)grad_weight_or_null->data : nullptr;
     a.gb = grad_bias_or_null ? (float *)grad_bias_or_null->data : nullptr;
-    const size_t half = backward_workspace_bytes(p, false);
-    a.dS = (float *)workspace;
-    a.S = grad_weight_or_null ? (float *)((char *)workspace + half) : nullptr;
-    const hipError_t e = launch_backward(a, (hipStream_t)stream);
+    a.dS = (float *)workspace;  // the workspace base; launch_backward lays it out
+    a.S = nullptr;
+    const hipError_t e = launch_backward(a, dev.num_cus, (hipStream_t)stream);
     return e == hipSuccess ? DC1D_OK : DC1D_ERR_LAUNCH;
 }
 

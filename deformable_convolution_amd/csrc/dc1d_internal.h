@@ -147,7 +147,12 @@ struct BwdParams {
     float *gx, *goff, *gmask, *gw, *gb;
     float *dS, *S;
 };
-size_t backward_workspace_bytes(const Params &p, bool want_weight);
-hipError_t launch_backward(BwdParams a, hipStream_t stream);
+// Plain fp32 GEMM on the MFMA kernel (k_mfma.hip): C[b][m][j] =
+// sum_k A[m][k] * x[b*bbatch + j + k*brow] with A = q.w [q.C_out][q.Kred],
+// C = q.out [q.B][q.C_out][q.L_out]; split partials in q.ws.
+size_t gemm_workspace_bytes(const Params &q, int num_cus);
+hipError_t launch_gemm_f32(const Params &q, int64_t brow, int64_t bbatch, int num_cus, hipStream_t stream);
+size_t backward_workspace_bytes(const Params &p, bool want_weight, int num_cus);
+hipError_t launch_backward(BwdParams a, int num_cus, hipStream_t stream);
 
 }  // namespace dc1d

@@ -193,6 +193,55 @@ MfmaPlan plan_mfma(const Params &p, int num_cus) {
     return pl;
 }
 
+size_t gemm_workspace_bytes(const Params &q, int num_cus) {
+    using Tr = TrF32;
+    constexpr int BM = Geo<Tr>::BM, BN = Geo<Tr>::BN;
+    MfmaPlan pl = {};
+    const int64_t N = (int64_t)q.B * q.L_out;
+    pl.tiles_m = (q.C_out + BM - 1) / BM;
+    pl.tiles_n = (int)((N + BN - 1) / BN);
+    pl.chunks = (q.Kred + BK - 1) / BK;
+    plan_splits((int64_t)pl.tiles_m * pl.tiles_n, pl.chunks, num_cus, pl);
+    return pl.splits > 1 ? (size_t)pl.tiles_m * pl.tiles_n * pl.splits * BM * BN * 4 : 0;
+}
+
+hipError_t launch_gemm_f32(const Params &q, int64_t brow, int64_t bbatch, int num_cus, hipStream_t stream) {
+    using Tr = TrF32;
+    constexpr int BM = Geo<Tr>::BM, BN = Geo<Tr>::BN;
+    MfmaPlan pl = {};
+    const int64_t N = (int64_t)q.B * q.L_out;
+    if (N == 0 || q.C_out == 0) return hipSuccess;
+    pl.tiles_m = (q.C_out + BM - 1) / BM;
+    pl.tiles_n = (int)((N + BN - 1) / BN);
+    pl.chunks = (q.Kred + BK - 1) / BK;
+    plan_splits((int64_t)pl.tiles_m * pl.tiles_n, pl.chunks, num_cus, pl);
+    MfmaArgs a = {};
+    a.p = q;
+    a.fd_Lout = make_fastdiv((uint32_t)q.L_out);
+    a.fd_K = a.fd_cpo = a.fd_nkb = make_fastdiv(1);
+    a.tiles_m = pl.tiles_m;
+    a.tiles_n = pl.tiles_n;
+    a.splits = pl.splits;
+    a.chunks = pl.chunks;
+    a.N = N;
+    a.vec_w = (q.Kred % 4 == 0) && (((uintptr_t)q.w & 15) == 0);
+    a.off_w = 0;
+    a.off_s = 2 * BM * BK * 4;
+    a.partials = pl.splits > 1 ? (float *)q.ws : nullptr;
+    a.brow = brow;
+    a.bbatch = bbatch;
+    const size_t lds = (size_t)a.off_s + 2 * (size_t)BN * Tr::SLD * 4;
+    hipLaunchKernelGGL((k_gemm<Tr>), dim3((unsigned)pl.blocks), dim3(NTT), lds, stream, a);
+    if (pl.splits > 1) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t tiles = (int64_t)pl.tiles_m * pl.tiles_n;
+        const int64_t vecs = tiles * (BM * BN / 4);
+        hipLaunchKernelGGL((k_split_reduce<Tr>), dim3((unsigned)((vecs + 255) / 256)), dim3(256), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_mfma(const Params &p, const MfmaPlan &pl, hipStream_t stream) {
     if (pl.blocks == 0) return hipSuccess;
     if (p.dtype == kF32) return p.mask ? launch_mfma_f32_mask(p, pl, stream) : launch_mfma_f32(p, pl, stream);

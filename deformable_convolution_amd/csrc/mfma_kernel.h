@@ -97,6 +97,9 @@ struct MfmaArgs {
     const void *wb;
     int ncb, nkb;
     FastDiv fd_nkb;
+    // plain GEMM only (k_gemm): B element (k, n = b*L_out + j) sits at
+    // x[b*bbatch + j + k*brow]
+    int64_t brow, bbatch;
 };
 
 __device__ __forceinline__ int remap_xcd(int u, int U) {
@@ -956,6 +959,86 @@ __global__ void __launch_bounds__(256) k_weight_blocks(const T *__restrict__ w, 
         const int ci = (j >> 5) * cbs + (r >> tpc_log2), k = (kb << tpc_log2) + (r & tmask);
         dst[j] = (ci < C_in && k < K) ? wm[ci * K + k] : (T)0;
     }
+}
+
+// ---- plain GEMM (used by the backward) -------------------------------------------
+//
+// C[b][m][j] = sum_k A[m][k] * B(k, n),  n = b*L_out + j, for A = p.w row-major
+// [M = p.C_out][p.Kred] and B(k, n) = p.x[b*bbatch + j + k*brow]; C = p.out
+// [B][M][L_out].  The MFMA role is the forward's (weights = A); the second
+// role loads the B tile instead of sampling it: thread (h, col) loads rows
+// 16h .. 16h+15 of its column one chunk ahead into registers and writes them
+// to the sample tile an iteration later, so the load latency hides behind
+// the MFMAs.
+template <class Tr>
+__device__ __forceinline__ void loader_role(const MfmaArgs &a, const Tile &tl, typename Tr::T *s_S) {
+    using D = typename Tr::D;
+    using T = typename Tr::T;
+    constexpr int BN = Geo<Tr>::BN, SLD = Tr::SLD;
+    const Params &p = a.p;
+    const int ts = threadIdx.x - NTM;
+    const int lane = ts % 64;
+    const int sw = __builtin_amdgcn_readfirstlane(ts / 64);
+    const int h = sw & 1;
+    const int col = 64 * (sw >> 1) + lane;
+    const int n = (int)tl.n0 + col;
+    const bool cok = n < a.N;
+    const int b = cok ? (int)fdiv((uint32_t)n, a.fd_Lout) : 0;
+    const T *__restrict__ bcol = (const T *)p.x + (cok ? (int64_t)b * a.bbatch + (n - b * p.L_out) : 0);
+    const int Kred = p.Kred;
+    float breg[16];
+    auto fetch = [&](int c) {  // clamped addresses; rows past Kred are zeroed in put
+        const int r0 = c * BK + 16 * h;
+#pragma unroll
+        for (int s2 = 0; s2 < 16; ++s2) breg[s2] = D::ld(bcol, (int64_t)min(r0 + s2, Kred - 1) * a.brow);
+    };
+    auto put = [&](int c) {
+        const int r0 = c * BK + 16 * h;
+        float v[16];
+#pragma unroll
+        for (int s2 = 0; s2 < 16; ++s2) v[s2] = (cok && r0 + s2 < Kred) ? breg[s2] : 0.0f;
+        Tr::store_b(s_S + (c & 1) * BN * SLD + col * SLD + 16 * h, v);
+    };
+    const int c0 = tl.c_begin, c1 = tl.c_end;
+    if (c0 < c1) {
+        fetch(c0);
+        put(c0);
+    }
+    if (c0 + 1 < c1) fetch(c0 + 1);
+    // the MFMA role's two prologue barriers
+    __syncthreads();
+    __syncthreads();
+    for (int c = c0; c < c1; ++c) {
+        if (c + 1 < c1) put(c + 1);    // loaded during the previous iteration
+        if (c + 2 < c1) fetch(c + 2);
+        __syncthreads();
+    }
+}
+
+template <class Tr>
+__global__ void __launch_bounds__(NTT) k_gemm(MfmaArgs a) {
+    using T = typename Tr::T;
+    constexpr int BM = Geo<Tr>::BM, BN = Geo<Tr>::BN;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    T *s_w = (T *)(smem + a.off_w);  // [2][BM][BK], swizzled
+    T *s_S = (T *)(smem + a.off_s);  // [2][BN][SLD]
+    const int U = a.tiles_m * a.tiles_n * a.splits;
+    const int u = remap_xcd(blockIdx.x, U);
+    Tile tl;
+    tl.tn = u % a.tiles_n;
+    const int rest = u / a.tiles_n;
+    tl.sp = rest % a.splits;
+    tl.tm = rest / a.splits;
+    tl.m0 = tl.tm * BM;
+    tl.n0 = (int64_t)tl.tn * BN;
+    tl.c_begin = (int)((int64_t)tl.sp * a.chunks / a.splits);
+    tl.c_end = (int)((int64_t)(tl.sp + 1) * a.chunks / a.splits);
+    tl.win = false;
+    tl.WT = tl.nseg = tl.b_first = 0;
+    if (threadIdx.x < NTM)
+        mfma_role<Tr, 0>(a, tl, s_w, s_S);
+    else
+        loader_role<Tr>(a, tl, s_S);
 }
 
 // Sum of the split partial tiles (in split order), plus bias, into out.
