@@ -342,7 +342,7 @@ int dc1d_backward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_t
     for (const dc1d_tensor *o : outs)
         if (o && workspace && overlaps(o->data, (size_t)numel(o) * 4, workspace, need)) return DC1D_ERR_ALIAS;
     const bool want_ds = grad_x_or_null || grad_offsets_or_null || grad_mask_or_null || grad_weight_or_null;
-    if (want_ds && (int64_t)p.B * p.C_in * p.K * p.L_out > 0) {
+    if (want_ds && need > 0 && (int64_t)p.B * p.C_in * p.K * p.L_out > 0) {
         if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255)) return DC1D_ERR_WORKSPACE;
         for (const dc1d_tensor *t : ins)
             if (t && overlaps(workspace, need, t->data, (size_t)numel(t) * 4)) return DC1D_ERR_ALIAS;

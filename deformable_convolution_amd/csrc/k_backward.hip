@@ -16,19 +16,21 @@
 // interpolation formula's with i0 held fixed (the right derivative at
 // integer offsets).
 //
-// Dense shapes (groups == 1), in order on the caller's stream:
-//   k_bwd_zero       clears grad_x (it is accumulated with atomics);
-//   k_transpose      W -> W^T [C_in*K][C_out] (workspace);
-//   k_gemm           dS = W^T dout on the MFMA kernel, [B][C_in*K][L_out];
-//   k_bwd_samples_t  per (b, l, ci, k): the sample S in [(b,l)][C_in*K]
-//                    (for the weight gradient) and dS scattered into grad_x;
-//   k_bwd_offmask    per (b, g, l, k): offset and mask gradients from dS;
-//   k_restride_dout  dout -> [C_out][B*L_out];
-//   k_gemm           grad_weight = dout S^T on the MFMA kernel;
+// Kernels, in order on the caller's stream:
+//   k_bwd_zero       clears grad_x (and the offset / mask gradients when they
+//                    are accumulated over several channel blocks);
+//   dS               dense shapes (groups == 1): k_transpose W -> W^T, then
+//                    k_gemm dS = W^T dout on the MFMA kernel; other shapes:
+//                    k_bwd_samples (a loop over the group's output channels);
+//                    dS is [B][C_in][K][L_out] in the workspace;
+//   samples          for the weight gradient: k_bwd_samples_t writes them in
+//                    the weight GEMM's layout [(b, l)][C_in*K] (dense), or
+//                    k_bwd_samples beside dS as [B][C_in][K][L_out];
+//   k_bwd_dx         grad_x, grad_offsets, grad_mask from dS (tiled, LDS
+//                    windows);
+//   weight gradient  dense: k_restride_dout then k_gemm grad_weight =
+//                    dout S^T; other shapes: k_bwd_weight;
 //   k_bwd_bias       one workgroup per output channel.
-// Other shapes: k_bwd_samples (dS by a loop over the group's output
-// channels, S and the grad_x scatter per (b, ci, k, l)), k_bwd_offmask,
-// k_bwd_weight (one workgroup per (co, ci_local)), k_bwd_bias.
 #include "dc1d_internal.h"
 
 #include <algorithm>
@@ -73,71 +75,32 @@ __global__ void __launch_bounds__(256) k_bwd_samples(BwdParams a) {
             const float x0 = v0 ? xrow[i0] : 0.0f, x1 = v1 ? xrow[i0 + 1] : 0.0f;
             a.S[e] = fmaf(f, x1 - x0, x0) * m;
         }
-        if (a.gx) {
-            float *grow = a.gx + ((int64_t)b * p.C_in + ci) * p.L_in;
-            const float dm = ds * m;
-            if (v0) unsafeAtomicAdd(grow + i0, dm * (1.0f - f));
-            if (v1) unsafeAtomicAdd(grow + i0 + 1, dm * f);
-        }
     }
 }
 
-__global__ void __launch_bounds__(256) k_bwd_offmask(BwdParams a) {
-    const Params &p = a.p;
-    const float *__restrict__ x = (const float *)p.x;
-    const float *__restrict__ off = (const float *)p.off;
-    const float *__restrict__ mask = (const float *)p.mask;
-    const int64_t n = (int64_t)p.B * p.G * p.L_out * p.K;
-    for (int64_t oi = (int64_t)blockIdx.x * 256 + threadIdx.x; oi < n; oi += (int64_t)gridDim.x * 256) {
-        const int k = (int)(oi % p.K);
-        const int64_t r1 = oi / p.K;
-        const int l = (int)(r1 % p.L_out);
-        const int64_t r2 = r1 / p.L_out;
-        const int g = (int)(r2 % p.G);
-        const int b = (int)(r2 / p.G);
-        int i0;
-        float f;
-        split_position(off[oi], l * p.stride - p.padding + k * p.dilation, i0, f);
-        const float m = mask ? mask[oi] : 1.0f;
-        const bool v0 = i0 >= 0 && i0 < p.L_in, v1 = i0 + 1 >= 0 && i0 + 1 < p.L_in;
-        float ao = 0.0f, am = 0.0f;
-        for (int ci = g * p.cpo; ci < (g + 1) * p.cpo; ++ci) {
-            const float *xrow = x + ((int64_t)b * p.C_in + ci) * p.L_in;
-            const float x0 = v0 ? xrow[i0] : 0.0f, x1 = v1 ? xrow[i0 + 1] : 0.0f;
-            const float ds = a.dS[(((int64_t)b * p.C_in + ci) * p.K + k) * p.L_out + l];
-            ao = fmaf(ds * m, x1 - x0, ao);
-            am = fmaf(ds, fmaf(f, x1 - x0, x0), am);
-        }
-        if (a.goff) a.goff[oi] = ao;
-        if (a.gmask) a.gmask[oi] = am;
-    }
-}
-
-// One workgroup per (co, cl): its K weight gradients, each a sum over
-// (b, l) of dout[b, co, l] * S[b, ci, k, l]; threads stride over l, then a
-// tree reduction in LDS (fixed order: deterministic).
+// One workgroup per weight element (co, cl, k): a sum over (b, l) of
+// dout[b, co, l] * S[b, ci, k, l]; threads stride over l, then a tree
+// reduction in LDS (fixed order: deterministic).
 __global__ void __launch_bounds__(256) k_bwd_weight(BwdParams a) {
     const Params &p = a.p;
     __shared__ float s_red[256];
-    const int row = blockIdx.x;  // co * cpg + cl
+    const int e = blockIdx.x;  // (co * cpg + cl) * K + k
+    const int k = e % p.K, row = e / p.K;
     const int co = row / p.cpg, cl = row - co * p.cpg;
     const int ci = (co / p.opg) * p.cpg + cl;
-    for (int k = 0; k < p.K; ++k) {
-        float acc = 0.0f;
-        for (int b = 0; b < p.B; ++b) {
-            const float *d = a.dout + ((int64_t)b * p.C_out + co) * p.L_out;
-            const float *srow = a.S + (((int64_t)b * p.C_in + ci) * p.K + k) * p.L_out;
-            for (int l = threadIdx.x; l < p.L_out; l += 256) acc = fmaf(d[l], srow[l], acc);
-        }
-        s_red[threadIdx.x] = acc;
-        __syncthreads();
-        for (int h = 128; h > 0; h >>= 1) {
-            if ((int)threadIdx.x < h) s_red[threadIdx.x] += s_red[threadIdx.x + h];
-            __syncthreads();
-        }
-        if (threadIdx.x == 0) a.gw[(int64_t)row * p.K + k] = s_red[0];
+    float acc = 0.0f;
+    for (int b = 0; b < p.B; ++b) {
+        const float *d = a.dout + ((int64_t)b * p.C_out + co) * p.L_out;
+        const float *srow = a.S + (((int64_t)b * p.C_in + ci) * p.K + k) * p.L_out;
+        for (int l = threadIdx.x; l < p.L_out; l += 256) acc = fmaf(d[l], srow[l], acc);
+    }
+    s_red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if ((int)threadIdx.x < h) s_red[threadIdx.x] += s_red[threadIdx.x + h];
         __syncthreads();
     }
+    if (threadIdx.x == 0) a.gw[e] = s_red[0];
 }
 
 __global__ void __launch_bounds__(256) k_bwd_bias(BwdParams a) {
@@ -161,7 +124,7 @@ __global__ void __launch_bounds__(256) k_bwd_bias(BwdParams a) {
 // Dense path (groups == 1): dS = W^T dout and grad_weight = dout S^T are
 // two plain GEMMs on the MFMA kernel.  This kernel writes the samples for
 // the weight gradient in the GEMM's layout [(b, l)][ci*K + k] (one thread
-// per element, (ci, k) fastest) and scatters dS into grad_x.
+// per element, (ci, k) fastest).
 __global__ void __launch_bounds__(256) k_bwd_samples_t(BwdParams a) {
     const Params &p = a.p;
     const float *__restrict__ x = (const float *)p.x;
@@ -186,12 +149,257 @@ __global__ void __launch_bounds__(256) k_bwd_samples_t(BwdParams a) {
             const float x0 = v0 ? xrow[i0] : 0.0f, x1 = v1 ? xrow[i0 + 1] : 0.0f;
             a.S[e] = fmaf(f, x1 - x0, x0) * m;
         }
-        if (a.gx) {
-            const float ds = a.dS[((int64_t)b * CK + r) * p.L_out + l];
-            float *grow = a.gx + ((int64_t)b * p.C_in + ci) * p.L_in;
-            const float dm = ds * m;
-            if (v0) unsafeAtomicAdd(grow + i0, dm * (1.0f - f));
-            if (v1) unsafeAtomicAdd(grow + i0 + 1, dm * f);
+    }
+}
+
+// grad_x, grad_offsets and grad_mask from dS, tiled.  A workgroup takes
+// one batch b, a block of CBX channels inside one offset group and LT
+// consecutive outputs; each thread owns fixed (k, l) pairs, splits their
+// positions once, and loops over the block's channels reading dS (coalesced
+// along l) and x from an LDS window of the rows (the tile's span plus
+// kBwdMargin on each side, zero outside [0, L_in)).  The grad_x
+// contributions accumulate in an LDS window (LDS atomics) that is added to
+// grad_x once at the end; samples moved outside the window use global
+// atomics directly.  The offset and mask gradients of a pair accumulate in
+// registers over the block's channels and are stored (a block holding the
+// whole offset group) or added atomically (several blocks per group).
+constexpr int kBwdMargin = 32;
+
+struct DxPlan {
+    int cbx, lt, win, tiles_l, ngrp_blocks;
+    bool atomic_om;  // several channel blocks per offset group
+    size_t lds;
+};
+
+__global__ void __launch_bounds__(256) k_bwd_dx(BwdParams a, DxPlan pl) {
+    const Params &p = a.p;
+    extern __shared__ float smem[];
+    const int CBX = pl.cbx, LT = pl.lt, W = pl.win;
+    float *xs = smem;                  // [CBX][W]
+    float *gacc = smem + CBX * W;      // [CBX][W]
+    const int K = p.K, L_in = p.L_in, L_out = p.L_out;
+    int blk = blockIdx.x;
+    const int tile = blk % pl.tiles_l;
+    blk /= pl.tiles_l;
+    const int cblk = blk % pl.ngrp_blocks;  // channel block over all of C_in
+    const int b = blk / pl.ngrp_blocks;
+    const int ci0 = cblk * CBX, g = ci0 / p.cpo;
+    const int l0 = tile * LT;
+    const int lo = l0 * p.stride - p.padding - kBwdMargin;
+    const float *__restrict__ x = (const float *)p.x + ((int64_t)b * p.C_in + ci0) * L_in;
+    for (int e = threadIdx.x; e < CBX * W; e += 256) {
+        const int c = e / W, j = e - c * W, pos = lo + j;
+        xs[e] = (pos >= 0 && pos < L_in) ? x[(int64_t)c * L_in + pos] : 0.0f;
+        gacc[e] = 0.0f;
+    }
+    __syncthreads();
+    const float *__restrict__ off = (const float *)p.off;
+    const float *__restrict__ mask = (const float *)p.mask;
+    float *__restrict__ gx = a.gx ? a.gx + ((int64_t)b * p.C_in + ci0) * L_in : nullptr;
+    // pairs (k, l) of the tile, l fastest; thread t owns pairs t, t+256, ...
+    const int npair = K * LT;
+    for (int pq = threadIdx.x; pq < npair; pq += 256) {
+        const int k = pq / LT, ll = pq - k * LT, l = l0 + ll;
+        if (l >= L_out) continue;
+        const int64_t oi = (((int64_t)b * p.G + g) * L_out + l) * K + k;
+        int i0;
+        float f;
+        split_position(off[oi], l * p.stride - p.padding + k * p.dilation, i0, f);
+        const float m = mask ? mask[oi] : 1.0f;
+        const int j = i0 - lo;
+        const bool inwin = W > 1 && (unsigned)j < (unsigned)(W - 1);
+        const bool v0 = i0 >= 0 && i0 < L_in, v1 = i0 + 1 >= 0 && i0 + 1 < L_in;
+        const float *__restrict__ dsp = a.dS + (((int64_t)b * p.C_in + ci0) * K + k) * L_out + l;
+        const int64_t dstride = (int64_t)K * L_out;
+        float ao = 0.0f, am = 0.0f;
+        for (int c0 = 0; c0 < CBX; c0 += 8) {
+            // eight channels' dS in flight at once (clamped reads; channels
+            // past the block are skipped below)
+            float dsv[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) dsv[u] = dsp[(int64_t)min(c0 + u, CBX - 1) * dstride];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+            const int c = c0 + u;
+            if (c >= CBX) break;
+            const float ds = dsv[u];
+            float x0, x1;
+            if (inwin) {
+                x0 = xs[c * W + j];
+                x1 = xs[c * W + j + 1];
+            } else {
+                const float *xr = x + (int64_t)c * L_in;
+                x0 = v0 ? xr[i0] : 0.0f;
+                x1 = v1 ? xr[i0 + 1] : 0.0f;
+            }
+            ao = fmaf(ds * m, x1 - x0, ao);
+            am = fmaf(ds, fmaf(f, x1 - x0, x0), am);
+            if (gx) {
+                const float dm = ds * m;
+                if (inwin) {
+                    atomicAdd(gacc + c * W + j, dm * (1.0f - f));
+                    atomicAdd(gacc + c * W + j + 1, dm * f);
+                } else {
+                    if (v0) unsafeAtomicAdd(gx + (int64_t)c * L_in + i0, dm * (1.0f - f));
+                    if (v1) unsafeAtomicAdd(gx + (int64_t)c * L_in + i0 + 1, dm * f);
+                }
+            }
+            }
+        }
+        if (pl.atomic_om) {
+            if (a.goff) unsafeAtomicAdd(a.goff + oi, ao);
+            if (a.gmask) unsafeAtomicAdd(a.gmask + oi, am);
+        } else {
+            if (a.goff) a.goff[oi] = ao;
+            if (a.gmask) a.gmask[oi] = am;
+        }
+    }
+    if (!gx) return;
+    __syncthreads();
+    for (int e = threadIdx.x; e < CBX * W; e += 256) {
+        const int c = e / W, j = e - c * W, pos = lo + j;
+        const float v = gacc[e];
+        if (pos >= 0 && pos < L_in && v != 0.0f) unsafeAtomicAdd(gx + (int64_t)c * L_in + pos, v);
+    }
+}
+
+DxPlan plan_dx(const Params &p) {
+    DxPlan pl;
+    int cbx = 1;  // the largest divisor of the offset group's channel count up to 32
+    for (int c = 32; c >= 1; --c)
+        if (p.cpo % c == 0) {
+            cbx = c;
+            break;
+        }
+    int lt = 2048 / p.K;  // about eight (k, l) pairs per thread
+    lt = lt < 32 ? 32 : (lt > 1024 ? 1024 : lt / 32 * 32);
+    if (lt > p.L_out) lt = (p.L_out + 31) / 32 * 32;
+    int64_t win = (int64_t)(lt - 1) * p.stride + (int64_t)(p.K - 1) * p.dilation + 2 + 2 * kBwdMargin;
+    while (2 * (size_t)cbx * win * 4 > 48 * 1024 && lt > 32) {  // keep the two windows within 48 KB
+        lt /= 2;
+        win = (int64_t)(lt - 1) * p.stride + (int64_t)(p.K - 1) * p.dilation + 2 + 2 * kBwdMargin;
+    }
+    if (2 * (size_t)cbx * win * 4 > 48 * 1024) win = 0;  // no window: everything through global memory
+    pl.cbx = cbx;
+    pl.lt = lt;
+    pl.win = (int)win;
+    pl.tiles_l = (p.L_out + lt - 1) / lt;
+    pl.ngrp_blocks = p.C_in / cbx;
+    pl.atomic_om = cbx < p.cpo;
+    pl.lds = 2 * (size_t)cbx * win * 4;
+    return pl;
+}
+
+// Depthwise shapes (one input channel per group and per output channel):
+// every gradient in one pass, nothing materialised.  A block takes 512
+// consecutive outputs l of one (b, c); thread t owns outputs l0 + 2t, +1 and
+// all their taps.  dS = w[c,k] * dout[b,c,l] is formed on the fly; x comes
+// from an LDS window of the row (the tile's span plus kDwbMargin each side)
+// and grad_x accumulates in a second LDS window, added to grad_x with one
+// atomic per touched position at the end (global atomics for samples moved
+// outside the window).  The offset and mask gradients are stored directly
+// (one channel per offset group) or added atomically (several); the weight
+// gradient's partial sums are reduced over the block (registers, wave
+// shuffles, LDS) and added to grad_weight with one atomic per tap.
+constexpr int kDwbMargin = 64;
+constexpr int kDwbOpt = 2;
+
+template <int KT>
+__global__ void __launch_bounds__(256) k_bwd_dw(BwdParams a, int WIN, int tiles_l) {
+    const Params &p = a.p;
+    extern __shared__ float smem[];
+    float *xs = smem;           // [WIN]
+    float *gacc = smem + WIN;   // [WIN]
+    __shared__ float wred[KT];
+    const int L_in = p.L_in, L_out = p.L_out;
+    const int tile = blockIdx.x % tiles_l;
+    const int row = blockIdx.x / tiles_l;  // b * C_in + c
+    const int c = row % p.C_in, b = row / p.C_in;
+    const int g = c / p.cpo;
+    const int l0 = tile * (256 * kDwbOpt);
+    const int lo = l0 * p.stride - p.padding - kDwbMargin;
+    const float *__restrict__ xrow = (const float *)p.x + (int64_t)row * L_in;
+    for (int j = threadIdx.x; j < WIN; j += 256) {
+        const int pos = lo + j;
+        xs[j] = (pos >= 0 && pos < L_in) ? xrow[pos] : 0.0f;
+        gacc[j] = 0.0f;
+    }
+    if (threadIdx.x < KT) wred[threadIdx.x] = 0.0f;
+    __syncthreads();
+    const float *__restrict__ off = (const float *)p.off;
+    const float *__restrict__ mask = (const float *)p.mask;
+    const float *__restrict__ w = (const float *)p.w + (int64_t)c * KT;  // co = c (one output per input)
+    const float *__restrict__ dout = a.dout + (int64_t)row * L_out;     // [b][co = c][l]
+    float *__restrict__ gxr = a.gx ? a.gx + (int64_t)row * L_in : nullptr;
+    const bool om_atomic = p.cpo > 1;
+    float wk[KT], wacc[KT];
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+        wk[k] = w[k];
+        wacc[k] = 0.0f;
+    }
+#pragma unroll
+    for (int o = 0; o < kDwbOpt; ++o) {
+        const int l = l0 + kDwbOpt * threadIdx.x + o;
+        if (l >= L_out) break;
+        const float d = dout[l];
+        const int64_t ob = (((int64_t)b * p.G + g) * L_out + l) * KT;
+        const int base0 = l * p.stride - p.padding;
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+            int i0;
+            float f;
+            split_position(off[ob + k], base0 + k * p.dilation, i0, f);
+            const float m = mask ? mask[ob + k] : 1.0f;
+            const int j = i0 - lo;
+            const bool inwin = WIN > 1 && (unsigned)j < (unsigned)(WIN - 1);
+            float x0, x1;
+            if (inwin) {
+                x0 = xs[j];
+                x1 = xs[j + 1];
+            } else {
+                x0 = (i0 >= 0 && i0 < L_in) ? xrow[i0] : 0.0f;
+                x1 = (i0 + 1 >= 0 && i0 + 1 < L_in) ? xrow[i0 + 1] : 0.0f;
+            }
+            const float ds = wk[k] * d;
+            const float lerp = fmaf(f, x1 - x0, x0);
+            wacc[k] = fmaf(d, lerp * m, wacc[k]);
+            const float go = ds * m * (x1 - x0), gm = ds * lerp;
+            if (om_atomic) {
+                if (a.goff) unsafeAtomicAdd(a.goff + ob + k, go);
+                if (a.gmask) unsafeAtomicAdd(a.gmask + ob + k, gm);
+            } else {
+                if (a.goff) a.goff[ob + k] = go;
+                if (a.gmask) a.gmask[ob + k] = gm;
+            }
+            if (gxr) {
+                const float dm = ds * m;
+                if (inwin) {
+                    atomicAdd(gacc + j, dm * (1.0f - f));
+                    atomicAdd(gacc + j + 1, dm * f);
+                } else {
+                    if (i0 >= 0 && i0 < L_in) unsafeAtomicAdd(gxr + i0, dm * (1.0f - f));
+                    if (i0 + 1 >= 0 && i0 + 1 < L_in) unsafeAtomicAdd(gxr + i0 + 1, dm * f);
+                }
+            }
+        }
+    }
+    // weight gradient partials: wave sums, then LDS, then one atomic per tap
+    if (a.gw) {
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+            float v = wacc[k];
+            for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+            if ((threadIdx.x & 63) == 0) atomicAdd(wred + k, v);
+        }
+    }
+    __syncthreads();
+    if (a.gw && threadIdx.x < KT) unsafeAtomicAdd(a.gw + (int64_t)c * KT + threadIdx.x, wred[threadIdx.x]);
+    if (gxr) {
+        for (int j = threadIdx.x; j < WIN; j += 256) {
+            const int pos = lo + j;
+            const float v = gacc[j];
+            if (pos >= 0 && pos < L_in && v != 0.0f) unsafeAtomicAdd(gxr + pos, v);
         }
     }
 }
@@ -266,8 +474,15 @@ struct BwdLayout {
     size_t dS, wt, S, A, part, total;
 };
 
+// The fused depthwise pass serves C_in == C_out == groups with K in 1..9.
+bool depthwise_path(const Params &p) {
+    return p.cpg == 1 && p.opg == 1 && p.K >= 1 && p.K <= 9 && p.K != 6 && p.K != 8 &&
+           (int64_t)p.B * p.C_in * ((p.L_out + 256 * kDwbOpt - 1) / (256 * kDwbOpt)) < ((int64_t)1 << 31);
+}
+
 BwdLayout layout(const Params &p, bool want_weight, int num_cus) {
     BwdLayout L = {};
+    if (depthwise_path(p)) return L;  // nothing materialised
     const size_t nds = (size_t)p.B * p.C_in * p.K * p.L_out * 4;
     size_t o = 0;
     L.dS = o;
@@ -299,45 +514,96 @@ size_t backward_workspace_bytes(const Params &p, bool want_weight, int num_cus) 
     return layout(p, want_weight, num_cus).total;
 }
 
+hipError_t launch_backward_dw(BwdParams a, hipStream_t stream) {
+    const Params &p = a.p;
+    const int LT = 256 * kDwbOpt;
+    const int tiles_l = (p.L_out + LT - 1) / LT;
+    int64_t win = (int64_t)(LT - 1) * p.stride + (int64_t)(p.K - 1) * p.dilation + 2 + 2 * kDwbMargin;
+    win = (win + 63) / 64 * 64;
+    if (win > 6144) win = 0;  // wider spans: global memory only
+    const size_t lds = 2 * (size_t)win * 4;
+    const int64_t no = (int64_t)p.B * p.G * p.L_out * p.K;
+    if (p.cpo > 1) {
+        if (a.goff) hipLaunchKernelGGL(k_bwd_zero, dim3(grid_for(no)), dim3(256), 0, stream, a.goff, no);
+        if (a.gmask) hipLaunchKernelGGL(k_bwd_zero, dim3(grid_for(no)), dim3(256), 0, stream, a.gmask, no);
+    }
+    if (a.gw) {
+        const int64_t nw = (int64_t)p.C_out * p.K;
+        hipLaunchKernelGGL(k_bwd_zero, dim3(grid_for(nw)), dim3(256), 0, stream, a.gw, nw);
+    }
+    const dim3 grid((unsigned)((int64_t)p.B * p.C_in * tiles_l));
+    switch (p.K) {
+#define DC1D_BDW(KK) \
+    case KK: hipLaunchKernelGGL((k_bwd_dw<KK>), grid, dim3(256), lds, stream, a, (int)win, tiles_l); break;
+        DC1D_BDW(1)
+        DC1D_BDW(2)
+        DC1D_BDW(3)
+        DC1D_BDW(4)
+        DC1D_BDW(5)
+        DC1D_BDW(7)
+        DC1D_BDW(9)
+#undef DC1D_BDW
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_backward(BwdParams a, int num_cus, hipStream_t stream) {
     const Params &p = a.p;
     const int64_t n = (int64_t)p.B * p.C_in * p.K * p.L_out;
     char *ws = (char *)a.dS;  // the workspace base
     const BwdLayout L = layout(p, a.gw != nullptr, num_cus);
+    const DxPlan dx = plan_dx(p);
     if (a.gx) {
         const int64_t nx = (int64_t)p.B * p.C_in * p.L_in;
         hipLaunchKernelGGL(k_bwd_zero, dim3(grid_for(nx)), dim3(256), 0, stream, a.gx, nx);
     }
-    const bool want_ds = a.gx || a.goff || a.gmask || a.gw;
-    if (n > 0 && want_ds && dense_path(p)) {
-        float *wt = (float *)(ws + L.wt);
-        const int CK = p.C_in * p.K;
-        hipLaunchKernelGGL(k_transpose, dim3((unsigned)((CK + 31) / 32), (unsigned)((p.C_out + 31) / 32)), dim3(256),
-                           0, stream, (const float *)p.w, wt, p.C_out, CK);
-        hipError_t e = launch_gemm_f32(gemm_ds(p, wt, a.dout, a.dS, ws + L.part), p.L_out, (int64_t)p.C_out * p.L_out,
-                                       num_cus, stream);
+    const int64_t no = (int64_t)p.B * p.G * p.L_out * p.K;
+    if (dx.atomic_om && n > 0) {  // offset and mask gradients are accumulated
+        if (a.goff) hipLaunchKernelGGL(k_bwd_zero, dim3(grid_for(no)), dim3(256), 0, stream, a.goff, no);
+        if (a.gmask) hipLaunchKernelGGL(k_bwd_zero, dim3(grid_for(no)), dim3(256), 0, stream, a.gmask, no);
+    }
+    const bool want_dx = a.gx || a.goff || a.gmask;
+    if (n > 0 && (want_dx || a.gw) && depthwise_path(p)) {
+        const hipError_t e = launch_backward_dw(a, stream);
         if (e != hipSuccess) return e;
-        a.S = a.gw ? (float *)(ws + L.S) : nullptr;
-        if (a.gx || a.S) hipLaunchKernelGGL(k_bwd_samples_t, dim3(grid_for(n)), dim3(256), 0, stream, a);
-        if (a.goff || a.gmask) {
-            const int64_t no = (int64_t)p.B * p.G * p.L_out * p.K;
-            hipLaunchKernelGGL(k_bwd_offmask, dim3(grid_for(no)), dim3(256), 0, stream, a);
-        }
-        if (a.gw) {
-            float *A = (float *)(ws + L.A);
-            const int64_t nd = (int64_t)p.B * p.C_out * p.L_out;
-            hipLaunchKernelGGL(k_restride_dout, dim3(grid_for(nd)), dim3(256), 0, stream, a, A);
-            e = launch_gemm_f32(gemm_dw(p, A, a.S, a.gw, ws + L.part), CK, 0, num_cus, stream);
+        if (a.gb) hipLaunchKernelGGL(k_bwd_bias, dim3((unsigned)p.C_out), dim3(256), 0, stream, a);
+        return hipGetLastError();
+    }
+    const int64_t dx_blocks = (int64_t)p.B * dx.ngrp_blocks * dx.tiles_l;
+    if (dx_blocks >= ((int64_t)1 << 31) || (int64_t)p.C_out * p.cpg * p.K >= ((int64_t)1 << 31))
+        return hipErrorInvalidValue;  // grids beyond the launch limits
+    if (n > 0 && (want_dx || a.gw)) {
+        const bool dense = dense_path(p);
+        BwdParams s = a;  // the samples pass: no grad_x scatter here
+        s.gx = nullptr;
+        s.S = a.gw ? (float *)(ws + L.S) : nullptr;
+        if (dense) {
+            float *wt = (float *)(ws + L.wt);
+            const int CK = p.C_in * p.K;
+            hipLaunchKernelGGL(k_transpose, dim3((unsigned)((CK + 31) / 32), (unsigned)((p.C_out + 31) / 32)),
+                               dim3(256), 0, stream, (const float *)p.w, wt, p.C_out, CK);
+            const hipError_t e = launch_gemm_f32(gemm_ds(p, wt, a.dout, a.dS, ws + L.part), p.L_out,
+                                                 (int64_t)p.C_out * p.L_out, num_cus, stream);
             if (e != hipSuccess) return e;
+            if (s.S) hipLaunchKernelGGL(k_bwd_samples_t, dim3(grid_for(n)), dim3(256), 0, stream, s);
+        } else {
+            hipLaunchKernelGGL(k_bwd_samples, dim3(grid_for(n)), dim3(256), 0, stream, s);
         }
-    } else if (n > 0 && want_ds) {
-        a.S = a.gw ? (float *)(ws + L.S) : nullptr;
-        hipLaunchKernelGGL(k_bwd_samples, dim3(grid_for(n)), dim3(256), 0, stream, a);
-        if (a.goff || a.gmask) {
-            const int64_t no = (int64_t)p.B * p.G * p.L_out * p.K;
-            hipLaunchKernelGGL(k_bwd_offmask, dim3(grid_for(no)), dim3(256), 0, stream, a);
+        if (want_dx && dx_blocks > 0)
+            hipLaunchKernelGGL(k_bwd_dx, dim3((unsigned)dx_blocks), dim3(256), dx.lds, stream, a, dx);
+        if (a.gw) {
+            if (dense) {
+                float *A = (float *)(ws + L.A);
+                const int64_t nd = (int64_t)p.B * p.C_out * p.L_out;
+                hipLaunchKernelGGL(k_restride_dout, dim3(grid_for(nd)), dim3(256), 0, stream, a, A);
+                const hipError_t e = launch_gemm_f32(gemm_dw(p, A, s.S, a.gw, ws + L.part), p.C_in * p.K, 0,
+                                                     num_cus, stream);
+                if (e != hipSuccess) return e;
+            } else {
+                hipLaunchKernelGGL(k_bwd_weight, dim3((unsigned)(p.C_out * p.cpg * p.K)), dim3(256), 0, stream, s);
+            }
         }
-        if (a.gw) hipLaunchKernelGGL(k_bwd_weight, dim3((unsigned)(p.C_out * p.cpg)), dim3(256), 0, stream, a);
     }
     if (a.gw && n == 0) {
         const int64_t nw = (int64_t)p.C_out * p.cpg * p.K;

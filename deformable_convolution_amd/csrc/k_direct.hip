@@ -238,7 +238,7 @@ __global__ void __launch_bounds__(kDwThreads) k_depthwise(Params p, int WIN, int
             split_position(ofs, base0 + k * p.dilation, i0, f);
             const int j = i0 - lo;
             float x0, x1;
-            if ((unsigned)j < (unsigned)(WIN - 1)) {
+            if (WIN > 1 && (unsigned)j < (unsigned)(WIN - 1)) {
                 x0 = s_x[j];
                 x1 = s_x[j + 1];
             } else {
