@@ -30,7 +30,7 @@
 //                    windows);
 //   weight gradient  dense: k_restride_dout then k_gemm grad_weight =
 //                    dout S^T; other shapes: k_bwd_weight;
-//   k_bwd_bias       one workgroup per output channel.
+//   k_bwd_bias       one workgroup per (output channel, batch), atomics.
 #include "dc1d_internal.h"
 
 #include <algorithm>
@@ -103,22 +103,22 @@ __global__ void __launch_bounds__(256) k_bwd_weight(BwdParams a) {
     if (threadIdx.x == 0) a.gw[e] = s_red[0];
 }
 
+// One workgroup per (co, b): the row's sum, added to grad_bias[co] (cleared
+// first) with one atomic.
 __global__ void __launch_bounds__(256) k_bwd_bias(BwdParams a) {
     const Params &p = a.p;
     __shared__ float s_red[256];
-    const int co = blockIdx.x;
+    const int co = blockIdx.x % p.C_out, b = blockIdx.x / p.C_out;
+    const float *d = a.dout + ((int64_t)b * p.C_out + co) * p.L_out;
     float acc = 0.0f;
-    for (int b = 0; b < p.B; ++b) {
-        const float *d = a.dout + ((int64_t)b * p.C_out + co) * p.L_out;
-        for (int l = threadIdx.x; l < p.L_out; l += 256) acc += d[l];
-    }
+    for (int l = threadIdx.x; l < p.L_out; l += 256) acc += d[l];
     s_red[threadIdx.x] = acc;
     __syncthreads();
     for (int h = 128; h > 0; h >>= 1) {
         if ((int)threadIdx.x < h) s_red[threadIdx.x] += s_red[threadIdx.x + h];
         __syncthreads();
     }
-    if (threadIdx.x == 0) a.gb[co] = s_red[0];
+    if (threadIdx.x == 0) unsafeAtomicAdd(a.gb + co, s_red[0]);
 }
 
 // Dense path (groups == 1): dS = W^T dout and grad_weight = dout S^T are
@@ -338,19 +338,55 @@ __global__ void __launch_bounds__(256) k_bwd_dw(BwdParams a, int WIN, int tiles_
         wk[k] = w[k];
         wacc[k] = 0.0f;
     }
+    // this thread's two outputs: their 2*KT offsets (and mask values) are
+    // one contiguous run, loaded up front (8-byte vectors when aligned)
+    constexpr int NV = kDwbOpt * KT;
+    const int lt = l0 + kDwbOpt * threadIdx.x;
+    const int nvalid = min(kDwbOpt, L_out - lt);
+    const int64_t e0 = (((int64_t)b * p.G + g) * L_out + lt) * KT;
+    const bool vec = nvalid == kDwbOpt && ((((uintptr_t)(off + e0)) & 7) == 0) &&
+                     (!mask || (((uintptr_t)(mask + e0)) & 7) == 0);
+    float ov[NV], mv[NV], dv[kDwbOpt];
+    if (nvalid > 0) {
+        if (vec) {
+#pragma unroll
+            for (int q = 0; q < NV; q += 2) {
+                const float2 t = *(const float2 *)(off + e0 + q);
+                ov[q] = t.x;
+                ov[q + 1] = t.y;
+                if (mask) {
+                    const float2 u = *(const float2 *)(mask + e0 + q);
+                    mv[q] = u.x;
+                    mv[q + 1] = u.y;
+                } else {
+                    mv[q] = mv[q + 1] = 1.0f;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < NV; ++q) {
+                const bool ok = q < nvalid * KT;
+                ov[q] = ok ? off[e0 + q] : 0.0f;
+                mv[q] = (ok && mask) ? mask[e0 + q] : 1.0f;
+            }
+        }
+#pragma unroll
+        for (int o = 0; o < kDwbOpt; ++o) dv[o] = o < nvalid ? dout[lt + o] : 0.0f;
+    }
+    float go[NV], gm[NV];
 #pragma unroll
     for (int o = 0; o < kDwbOpt; ++o) {
-        const int l = l0 + kDwbOpt * threadIdx.x + o;
-        if (l >= L_out) break;
-        const float d = dout[l];
-        const int64_t ob = (((int64_t)b * p.G + g) * L_out + l) * KT;
+        const int l = lt + o;
         const int base0 = l * p.stride - p.padding;
 #pragma unroll
         for (int k = 0; k < KT; ++k) {
+            const int q = o * KT + k;
+            go[q] = gm[q] = 0.0f;
+            if (o >= nvalid) continue;
             int i0;
             float f;
-            split_position(off[ob + k], base0 + k * p.dilation, i0, f);
-            const float m = mask ? mask[ob + k] : 1.0f;
+            split_position(ov[q], base0 + k * p.dilation, i0, f);
+            const float m = mv[q];
             const int j = i0 - lo;
             const bool inwin = WIN > 1 && (unsigned)j < (unsigned)(WIN - 1);
             float x0, x1;
@@ -361,17 +397,12 @@ __global__ void __launch_bounds__(256) k_bwd_dw(BwdParams a, int WIN, int tiles_
                 x0 = (i0 >= 0 && i0 < L_in) ? xrow[i0] : 0.0f;
                 x1 = (i0 + 1 >= 0 && i0 + 1 < L_in) ? xrow[i0 + 1] : 0.0f;
             }
+            const float d = dv[o];
             const float ds = wk[k] * d;
             const float lerp = fmaf(f, x1 - x0, x0);
             wacc[k] = fmaf(d, lerp * m, wacc[k]);
-            const float go = ds * m * (x1 - x0), gm = ds * lerp;
-            if (om_atomic) {
-                if (a.goff) unsafeAtomicAdd(a.goff + ob + k, go);
-                if (a.gmask) unsafeAtomicAdd(a.gmask + ob + k, gm);
-            } else {
-                if (a.goff) a.goff[ob + k] = go;
-                if (a.gmask) a.gmask[ob + k] = gm;
-            }
+            go[q] = ds * m * (x1 - x0);
+            gm[q] = ds * lerp;
             if (gxr) {
                 const float dm = ds * m;
                 if (inwin) {
@@ -382,6 +413,30 @@ __global__ void __launch_bounds__(256) k_bwd_dw(BwdParams a, int WIN, int tiles_
                     if (i0 + 1 >= 0 && i0 + 1 < L_in) unsafeAtomicAdd(gxr + i0 + 1, dm * f);
                 }
             }
+        }
+    }
+    // offset and mask gradients of the two outputs
+    if (nvalid > 0 && (a.goff || a.gmask)) {
+        if (om_atomic) {
+#pragma unroll
+            for (int q = 0; q < NV; ++q)
+                if (q < nvalid * KT) {
+                    if (a.goff) unsafeAtomicAdd(a.goff + e0 + q, go[q]);
+                    if (a.gmask) unsafeAtomicAdd(a.gmask + e0 + q, gm[q]);
+                }
+        } else if (vec) {
+#pragma unroll
+            for (int q = 0; q < NV; q += 2) {
+                if (a.goff) *(float2 *)(a.goff + e0 + q) = float2{go[q], go[q + 1]};
+                if (a.gmask) *(float2 *)(a.gmask + e0 + q) = float2{gm[q], gm[q + 1]};
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < NV; ++q)
+                if (q < nvalid * KT) {
+                    if (a.goff) a.goff[e0 + q] = go[q];
+                    if (a.gmask) a.gmask[e0 + q] = gm[q];
+                }
         }
     }
     // weight gradient partials: wave sums, then LDS, then one atomic per tap
@@ -473,6 +528,17 @@ Params gemm_dw(const Params &p, const float *A, const float *S, float *gw, void 
 struct BwdLayout {
     size_t dS, wt, S, A, part, total;
 };
+
+hipError_t launch_bias(const BwdParams &a, hipStream_t stream) {
+    const Params &p = a.p;
+    if (a.gb) {
+        hipLaunchKernelGGL(k_bwd_zero, dim3(grid_for(p.C_out)), dim3(256), 0, stream, a.gb, (int64_t)p.C_out);
+        const int64_t blocks = (int64_t)p.C_out * p.B;
+        if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+        if (blocks > 0) hipLaunchKernelGGL(k_bwd_bias, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    }
+    return hipGetLastError();
+}
 
 // The fused depthwise pass serves C_in == C_out == groups with K in 1..9.
 bool depthwise_path(const Params &p) {
@@ -567,8 +633,7 @@ hipError_t launch_backward(BwdParams a, int num_cus, hipStream_t stream) {
     if (n > 0 && (want_dx || a.gw) && depthwise_path(p)) {
         const hipError_t e = launch_backward_dw(a, stream);
         if (e != hipSuccess) return e;
-        if (a.gb) hipLaunchKernelGGL(k_bwd_bias, dim3((unsigned)p.C_out), dim3(256), 0, stream, a);
-        return hipGetLastError();
+        return launch_bias(a, stream);
     }
     const int64_t dx_blocks = (int64_t)p.B * dx.ngrp_blocks * dx.tiles_l;
     if (dx_blocks >= ((int64_t)1 << 31) || (int64_t)p.C_out * p.cpg * p.K >= ((int64_t)1 << 31))
@@ -609,8 +674,7 @@ hipError_t launch_backward(BwdParams a, int num_cus, hipStream_t stream) {
         const int64_t nw = (int64_t)p.C_out * p.cpg * p.K;
         hipLaunchKernelGGL(k_bwd_zero, dim3(grid_for(nw)), dim3(256), 0, stream, a.gw, nw);
     }
-    if (a.gb) hipLaunchKernelGGL(k_bwd_bias, dim3((unsigned)p.C_out), dim3(256), 0, stream, a);
-    return hipGetLastError();
+    return launch_bias(a, stream);
 }
 
 }  // namespace dc1d

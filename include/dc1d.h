@@ -170,15 +170,16 @@ int dc1d_forward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_te
  * checks their gradient against a finite difference, section Demo
  * notebook).  The offset gradient is that of the interpolation formula with
  * i0 held fixed, i.e. the right derivative at integer offsets.  Every
- * requested gradient is overwritten (grad_x is cleared, then accumulated
- * with atomics, so its last bits may differ between runs).  grad_mask needs
- * a mask.  Gradients must not overlap the inputs, each other or the
- * workspace.
+ * requested gradient is overwritten.  grad_x and grad_bias (and, for some
+ * shapes, the others) are cleared and then accumulated with atomics, so
+ * their last bits may differ between runs.  grad_mask needs a mask.
+ * Gradients must not overlap the inputs, each other or the workspace.
  *
  * workspace: at least dc1d_backward_workspace_bytes() bytes, 256-byte
- * aligned, when any of grad_x, grad_offsets, grad_mask, grad_weight is
- * requested and B*C_in*K*L_out > 0 (it holds dS, and the samples S when
- * grad_weight is requested); no initialisation; nothing kept.
+ * aligned, when that is not 0 (it holds dS = the gradient of the samples,
+ * the transposed weight and the samples for the weight gradient, and split
+ * partial sums, depending on the shape; depthwise shapes need none); no
+ * initialisation; nothing kept.
  */
 int dc1d_backward_workspace_bytes(const dc1d_tensor *x, const dc1d_tensor *offsets,
                                   const dc1d_tensor *mask_or_null, const dc1d_tensor *weight,
