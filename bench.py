@@ -262,7 +262,7 @@ def main_backward(args, w):
         achieved = nbytes / (ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm_GBps"], "unit": "GB/s",
                 "frac": round(achieved / PEAK["hbm_GBps"], 4)}
-    roof["traffic"] = None
+    roof["traffic"] = read_traffic(w.name, "backward", kernel_hash())
     roof["kernel"] = "backward"
     roof["kernel_ms"] = round(ms, 5)
     line = {
@@ -346,7 +346,7 @@ def main():
         raise SystemExit(2)
     if args.summarize_profile:
         if not args.kernel:
-            raise SystemExit("--summarize-profile needs --kernel (the plan's kernel name)")
+            raise SystemExit("--summarize-profile needs --kernel (the plan's kernel name, or backward)")
         write_profile_md(args.summarize_profile, args.workload, args.kernel)
         return
 
@@ -435,18 +435,18 @@ def main():
 
 
 PROFILE_COMMANDS = """\
-cd /tmp && export TMPDIR=/tmp; R=<repo root>; P=$R/gpurun_out/prof/{wl}
+cd /tmp && export TMPDIR=/tmp; R=<repo root>; P=$R/gpurun_out/prof/{wl}{suffix}
 rocprofv3 --kernel-trace --stats --output-format csv -d $P/trace -o run -- \\
-    python3 $R/bench.py --workload {wl} --profile-run --steps 20 --warmup 3
+    python3 $R/bench.py --workload {wl}{flag} --profile-run --steps 20 --warmup 3
 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $P/fetch -o run -- \\
-    python3 $R/bench.py --workload {wl} --profile-run --steps 5 --warmup 1
+    python3 $R/bench.py --workload {wl}{flag} --profile-run --steps 5 --warmup 1
 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $P/write -o run -- \\
-    python3 $R/bench.py --workload {wl} --profile-run --steps 5 --warmup 1
+    python3 $R/bench.py --workload {wl}{flag} --profile-run --steps 5 --warmup 1
 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $P/copy_fetch -o run -- \\
     python3 $R/bench.py --copy-calibration 512
 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $P/copy_write -o run -- \\
     python3 $R/bench.py --copy-calibration 512
-python3 $R/bench.py --workload {wl} --summarize-profile $P --kernel {kernel}
+python3 $R/bench.py --workload {wl}{flag} --summarize-profile $P --kernel {kernel}
 """
 
 
@@ -497,13 +497,17 @@ def summarize_profile(d, workload):
     f_scale = copy_bytes / cf_v if cf_v > 0 else None
     w_scale = copy_bytes / cw_v if cw_v > 0 else None
 
+    # launches in the counter runs: the fewest dispatches any of our kernels
+    # had (every kernel runs at least once per launch)
+    ours_f = {k: v for k, v in fetch.items() if ours(k)}
+    ours_w = {k: v for k, v in write.items() if ours(k)}
+    nf = min((len(v) for v in ours_f.values()), default=1)
+    nw = min((len(v) for v in ours_w.values()), default=1)
     rows_k = []
     total_bytes = 0.0
-    for name in sorted(set(fetch) | set(write)):
-        if not ours(name):
-            continue
-        fv = float(np.mean(fetch.get(name, [0.0])))
-        wv = float(np.mean(write.get(name, [0.0])))
+    for name in sorted(set(ours_f) | set(ours_w)):
+        fv = float(np.sum(ours_f.get(name, [0.0]))) / nf  # counter units per launch
+        wv = float(np.sum(ours_w.get(name, [0.0]))) / nw
         fb = fv * f_scale if f_scale else None
         wb = wv * w_scale if w_scale else None
         if fb is not None and wb is not None:
@@ -514,9 +518,10 @@ def summarize_profile(d, workload):
 
 def write_profile_md(d, workload, kernel):
     stats, rows_k, total_bytes, (cf_v, cw_v, f_scale, w_scale), w = summarize_profile(d, workload)
-    _, _, alg_bytes = work(w)
-    contraction, sampling, _ = work(w)
-    fwd_ns = sum(float(r["AverageNs"]) for r in stats)
+    contraction, sampling, alg_bytes = work_backward(w) if kernel == "backward" else work(w)
+    # launches in the trace run: the fewest calls of any of our kernels
+    n_launch = min((int(r["Calls"]) for r in stats), default=1)
+    fwd_ns = sum(float(r["TotalDurationNs"]) for r in stats) / max(n_launch, 1)
     out = []
     out.append("# %s -- %s" % (workload_label(w), kernel))
     out.append("")
@@ -525,12 +530,15 @@ def write_profile_md(d, workload, kernel):
     if rows_k and f_scale and w_scale:
         out.append("<!-- hbm_bytes_per_launch=%.0f -->" % total_bytes)
     out.append("")
-    out.append("One launch = one forward call (every kernel it enqueues, back to back on one stream).")
+    out.append("One launch = one %s call (every kernel it enqueues, back to back on one stream)."
+               % ("backward (all five gradients)" if kernel == "backward" else "forward"))
     out.append("")
     out.append("Commands (rocprofv3, ROCm 7.2, one MI355X):")
     out.append("")
     out.append("```")
-    out.append(PROFILE_COMMANDS.format(wl=workload, kernel=kernel).rstrip())
+    bwd = kernel == "backward"
+    out.append(PROFILE_COMMANDS.format(wl=workload, kernel=kernel, flag=" --backward" if bwd else "",
+                                       suffix="_backward" if bwd else "").rstrip())
     out.append("```")
     out.append("")
     out.append("## Kernel trace (--kernel-trace --stats)")
@@ -541,11 +549,11 @@ def write_profile_md(d, workload, kernel):
         out.append("| %s | %s | %.2f | %.1f |" % (short(r["Name"]), r["Calls"],
                                                float(r["AverageNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e3))
     out.append("")
-    out.append("Sum of the averages of one forward's kernels: %.2f us; contraction %.3f GFLOP -> %.1f TFLOP/s "
-               "over that time." % (fwd_ns / 1e3, contraction / 1e9, contraction / (fwd_ns * 1e-9) / 1e12
-                                    if fwd_ns else 0.0))
+    out.append("Kernel time per launch (all its kernels' total over %d launches): %.2f us; contraction %.3f GFLOP "
+               "-> %.1f TFLOP/s over that time." % (n_launch, fwd_ns / 1e3, contraction / 1e9,
+                                                    contraction / (fwd_ns * 1e-9) / 1e12 if fwd_ns else 0.0))
     out.append("")
-    out.append("## HBM traffic (--pmc FETCH_SIZE, --pmc WRITE_SIZE; KiB per dispatch)")
+    out.append("## HBM traffic (--pmc FETCH_SIZE, --pmc WRITE_SIZE; counter units per launch, all dispatches)")
     out.append("")
     if f_scale and w_scale:
         out.append("Copy calibration: a 512 MiB device-to-device copy reads as FETCH_SIZE %.0f and WRITE_SIZE %.0f; "
@@ -559,7 +567,7 @@ def write_profile_md(d, workload, kernel):
         out.append("| %s | %.0f | %.0f | %s | %s |" % (name, fv, wv, "%.2f" % (fb / 1e6) if fb else "-",
                                                    "%.2f" % (wb / 1e6) if wb else "-"))
     out.append("")
-    out.append("Per forward: %.2f MB of HBM traffic against %.2f MB of algorithmic bytes (each tensor moved once)."
+    out.append("Per launch: %.2f MB of HBM traffic against %.2f MB of algorithmic bytes (each tensor moved once)."
                % (total_bytes / 1e6, alg_bytes / 1e6))
     path = os.path.join(ROOT, "profiles", "%s__%s.md" % (workload, kernel))
     os.makedirs(os.path.dirname(path), exist_ok=True)
