@@ -121,7 +121,7 @@ hipError_t launch_direct(const Params &p, hipStream_t stream) {
 
 constexpr int kDwThreads = 256;
 constexpr int kDwOpt = 2;      // outputs per thread (few registers: high occupancy)
-constexpr int kDwMargin = 64;  // window margin per side (input positions)
+constexpr int kDwMargin = 16;  // window margin per side (input positions)
 
 // VW consecutive elements (VW = 2 or 4) as floats, in one load.
 template <class D, int VW>
