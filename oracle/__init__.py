@@ -10,6 +10,8 @@ Two independent formulations live here:
 * ``forward`` / ``forward_points`` / ``positions`` / ``backward`` -- ctypes
   front end of ``dc1d_oracle.c``: the two-stage definition (sample, then
   contract) in plain C loops over doubles, and its term-by-term derivative.
+* ``packed_heads`` / ``packed_forward`` -- the packed layer's offset (and
+  mask) generator in the same C file, then ``forward``.
 * ``hat.forward`` -- a NumPy brute force that never splits a position into
   integer and fractional parts; it is the pin for the C oracle's
   floor/fraction logic and its zero-fill boundary.
@@ -61,6 +63,8 @@ class _Lib:
         lib.oracle_forward_points.argtypes = [p] * 5 + [i64] * 10 + [p, i64, p]
         lib.oracle_backward.restype = ctypes.c_int
         lib.oracle_backward.argtypes = [p] * 5 + [i64] * 10 + [p] * 5
+        lib.oracle_packed_heads.restype = ctypes.c_int
+        lib.oracle_packed_heads.argtypes = [p] * 7 + [i64] * 7 + [p] * 2
         self.lib = lib
 
 
@@ -189,3 +193,48 @@ def backward(x, offsets, weight, dout, mask=None, stride=1, padding=0, dilation=
     if st:
         raise ValueError("oracle_backward: " + _ERR.get(st, str(st)))
     return {"x": gx, "offsets": goff, "mask": gmask, "weight": gw, "bias": gb}
+
+
+def packed_heads(x, trunk_weight, trunk_bias, off_weight, off_bias, mask_weight=None, mask_bias=None,
+                 stride=1, padding=0, dilation=1, lib=None):
+    """Offsets (and mask) the packed layer's generator computes from x, in
+    float64: trunk_weight [C_in, 1, K], off_weight / mask_weight
+    [G*K, C_in, 1] (biases [C_in], [G*K], or None).  Returns (offsets, mask)
+    with shapes [B, G, L_out, K]; mask is None without mask_weight."""
+    x, tw, tb, ow, ob, mw, mb = map(_f64, (x, trunk_weight, trunk_bias, off_weight, off_bias, mask_weight,
+                                          mask_bias))
+    B, C_in, L_in = x.shape
+    if tw.ndim != 3 or tw.shape[:2] != (C_in, 1):
+        raise ValueError("trunk_weight must be [C_in, 1, K]")
+    K = tw.shape[2]
+    if ow.ndim != 3 or ow.shape[1:] != (C_in, 1) or ow.shape[0] % K:
+        raise ValueError("off_weight must be [G*K, C_in, 1]")
+    G = ow.shape[0] // K
+    if mw is not None and mw.shape != ow.shape:
+        raise ValueError("mask_weight must have off_weight's shape")
+    if tb is not None and tb.shape != (C_in,):
+        raise ValueError("trunk_bias must be [C_in]")
+    for bb in (ob, mb):
+        if bb is not None and bb.shape != (G * K,):
+            raise ValueError("head biases must be [G*K]")
+    L_out = output_length(L_in, K, stride, padding, dilation, lib)
+    if L_out < 1:
+        raise ValueError("no output positions")
+    off = np.empty((B, G, L_out, K), dtype=np.float64)
+    mask = np.empty_like(off) if mw is not None else None
+    st = _load(lib).oracle_packed_heads(_ptr(x), _ptr(tw), _ptr(tb), _ptr(ow), _ptr(ob), _ptr(mw),
+                                        _ptr(mb if mw is not None else None), B, C_in, L_in, K, stride,
+                                        padding, dilation, G, _ptr(off), _ptr(mask))
+    if st:
+        raise ValueError("oracle_packed_heads: " + _ERR.get(st, str(st)))
+    return off, mask
+
+
+def packed_forward(x, trunk_weight, trunk_bias, off_weight, off_bias, weight, bias=None, mask_weight=None,
+                   mask_bias=None, stride=1, padding=0, dilation=1, groups=1, lib=None):
+    """The packed layer: its generator's offsets (and mask), then the
+    deformable forward.  Returns (out, offsets, mask)."""
+    off, mask = packed_heads(x, trunk_weight, trunk_bias, off_weight, off_bias, mask_weight, mask_bias,
+                             stride, padding, dilation, lib)
+    out = forward(x, off, weight, bias, mask, stride, padding, dilation, groups, lib)
+    return out, off, mask

@@ -407,3 +407,78 @@ int oracle_backward(const double *x, const double *offsets, const double *mask,
     }
     return OR_OK;
 }
+
+/*
+ * The offset (and mask) generator of the packed layer (dc1d page, section
+ * PackedDeformConv1d, and its Modulation (DCNv2) paragraph): the layer
+ * computes its own offsets from the input with a depthwise-separable
+ * convolutional block, and when modulated, a second pointwise branch off
+ * the same depthwise trunk, ending in a sigmoid, predicts the mask.  The
+ * page only sketches the block; the readings taken here:
+ *
+ *  - trunk: one depthwise conv1d over x with the layer's kernel size,
+ *    stride, padding and dilation (so it yields the L_out positions the
+ *    offsets need), optional bias, no normalisation or activation:
+ *        t[b,c,l] = tb[c] + sum_k tw[c,k] * x~[b,c, l*s - p + k*d];
+ *  - offset head: a pointwise conv C_in -> G*K with optional bias;
+ *    output channel g*K + k holds offsets[b,g,l,k]:
+ *        offsets[b,g,l,k] = ob[g*K+k] + sum_c ow[g*K+k, c] * t[b,c,l];
+ *  - mask head (only when mw is given): the same with (mw, mb), then the
+ *    logistic sigmoid 1 / (1 + exp(-z)).
+ *
+ * Sums run over k (trunk) and c (heads) in ascending order, bias added
+ * last.  tw is [C_in, K] (a [C_in, 1, K] depthwise weight), ow and mw are
+ * [G*K, C_in] (pointwise [G*K, C_in, 1]).  mask_out is written only when
+ * mw is given.
+ */
+int oracle_packed_heads(const double *x, const double *tw, const double *tb, const double *ow,
+                        const double *ob, const double *mw, const double *mb, int64_t B, int64_t C_in,
+                        int64_t L_in, int64_t K, int64_t s, int64_t p, int64_t d, int64_t G,
+                        double *offsets_out, double *mask_out)
+{
+    if (B < 0 || C_in < 1 || G < 1 || C_in % G)
+        return OR_BAD_ARG;
+    int64_t L_out = oracle_output_length(L_in, K, s, p, d);
+    if (L_out < 1)
+        return OR_BAD_ARG;
+    if (!all_finite(x, B * C_in * L_in) || !all_finite(tw, C_in * K) || (tb && !all_finite(tb, C_in)) ||
+        !all_finite(ow, G * K * C_in) || (ob && !all_finite(ob, G * K)) || (mw && !all_finite(mw, G * K * C_in)) ||
+        (mw && mb && !all_finite(mb, G * K)))
+        return OR_NONFINITE;
+    double *t = (double *)malloc((size_t)(C_in * L_out > 0 ? C_in * L_out : 1) * sizeof(double));
+    if (!t)
+        return OR_NOMEM;
+    for (int64_t b = 0; b < B; ++b) {
+        /* trunk */
+        for (int64_t c = 0; c < C_in; ++c) {
+            const double *row = x + (b * C_in + c) * L_in;
+            for (int64_t l = 0; l < L_out; ++l) {
+                double acc = 0.0;
+                for (int64_t k = 0; k < K; ++k)
+                    acc += tw[c * K + k] * x_ext(row, L_in, l * s - p + k * d);
+                t[c * L_out + l] = tb ? acc + tb[c] : acc;
+            }
+        }
+        /* heads */
+#pragma omp parallel for schedule(static)
+        for (int64_t gk = 0; gk < G * K; ++gk) {
+            const int64_t g = gk / K, k = gk % K;
+            for (int64_t l = 0; l < L_out; ++l) {
+                double zo = 0.0, zm = 0.0;
+                for (int64_t c = 0; c < C_in; ++c) {
+                    zo += ow[gk * C_in + c] * t[c * L_out + l];
+                    if (mw)
+                        zm += mw[gk * C_in + c] * t[c * L_out + l];
+                }
+                const int64_t o = ((b * G + g) * L_out + l) * K + k;
+                offsets_out[o] = ob ? zo + ob[gk] : zo;
+                if (mw) {
+                    const double z = mb ? zm + mb[gk] : zm;
+                    mask_out[o] = 1.0 / (1.0 + exp(-z));
+                }
+            }
+        }
+    }
+    free(t);
+    return OR_OK;
+}

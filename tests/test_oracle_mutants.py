@@ -15,6 +15,7 @@ import pytest
 
 import oracle
 import test_oracle_backward as bwd
+import test_oracle_packed as pk
 import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "dc1d_oracle.c")
@@ -59,6 +60,15 @@ MUTANTS = {
         "                                   sample(row, L_in, l * s - p + k * d, offsets[oi], NULL);"),
     "bwd bias over the first batch only": ("            for (int64_t b = 0; b < B; ++b)\n                for (int64_t l = 0; l < L_out; ++l)\n                    acc += dout",
                                            "            for (int64_t b = 0; b < 1; ++b)\n                for (int64_t l = 0; l < L_out; ++l)\n                    acc += dout"),
+    # the packed layer's generator
+    "gen head channels k-major": ("const int64_t g = gk / K, k = gk % K;", "const int64_t g = gk % G, k = gk / G;"),
+    "gen trunk dilation ignored": ("acc += tw[c * K + k] * x_ext(row, L_in, l * s - p + k * d);",
+                                   "acc += tw[c * K + k] * x_ext(row, L_in, l * s - p + k);"),
+    "gen trunk bias dropped": ("t[c * L_out + l] = tb ? acc + tb[c] : acc;", "t[c * L_out + l] = acc;"),
+    "gen sigmoid sign": ("mask_out[o] = 1.0 / (1.0 + exp(-z));", "mask_out[o] = 1.0 / (1.0 + exp(z));"),
+    "gen mask from the offset head": ("zm += mw[gk * C_in + c] * t[c * L_out + l];",
+                                      "zm += ow[gk * C_in + c] * t[c * L_out + l];"),
+    "gen offset bias dropped": ("offsets_out[o] = ob ? zo + ob[gk] : zo;", "offsets_out[o] = zo;"),
 }
 
 PIN_CALLS = [
@@ -79,6 +89,9 @@ PIN_CALLS = [
     ("backward = finite differences", lambda: bwd.test_backward_equals_finite_differences(bwd.SHAPES[1])),
     ("backward = hat-form autograd", lambda: bwd.test_backward_matches_hat_form_autograd(bwd.SHAPES[3])),
     ("backward = conv1d autograd", lambda: bwd.test_zero_offsets_match_conv1d_autograd(bwd.SHAPES[1])),
+    ("generator = conv1d composition", lambda: pk.test_generator_equals_conv1d_composition(pk.SHAPES[0])),
+    ("generator: zero mask head halves", pk.test_zero_mask_projection_halves_the_output),
+    ("generator: bias-only head", pk.test_bias_only_offset_head_places_each_channel),
 ]
 
 
