@@ -280,6 +280,118 @@ def main_backward(args, w):
     print(json.dumps(line), flush=True)
 
 
+def work_packed(w):
+    """Work of one packed-layer forward: flops of the trunk, the heads and the
+    forward's contraction and sampling; the bytes each of its kernels reads
+    and writes once (trunk: x, t; heads: t per head, offsets and mask;
+    forward: x, offsets, mask, out), and the layer's compulsory bytes (x,
+    parameters, out)."""
+    GK = w.G * w.K
+    heads = 2 if w.modulated else 1
+    flops = (2 * w.B * w.C_in * w.L_out * w.K + 2 * w.B * w.L_out * w.C_in * GK * heads
+             + 2 * w.B * w.C_out * w.L_out * (w.C_in // w.groups) * w.K
+             + (4 if w.modulated else 3) * w.B * w.C_in * w.L_out * w.K)
+    x, t, out = w.B * w.C_in * w.L_in, w.B * w.C_in * w.L_out, w.B * w.C_out * w.L_out
+    gen = w.B * GK * w.L_out * heads
+    params = w.C_in * (w.K + 1) + (GK * w.C_in + GK) * heads + w.C_out * ((w.C_in // w.groups) * w.K + 1)
+    pipeline = 4 * ((x + t) + (t * heads + gen) + (x + gen + out) + params)
+    compulsory = 4 * (x + params + out)
+    return flops, pipeline, compulsory
+
+
+def packed_label(w):
+    return "%s B%d Cin%d Cout%d L%d K%d s%d p%d d%d groups%d G%d%s f32" % (
+        w.name, w.B, w.C_in, w.C_out, w.L_in, w.K, w.stride, w.padding, w.dilation, w.groups, w.G,
+        " modulated" if w.modulated else "")
+
+
+def run_packed(w, steps, warmup, check=True, baseline=True):
+    """Time the packed layer (generator + forward) on the GPU; check every
+    output against one full oracle run, which is also the CPU baseline."""
+    import torch
+    from deformable_convolution_amd import dc1d, inputs
+
+    dev = torch.device("cuda:0")
+    t = inputs.make_packed_inputs(w, seed=0)
+    g = {k: (v.to(dev) if v is not None else None) for k, v in t.items()}
+    kw = dict(stride=w.stride, padding=w.padding, dilation=w.dilation, groups=w.groups)
+    args = (g["x"], g["trunk_weight"], g["trunk_bias"], g["off_weight"], g["off_bias"], g["weight"], g["bias"],
+            g["mask_weight"], g["mask_bias"])
+    out = torch.empty((w.B, w.C_out, w.L_out), dtype=torch.float32, device=dev)
+
+    def step():
+        dc1d.packed_forward(*args, out=out, **kw)
+
+    step()
+    torch.cuda.synchronize()
+    parity = cpu = None
+    if check or baseline:
+        import oracle
+        cores = len(os.sched_getaffinity(0))
+        os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+        t0 = time.perf_counter()
+        ref, r_off, r_mask = oracle.packed_forward(t["x"], t["trunk_weight"], t["trunk_bias"], t["off_weight"],
+                                                   t["off_bias"], t["weight"], t["bias"], t["mask_weight"],
+                                                   t["mask_bias"], **kw)
+        el = time.perf_counter() - t0
+        flops, _, _ = work_packed(w)
+        cpu = {"value": flops / el / 1e9, "unit": "GFLOP/s",
+               "cores": min(int(os.environ["OMP_NUM_THREADS"]), cores), "kind": "oracle",
+               "sample": "1 full packed-layer forward (generator and forward, all %d outputs), %.1f s, on %s"
+               % (w.B * w.C_out * w.L_out, el, cpu_model())}
+        # the forward's tolerance plus the generated inputs' tolerances carried
+        # through the interpolation (Lipschitz in the position, constant
+        # <= 2 max|x|), as in the packed parity tests
+        a = out.double().cpu().numpy()
+        rms = lambda v: math.sqrt(float(np.mean(v ** 2)))
+        n = (w.C_in // w.groups) * w.K
+        tol_o = 1e-5 * math.sqrt(w.C_in) * max(rms(r_off), 1.0)
+        tol_m = tol_o / 4 + 2.0 ** -20
+        mmax = float(np.abs(r_mask).max()) if r_mask is not None else 1.0
+        tol = (1e-5 * math.sqrt(n) * max(rms(ref), 1.0)
+               + n * float(t["weight"].abs().max()) * float(t["x"].abs().max()) * (2 * tol_o * mmax + tol_m))
+        err = float(np.abs(a - ref).max())
+        parity = {"elements": int(ref.size), "max_err": err, "tol": tol, "ok": bool(err <= tol)}
+        if not parity["ok"]:
+            raise SystemExit("packed parity check failed: %r" % parity)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        step()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i].record(stream)
+        step()
+    ev[steps].record(stream)
+    torch.cuda.synchronize()
+    launch_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return {"region_ms": ev[0].elapsed_time(ev[steps]), "launch_ms": launch_ms, "parity": parity, "cpu": cpu}
+
+
+def main_packed(args, w):
+    r = run_packed(w, args.steps, args.warmup, baseline=not args.no_cpu_baseline)
+    flops, pipeline, compulsory = work_packed(w)
+    ms = r["region_ms"] / args.steps
+    achieved = pipeline / (ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm_GBps"], "unit": "GB/s",
+            "frac": round(achieved / PEAK["hbm_GBps"], 4), "traffic": read_traffic(w.name, "packed", kernel_hash()),
+            "kernel": "packed", "kernel_ms": round(ms, 5)}
+    line = {
+        "metric": "Packed DeformConv1d fwd GFLOP/s (offset/mask generator + forward)",
+        "value": round(flops / (ms * 1e-3) / 1e9, 1),
+        "unit": "GFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic, seeded (deformable_convolution_amd/inputs.py; no dataset)",
+        "config": {"workload": packed_label(w), "pass": "packed forward",
+                   "compulsory_gb_per_s": round(compulsory / (ms * 1e-3) / 1e9, 1),
+                   "parity": r["parity"], "forward_ms": {"warm": pct(r["launch_ms"])}},
+        "roofline": roof,
+    }
+    if r["cpu"] is not None:
+        line["cpu_baseline"] = r["cpu"]
+    print(json.dumps(line), flush=True)
+
+
 def pct(v):
     """median, p10, p90 of a list of times (ms)."""
     if not v:
@@ -363,6 +475,14 @@ def main():
         print("copied %d bytes" % n, flush=True)
         return
 
+    if args.workload in inputs.PACKED_WORKLOADS:
+        w = inputs.PACKED_WORKLOADS[args.workload]
+        if args.profile_run:
+            run_packed(w, args.steps, args.warmup, check=False, baseline=False)
+            print("profile run: %s packed, %d timed launches" % (w.name, args.steps), flush=True)
+            return
+        main_packed(args, w)
+        return
     w = inputs.WORKLOADS[args.workload]
     if args.backward:
         if w.dtype != "f32":
@@ -467,7 +587,7 @@ def summarize_profile(d, workload):
 
     from deformable_convolution_amd import inputs
 
-    w = inputs.WORKLOADS[workload]
+    w = inputs.PACKED_WORKLOADS[workload] if workload in inputs.PACKED_WORKLOADS else inputs.WORKLOADS[workload]
 
     def csvs(sub, pattern):
         out = []
@@ -518,12 +638,15 @@ def summarize_profile(d, workload):
 
 def write_profile_md(d, workload, kernel):
     stats, rows_k, total_bytes, (cf_v, cw_v, f_scale, w_scale), w = summarize_profile(d, workload)
-    contraction, sampling, alg_bytes = work_backward(w) if kernel == "backward" else work(w)
+    if kernel == "packed":
+        contraction, alg_bytes, _ = work_packed(w)
+    else:
+        contraction, sampling, alg_bytes = work_backward(w) if kernel == "backward" else work(w)
     # launches in the trace run: the fewest calls of any of our kernels
     n_launch = min((int(r["Calls"]) for r in stats), default=1)
     fwd_ns = sum(float(r["TotalDurationNs"]) for r in stats) / max(n_launch, 1)
     out = []
-    out.append("# %s -- %s" % (workload_label(w), kernel))
+    out.append("# %s -- %s" % (packed_label(w) if kernel == "packed" else workload_label(w), kernel))
     out.append("")
     out.append("<!-- kernel=%s -->" % kernel)
     out.append("<!-- kernel_sources=%s -->" % kernel_hash())
@@ -531,7 +654,8 @@ def write_profile_md(d, workload, kernel):
         out.append("<!-- hbm_bytes_per_launch=%.0f -->" % total_bytes)
     out.append("")
     out.append("One launch = one %s call (every kernel it enqueues, back to back on one stream)."
-               % ("backward (all five gradients)" if kernel == "backward" else "forward"))
+               % {"backward": "backward (all five gradients)", "packed": "packed-layer forward (generator and "
+                  "forward)"}.get(kernel, "forward"))
     out.append("")
     out.append("Commands (rocprofv3, ROCm 7.2, one MI355X):")
     out.append("")
@@ -549,8 +673,10 @@ def write_profile_md(d, workload, kernel):
         out.append("| %s | %s | %.2f | %.1f |" % (short(r["Name"]), r["Calls"],
                                                float(r["AverageNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e3))
     out.append("")
-    out.append("Kernel time per launch (all its kernels' total over %d launches): %.2f us; contraction %.3f GFLOP "
-               "-> %.1f TFLOP/s over that time." % (n_launch, fwd_ns / 1e3, contraction / 1e9,
+    out.append("Kernel time per launch (all its kernels' total over %d launches): %.2f us; %s %.3f GFLOP "
+               "-> %.1f TFLOP/s over that time." % (n_launch, fwd_ns / 1e3,
+                                                    "all flops" if kernel == "packed" else "contraction",
+                                                    contraction / 1e9,
                                                     contraction / (fwd_ns * 1e-9) / 1e12 if fwd_ns else 0.0))
     out.append("")
     out.append("## HBM traffic (--pmc FETCH_SIZE, --pmc WRITE_SIZE; counter units per launch, all dispatches)")

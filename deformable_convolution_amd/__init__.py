@@ -1,4 +1,5 @@
-"""MI355X-native 1D deformable convolution (DeformConv1d): forward and backward.
+"""MI355X-native 1D deformable convolution (DeformConv1d): forward, backward, and
+the packed layer whose offsets (and mask) are generated from its input.
 
 The compute lives in ``libdc1d.so`` (HIP kernels for gfx950 behind a C ABI
 declared in ``include/dc1d.h``); ``deformable_convolution_amd.dc1d`` is the
@@ -14,6 +15,7 @@ from .dc1d import (  # noqa: F401
     library_path,
     load_library,
     output_length,
+    packed_forward,
     plan,
     resolve_padding,
     status_string,

@@ -361,6 +361,212 @@ int dc1d_backward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_t
     return e == hipSuccess ? DC1D_OK : DC1D_ERR_LAUNCH;
 }
 
+}  // extern "C"
+
+namespace {
+
+// The packed layer's call: the forward's parameters (offsets and mask point
+// at the generated tensors once the workspace is known), the trunk, the two
+// heads and the workspace layout.
+struct Packed {
+    Params fwd;
+    TrunkArgs trunk;
+    const float *ow, *ob, *mw, *mb;
+    int G, K;
+    bool given_off, given_mask;
+    size_t t_bytes, off_bytes, mask_bytes, cat_bytes, shared_bytes, total;
+};
+
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// The heads' GEMM: rows g*K + k (the offset head; with a mask, the mask
+// head's rows follow, M = 2*G*K), reduction over the C_in trunk channels,
+// columns (b, l); stored offsets-shaped by the head epilogue.
+Params head_gemm(const Packed &pk, const float *hw, const float *hb, void *off, void *mask, void *ws) {
+    Params q = {};
+    q.dtype = kF32;
+    q.w = hw;
+    q.x = pk.trunk.t;  // B(k = c, n = (b, l)) = t[b][c][l]
+    q.out = off;
+    q.mask = mask;
+    q.bias = hb;
+    q.B = pk.fwd.B;
+    q.C_out = pk.G * pk.K * (pk.mw ? 2 : 1);
+    q.Kred = pk.fwd.C_in;
+    q.L_out = pk.fwd.L_out;
+    q.K = pk.K;
+    q.G = pk.G;
+    q.ws = ws;
+    return q;
+}
+
+int validate_packed(const dc1d_tensor *x, const dc1d_tensor *tw, const dc1d_tensor *tb, const dc1d_tensor *ow,
+                    const dc1d_tensor *ob, const dc1d_tensor *mw, const dc1d_tensor *mb, const dc1d_tensor *w,
+                    const dc1d_tensor *bias, const dc1d_tensor *out, const dc1d_tensor *off_out,
+                    const dc1d_tensor *mask_out, int64_t stride, int64_t padding, int64_t dilation,
+                    int64_t groups, const DeviceInfo *dev, Packed *pk) {
+    if (!x || !tw || !ow || !w) return DC1D_ERR_NULL_PTR;
+    if (stride < 1 || padding < 0 || dilation < 1 || groups < 1) return DC1D_ERR_BAD_ARG;
+    if (!mw && (mb || mask_out)) return DC1D_ERR_BAD_ARG;
+    const dc1d_tensor *all[12] = {x, tw, tb, ow, ob, mw, mb, w, bias, out, off_out, mask_out};
+    for (const dc1d_tensor *t : all)
+        if (t && t->dtype != DC1D_F32) return DC1D_ERR_BAD_DTYPE;
+    if (x->ndim != 3 || tw->ndim != 3 || ow->ndim != 3) return DC1D_ERR_BAD_SHAPE;
+    const int64_t B = x->shape[0], C_in = x->shape[1], L_in = x->shape[2], K = tw->shape[2];
+    if (C_in < 1 || K < 1 || tw->shape[0] != C_in || tw->shape[1] != 1) return DC1D_ERR_BAD_SHAPE;
+    if (ow->shape[0] < 1 || ow->shape[0] % K || ow->shape[1] != C_in || ow->shape[2] != 1) return DC1D_ERR_BAD_SHAPE;
+    const int64_t G = ow->shape[0] / K;
+    if (C_in % G) return DC1D_ERR_BAD_ARG;
+    if (mw && !shape_is(mw, 3, ow->shape)) return DC1D_ERR_BAD_SHAPE;
+    const int64_t sc[1] = {C_in}, sh[1] = {G * K};
+    if (tb && !shape_is(tb, 1, sc)) return DC1D_ERR_BAD_SHAPE;
+    if ((ob && !shape_is(ob, 1, sh)) || (mb && !shape_is(mb, 1, sh))) return DC1D_ERR_BAD_SHAPE;
+    const int64_t L_out = dc1d_output_length(L_in, K, stride, padding, dilation);
+    if (L_out < 1) return DC1D_ERR_BAD_SHAPE;
+    dc1d_tensor offT = {nullptr, DC1D_F32, 4, {B, G, L_out, K}};
+    int st = validate(x, &offT, mw ? &offT : nullptr, w, bias, out, stride, padding, dilation, groups, G,
+                      &pk->fwd);
+    if (st) return st;
+    if (off_out && !shape_is(off_out, 4, offT.shape)) return DC1D_ERR_BAD_SHAPE;
+    if (mask_out && !shape_is(mask_out, 4, offT.shape)) return DC1D_ERR_BAD_SHAPE;
+    if (B * L_out >= ((int64_t)1 << 31)) return DC1D_ERR_BAD_SHAPE;
+    pk->G = (int)G;
+    pk->K = (int)K;
+    pk->ow = (const float *)ow->data;
+    pk->ob = ob ? (const float *)ob->data : nullptr;
+    pk->mw = mw ? (const float *)mw->data : nullptr;
+    pk->mb = mb ? (const float *)mb->data : nullptr;
+    pk->given_off = off_out != nullptr;
+    pk->given_mask = mask_out != nullptr;
+    TrunkArgs &t = pk->trunk;
+    t = TrunkArgs{};
+    t.x = x->data;
+    t.tw = (const float *)tw->data;
+    t.tb = tb ? (const float *)tb->data : nullptr;
+    t.dtype = kF32;
+    t.B = (int)B;
+    t.C = (int)C_in;
+    t.L_in = (int)L_in;
+    t.L_out = (int)L_out;
+    t.K = (int)K;
+    t.stride = (int)stride;
+    t.padding = (int)padding;
+    t.dilation = (int)dilation;
+    // workspace: trunk | offsets | mask | stacked head weights and biases
+    // (with a mask) | max(head GEMM partials, the forward's workspace)
+    const size_t n_off = (size_t)B * G * L_out * K * 4;
+    pk->t_bytes = round256((size_t)B * C_in * L_out * 4);
+    pk->off_bytes = round256(n_off);
+    pk->mask_bytes = mw ? round256(n_off) : 0;
+    pk->cat_bytes = mw ? round256((size_t)2 * G * K * C_in * 4) + round256((size_t)2 * G * K * 4) : 0;
+    const size_t gemm =
+        gemm_workspace_bytes(head_gemm(*pk, nullptr, nullptr, nullptr, nullptr, nullptr), 1, dev->num_cus);
+    const size_t fwd = make_plan(pk->fwd, *dev).ws_bytes;
+    pk->shared_bytes = round256(gemm > fwd ? gemm : fwd);
+    pk->total = pk->t_bytes + pk->off_bytes + pk->mask_bytes + pk->cat_bytes + pk->shared_bytes;
+    return DC1D_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dc1d_packed_workspace_bytes(const dc1d_tensor *x, const dc1d_tensor *trunk_weight,
+                                const dc1d_tensor *off_weight, const dc1d_tensor *mask_weight_or_null,
+                                const dc1d_tensor *weight, int64_t stride, int64_t padding, int64_t dilation,
+                                int64_t groups, size_t *bytes_out) {
+    if (!bytes_out) return DC1D_ERR_NULL_PTR;
+    DeviceInfo dev;
+    int st = current_device(&dev);
+    if (st) return st;
+    Packed pk;
+    st = validate_packed(x, trunk_weight, nullptr, off_weight, nullptr, mask_weight_or_null, nullptr, weight,
+                         nullptr, nullptr, nullptr, nullptr, stride, padding, dilation, groups, &dev, &pk);
+    if (st) return st;
+    *bytes_out = pk.total;
+    return DC1D_OK;
+}
+
+int dc1d_packed_forward(const dc1d_tensor *x, const dc1d_tensor *trunk_weight,
+                        const dc1d_tensor *trunk_bias_or_null, const dc1d_tensor *off_weight,
+                        const dc1d_tensor *off_bias_or_null, const dc1d_tensor *mask_weight_or_null,
+                        const dc1d_tensor *mask_bias_or_null, const dc1d_tensor *weight,
+                        const dc1d_tensor *bias_or_null, const dc1d_tensor *out,
+                        const dc1d_tensor *offsets_out_or_null, const dc1d_tensor *mask_out_or_null,
+                        int64_t stride, int64_t padding, int64_t dilation, int64_t groups, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    if (!out) return DC1D_ERR_NULL_PTR;
+    DeviceInfo dev;
+    int st = current_device(&dev);
+    if (st) return st;
+    Packed pk;
+    st = validate_packed(x, trunk_weight, trunk_bias_or_null, off_weight, off_bias_or_null, mask_weight_or_null,
+                         mask_bias_or_null, weight, bias_or_null, out, offsets_out_or_null, mask_out_or_null,
+                         stride, padding, dilation, groups, &dev, &pk);
+    if (st) return st;
+    const dc1d_tensor *ins[9] = {x, trunk_weight, trunk_bias_or_null, off_weight, off_bias_or_null,
+                                 mask_weight_or_null, mask_bias_or_null, weight, bias_or_null};
+    const dc1d_tensor *outs[3] = {out, offsets_out_or_null, mask_out_or_null};
+    for (const dc1d_tensor *t : ins)
+        if (t && numel(t) > 0 && !t->data) return DC1D_ERR_NULL_PTR;
+    for (const dc1d_tensor *t : outs)
+        if (t && numel(t) > 0 && !t->data) return DC1D_ERR_NULL_PTR;
+    for (int i = 0; i < 3; ++i) {
+        const dc1d_tensor *o = outs[i];
+        if (!o) continue;
+        const size_t ob = (size_t)numel(o) * 4;
+        for (const dc1d_tensor *t : ins)
+            if (t && overlaps(o->data, ob, t->data, (size_t)numel(t) * 4)) return DC1D_ERR_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (outs[j] && overlaps(o->data, ob, outs[j]->data, (size_t)numel(outs[j]) * 4)) return DC1D_ERR_ALIAS;
+    }
+    if (pk.total > 0) {
+        if (!workspace || workspace_bytes < pk.total || ((uintptr_t)workspace & 255)) return DC1D_ERR_WORKSPACE;
+        for (const dc1d_tensor *t : ins)
+            if (t && overlaps(workspace, pk.total, t->data, (size_t)numel(t) * 4)) return DC1D_ERR_ALIAS;
+        for (const dc1d_tensor *t : outs)
+            if (t && overlaps(workspace, pk.total, t->data, (size_t)numel(t) * 4)) return DC1D_ERR_ALIAS;
+    }
+    if (pk.fwd.B == 0) return DC1D_OK;
+
+    char *ws = (char *)workspace;
+    float *t = (float *)ws;
+    void *off = pk.given_off ? offsets_out_or_null->data : (void *)(ws + pk.t_bytes);
+    void *mask = pk.mw ? (pk.given_mask ? mask_out_or_null->data : (void *)(ws + pk.t_bytes + pk.off_bytes))
+                       : nullptr;
+    char *cat = ws + pk.t_bytes + pk.off_bytes + pk.mask_bytes;
+    void *shared = cat + pk.cat_bytes;
+    hipStream_t s = (hipStream_t)stream;
+    pk.trunk.t = t;
+    hipError_t e = launch_trunk(pk.trunk, s);
+    if (e != hipSuccess) return DC1D_ERR_LAUNCH;
+    const int64_t brow = pk.fwd.L_out, bbatch = (int64_t)pk.fwd.C_in * pk.fwd.L_out;
+    if (pk.mw) {
+        // one GEMM for both heads: their weights and biases stacked
+        const int GK = pk.G * pk.K;
+        float *wcat = (float *)cat;
+        float *bcat = (float *)(cat + round256((size_t)2 * GK * pk.fwd.C_in * 4));
+        e = launch_stack_heads(pk.ow, pk.ob, pk.mw, pk.mb, GK, pk.fwd.C_in, wcat, bcat, s);
+        if (e != hipSuccess) return DC1D_ERR_LAUNCH;
+        e = launch_gemm_f32(head_gemm(pk, wcat, bcat, off, mask, shared), brow, bbatch, 2, dev.num_cus, s);
+    } else {
+        e = launch_gemm_f32(head_gemm(pk, pk.ow, pk.ob, off, nullptr, shared), brow, bbatch, 1, dev.num_cus, s);
+    }
+    if (e != hipSuccess) return DC1D_ERR_LAUNCH;
+    Params p = pk.fwd;
+    p.off = off;
+    p.mask = mask;
+    p.ws = shared;
+    p.ws_bytes = pk.shared_bytes;
+    const Plan pl = make_plan(p, dev);
+    switch (pl.kernel) {
+    case kMfma: e = launch_mfma(p, pl.mfma, s); break;
+    case kDepthwise: e = launch_depthwise(p, pl.dw, s); break;
+    default: e = launch_direct(p, s); break;
+    }
+    return e == hipSuccess ? DC1D_OK : DC1D_ERR_LAUNCH;
+}
+
 int dc1d_debug_positions(const dc1d_tensor *offsets, int64_t L_in, int64_t stride, int64_t padding,
                          int64_t dilation, int32_t *i0, float *frac, uint8_t *valid, void *stream) {
     if (!offsets) return DC1D_ERR_NULL_PTR;

@@ -149,9 +149,27 @@ struct BwdParams {
 };
 // Plain fp32 GEMM on the MFMA kernel (k_mfma.hip): C[b][m][j] =
 // sum_k A[m][k] * x[b*bbatch + j + k*brow] with A = q.w [q.C_out][q.Kred],
-// C = q.out [q.B][q.C_out][q.L_out]; split partials in q.ws.
-size_t gemm_workspace_bytes(const Params &q, int num_cus);
-hipError_t launch_gemm_f32(const Params &q, int64_t brow, int64_t bbatch, int num_cus, hipStream_t stream);
+// C = q.out [q.B][q.C_out][q.L_out]; split partials in q.ws.  out_mode 1 and
+// 2 store instead the packed layer's generator heads: row g*q.K + k (g <
+// q.G) of column (b, l) at q.out[((b*q.G + g)*q.L_out + l)*q.K + k]; with
+// out_mode 2 the rows q.G*q.K + g*q.K + k are the mask head, stored the same
+// way into q.mask through the logistic sigmoid.
+size_t gemm_workspace_bytes(const Params &q, int out_mode, int num_cus);
+hipError_t launch_gemm_f32(const Params &q, int64_t brow, int64_t bbatch, int out_mode, int num_cus,
+                           hipStream_t stream);
+// The packed layer's trunk (fp32 storage): t[b,c,l] = tb[c] +
+// sum_k tw[c,k] * x~[b,c, l*stride - padding + k*dilation], t [B][C][L_out].
+struct TrunkArgs {
+    const void *x;
+    const float *tw, *tb;  // [C][K], [C] or null
+    float *t;
+    int dtype, B, C, L_in, L_out, K, stride, padding, dilation;
+};
+hipError_t launch_trunk(const TrunkArgs &a, hipStream_t stream);
+// wcat = [ow; mw] ([2*GK][C] row-major), bcat = [ob; mb] (null biases as
+// zeros): the packed layer's two heads stacked for one GEMM.
+hipError_t launch_stack_heads(const float *ow, const float *ob, const float *mw, const float *mb, int GK, int C,
+                              float *wcat, float *bcat, hipStream_t stream);
 size_t backward_workspace_bytes(const Params &p, bool want_weight, int num_cus);
 hipError_t launch_backward(BwdParams a, int num_cus, hipStream_t stream);
 

@@ -556,13 +556,13 @@ BwdLayout layout(const Params &p, bool want_weight, int num_cus) {
     if (dense_path(p)) {
         L.wt = o;
         o += align256((size_t)p.C_out * p.C_in * p.K * 4);
-        size_t part = gemm_workspace_bytes(gemm_ds(p, nullptr, nullptr, nullptr, nullptr), num_cus);
+        size_t part = gemm_workspace_bytes(gemm_ds(p, nullptr, nullptr, nullptr, nullptr), 0, num_cus);
         if (want_weight) {
             L.S = o;
             o += align256(nds);
             L.A = o;
             o += align256((size_t)p.B * p.C_out * p.L_out * 4);
-            part = std::max(part, gemm_workspace_bytes(gemm_dw(p, nullptr, nullptr, nullptr, nullptr), num_cus));
+            part = std::max(part, gemm_workspace_bytes(gemm_dw(p, nullptr, nullptr, nullptr, nullptr), 0, num_cus));
         }
         L.part = o;
         o += align256(part);
@@ -649,7 +649,7 @@ hipError_t launch_backward(BwdParams a, int num_cus, hipStream_t stream) {
             hipLaunchKernelGGL(k_transpose, dim3((unsigned)((CK + 31) / 32), (unsigned)((p.C_out + 31) / 32)),
                                dim3(256), 0, stream, (const float *)p.w, wt, p.C_out, CK);
             const hipError_t e = launch_gemm_f32(gemm_ds(p, wt, a.dout, a.dS, ws + L.part), p.L_out,
-                                                 (int64_t)p.C_out * p.L_out, num_cus, stream);
+                                                 (int64_t)p.C_out * p.L_out, 0, num_cus, stream);
             if (e != hipSuccess) return e;
             if (s.S) hipLaunchKernelGGL(k_bwd_samples_t, dim3(grid_for(n)), dim3(256), 0, stream, s);
         } else {
@@ -663,7 +663,7 @@ hipError_t launch_backward(BwdParams a, int num_cus, hipStream_t stream) {
                 const int64_t nd = (int64_t)p.B * p.C_out * p.L_out;
                 hipLaunchKernelGGL(k_restride_dout, dim3(grid_for(nd)), dim3(256), 0, stream, a, A);
                 const hipError_t e = launch_gemm_f32(gemm_dw(p, A, s.S, a.gw, ws + L.part), p.C_in * p.K, 0,
-                                                     num_cus, stream);
+                                                     0, num_cus, stream);
                 if (e != hipSuccess) return e;
             } else {
                 hipLaunchKernelGGL(k_bwd_weight, dim3((unsigned)(p.C_out * p.cpg * p.K)), dim3(256), 0, stream, s);

@@ -193,8 +193,10 @@ MfmaPlan plan_mfma(const Params &p, int num_cus) {
     return pl;
 }
 
-size_t gemm_workspace_bytes(const Params &q, int num_cus) {
-    using Tr = TrF32;
+// The plain GEMM's tiling: 256 x 128 tiles for the backward's contractions
+// (out_mode 0), 128 x 128 for the packed layer's heads (out_mode 1, 2).
+template <class Tr>
+MfmaPlan gemm_plan(const Params &q, int num_cus) {
     constexpr int BM = Geo<Tr>::BM, BN = Geo<Tr>::BN;
     MfmaPlan pl = {};
     const int64_t N = (int64_t)q.B * q.L_out;
@@ -202,23 +204,26 @@ size_t gemm_workspace_bytes(const Params &q, int num_cus) {
     pl.tiles_n = (int)((N + BN - 1) / BN);
     pl.chunks = (q.Kred + BK - 1) / BK;
     plan_splits((int64_t)pl.tiles_m * pl.tiles_n, pl.chunks, num_cus, pl);
-    return pl.splits > 1 ? (size_t)pl.tiles_m * pl.tiles_n * pl.splits * BM * BN * 4 : 0;
+    return pl;
 }
 
-hipError_t launch_gemm_f32(const Params &q, int64_t brow, int64_t bbatch, int num_cus, hipStream_t stream) {
-    using Tr = TrF32;
+template <class Tr>
+size_t gemm_ws(const Params &q, int num_cus) {
+    const MfmaPlan pl = gemm_plan<Tr>(q, num_cus);
+    return pl.splits > 1 ? (size_t)pl.tiles_m * pl.tiles_n * pl.splits * Geo<Tr>::BM * Geo<Tr>::BN * 4 : 0;
+}
+
+template <class Tr, int OUT>
+hipError_t launch_gemm_t(const Params &q, int64_t brow, int64_t bbatch, int num_cus, hipStream_t stream) {
     constexpr int BM = Geo<Tr>::BM, BN = Geo<Tr>::BN;
-    MfmaPlan pl = {};
     const int64_t N = (int64_t)q.B * q.L_out;
     if (N == 0 || q.C_out == 0) return hipSuccess;
-    pl.tiles_m = (q.C_out + BM - 1) / BM;
-    pl.tiles_n = (int)((N + BN - 1) / BN);
-    pl.chunks = (q.Kred + BK - 1) / BK;
-    plan_splits((int64_t)pl.tiles_m * pl.tiles_n, pl.chunks, num_cus, pl);
+    const MfmaPlan pl = gemm_plan<Tr>(q, num_cus);
     MfmaArgs a = {};
     a.p = q;
     a.fd_Lout = make_fastdiv((uint32_t)q.L_out);
     a.fd_K = a.fd_cpo = a.fd_nkb = make_fastdiv(1);
+    if (OUT != 0) a.fd_K = make_fastdiv((uint32_t)q.K);  // the head write-out's tap divisor
     a.tiles_m = pl.tiles_m;
     a.tiles_n = pl.tiles_n;
     a.splits = pl.splits;
@@ -230,16 +235,35 @@ hipError_t launch_gemm_f32(const Params &q, int64_t brow, int64_t bbatch, int nu
     a.partials = pl.splits > 1 ? (float *)q.ws : nullptr;
     a.brow = brow;
     a.bbatch = bbatch;
-    const size_t lds = (size_t)a.off_s + 2 * (size_t)BN * Tr::SLD * 4;
-    hipLaunchKernelGGL((k_gemm<Tr>), dim3((unsigned)pl.blocks), dim3(NTT), lds, stream, a);
+    size_t lds = (size_t)a.off_s + 2 * (size_t)BN * Tr::SLD * 4;
+    if (OUT != 0) {
+        if (BN + 1 != kHeadLd || q.K < 1 || (int64_t)BN * q.K >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+        lds = std::max(lds, (size_t)BM * (kHeadLd + 1) * 4);  // the staged head tile and its biases
+    }
+    hipLaunchKernelGGL((k_gemm<Tr, OUT>), dim3((unsigned)pl.blocks), dim3(NTT), lds, stream, a);
     if (pl.splits > 1) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int64_t tiles = (int64_t)pl.tiles_m * pl.tiles_n;
         const int64_t vecs = tiles * (BM * BN / 4);
-        hipLaunchKernelGGL((k_split_reduce<Tr>), dim3((unsigned)((vecs + 255) / 256)), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((k_split_reduce<Tr, OUT>), dim3((unsigned)((vecs + 255) / 256)), dim3(256), 0, stream,
+                           a);
     }
     return hipGetLastError();
+}
+
+size_t gemm_workspace_bytes(const Params &q, int out_mode, int num_cus) {
+    return out_mode == 0 ? gemm_ws<TrF32>(q, num_cus) : gemm_ws<TrF32H>(q, num_cus);
+}
+
+hipError_t launch_gemm_f32(const Params &q, int64_t brow, int64_t bbatch, int out_mode, int num_cus,
+                           hipStream_t stream) {
+    switch (out_mode) {
+    case 0: return launch_gemm_t<TrF32, 0>(q, brow, bbatch, num_cus, stream);
+    case 1: return launch_gemm_t<TrF32H, 1>(q, brow, bbatch, num_cus, stream);
+    case 2: return launch_gemm_t<TrF32H, 2>(q, brow, bbatch, num_cus, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_mfma(const Params &p, const MfmaPlan &pl, hipStream_t stream) {

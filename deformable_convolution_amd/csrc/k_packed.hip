@@ -1,0 +1,124 @@
+// k_packed.hip -- the trunk of the packed layer's offset generator.
+//
+// The packed layer (dc1d page, section PackedDeformConv1d) computes its
+// offsets from its input with a depthwise-separable block; its trunk is a
+// depthwise conv1d with the layer's kernel size, stride, padding and
+// dilation, so that it yields one column per output position:
+//     t[b,c,l] = tb[c] + sum_k tw[c,k] * x~[b,c, l*s - p + k*d]
+// (x~ zero outside [0, L_in)).  The pointwise heads that follow are the
+// MFMA GEMM (k_gemm with a head epilogue) and the deformable forward is the
+// library's own; this file holds only the trunk.
+//
+// One block takes kTrLT consecutive outputs of one (b, c) row.  The row's
+// input span for those outputs is staged in LDS, sized to the span, when it
+// fits (each x element then leaves HBM once), else every tap reads global
+// memory (bounds-checked).  Thread t computes outputs l0 + t + 256*j (j < kTrOpt),
+// so every load and store of a j is coalesced.
+#include "dc1d_internal.h"
+
+namespace dc1d {
+namespace {
+
+constexpr int kTrThreads = 256;
+constexpr int kTrOpt = 4;
+constexpr int kTrLT = kTrThreads * kTrOpt;  // outputs per block
+constexpr int kTrWinMax = 16384;            // largest LDS window (floats)
+constexpr int kTrFill = 5;                  // window loads per thread in flight together
+
+// win: the LDS window's capacity in floats (the span of a full tile), or 0
+// when that would exceed kTrWinMax (every tap then reads global memory).
+template <class D>
+__global__ void __launch_bounds__(kTrThreads) k_trunk(TrunkArgs a, int tiles_l, int win_cap) {
+    using T = typename D::T;
+    extern __shared__ float s_x[];
+    const int64_t blk = blockIdx.x;
+    const int64_t row = blk / tiles_l;  // b*C + c
+    const int tile = (int)(blk - row * tiles_l);
+    const int c = (int)(row % a.C);
+    const int l0 = tile * kTrLT;
+    const T *__restrict__ xr = (const T *)a.x + row * a.L_in;
+    const int K = a.K, s = a.stride, d = a.dilation;
+    const int lo = l0 * s - a.padding;
+    const int nout = min(kTrLT, a.L_out - l0);
+    const int span = (nout - 1) * s + (K - 1) * d + 1;
+    const bool win = span <= win_cap;
+    if (win) {
+        // kTrFill loads per thread issued together, then the rest (spans
+        // beyond kTrFill * kTrThreads: strides or dilations above one)
+        float v[kTrFill];
+#pragma unroll
+        for (int q = 0; q < kTrFill; ++q) {
+            const int i = threadIdx.x + kTrThreads * q, pos = lo + i;
+            v[q] = (i < span && pos >= 0 && pos < a.L_in) ? D::ld(xr, pos) : 0.0f;
+        }
+#pragma unroll
+        for (int q = 0; q < kTrFill; ++q) {
+            const int i = threadIdx.x + kTrThreads * q;
+            if (i < span) s_x[i] = v[q];
+        }
+        for (int i = threadIdx.x + kTrThreads * kTrFill; i < span; i += kTrThreads) {
+            const int pos = lo + i;
+            s_x[i] = (pos >= 0 && pos < a.L_in) ? D::ld(xr, pos) : 0.0f;
+        }
+        __syncthreads();
+    }
+    const float *__restrict__ tw = a.tw + (int64_t)c * K;
+    const float bias = a.tb ? a.tb[c] : 0.0f;
+    float *__restrict__ tr = a.t + row * a.L_out;
+#pragma unroll
+    for (int j = 0; j < kTrOpt; ++j) {
+        const int lo_j = threadIdx.x + kTrThreads * j;  // output index inside the tile
+        if (lo_j >= nout) break;
+        float acc = 0.0f;
+        if (win) {
+            for (int k = 0; k < K; ++k) acc += tw[k] * s_x[lo_j * s + k * d];
+        } else {
+            for (int k = 0; k < K; ++k) {
+                const int pos = lo + lo_j * s + k * d;
+                acc += tw[k] * ((pos >= 0 && pos < a.L_in) ? D::ld(xr, pos) : 0.0f);
+            }
+        }
+        tr[l0 + lo_j] = acc + bias;
+    }
+}
+
+__global__ void __launch_bounds__(256) k_stack_heads(const float *__restrict__ ow, const float *__restrict__ ob,
+                                                     const float *__restrict__ mw, const float *__restrict__ mb,
+                                                     int64_t nw, int GK, float *__restrict__ wcat,
+                                                     float *__restrict__ bcat) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < nw) {
+        wcat[i] = ow[i];
+        wcat[nw + i] = mw[i];
+    }
+    if (i < GK) {
+        bcat[i] = ob ? ob[i] : 0.0f;
+        bcat[GK + i] = mb ? mb[i] : 0.0f;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_stack_heads(const float *ow, const float *ob, const float *mw, const float *mb, int GK, int C,
+                              float *wcat, float *bcat, hipStream_t stream) {
+    const int64_t nw = (int64_t)GK * C;
+    const int64_t n = nw > GK ? nw : GK;
+    hipLaunchKernelGGL(k_stack_heads, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, ow, ob, mw, mb, nw,
+                       GK, wcat, bcat);
+    return hipGetLastError();
+}
+
+hipError_t launch_trunk(const TrunkArgs &a, hipStream_t stream) {
+    if (a.B == 0 || a.L_out == 0) return hipSuccess;
+    const int tiles_l = (a.L_out + kTrLT - 1) / kTrLT;
+    const int64_t blocks = (int64_t)a.B * a.C * tiles_l;
+    if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    if (a.dtype != kF32) return hipErrorInvalidValue;
+    const int64_t span = (int64_t)(kTrLT - 1) * a.stride + (int64_t)(a.K - 1) * a.dilation + 1;
+    const int win_cap = span <= kTrWinMax ? (int)span : 0;
+    hipLaunchKernelGGL((k_trunk<F32>), dim3((unsigned)blocks), dim3(kTrThreads), (size_t)win_cap * 4, stream, a,
+                       tiles_l, win_cap);
+    return hipGetLastError();
+}
+
+}  // namespace dc1d

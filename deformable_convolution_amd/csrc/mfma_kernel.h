@@ -156,6 +156,13 @@ struct TrF32 {
     }
 };
 
+// fp32 with half the rows per MFMA wave (a 128 x 128 tile): the packed
+// layer's head GEMM, whose short reduction makes the tile's write-out, not
+// its MFMAs, the long phase; the smaller tile lets two workgroups share a CU.
+struct TrF32H : TrF32 {
+    static constexpr int MB = 2;
+};
+
 // Two floats -> two bfloat16 (round to nearest even), packed low/high.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     const bf2 r = __builtin_convertvector(f2{lo, hi}, bf2);
@@ -213,6 +220,44 @@ struct Tile {
     int WT, nseg, b_first;
 };
 
+// GEMMs whose rows are the packed layer's generator head channels store
+// their output offsets-shaped.  OUT 1: rows g*K + k (g < G) go to p.out
+// [B][G][L_out][K].  OUT 2: the offset and mask heads stacked, rows
+// [0, G*K) as OUT 1 and rows G*K + g*K + k to the mask tensor (p.mask, same
+// shape) through the logistic sigmoid.  OUT 0 is the convolution's
+// [B][M][L_out].
+__device__ __forceinline__ float sigmoid(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+// Destination row (b, g) of the run of L_out*K elements that holds head
+// group gg (offset group gg, or mask group gg - G), and whether it is a
+// mask group.
+template <class Tr, int OUT>
+__device__ __forceinline__ typename Tr::T *head_run(const Params &p, int b, int gg, bool &is_mask) {
+    using T = typename Tr::T;
+    is_mask = OUT == 2 && gg >= p.G;
+    T *base = is_mask ? (T *)p.mask : (T *)p.out;
+    const int g = is_mask ? gg - p.G : gg;
+    return base + ((int64_t)b * p.G + g) * p.L_out * p.K;
+}
+
+// One element, stored where it belongs (the split-K reduction's path).
+template <class Tr, int OUT>
+__device__ __forceinline__ void store_head(const Params &p, int b, int l, int row, float v) {
+    static_assert(OUT == 1 || OUT == 2, "head layouts only");
+    const int gg = row / p.K, k = row - gg * p.K;
+    bool is_mask;
+    typename Tr::T *run = head_run<Tr, OUT>(p, b, gg, is_mask);
+    Tr::D::st(run, (int64_t)l * p.K + k, is_mask ? sigmoid(v) : v);
+}
+
+// The direct path stages the finished tile (without bias) in LDS as
+// [BM][BN + 1] floats, followed by the tile rows' biases, and then all the
+// workgroup's threads write it out in destination order: for each offset
+// group g the tile covers, its columns l0 .. l0+BN-1 times its K taps are one
+// contiguous run of the output (per batch), so consecutive threads store
+// consecutive addresses.
+constexpr int kHeadLd = 128 + 1;  // staging row pitch (floats) for BN = 128
+
 // ---- the MFMA role -------------------------------------------------------------
 //
 // Weight layout WL: 0: the weight viewed as [C_out][Kred], chunk c at
@@ -220,7 +265,7 @@ struct Tile {
 // order, rows of 32 contiguous elements, always in bounds); 2: channel-block
 // order read straight from the weight when a chunk row's four taps of one
 // channel are one aligned 16-byte word (fp32, 32/CB == 4, K % 4 == 0).
-template <class Tr, int WL>
+template <class Tr, int WL, int OUT = 0>
 __device__ __forceinline__ void mfma_role(const MfmaArgs &a, const Tile &tl, typename Tr::T *s_w,
                                           const typename Tr::T *s_S) {
     using D = typename Tr::D;
@@ -369,6 +414,21 @@ __device__ __forceinline__ void mfma_role(const MfmaArgs &a, const Tile &tl, typ
         }
         return;
     }
+    if constexpr (OUT != 0) {
+        // stage for the workgroup-wide write-out (every LDS read of the
+        // main loop is behind its last barrier)
+        static_assert(BN + 1 == kHeadLd, "staging pitch");
+        float *s_out = (float *)s_w;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int rl = row0 + 32 * mb + 8 * (q >> 2) + 4 * lh + (q & 3);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) s_out[rl * kHeadLd + col0 + 32 * nb + li] = acc[mb][nb][q];
+            }
+        return;
+    }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const int col = (int)tl.n0 + col0 + 32 * nb + li;
@@ -383,6 +443,40 @@ __device__ __forceinline__ void mfma_role(const MfmaArgs &a, const Tile &tl, typ
                 const int row = tl.m0 + row0 + 32 * mb + 8 * (q >> 2) + 4 * lh + (q & 3);
                 if (row < M) D::st(ob, (int64_t)row * L_out, acc[mb][nb][q] + (bias ? D::ld(bias, row) : 0.0f));
             }
+    }
+}
+
+// The write-out of a staged head tile (all threads of the workgroup; see
+// kHeadLd).  Thread t takes the pairs j = t, t + NTT, ... of (column c, tap
+// k) = (j / K, j % K) and, for each offset group g the tile covers, the
+// element at row g*K + k: consecutive threads hold consecutive addresses of
+// one group's run.  Bias and the head's sigmoid are applied here.
+template <class Tr, int OUT>
+__device__ __forceinline__ void head_writeout(const MfmaArgs &a, const Tile &tl, const float *s_out,
+                                              const float *s_bias) {
+    constexpr int BM = Geo<Tr>::BM, BN = Geo<Tr>::BN;
+    const Params &p = a.p;
+    const int K = p.K, M = p.C_out, L_out = p.L_out;
+    const int rows = min(BM, M - tl.m0);
+    const int ncol = (int)min((int64_t)BN, a.N - tl.n0);
+    const int g_first = (int)fdiv((uint32_t)tl.m0, a.fd_K);
+    const int ng = (int)fdiv((uint32_t)(tl.m0 + rows - 1), a.fd_K) - g_first + 1;
+    for (int j = threadIdx.x; j < BN * K; j += NTT) {
+        const int c = (int)fdiv((uint32_t)j, a.fd_K);
+        const int k = j - c * K;
+        if (c >= ncol) continue;
+        const int n = (int)tl.n0 + c;
+        const int b = (int)fdiv((uint32_t)n, a.fd_Lout);
+        const int64_t at = (int64_t)(n - b * L_out) * K + k;  // (l, k) inside a run
+        int rl = g_first * K + k - tl.m0;
+#pragma unroll 4
+        for (int gi = 0; gi < ng; ++gi, rl += K) {
+            if (rl < 0 || rl >= rows) continue;
+            bool is_mask;
+            typename Tr::T *run = head_run<Tr, OUT>(p, b, g_first + gi, is_mask);
+            const float v = s_out[rl * kHeadLd + c] + s_bias[rl];
+            Tr::D::st(run, at, is_mask ? sigmoid(v) : v);
+        }
     }
 }
 
@@ -1015,7 +1109,7 @@ __device__ __forceinline__ void loader_role(const MfmaArgs &a, const Tile &tl, t
     }
 }
 
-template <class Tr>
+template <class Tr, int OUT>
 __global__ void __launch_bounds__(NTT) k_gemm(MfmaArgs a) {
     using T = typename Tr::T;
     constexpr int BM = Geo<Tr>::BM, BN = Geo<Tr>::BN;
@@ -1036,9 +1130,21 @@ __global__ void __launch_bounds__(NTT) k_gemm(MfmaArgs a) {
     tl.win = false;
     tl.WT = tl.nseg = tl.b_first = 0;
     if (threadIdx.x < NTM)
-        mfma_role<Tr, 0>(a, tl, s_w, s_S);
+        mfma_role<Tr, 0, OUT>(a, tl, s_w, s_S);
     else
         loader_role<Tr>(a, tl, s_S);
+    if constexpr (OUT != 0) {
+        if (a.splits == 1) {  // uniform: the direct path staged the tile in LDS
+            float *s_bias = (float *)s_w + BM * kHeadLd;
+            const T *__restrict__ bias = (const T *)a.p.bias;
+            for (int r = threadIdx.x - NTM; r >= 0 && r < BM; r += NTT - NTM) {
+                const int row = tl.m0 + r;
+                s_bias[r] = (bias && row < a.p.C_out) ? Tr::D::ld(bias, row) : 0.0f;
+            }
+            __syncthreads();
+            head_writeout<Tr, OUT>(a, tl, (const float *)s_w, s_bias);
+        }
+    }
 }
 
 // Sum of the split partial tiles (in split order), plus bias, into out.
@@ -1046,7 +1152,7 @@ __global__ void __launch_bounds__(NTT) k_gemm(MfmaArgs a) {
 // MFMA thread t of every split's workgroup kept in its register group q4, so
 // the register-order layout maps back to (row, column) exactly as in the
 // direct epilogue.
-template <class Tr>
+template <class Tr, int OUT = 0>
 __global__ void __launch_bounds__(256) k_split_reduce(MfmaArgs a) {
     using D = typename Tr::D;
     using T = typename Tr::T;
@@ -1076,7 +1182,12 @@ __global__ void __launch_bounds__(256) k_split_reduce(MfmaArgs a) {
     for (int z = 0; z < 4; ++z) {
         const int q = qq + z;
         const int row = tm * BM + Geo<Tr>::row0(wv) + 32 * mb + 8 * (q >> 2) + 4 * lh + (q & 3);
-        if (row < M) D::st(ob, (int64_t)row * L_out, tot[z] + (bias ? D::ld(bias, row) : 0.0f));
+        if (row >= M) continue;
+        const float val = tot[z] + (bias ? D::ld(bias, row) : 0.0f);
+        if constexpr (OUT == 0)
+            D::st(ob, (int64_t)row * L_out, val);
+        else
+            store_head<Tr, OUT>(p, b, l, row, val);
     }
 }
 

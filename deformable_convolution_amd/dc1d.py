@@ -76,6 +76,10 @@ def load_library():
                 ctypes.POINTER(ctypes.c_size_t)]
             lib.dc1d_backward.restype = ctypes.c_int
             lib.dc1d_backward.argtypes = [T] * 10 + [i64] * 5 + [p, ctypes.c_size_t, p]
+            lib.dc1d_packed_workspace_bytes.restype = ctypes.c_int
+            lib.dc1d_packed_workspace_bytes.argtypes = [T] * 5 + [i64] * 4 + [ctypes.POINTER(ctypes.c_size_t)]
+            lib.dc1d_packed_forward.restype = ctypes.c_int
+            lib.dc1d_packed_forward.argtypes = [T] * 12 + [i64] * 4 + [p, ctypes.c_size_t, p]
             lib.dc1d_status_string.restype = ctypes.c_char_p
             lib.dc1d_status_string.argtypes = [ctypes.c_int]
             _lib = lib
@@ -256,6 +260,54 @@ def backward(x, offsets, weight, grad_out, mask=None, stride=1, padding=0, dilat
                                  _ref(gd.get("weight")), _ref(gd.get("bias")), stride, padding, dilation,
                                  groups, G, ws_ptr, ws_len, stream), "dc1d_backward")
     return grads
+
+
+def packed_forward(x, trunk_weight, trunk_bias, off_weight, off_bias, weight, bias=None, mask_weight=None,
+                   mask_bias=None, stride=1, padding=0, dilation=1, groups=1, with_offsets=False, out=None,
+                   workspace=None):
+    """The packed layer on the GPU (fp32): offsets (and, with mask_weight, the
+    mask) generated from x by the depthwise trunk and pointwise heads, then
+    the deformable forward.  trunk_weight [C_in, 1, K], off_weight and
+    mask_weight [G*K, C_in, 1].  Returns out (allocated unless given), or
+    with with_offsets (out, offsets) / (out, (offsets, mask)).  Enqueued on
+    torch's current stream."""
+    lib = load_library()
+    names = ("x", "trunk_weight", "trunk_bias", "off_weight", "off_bias", "weight", "bias", "mask_weight",
+             "mask_bias")
+    x, tw, tb, ow, ob, w, b, mw, mb = (_contig(t, n) for t, n in zip(
+        (x, trunk_weight, trunk_bias, off_weight, off_bias, weight, bias, mask_weight, mask_bias), names))
+    if x.dim() != 3 or w.dim() != 3 or ow.dim() != 3 or tw.dim() != 3 or tw.shape[2] < 1:
+        raise Dc1dValueError(ERR_BAD_SHAPE, "dc1d_packed_forward")
+    K = tw.shape[2]
+    padding = resolve_padding(padding, K, stride, dilation)
+    L_out = output_length(x.shape[-1], K, stride, padding, dilation)
+    if L_out < 1 or ow.shape[0] % K:
+        raise Dc1dValueError(ERR_BAD_SHAPE, "dc1d_packed_forward")
+    G = ow.shape[0] // K
+    if out is None:
+        out = torch.empty((x.shape[0], w.shape[0], L_out), dtype=x.dtype, device=x.device)
+    offs = msk = None
+    if with_offsets:
+        offs = torch.empty((x.shape[0], G, L_out, K), dtype=x.dtype, device=x.device)
+        if mw is not None:
+            msk = torch.empty_like(offs)
+    d = [_desc(t) for t in (x, tw, tb, ow, ob, mw, mb, w, b, out, offs, msk)]
+    if workspace is None:
+        n = ctypes.c_size_t(0)
+        with torch.cuda.device(x.device):
+            _check(lib.dc1d_packed_workspace_bytes(_ref(d[0]), _ref(d[1]), _ref(d[3]), _ref(d[5]), _ref(d[7]),
+                                                   stride, padding, dilation, groups, ctypes.byref(n)),
+                   "dc1d_packed_workspace_bytes")
+            workspace = _workspace(int(n.value), x.device)
+    ws_ptr = None if workspace is None else workspace.data_ptr()
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        _check(lib.dc1d_packed_forward(*[_ref(t) for t in d], stride, padding, dilation, groups, ws_ptr, ws_len,
+                                       stream), "dc1d_packed_forward")
+    if not with_offsets:
+        return out
+    return (out, (offs, msk)) if mw is not None else (out, offs)
 
 
 def debug_positions(offsets, L_in, stride=1, padding=0, dilation=1):

@@ -118,3 +118,65 @@ def custom(name="custom", *, B, C_in, C_out, L_in, K, stride=1, padding=0, dilat
         w_var = 1.0 / max(1, (C_in // groups) * K)
     return Workload(name, B, C_in, C_out, L_in, K, stride, padding, dilation, groups, G, L_out, dtype,
                     x_dist, off_dist, mask_dist, w_var, bias)
+
+
+@dataclasses.dataclass(frozen=True)
+class PackedWorkload:
+    """The packed layer (offsets, and optionally the mask, generated from x by
+    a depthwise trunk and pointwise heads); fp32 storage."""
+    name: str
+    B: int
+    C_in: int
+    C_out: int
+    L_in: int
+    K: int
+    stride: int
+    padding: int
+    dilation: int
+    groups: int
+    G: int
+    L_out: int
+    modulated: bool
+    off_var: float = 4.0  # offset head weight variance times C_in: offsets of a few positions
+
+    def with_batch(self, B: int) -> "PackedWorkload":
+        return dataclasses.replace(self, B=B, name="%s[B=%d]" % (self.name, B))
+
+
+# The dc1d page's PackedDeformConv1d usage example (C 64, K 3, dilation 4,
+# groups 64, offset groups 64, "same"; input [4, 64, 256]), its modulated
+# variant, and the same layer on a longer, larger batch for measurement.
+PACKED_WORKLOADS = {
+    "packed_page": PackedWorkload("packed_page", 4, 64, 64, 256, 3, 1, 4, 4, 64, 64, 256, False),
+    "packed_page_modulated": PackedWorkload("packed_page_modulated", 4, 64, 64, 256, 3, 1, 4, 4, 64, 64, 256, True),
+    "packed": PackedWorkload("packed", 32, 64, 64, 8192, 3, 1, 4, 4, 64, 64, 8192, True),
+}
+
+
+def make_packed_inputs(w: PackedWorkload, seed: int = 0) -> dict:
+    """CPU float32 tensors for the packed layer, drawn in the order x,
+    trunk_weight, trunk_bias, off_weight, off_bias, mask_weight, mask_bias
+    (both None unless modulated), weight, bias:
+    x ~ N(0, 1); trunk_weight ~ N(0, 1/K); off_weight ~ N(0, off_var/C_in);
+    mask_weight ~ N(0, 1/C_in); weight ~ N(0, 1/((C_in/groups)*K)); every
+    bias ~ N(0, 0.1)."""
+    gen = torch.Generator().manual_seed(seed)
+    n = lambda shape, var: torch.randn(shape, generator=gen, dtype=torch.float32) * math.sqrt(var)
+    GK = w.G * w.K
+    t = {"x": n((w.B, w.C_in, w.L_in), 1.0),
+         "trunk_weight": n((w.C_in, 1, w.K), 1.0 / w.K),
+         "trunk_bias": n((w.C_in,), 0.1),
+         "off_weight": n((GK, w.C_in, 1), w.off_var / w.C_in),
+         "off_bias": n((GK,), 0.1)}
+    t["mask_weight"] = n((GK, w.C_in, 1), 1.0 / w.C_in) if w.modulated else None
+    t["mask_bias"] = n((GK,), 0.1) if w.modulated else None
+    t["weight"] = n((w.C_out, w.C_in // w.groups, w.K), 1.0 / ((w.C_in // w.groups) * w.K))
+    t["bias"] = n((w.C_out,), 0.1)
+    return t
+
+
+def packed_custom(name="packed_custom", *, B, C_in, C_out, L_in, K, stride=1, padding=0, dilation=1, groups=1,
+                  G=1, L_out, modulated=False, off_var=4.0) -> PackedWorkload:
+    """A packed-layer workload of arbitrary shape (L_out supplied by the caller)."""
+    return PackedWorkload(name, B, C_in, C_out, L_in, K, stride, padding, dilation, groups, G, L_out, modulated,
+                          off_var)

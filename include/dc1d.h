@@ -196,6 +196,52 @@ int dc1d_backward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_t
                   size_t workspace_bytes, void *stream);
 
 /*
+ * The packed layer (fp32 storage only; DC1D_ERR_BAD_DTYPE otherwise): the
+ * layer computes its own offsets, and optionally its mask, from its input,
+ * then runs the forward above with them (dc1d page, section
+ * PackedDeformConv1d: offsets from a depthwise-separable convolutional
+ * block; section Modulation (DCNv2): a second pointwise branch off the same
+ * depthwise trunk, ending in a sigmoid, predicts the mask).  The block's
+ * layers are only sketched there; this library reads them as:
+ *
+ *   t[b,c,l]          = trunk_bias[c] + sum_k trunk_weight[c,0,k] * x~[b,c, l*stride - padding + k*dilation]
+ *   offsets[b,g,l,k]  = off_bias[g*K+k] + sum_c off_weight[g*K+k, c, 0] * t[b,c,l]
+ *   mask[b,g,l,k]     = sigmoid(mask_bias[g*K+k] + sum_c mask_weight[g*K+k, c, 0] * t[b,c,l])
+ *   out               = dc1d_forward(x, offsets, mask or none, weight, bias)
+ *
+ * i.e. a depthwise conv1d with the layer's K, stride, padding and dilation
+ * (so it yields L_out columns), no activation, then pointwise convs whose
+ * output channel g*K + k is tap k of offset group g; sigmoid(z) =
+ * 1 / (1 + exp(-z)).  Shapes: x [B, C_in, L_in]; trunk_weight [C_in, 1, K];
+ * trunk_bias [C_in]; off_weight and mask_weight [G*K, C_in, 1] (G = offset
+ * groups, dividing C_in, implied by the shape); off_bias and mask_bias
+ * [G*K]; weight, bias, out as in dc1d_forward; offsets_out and mask_out
+ * [B, G, L_out, K].  Biases may be NULL (zero); mask_weight NULL means no
+ * mask (then mask_bias and mask_out must be NULL too).  offsets_out /
+ * mask_out, when given, receive the generated offsets / mask (the layer's
+ * with_offsets output); otherwise they live in the workspace.  Outputs
+ * must not overlap the inputs, each other or the workspace.
+ * B * L_out must be below 2^31.
+ *
+ * workspace: at least dc1d_packed_workspace_bytes() bytes, 256-byte
+ * aligned, when that is not 0 (the trunk [B, C_in, L_out], the offsets and
+ * mask, and the forward's own workspace); no initialisation; nothing kept.
+ */
+int dc1d_packed_workspace_bytes(const dc1d_tensor *x, const dc1d_tensor *trunk_weight,
+                                const dc1d_tensor *off_weight, const dc1d_tensor *mask_weight_or_null,
+                                const dc1d_tensor *weight, int64_t stride, int64_t padding,
+                                int64_t dilation, int64_t groups, size_t *bytes_out);
+
+int dc1d_packed_forward(const dc1d_tensor *x, const dc1d_tensor *trunk_weight,
+                        const dc1d_tensor *trunk_bias_or_null, const dc1d_tensor *off_weight,
+                        const dc1d_tensor *off_bias_or_null, const dc1d_tensor *mask_weight_or_null,
+                        const dc1d_tensor *mask_bias_or_null, const dc1d_tensor *weight,
+                        const dc1d_tensor *bias_or_null, const dc1d_tensor *out,
+                        const dc1d_tensor *offsets_out_or_null, const dc1d_tensor *mask_out_or_null,
+                        int64_t stride, int64_t padding, int64_t dilation, int64_t groups,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Test aid: the sampling positions the forward kernels use, from the same
  * device function.  For every (b, g, l, k) of offsets [B, G, L_out, K]
  * (K = offsets->shape[3]; L_out must equal dc1d_output_length(L_in, K, ...)):
