@@ -101,7 +101,7 @@ def read_traffic(name, kernel, khash):
         return None
 
 
-def run_gpu(w, steps, warmup, check=True, cold_reps=0):
+def run_gpu(w, steps, warmup, check=True, cold_reps=0, constrained=False):
     import torch
     from deformable_convolution_amd import dc1d, inputs
 
@@ -115,7 +115,8 @@ def run_gpu(w, steps, warmup, check=True, cold_reps=0):
     ws = torch.zeros(max(nws, 1), dtype=torch.uint8, device=dev) if nws else None
 
     def step():
-        dc1d.forward(g["x"], g["offsets"], g["weight"], g["bias"], g["mask"], out=out, workspace=ws, **kw)
+        dc1d.forward(g["x"], g["offsets"], g["weight"], g["bias"], g["mask"], out=out, workspace=ws,
+                     constrained=constrained, **kw)
 
     step()
     torch.cuda.synchronize()
@@ -125,7 +126,8 @@ def run_gpu(w, steps, warmup, check=True, cold_reps=0):
         rng = np.random.default_rng(1)
         n = 512
         pts = np.stack([rng.integers(0, w.B, n), rng.integers(0, w.C_out, n), rng.integers(0, w.L_out, n)], 1)
-        ref = oracle.forward_points(t["x"], t["offsets"], t["weight"], pts, t["bias"], t["mask"], **kw)
+        ref = oracle.forward_points(t["x"], t["offsets"], t["weight"], pts, t["bias"], t["mask"],
+                                    constrained=constrained, **kw)
         got = out[pts[:, 0], pts[:, 1], pts[:, 2]].double().cpu().numpy()
         if w.dtype == "f32":
             err = float(np.abs(got - ref).max())
@@ -411,7 +413,7 @@ def cpu_model():
     return "unknown"
 
 
-def cpu_baseline(w, budget_s=12.0, max_reps=200):
+def cpu_baseline(w, budget_s=12.0, max_reps=200, constrained=False):
     """The oracle, untouched, on this host's cores: full forwards of the same
     workload repeated until about budget_s seconds have passed."""
     import oracle
@@ -422,10 +424,11 @@ def cpu_baseline(w, budget_s=12.0, max_reps=200):
     os.environ.setdefault("OMP_NUM_THREADS", str(cores))
     kw = dict(stride=w.stride, padding=w.padding, dilation=w.dilation, groups=w.groups)
     contraction, sampling, _ = work(w)
-    oracle.forward(t["x"], t["offsets"], t["weight"], t["bias"], t["mask"], **kw)  # warm (untimed)
+    oracle.forward(t["x"], t["offsets"], t["weight"], t["bias"], t["mask"], constrained=constrained,
+                   **kw)  # warm (untimed)
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.forward(t["x"], t["offsets"], t["weight"], t["bias"], t["mask"], **kw)
+        oracle.forward(t["x"], t["offsets"], t["weight"], t["bias"], t["mask"], constrained=constrained, **kw)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= max_reps:
@@ -447,6 +450,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--backward", action="store_true", help="time the backward (fp32 workloads) instead")
+    ap.add_argument("--constrained", action="store_true",
+                    help="the forward in constrained mode (every tap kept inside its kernel window)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB")
     ap.add_argument("--summarize-profile", default=None, metavar="DIR")
     ap.add_argument("--kernel", default=None, help="the plan's kernel name, for --summarize-profile")
@@ -485,6 +490,8 @@ def main():
         return
     w = inputs.WORKLOADS[args.workload]
     if args.backward:
+        if args.constrained:
+            raise SystemExit("--constrained times the forward")
         if w.dtype != "f32":
             raise SystemExit("the backward runs on fp32 workloads")
         if args.profile_run:
@@ -494,12 +501,12 @@ def main():
         main_backward(args, w)
         return
     if args.profile_run:
-        r = run_gpu(w, args.steps, args.warmup, check=False)
+        r = run_gpu(w, args.steps, args.warmup, check=False, constrained=args.constrained)
         print("profile run: %s %s, %d timed launches, %.4f ms/launch" % (
             w.name, r["plan"]["kernel"], args.steps, float(np.mean(r["launch_ms"]))), flush=True)
         return
 
-    r = run_gpu(w, args.steps, args.warmup, cold_reps=20)
+    r = run_gpu(w, args.steps, args.warmup, cold_reps=20, constrained=args.constrained)
     contraction, sampling, nbytes = work(w)
     ms = r["region_ms"] / args.steps
     kern_ms = float(np.mean(r["launch_ms"]))
@@ -513,7 +520,7 @@ def main():
         achieved = nbytes / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm_GBps"], "unit": "GB/s",
                 "frac": round(achieved / PEAK["hbm_GBps"], 4)}
-    traffic = read_traffic(w.name, kern, kernel_hash())
+    traffic = read_traffic(w.name, kern + ("_constrained" if args.constrained else ""), kernel_hash())
     roof["traffic"] = traffic
     roof["kernel"] = kern
     roof["kernel_ms"] = round(kern_ms, 5)
@@ -530,7 +537,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32" if w.dtype == "f32" else "bf16",
         "data": "synthetic, seeded (deformable_convolution_amd/inputs.py; no dataset)",
-        "config": {"workload": workload_label(w), "plan": r["plan"],
+        "config": {"workload": workload_label(w) + (" constrained" if args.constrained else ""), "plan": r["plan"],
                    "gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "parity": r["parity"],
                    "forward_ms": {"warm": pct(r["launch_ms"]), "cold": pct(r["cold_ms"])}},
         "roofline": roof,
@@ -550,7 +557,7 @@ def main():
             rec["hbm_frac"] = round(b2 / (m2 * 1e-3) / 1e9 / PEAK["hbm_GBps"], 4)
             print(json.dumps(rec), file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w)
+        line["cpu_baseline"] = cpu_baseline(w, constrained=args.constrained)
     print(json.dumps(line), flush=True)
 
 
@@ -660,9 +667,10 @@ def write_profile_md(d, workload, kernel):
     out.append("Commands (rocprofv3, ROCm 7.2, one MI355X):")
     out.append("")
     out.append("```")
-    bwd = kernel == "backward"
-    out.append(PROFILE_COMMANDS.format(wl=workload, kernel=kernel, flag=" --backward" if bwd else "",
-                                       suffix="_backward" if bwd else "").rstrip())
+    bwd, con = kernel == "backward", kernel.endswith("_constrained")
+    out.append(PROFILE_COMMANDS.format(wl=workload, kernel=kernel,
+                                       flag=" --backward" if bwd else (" --constrained" if con else ""),
+                                       suffix="_backward" if bwd else ("_constrained" if con else "")).rstrip())
     out.append("```")
     out.append("")
     out.append("## Kernel trace (--kernel-trace --stats)")

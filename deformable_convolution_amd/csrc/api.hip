@@ -214,15 +214,24 @@ int dc1d_plan(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_tenso
     return DC1D_OK;
 }
 
-int dc1d_forward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_tensor *mask_or_null,
+}  // extern "C"
+
+namespace {
+
+// The constrained mode's tap bounds -k*d and (K-1-k)*d must be exact floats.
+bool constrained_ok(const Params &p) { return (int64_t)(p.K - 1) * p.dilation < ((int64_t)1 << 24); }
+
+int forward_impl(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_tensor *mask_or_null,
                  const dc1d_tensor *weight, const dc1d_tensor *bias_or_null, const dc1d_tensor *out,
                  int64_t stride, int64_t padding, int64_t dilation, int64_t groups, int64_t offset_groups,
-                 void *workspace, size_t workspace_bytes, void *stream) {
+                 void *workspace, size_t workspace_bytes, void *stream, int constrained) {
     if (!out) return DC1D_ERR_NULL_PTR;
     Params p;
     int st = validate(x, offsets, mask_or_null, weight, bias_or_null, out, stride, padding, dilation, groups,
                       offset_groups, &p);
     if (st) return st;
+    if (constrained && !constrained_ok(p)) return DC1D_ERR_BAD_ARG;
+    p.constrained = constrained;
     // data pointers: required for every tensor with elements
     const dc1d_tensor *all[6] = {x, offsets, mask_or_null, weight, bias_or_null, out};
     for (const dc1d_tensor *t : all)
@@ -255,6 +264,26 @@ int dc1d_forward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_te
     default: e = launch_direct(p, s); break;
     }
     return e == hipSuccess ? DC1D_OK : DC1D_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dc1d_forward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_tensor *mask_or_null,
+                 const dc1d_tensor *weight, const dc1d_tensor *bias_or_null, const dc1d_tensor *out,
+                 int64_t stride, int64_t padding, int64_t dilation, int64_t groups, int64_t offset_groups,
+                 void *workspace, size_t workspace_bytes, void *stream) {
+    return forward_impl(x, offsets, mask_or_null, weight, bias_or_null, out, stride, padding, dilation, groups,
+                        offset_groups, workspace, workspace_bytes, stream, 0);
+}
+
+int dc1d_forward_constrained(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_tensor *mask_or_null,
+                             const dc1d_tensor *weight, const dc1d_tensor *bias_or_null, const dc1d_tensor *out,
+                             int64_t stride, int64_t padding, int64_t dilation, int64_t groups,
+                             int64_t offset_groups, void *workspace, size_t workspace_bytes, void *stream) {
+    return forward_impl(x, offsets, mask_or_null, weight, bias_or_null, out, stride, padding, dilation, groups,
+                        offset_groups, workspace, workspace_bytes, stream, 1);
 }
 
 }  // extern "C"
@@ -307,17 +336,23 @@ int dc1d_backward_workspace_bytes(const dc1d_tensor *x, const dc1d_tensor *offse
     return DC1D_OK;
 }
 
-int dc1d_backward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_tensor *mask_or_null,
+}  // extern "C"
+
+namespace {
+
+int backward_impl(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_tensor *mask_or_null,
                   const dc1d_tensor *weight, const dc1d_tensor *grad_out, const dc1d_tensor *grad_x_or_null,
                   const dc1d_tensor *grad_offsets_or_null, const dc1d_tensor *grad_mask_or_null,
                   const dc1d_tensor *grad_weight_or_null, const dc1d_tensor *grad_bias_or_null, int64_t stride,
                   int64_t padding, int64_t dilation, int64_t groups, int64_t offset_groups, void *workspace,
-                  size_t workspace_bytes, void *stream) {
+                  size_t workspace_bytes, void *stream, int constrained) {
     Params p;
     int st = validate_backward(x, offsets, mask_or_null, weight, grad_out, grad_x_or_null, grad_offsets_or_null,
                                grad_mask_or_null, grad_weight_or_null, grad_bias_or_null, stride, padding,
                                dilation, groups, offset_groups, &p);
     if (st) return st;
+    if (constrained && !constrained_ok(p)) return DC1D_ERR_BAD_ARG;
+    p.constrained = constrained;
     const dc1d_tensor *ins[5] = {x, offsets, mask_or_null, weight, grad_out};
     const dc1d_tensor *outs[5] = {grad_x_or_null, grad_offsets_or_null, grad_mask_or_null, grad_weight_or_null,
                                   grad_bias_or_null};
@@ -359,6 +394,33 @@ int dc1d_backward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_t
     a.S = nullptr;
     const hipError_t e = launch_backward(a, dev.num_cus, (hipStream_t)stream);
     return e == hipSuccess ? DC1D_OK : DC1D_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dc1d_backward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_tensor *mask_or_null,
+                  const dc1d_tensor *weight, const dc1d_tensor *grad_out, const dc1d_tensor *grad_x_or_null,
+                  const dc1d_tensor *grad_offsets_or_null, const dc1d_tensor *grad_mask_or_null,
+                  const dc1d_tensor *grad_weight_or_null, const dc1d_tensor *grad_bias_or_null, int64_t stride,
+                  int64_t padding, int64_t dilation, int64_t groups, int64_t offset_groups, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+    return backward_impl(x, offsets, mask_or_null, weight, grad_out, grad_x_or_null, grad_offsets_or_null,
+                         grad_mask_or_null, grad_weight_or_null, grad_bias_or_null, stride, padding, dilation, groups,
+                         offset_groups, workspace, workspace_bytes, stream, 0);
+}
+
+int dc1d_backward_constrained(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_tensor *mask_or_null,
+                              const dc1d_tensor *weight, const dc1d_tensor *grad_out,
+                              const dc1d_tensor *grad_x_or_null, const dc1d_tensor *grad_offsets_or_null,
+                              const dc1d_tensor *grad_mask_or_null, const dc1d_tensor *grad_weight_or_null,
+                              const dc1d_tensor *grad_bias_or_null, int64_t stride, int64_t padding,
+                              int64_t dilation, int64_t groups, int64_t offset_groups, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+    return backward_impl(x, offsets, mask_or_null, weight, grad_out, grad_x_or_null, grad_offsets_or_null,
+                         grad_mask_or_null, grad_weight_or_null, grad_bias_or_null, stride, padding, dilation, groups,
+                         offset_groups, workspace, workspace_bytes, stream, 1);
 }
 
 }  // extern "C"

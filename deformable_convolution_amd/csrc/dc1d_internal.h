@@ -27,6 +27,7 @@ struct Params {
     int opg;   // output channels per conv group (C_out / groups)
     int cpo;   // input channels per offset group (C_in / G)
     int Kred;  // reduction length of one output: cpg * K
+    int constrained;  // taps kept inside the undeformed kernel window (tap_range)
     void *ws;
     size_t ws_bytes;
 };
@@ -88,6 +89,31 @@ __device__ __forceinline__ void split_position(float o, int base, int &i0, float
     const float fl = floorf(o);
     i0 = base + (int)fl;
     f = o - fl;
+}
+
+// The offsets tap k may use.  Constrained mode (the dc1d page's default,
+// section Usage / DeformConv1d: each tap stays inside its receptive field;
+// read as the undeformed kernel's window [l*s - p, l*s - p + (K-1)*d] of its
+// output) clamps the offset to [-k*d, (K-1-k)*d]; otherwise only the global
+// clamp applies.  The bounds are exact floats ((K-1)*d < 2^24 is checked).
+struct TapRange {
+    float lo, hi;
+};
+__device__ __forceinline__ TapRange tap_range(const Params &p, int k) {
+    if (p.constrained) return {-(float)(k * p.dilation), (float)((p.K - 1 - k) * p.dilation)};
+    return {-kOffsetClamp, kOffsetClamp};
+}
+__device__ __forceinline__ void split_position(float o, int base, TapRange r, int &i0, float &f) {
+    o = fminf(fmaxf(o, r.lo), r.hi);  // a NaN becomes r.lo
+    const float fl = floorf(o);
+    i0 = base + (int)fl;
+    f = o - fl;
+}
+// Whether moving the offset up moves the sample (the right derivative of the
+// clamp: 1 on [lo, hi), 0 at and beyond hi and below lo); always in
+// unconstrained mode.
+__device__ __forceinline__ bool tap_moves(const Params &p, float o, TapRange r) {
+    return !p.constrained || (o >= r.lo && o < r.hi);
 }
 
 // ---- launchers ------------------------------------------------------------

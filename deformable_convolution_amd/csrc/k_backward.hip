@@ -67,7 +67,7 @@ __global__ void __launch_bounds__(256) k_bwd_samples(BwdParams a) {
         const int64_t oi = (((int64_t)b * p.G + g) * p.L_out + l) * p.K + k;
         int i0;
         float f;
-        split_position(off[oi], l * p.stride - p.padding + k * p.dilation, i0, f);
+        split_position(off[oi], l * p.stride - p.padding + k * p.dilation, tap_range(p, k), i0, f);
         const float m = mask ? mask[oi] : 1.0f;
         const float *xrow = x + ((int64_t)b * p.C_in + ci) * p.L_in;
         const bool v0 = i0 >= 0 && i0 < p.L_in, v1 = i0 + 1 >= 0 && i0 + 1 < p.L_in;
@@ -141,7 +141,7 @@ __global__ void __launch_bounds__(256) k_bwd_samples_t(BwdParams a) {
         const int64_t oi = (((int64_t)b * p.G + g) * p.L_out + l) * p.K + k;
         int i0;
         float f;
-        split_position(off[oi], l * p.stride - p.padding + k * p.dilation, i0, f);
+        split_position(off[oi], l * p.stride - p.padding + k * p.dilation, tap_range(p, k), i0, f);
         const float m = mask ? mask[oi] : 1.0f;
         const float *xrow = x + ((int64_t)b * p.C_in + ci) * p.L_in;
         const bool v0 = i0 >= 0 && i0 < p.L_in, v1 = i0 + 1 >= 0 && i0 + 1 < p.L_in;
@@ -204,7 +204,7 @@ __global__ void __launch_bounds__(256) k_bwd_dx(BwdParams a, DxPlan pl) {
         const int64_t oi = (((int64_t)b * p.G + g) * L_out + l) * K + k;
         int i0;
         float f;
-        split_position(off[oi], l * p.stride - p.padding + k * p.dilation, i0, f);
+        split_position(off[oi], l * p.stride - p.padding + k * p.dilation, tap_range(p, k), i0, f);
         const float m = mask ? mask[oi] : 1.0f;
         const int j = i0 - lo;
         const bool inwin = W > 1 && (unsigned)j < (unsigned)(W - 1);
@@ -246,6 +246,7 @@ __global__ void __launch_bounds__(256) k_bwd_dx(BwdParams a, DxPlan pl) {
             }
             }
         }
+        if (!tap_moves(p, off[oi], tap_range(p, k))) ao = 0.0f;  // a clamped tap: its offset has no effect
         if (pl.atomic_om) {
             if (a.goff) unsafeAtomicAdd(a.goff + oi, ao);
             if (a.gmask) unsafeAtomicAdd(a.gmask + oi, am);
@@ -385,7 +386,8 @@ __global__ void __launch_bounds__(256) k_bwd_dw(BwdParams a, int WIN, int tiles_
             if (o >= nvalid) continue;
             int i0;
             float f;
-            split_position(ov[q], base0 + k * p.dilation, i0, f);
+            const TapRange r = tap_range(p, k);
+            split_position(ov[q], base0 + k * p.dilation, r, i0, f);
             const float m = mv[q];
             const int j = i0 - lo;
             const bool inwin = WIN > 1 && (unsigned)j < (unsigned)(WIN - 1);
@@ -401,7 +403,7 @@ __global__ void __launch_bounds__(256) k_bwd_dw(BwdParams a, int WIN, int tiles_
             const float ds = wk[k] * d;
             const float lerp = fmaf(f, x1 - x0, x0);
             wacc[k] = fmaf(d, lerp * m, wacc[k]);
-            go[q] = ds * m * (x1 - x0);
+            go[q] = tap_moves(p, ov[q], r) ? ds * m * (x1 - x0) : 0.0f;
             gm[q] = ds * lerp;
             if (gxr) {
                 const float dm = ds * m;

@@ -80,7 +80,8 @@ __global__ void __launch_bounds__(256) k_direct(Params p) {
             for (int k = 0; k < p.K; ++k) {
                 int i0;
                 float f;
-                split_position(D::ld(off, ob + k), l * p.stride - p.padding + k * p.dilation, i0, f);
+                split_position(D::ld(off, ob + k), l * p.stride - p.padding + k * p.dilation, tap_range(p, k), i0,
+                               f);
                 const float x0 = (i0 >= 0 && i0 < p.L_in) ? D::ld(xrow, i0) : 0.0f;
                 const float x1 = (i0 + 1 >= 0 && i0 + 1 < p.L_in) ? D::ld(xrow, i0 + 1) : 0.0f;
                 float v = fmaf(f, x1 - x0, x0);
@@ -235,7 +236,7 @@ __global__ void __launch_bounds__(kDwThreads) k_depthwise(Params p, int WIN, int
             }
             int i0;
             float f;
-            split_position(ofs, base0 + k * p.dilation, i0, f);
+            split_position(ofs, base0 + k * p.dilation, tap_range(p, k), i0, f);
             const int j = i0 - lo;
             float x0, x1;
             if (WIN > 1 && (unsigned)j < (unsigned)(WIN - 1)) {

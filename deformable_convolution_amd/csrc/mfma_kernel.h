@@ -723,7 +723,7 @@ __device__ __forceinline__ void setup_tile(const MfmaArgs &a, Tile &tl, Pos *s_t
                 Pos ps = {0, 0.0f};
                 if (cok) {
                     int i0;
-                    split_position(ov[q], grid0 + k * p.dilation, i0, ps.f);
+                    split_position(ov[q], grid0 + k * p.dilation, tap_range(p, k), i0, ps.f);
                     ps.j = min(max(i0, -2), L_in);  // x~ reads zero at both neighbours beyond these bounds
                     lo = min(lo, ps.j);
                     hi = max(hi, ps.j);

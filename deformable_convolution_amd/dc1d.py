@@ -76,6 +76,10 @@ def load_library():
                 ctypes.POINTER(ctypes.c_size_t)]
             lib.dc1d_backward.restype = ctypes.c_int
             lib.dc1d_backward.argtypes = [T] * 10 + [i64] * 5 + [p, ctypes.c_size_t, p]
+            lib.dc1d_forward_constrained.restype = ctypes.c_int
+            lib.dc1d_forward_constrained.argtypes = lib.dc1d_forward.argtypes
+            lib.dc1d_backward_constrained.restype = ctypes.c_int
+            lib.dc1d_backward_constrained.argtypes = lib.dc1d_backward.argtypes
             lib.dc1d_packed_workspace_bytes.restype = ctypes.c_int
             lib.dc1d_packed_workspace_bytes.argtypes = [T] * 5 + [i64] * 4 + [ctypes.POINTER(ctypes.c_size_t)]
             lib.dc1d_packed_forward.restype = ctypes.c_int
@@ -190,10 +194,12 @@ def plan(x, offsets, weight, bias=None, mask=None, stride=1, padding=0, dilation
 
 
 def forward(x, offsets, weight, bias=None, mask=None, stride=1, padding=0, dilation=1, groups=1,
-            out=None, workspace=None):
+            out=None, workspace=None, constrained=False):
     """DeformConv1d forward on the GPU.  Tensors must be contiguous device
     tensors of one dtype (float32 or bfloat16); returns out [B, C_out, L_out]
-    (allocated unless given).  Enqueued on torch's current stream."""
+    (allocated unless given).  constrained=True keeps every tap inside the
+    undeformed kernel window of its output (dc1d_forward_constrained).
+    Enqueued on torch's current stream."""
     lib = load_library()
     x, offsets, weight, bias, mask = (_contig(t, n) for t, n in ((x, "x"), (offsets, "offsets"),
                                                                    (weight, "weight"), (bias, "bias"),
@@ -215,17 +221,19 @@ def forward(x, offsets, weight, bias=None, mask=None, stride=1, padding=0, dilat
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
     with torch.cuda.device(x.device):
         stream = torch.cuda.current_stream(x.device).cuda_stream
-        _check(lib.dc1d_forward(_ref(dx), _ref(do), _ref(dm), _ref(dw), _ref(db), _ref(dout), stride, padding,
-                                dilation, groups, G, ws_ptr, ws_len, stream), "dc1d_forward")
+        fn = lib.dc1d_forward_constrained if constrained else lib.dc1d_forward
+        _check(fn(_ref(dx), _ref(do), _ref(dm), _ref(dw), _ref(db), _ref(dout), stride, padding, dilation, groups,
+                  G, ws_ptr, ws_len, stream), "dc1d_forward")
     return out
 
 
 def backward(x, offsets, weight, grad_out, mask=None, stride=1, padding=0, dilation=1, groups=1,
-             need=("x", "offsets", "mask", "weight", "bias"), workspace=None):
+             need=("x", "offsets", "mask", "weight", "bias"), workspace=None, constrained=False):
     """Gradients of sum(grad_out * forward(...)) on the GPU (fp32 tensors).
     Returns a dict with the requested keys among x, offsets, mask (only with
     a mask), weight, bias; tensors are allocated here, the arithmetic runs in
-    the library's kernels on torch's current stream."""
+    the library's kernels on torch's current stream.  constrained=True: the
+    backward of the constrained forward."""
     lib = load_library()
     x, offsets, weight, grad_out, mask = (_contig(t, n) for t, n in ((x, "x"), (offsets, "offsets"),
                                                                       (weight, "weight"),
@@ -255,10 +263,10 @@ def backward(x, offsets, weight, grad_out, mask=None, stride=1, padding=0, dilat
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
     with torch.cuda.device(x.device):
         stream = torch.cuda.current_stream(x.device).cuda_stream
-        _check(lib.dc1d_backward(_ref(dx), _ref(do), _ref(dm), _ref(dw), _ref(dg),
-                                 _ref(gd.get("x")), _ref(gd.get("offsets")), _ref(gd.get("mask")),
-                                 _ref(gd.get("weight")), _ref(gd.get("bias")), stride, padding, dilation,
-                                 groups, G, ws_ptr, ws_len, stream), "dc1d_backward")
+        fn = lib.dc1d_backward_constrained if constrained else lib.dc1d_backward
+        _check(fn(_ref(dx), _ref(do), _ref(dm), _ref(dw), _ref(dg), _ref(gd.get("x")), _ref(gd.get("offsets")),
+                  _ref(gd.get("mask")), _ref(gd.get("weight")), _ref(gd.get("bias")), stride, padding, dilation,
+                  groups, G, ws_ptr, ws_len, stream), "dc1d_backward")
     return grads
 
 

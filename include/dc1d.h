@@ -153,6 +153,24 @@ int dc1d_forward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_te
                  int64_t offset_groups, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Constrained mode: dc1d_forward with every tap kept inside its receptive
+ * field (the dc1d page's default, section Usage / DeformConv1d: each kernel
+ * tap is constrained to its own receptive field unless the layer is made
+ * unconstrained).  The page does not give the rule; this library reads the
+ * receptive field as the undeformed kernel's window of the output,
+ * [l*stride - padding, l*stride - padding + (K-1)*dilation], so tap k's
+ * offset is clamped to [-k*dilation, (K-1-k)*dilation] before the position
+ * is split; positions in the window outside [0, L_in) still read zero.
+ * Same arguments, workspace and errors as dc1d_forward, plus
+ * DC1D_ERR_BAD_ARG when (K-1)*dilation >= 2^24.
+ */
+int dc1d_forward_constrained(const dc1d_tensor *x, const dc1d_tensor *offsets,
+                             const dc1d_tensor *mask_or_null, const dc1d_tensor *weight,
+                             const dc1d_tensor *bias_or_null, const dc1d_tensor *out, int64_t stride,
+                             int64_t padding, int64_t dilation, int64_t groups, int64_t offset_groups,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Backward (fp32 storage only; DC1D_ERR_BAD_DTYPE otherwise).  For
  * grad_out = dL/d(out) [B, C_out, L_out], writes the gradients of
  * L = sum(grad_out * out) with respect to the inputs of dc1d_forward, each
@@ -240,6 +258,21 @@ int dc1d_packed_forward(const dc1d_tensor *x, const dc1d_tensor *trunk_weight,
                         const dc1d_tensor *offsets_out_or_null, const dc1d_tensor *mask_out_or_null,
                         int64_t stride, int64_t padding, int64_t dilation, int64_t groups,
                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Backward of dc1d_forward_constrained: the gradients above at the clamped
+ * offsets, with grad_offsets multiplied by the clamp's right derivative
+ * (1 for an offset in [-k*dilation, (K-1-k)*dilation), 0 otherwise: a tap
+ * held at its window's edge does not move).  Same arguments, workspace and
+ * errors as dc1d_backward.
+ */
+int dc1d_backward_constrained(const dc1d_tensor *x, const dc1d_tensor *offsets,
+                              const dc1d_tensor *mask_or_null, const dc1d_tensor *weight,
+                              const dc1d_tensor *grad_out, const dc1d_tensor *grad_x_or_null,
+                              const dc1d_tensor *grad_offsets_or_null, const dc1d_tensor *grad_mask_or_null,
+                              const dc1d_tensor *grad_weight_or_null, const dc1d_tensor *grad_bias_or_null,
+                              int64_t stride, int64_t padding, int64_t dilation, int64_t groups,
+                              int64_t offset_groups, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Test aid: the sampling positions the forward kernels use, from the same

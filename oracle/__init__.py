@@ -12,6 +12,10 @@ Two independent formulations live here:
   contract) in plain C loops over doubles, and its term-by-term derivative.
 * ``packed_heads`` / ``packed_forward`` -- the packed layer's offset (and
   mask) generator in the same C file, then ``forward``.
+* ``constrain_offsets`` and the ``constrained=True`` option of ``forward``,
+  ``forward_points`` and ``backward`` -- the constrained mode: each offset
+  clamped to its tap's window, then the unconstrained definition (and, for
+  the offset gradient, the chain rule through the clamp).
 * ``hat.forward`` -- a NumPy brute force that never splits a position into
   integer and fractional parts; it is the pin for the C oracle's
   floor/fraction logic and its zero-fill boundary.
@@ -116,9 +120,26 @@ def _shapes(x, offsets, weight, groups):
     return B, C_in, L_in, C_out, K, G
 
 
-def forward(x, offsets, weight, bias=None, mask=None, stride=1, padding=0, dilation=1, groups=1, lib=None):
-    """Deformable conv1d forward in float64; returns out [B, C_out, L_out]."""
+def constrain_offsets(offsets, dilation):
+    """The constrained mode's offsets (dc1d page, section Usage /
+    DeformConv1d: by default each tap stays inside its receptive field; the
+    rule is not given there).  Reading: the receptive field of output l is
+    the undeformed kernel's window [l*s - p, l*s - p + (K-1)*d], so tap k's
+    position l*s - p + k*d + o must stay in it, i.e. o is clamped to
+    [-k*d, (K-1-k)*d].  offsets [B, G, L_out, K] (float64)."""
+    offsets = _f64(offsets)
+    K = offsets.shape[-1]
+    k = np.arange(K, dtype=np.float64)
+    return np.clip(offsets, -k * dilation, (K - 1 - k) * dilation)
+
+
+def forward(x, offsets, weight, bias=None, mask=None, stride=1, padding=0, dilation=1, groups=1, lib=None,
+            constrained=False):
+    """Deformable conv1d forward in float64; returns out [B, C_out, L_out].
+    constrained=True: the constrained mode (offsets clamped per tap first)."""
     x, offsets, weight, bias, mask = map(_f64, (x, offsets, weight, bias, mask))
+    if constrained:
+        offsets = constrain_offsets(offsets, dilation)
     B, C_in, L_in, C_out, K, G = _shapes(x, offsets, weight, groups)
     L_out = output_length(L_in, K, stride, padding, dilation, lib)
     if L_out < 1 or offsets.shape != (B, G, L_out, K):
@@ -137,9 +158,11 @@ def forward(x, offsets, weight, bias=None, mask=None, stride=1, padding=0, dilat
 
 
 def forward_points(x, offsets, weight, points, bias=None, mask=None, stride=1, padding=0,
-                   dilation=1, groups=1, lib=None):
+                   dilation=1, groups=1, lib=None, constrained=False):
     """Oracle outputs at the given (b, co, l) triples only (array [n, 3])."""
     x, offsets, weight, bias, mask = map(_f64, (x, offsets, weight, bias, mask))
+    if constrained:
+        offsets = constrain_offsets(offsets, dilation)
     B, C_in, L_in, C_out, K, G = _shapes(x, offsets, weight, groups)
     L_out = output_length(L_in, K, stride, padding, dilation, lib)
     if L_out < 1 or offsets.shape != (B, G, L_out, K):
@@ -170,10 +193,17 @@ def positions(offsets, L_in, K, stride=1, padding=0, dilation=1, lib=None):
     return i0, fr, va
 
 
-def backward(x, offsets, weight, dout, mask=None, stride=1, padding=0, dilation=1, groups=1, lib=None):
+def backward(x, offsets, weight, dout, mask=None, stride=1, padding=0, dilation=1, groups=1, lib=None,
+             constrained=False):
     """Gradients of sum(dout * forward(...)) in float64, as a dict with keys
-    x, offsets, mask (None without a mask), weight, bias."""
+    x, offsets, mask (None without a mask), weight, bias.  constrained=True:
+    the chain rule through the per-tap clamp -- every gradient taken at the
+    clamped offsets, the offset gradient times the clamp's right derivative
+    (1 on [-k*d, (K-1-k)*d), else 0)."""
     x, offsets, weight, dout, mask = map(_f64, (x, offsets, weight, dout, mask))
+    raw = offsets
+    if constrained:
+        offsets = constrain_offsets(offsets, dilation)
     B, C_in, L_in, C_out, K, G = _shapes(x, offsets, weight, groups)
     L_out = output_length(L_in, K, stride, padding, dilation, lib)
     if L_out < 1 or offsets.shape != (B, G, L_out, K):
@@ -192,6 +222,9 @@ def backward(x, offsets, weight, dout, mask=None, stride=1, padding=0, dilation=
                                  _ptr(gx), _ptr(goff), _ptr(gmask), _ptr(gw), _ptr(gb))
     if st:
         raise ValueError("oracle_backward: " + _ERR.get(st, str(st)))
+    if constrained:
+        k = np.arange(K, dtype=np.float64)
+        goff = goff * ((raw >= -k * dilation) & (raw < (K - 1 - k) * dilation))
     return {"x": gx, "offsets": goff, "mask": gmask, "weight": gw, "bias": gb}
 
 
