@@ -101,6 +101,49 @@ def read_traffic(name, kernel, khash):
         return None
 
 
+def timed(step, steps, warmup, dev, graph=False):
+    """Run `warmup` untimed steps, then time `steps` of them on the launch
+    stream: one HIP event on the stream before each step and one after the
+    last; step i lasts ev[i] -> ev[i+1] (its kernels run back to back on
+    that stream).  With graph=True the step is also captured once into a HIP
+    graph (torch.cuda.CUDAGraph) and the timed figures are its replays (on
+    this machine eager launches keep the GPU busy and time slightly faster,
+    so the bench uses eager launches); the eager times are always
+    returned."""
+    import torch
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        step()
+
+    def chain(run):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            ev[i].record(stream)
+            run()
+        ev[steps].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[steps]), [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+
+    eager_region, eager_ms = chain(step)
+    if not graph:
+        return {"region_ms": eager_region, "launch_ms": eager_ms, "eager_ms": eager_ms, "graph": False}
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step()
+    stream.wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    region, launch = chain(g.replay)
+    return {"region_ms": region, "launch_ms": launch, "eager_ms": eager_ms, "graph": True}
+
+
 def run_gpu(w, steps, warmup, check=True, cold_reps=0, constrained=False):
     import torch
     from deformable_convolution_amd import dc1d, inputs
@@ -145,18 +188,9 @@ def run_gpu(w, steps, warmup, check=True, cold_reps=0, constrained=False):
     # Timed region: one HIP event on the launch stream before each forward and
     # one after the last; forward i lasts ev[i] -> ev[i+1] (its kernels run
     # back to back on that stream), the region ev[0] -> ev[steps].
+    tm = timed(step, steps, warmup, dev)
+    launch_ms, region_ms = tm["launch_ms"], tm["region_ms"]
     stream = torch.cuda.current_stream(dev)
-    for _ in range(warmup):
-        step()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    torch.cuda.synchronize()
-    for i in range(steps):
-        ev[i].record(stream)
-        step()
-    ev[steps].record(stream)
-    torch.cuda.synchronize()
-    launch_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
-    region_ms = ev[0].elapsed_time(ev[steps])
     cold_ms = []
     if cold_reps:
         # cold: a 512 MiB write (twice the last-level cache) before each
@@ -171,7 +205,8 @@ def run_gpu(w, steps, warmup, check=True, cold_reps=0, constrained=False):
             torch.cuda.synchronize()
             cold_ms.append(a.elapsed_time(b))
         del flush
-    return {"plan": plan, "region_ms": region_ms, "launch_ms": launch_ms, "cold_ms": cold_ms, "parity": parity}
+    return {"plan": plan, "region_ms": region_ms, "launch_ms": launch_ms, "cold_ms": cold_ms, "parity": parity,
+            "eager_ms": tm["eager_ms"], "graph": tm["graph"]}
 
 
 def work_backward(w):
@@ -204,8 +239,11 @@ def run_backward(w, steps, warmup, check=True, baseline=True):
     gd = dout.to(dev)
     kw = dict(stride=w.stride, padding=w.padding, dilation=w.dilation, groups=w.groups)
 
+    nws = dc1d.backward_workspace_bytes(g["x"], g["offsets"], g["weight"], gd, g["mask"], **kw)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev) if nws else None
+
     def step():
-        return dc1d.backward(g["x"], g["offsets"], g["weight"], gd, g["mask"], **kw)
+        return dc1d.backward(g["x"], g["offsets"], g["weight"], gd, g["mask"], workspace=ws, **kw)
 
     got = step()
     torch.cuda.synchronize()
@@ -238,18 +276,9 @@ def run_backward(w, steps, warmup, check=True, baseline=True):
                   "ok": bool(worst <= 1.0)}
         if not parity["ok"]:
             raise SystemExit("backward parity check failed: %r" % parity)
-    stream = torch.cuda.current_stream(dev)
-    for _ in range(warmup):
-        step()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    torch.cuda.synchronize()
-    for i in range(steps):
-        ev[i].record(stream)
-        step()
-    ev[steps].record(stream)
-    torch.cuda.synchronize()
-    launch_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
-    return {"region_ms": ev[0].elapsed_time(ev[steps]), "launch_ms": launch_ms, "parity": parity, "cpu": cpu}
+    tm = timed(step, steps, warmup, dev)
+    return {"region_ms": tm["region_ms"], "launch_ms": tm["launch_ms"], "eager_ms": tm["eager_ms"],
+            "graph": tm["graph"], "parity": parity, "cpu": cpu}
 
 
 def main_backward(args, w):
@@ -274,7 +303,8 @@ def main_backward(args, w):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic, seeded (deformable_convolution_amd/inputs.py; no dataset)",
         "config": {"workload": workload_label(w), "pass": "backward", "gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                   "parity": r["parity"], "forward_ms": {"warm": pct(r["launch_ms"])}},
+                   "parity": r["parity"], "timing": "graph replay" if r["graph"] else "eager",
+                   "forward_ms": {"warm": pct(r["launch_ms"]), "eager": pct(r["eager_ms"])}},
         "roofline": roof,
     }
     if r["cpu"] is not None:
@@ -320,9 +350,11 @@ def run_packed(w, steps, warmup, check=True, baseline=True):
     args = (g["x"], g["trunk_weight"], g["trunk_bias"], g["off_weight"], g["off_bias"], g["weight"], g["bias"],
             g["mask_weight"], g["mask_bias"])
     out = torch.empty((w.B, w.C_out, w.L_out), dtype=torch.float32, device=dev)
+    nws = dc1d.packed_workspace_bytes(g["x"], g["trunk_weight"], g["off_weight"], g["weight"], g["mask_weight"], **kw)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev) if nws else None
 
     def step():
-        dc1d.packed_forward(*args, out=out, **kw)
+        dc1d.packed_forward(*args, out=out, workspace=ws, **kw)
 
     step()
     torch.cuda.synchronize()
@@ -356,18 +388,9 @@ def run_packed(w, steps, warmup, check=True, baseline=True):
         parity = {"elements": int(ref.size), "max_err": err, "tol": tol, "ok": bool(err <= tol)}
         if not parity["ok"]:
             raise SystemExit("packed parity check failed: %r" % parity)
-    stream = torch.cuda.current_stream(dev)
-    for _ in range(warmup):
-        step()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    torch.cuda.synchronize()
-    for i in range(steps):
-        ev[i].record(stream)
-        step()
-    ev[steps].record(stream)
-    torch.cuda.synchronize()
-    launch_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
-    return {"region_ms": ev[0].elapsed_time(ev[steps]), "launch_ms": launch_ms, "parity": parity, "cpu": cpu}
+    tm = timed(step, steps, warmup, dev)
+    return {"region_ms": tm["region_ms"], "launch_ms": tm["launch_ms"], "eager_ms": tm["eager_ms"],
+            "graph": tm["graph"], "parity": parity, "cpu": cpu}
 
 
 def main_packed(args, w):
@@ -386,7 +409,8 @@ def main_packed(args, w):
         "data": "synthetic, seeded (deformable_convolution_amd/inputs.py; no dataset)",
         "config": {"workload": packed_label(w), "pass": "packed forward",
                    "compulsory_gb_per_s": round(compulsory / (ms * 1e-3) / 1e9, 1),
-                   "parity": r["parity"], "forward_ms": {"warm": pct(r["launch_ms"])}},
+                   "parity": r["parity"], "timing": "graph replay" if r["graph"] else "eager",
+                   "forward_ms": {"warm": pct(r["launch_ms"]), "eager": pct(r["eager_ms"])}},
         "roofline": roof,
     }
     if r["cpu"] is not None:
@@ -539,7 +563,9 @@ def main():
         "data": "synthetic, seeded (deformable_convolution_amd/inputs.py; no dataset)",
         "config": {"workload": workload_label(w) + (" constrained" if args.constrained else ""), "plan": r["plan"],
                    "gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "parity": r["parity"],
-                   "forward_ms": {"warm": pct(r["launch_ms"]), "cold": pct(r["cold_ms"])}},
+                   "timing": "graph replay" if r["graph"] else "eager",
+                   "forward_ms": {"warm": pct(r["launch_ms"]), "cold": pct(r["cold_ms"]),
+                                  "eager": pct(r["eager_ms"])}},
         "roofline": roof,
     }
     if args.all:

@@ -10,12 +10,14 @@ never requires a GPU.
 from .dc1d import (  # noqa: F401
     Dc1dError,
     backward,
+    backward_workspace_bytes,
     debug_positions,
     forward,
     library_path,
     load_library,
     output_length,
     packed_forward,
+    packed_workspace_bytes,
     plan,
     resolve_padding,
     status_string,

@@ -153,6 +153,23 @@ def _args(x, offsets, weight, bias, mask, stride, padding, dilation, groups):
 
 
 _ws_cache = {}
+_ws_size_cache = {}
+
+
+class _nullctx:
+    def __enter__(self):
+        return None
+
+    def __exit__(self, *a):
+        return False
+
+
+def _device_ctx(device):
+    """torch.cuda.device(device), or nothing when it is already current (the
+    common case; entering the context costs more than the launch)."""
+    if device.index is None or device.index == torch.cuda.current_device():
+        return _nullctx()
+    return torch.cuda.device(device)
 
 
 def _workspace(nbytes: int, device):
@@ -212,14 +229,20 @@ def forward(x, offsets, weight, bias=None, mask=None, stride=1, padding=0, dilat
         out = torch.empty((x.shape[0], weight.shape[0], L_out), dtype=x.dtype, device=x.device)
     dx, do, dm, dw, db, dout = map(_desc, (x, offsets, mask, weight, bias, out))
     if workspace is None:
-        n = ctypes.c_size_t(0)
-        with torch.cuda.device(x.device):
-            _check(lib.dc1d_workspace_bytes(_ref(dx), _ref(do), _ref(dm), _ref(dw), _ref(db), stride, padding,
-                                            dilation, groups, G, ctypes.byref(n)), "dc1d_workspace_bytes")
-            workspace = _workspace(int(n.value), x.device)
+        # the size depends on shapes and arguments only (cached per call signature)
+        key = (x.device.index, x.dtype, tuple(x.shape), tuple(offsets.shape), mask is None, tuple(weight.shape),
+               bias is None, stride, padding, dilation, groups)
+        nbytes = _ws_size_cache.get(key)
+        with _device_ctx(x.device):
+            if nbytes is None:
+                n = ctypes.c_size_t(0)
+                _check(lib.dc1d_workspace_bytes(_ref(dx), _ref(do), _ref(dm), _ref(dw), _ref(db), stride, padding,
+                                                dilation, groups, G, ctypes.byref(n)), "dc1d_workspace_bytes")
+                nbytes = _ws_size_cache[key] = int(n.value)
+            workspace = _workspace(nbytes, x.device)
     ws_ptr = None if workspace is None else workspace.data_ptr()
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    with torch.cuda.device(x.device):
+    with _device_ctx(x.device):
         stream = torch.cuda.current_stream(x.device).cuda_stream
         fn = lib.dc1d_forward_constrained if constrained else lib.dc1d_forward
         _check(fn(_ref(dx), _ref(do), _ref(dm), _ref(dw), _ref(db), _ref(dout), stride, padding, dilation, groups,
@@ -316,6 +339,32 @@ def packed_forward(x, trunk_weight, trunk_bias, off_weight, off_bias, weight, bi
     if not with_offsets:
         return out
     return (out, (offs, msk)) if mw is not None else (out, offs)
+
+
+def backward_workspace_bytes(x, offsets, weight, grad_out, mask=None, stride=1, padding=0, dilation=1, groups=1,
+                             want_weight=True) -> int:
+    """Device workspace (bytes) a backward call with these arguments needs."""
+    padding, G = _args(x, offsets, weight, None, mask, stride, padding, dilation, groups)
+    n = ctypes.c_size_t(0)
+    dx, do, dm, dw, dg = map(_desc, (x, offsets, mask, weight, grad_out))
+    with _device_ctx(x.device):
+        _check(load_library().dc1d_backward_workspace_bytes(_ref(dx), _ref(do), _ref(dm), _ref(dw), _ref(dg),
+                                                            int(want_weight), stride, padding, dilation, groups, G,
+                                                            ctypes.byref(n)), "dc1d_backward_workspace_bytes")
+    return int(n.value)
+
+
+def packed_workspace_bytes(x, trunk_weight, off_weight, weight, mask_weight=None, stride=1, padding=0, dilation=1,
+                           groups=1) -> int:
+    """Device workspace (bytes) a packed-layer call with these arguments needs."""
+    K = trunk_weight.shape[-1]
+    padding = resolve_padding(padding, K, stride, dilation)
+    n = ctypes.c_size_t(0)
+    d = [_desc(t) for t in (x, trunk_weight, off_weight, mask_weight, weight)]
+    with _device_ctx(x.device):
+        _check(load_library().dc1d_packed_workspace_bytes(*[_ref(t) for t in d], stride, padding, dilation, groups,
+                                                          ctypes.byref(n)), "dc1d_packed_workspace_bytes")
+    return int(n.value)
 
 
 def debug_positions(offsets, L_in, stride=1, padding=0, dilation=1):
