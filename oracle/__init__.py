@@ -12,6 +12,8 @@ Two independent formulations live here:
   contract) in plain C loops over doubles, and its term-by-term derivative.
 * ``packed_heads`` / ``packed_forward`` -- the packed layer's offset (and
   mask) generator in the same C file, then ``forward``.
+* ``forward2d`` -- 2D modulated deformable convolution (DCNv2 with
+  torchvision's offset layout), same C file, same two stages.
 * ``constrain_offsets`` and the ``constrained=True`` option of ``forward``,
   ``forward_points`` and ``backward`` -- the constrained mode: each offset
   clamped to its tap's window, then the unconstrained definition (and, for
@@ -69,6 +71,8 @@ class _Lib:
         lib.oracle_backward.argtypes = [p] * 5 + [i64] * 10 + [p] * 5
         lib.oracle_packed_heads.restype = ctypes.c_int
         lib.oracle_packed_heads.argtypes = [p] * 7 + [i64] * 7 + [p] * 2
+        lib.oracle_forward2d.restype = ctypes.c_int
+        lib.oracle_forward2d.argtypes = [p] * 5 + [i64] * 15 + [p]
         self.lib = lib
 
 
@@ -271,3 +275,37 @@ def packed_forward(x, trunk_weight, trunk_bias, off_weight, off_bias, weight, bi
                              stride, padding, dilation, lib)
     out = forward(x, off, weight, bias, mask, stride, padding, dilation, groups, lib)
     return out, off, mask
+
+
+def output_size2d(H, W, kh, kw, stride=(1, 1), padding=(0, 0), dilation=(1, 1), lib=None):
+    """(H_out, W_out): the conv closed form per axis."""
+    return (output_length(H, kh, stride[0], padding[0], dilation[0], lib),
+            output_length(W, kw, stride[1], padding[1], dilation[1], lib))
+
+
+def forward2d(x, offsets, weight, bias=None, mask=None, stride=(1, 1), padding=(0, 0), dilation=(1, 1), groups=1,
+              lib=None):
+    """2D modulated deformable convolution in float64.  x [B, C_in, H, W],
+    offsets [B, 2*G*kh*kw, H_out, W_out] ((g, i, j, (row, column)) order),
+    mask [B, G*kh*kw, H_out, W_out] or None, weight [C_out, C_in/groups, kh,
+    kw]; returns out [B, C_out, H_out, W_out]."""
+    x, offsets, weight, bias, mask = map(_f64, (x, offsets, weight, bias, mask))
+    B, C_in, H, W = x.shape
+    C_out, cpg, kh, kw = weight.shape
+    if cpg * groups != C_in:
+        raise ValueError("weight shape does not match C_in / groups")
+    H_out, W_out = output_size2d(H, W, kh, kw, stride, padding, dilation, lib)
+    if H_out < 1 or W_out < 1 or offsets.ndim != 4 or offsets.shape[1] % (2 * kh * kw):
+        raise ValueError("bad output size or offsets")
+    G = offsets.shape[1] // (2 * kh * kw)
+    if offsets.shape != (B, 2 * G * kh * kw, H_out, W_out):
+        raise ValueError("offsets must be [B, 2*G*kh*kw, H_out, W_out]")
+    if mask is not None and mask.shape != (B, G * kh * kw, H_out, W_out):
+        raise ValueError("mask must be [B, G*kh*kw, H_out, W_out]")
+    out = np.empty((B, C_out, H_out, W_out), dtype=np.float64)
+    st = _load(lib).oracle_forward2d(_ptr(x), _ptr(offsets), _ptr(mask), _ptr(weight), _ptr(bias), B, C_in, H, W,
+                                     C_out, kh, kw, stride[0], stride[1], padding[0], padding[1], dilation[0],
+                                     dilation[1], groups, G, _ptr(out))
+    if st:
+        raise ValueError("oracle_forward2d: " + _ERR.get(st, str(st)))
+    return out

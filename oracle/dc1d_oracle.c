@@ -482,3 +482,101 @@ int oracle_packed_heads(const double *x, const double *tw, const double *tb, con
     free(t);
     return OR_OK;
 }
+
+/*
+ * 2D modulated deformable convolution (DCNv2), the variant the other pages
+ * describe: the deformable convolution article (section Deformable
+ * Convolution: the y(p0) formula, Step 2's bilinear sampling between the
+ * four surrounding pixels, Step 3's weighted sum) and the torchvision
+ * deform_conv2d issue (offset layout and its printed demo).
+ *
+ *   x       [B, C_in, H, W]
+ *   offsets [B, 2*G*kh*kw, H_out, W_out]; channel ((g*kh + i)*kw + j)*2 holds
+ *           the row (height) offset of tap (i, j) of offset group g, the next
+ *           channel its column (width) offset (the order the issue settles
+ *           on: groups, then kernel rows, then kernel columns, then the pair)
+ *   mask    [B, G*kh*kw, H_out, W_out] or NULL, channel (g*kh + i)*kw + j
+ *   weight  [C_out, C_in/groups, kh, kw]
+ *   bias    [C_out] or NULL
+ *   out     [B, C_out, H_out, W_out]
+ *
+ * Tap (i, j) of output (oh, ow) samples at row oh*sh - ph + i*dh + dy and
+ * column ow*sw - pw + j*dw + dx.  Each axis is split as in 1D (exact
+ * integer grid term plus the floor of the offset); the sample is the
+ * bilinear blend of the four neighbours with weights (1-fy)(1-fx),
+ * (1-fy)fx, fy(1-fx), fy fx, every neighbour outside the image reading 0;
+ * the mask multiplies it as given.  H_out, W_out follow the conv1d closed
+ * form per axis.  Contraction in ascending (ci_local, i, j), bias last.
+ */
+static double x_ext2(const double *plane, int64_t H, int64_t W, int64_t r, int64_t c)
+{
+    return (r >= 0 && r < H && c >= 0 && c < W) ? plane[r * W + c] : 0.0;
+}
+
+int oracle_forward2d(const double *x, const double *offsets, const double *mask, const double *weight,
+                     const double *bias, int64_t B, int64_t C_in, int64_t H, int64_t W, int64_t C_out,
+                     int64_t kh, int64_t kw, int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh,
+                     int64_t dw, int64_t groups, int64_t G, double *out)
+{
+    if (B < 0 || C_in < 1 || C_out < 1 || groups < 1 || G < 1 || C_in % groups || C_out % groups || C_in % G)
+        return OR_BAD_ARG;
+    const int64_t H_out = oracle_output_length(H, kh, sh, ph, dh);
+    const int64_t W_out = oracle_output_length(W, kw, sw, pw, dw);
+    if (H_out < 1 || W_out < 1)
+        return OR_BAD_ARG;
+    const int64_t cpg = C_in / groups, opg = C_out / groups, cpo = C_in / G, T = kh * kw;
+    const int64_t HWo = H_out * W_out;
+    if (!all_finite(x, B * C_in * H * W) || !all_finite(offsets, B * 2 * G * T * HWo) ||
+        (mask && !all_finite(mask, B * G * T * HWo)) || !all_finite(weight, C_out * cpg * T) ||
+        (bias && !all_finite(bias, C_out)))
+        return OR_NONFINITE;
+    if (B == 0)
+        return OR_OK;
+    /* Stage 1: S[b, ci, i, j, oh, ow] */
+    double *S = (double *)malloc(sizeof(double) * (size_t)(B * C_in * T * HWo));
+    if (!S)
+        return OR_NOMEM;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t ci = 0; ci < C_in; ++ci) {
+            const int64_t g = ci / cpo;
+            const double *plane = x + (b * C_in + ci) * H * W;
+            for (int64_t i = 0; i < kh; ++i)
+                for (int64_t j = 0; j < kw; ++j) {
+                    const int64_t tap = (g * kh + i) * kw + j;
+                    const double *oy = offsets + (b * 2 * G * T + 2 * tap) * HWo;
+                    const double *ox = oy + HWo;
+                    const double *mm = mask ? mask + (b * G * T + tap) * HWo : NULL;
+                    for (int64_t oh = 0; oh < H_out; ++oh)
+                        for (int64_t ow = 0; ow < W_out; ++ow) {
+                            const int64_t q = oh * W_out + ow;
+                            int64_t r0, c0;
+                            double fy, fx;
+                            split_position(oh * sh - ph + i * dh, oy[q], &r0, &fy);
+                            split_position(ow * sw - pw + j * dw, ox[q], &c0, &fx);
+                            double v = (1.0 - fy) * (1.0 - fx) * x_ext2(plane, H, W, r0, c0) +
+                                       (1.0 - fy) * fx * x_ext2(plane, H, W, r0, c0 + 1) +
+                                       fy * (1.0 - fx) * x_ext2(plane, H, W, r0 + 1, c0) +
+                                       fy * fx * x_ext2(plane, H, W, r0 + 1, c0 + 1);
+                            if (mm)
+                                v *= mm[q];
+                            S[((b * C_in + ci) * T + i * kw + j) * HWo + q] = v;
+                        }
+                }
+        }
+    /* Stage 2 */
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t co = 0; co < C_out; ++co) {
+            const int64_t grp = co / opg;
+            for (int64_t q = 0; q < HWo; ++q) {
+                double acc = 0.0;
+                for (int64_t cl = 0; cl < cpg; ++cl)
+                    for (int64_t t = 0; t < T; ++t)
+                        acc += weight[(co * cpg + cl) * T + t] * S[((b * C_in + grp * cpg + cl) * T + t) * HWo + q];
+                out[(b * C_out + co) * HWo + q] = acc + (bias ? bias[co] : 0.0);
+            }
+        }
+    free(S);
+    return OR_OK;
+}

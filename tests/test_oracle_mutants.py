@@ -16,6 +16,7 @@ import pytest
 import oracle
 import test_oracle_backward as bwd
 import test_oracle_packed as pk
+import test_oracle_2d as o2
 import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "dc1d_oracle.c")
@@ -69,6 +70,18 @@ MUTANTS = {
     "gen mask from the offset head": ("zm += mw[gk * C_in + c] * t[c * L_out + l];",
                                       "zm += ow[gk * C_in + c] * t[c * L_out + l];"),
     "gen offset bias dropped": ("offsets_out[o] = ob ? zo + ob[gk] : zo;", "offsets_out[o] = zo;"),
+    # 2D
+    "2d row and column offsets swapped": (
+        "split_position(oh * sh - ph + i * dh, oy[q], &r0, &fy);\n"
+        "                            split_position(ow * sw - pw + j * dw, ox[q], &c0, &fx);",
+        "split_position(oh * sh - ph + i * dh, ox[q], &r0, &fy);\n"
+        "                            split_position(ow * sw - pw + j * dw, oy[q], &c0, &fx);"),
+    "2d taps column-major": ("const int64_t tap = (g * kh + i) * kw + j;", "const int64_t tap = (g * kw + j) * kh + i;"),
+    "2d corner transposed": ("(1.0 - fy) * fx * x_ext2(plane, H, W, r0, c0 + 1)",
+                             "(1.0 - fy) * fx * x_ext2(plane, H, W, r0 + 1, c0)"),
+    "2d mask per group only": ("mask + (b * G * T + tap) * HWo", "mask + (b * G * T + g) * HWo"),
+    "2d row stride ignored": ("split_position(oh * sh - ph + i * dh, oy[q], &r0, &fy);",
+                              "split_position(oh - ph + i * dh, oy[q], &r0, &fy);"),
 }
 
 PIN_CALLS = [
@@ -92,6 +105,14 @@ PIN_CALLS = [
     ("generator = conv1d composition", lambda: pk.test_generator_equals_conv1d_composition(pk.SHAPES[0])),
     ("generator: zero mask head halves", pk.test_zero_mask_projection_halves_the_output),
     ("generator: bias-only head", pk.test_bias_only_offset_head_places_each_channel),
+    ("2d torchvision demo", o2.test_torchvision_issue_demo_2d),
+    ("2d zero offsets = conv2d", lambda: o2.test_zero_offsets_equal_conv2d(o2.SHAPES[1])),
+    ("2d integer shift", lambda: o2.test_integer_group_shift_is_shifted_conv2d(o2.SHAPES[1])),
+    ("2d one row = 1d", lambda: o2.test_one_line_reduces_to_the_1d_oracle("column")),
+    ("2d one column = 1d", lambda: o2.test_one_line_reduces_to_the_1d_oracle("row")),
+    ("2d bilinear field", o2.test_bilinear_field_is_reproduced),
+    ("2d hat brute force", lambda: o2.test_equals_product_of_hats_brute_force(o2.SHAPES[1])),
+    ("2d mask invariants", o2.test_mask_invariants),
 ]
 
 
