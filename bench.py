@@ -418,6 +418,102 @@ def main_packed(args, w):
     print(json.dumps(line), flush=True)
 
 
+def work2d(w):
+    """Work of one 2D forward: contraction flops, sampling flops (the
+    bilinear blend of four neighbours: 7 per sample, 8 with the mask), and
+    the bytes of every input read once and the output written once."""
+    T, HWo = w.kh * w.kw, w.Ho * w.Wo
+    contraction = 2 * w.B * w.C_out * HWo * (w.C_in // w.groups) * T
+    sampling = (8 if w.modulated else 7) * w.B * w.C_in * T * HWo
+    es = 4 if w.dtype == "f32" else 2
+    elems = (w.B * w.C_in * w.H * w.W + w.B * w.G * T * HWo * (3 if w.modulated else 2)
+             + w.C_out * (w.C_in // w.groups) * T + w.C_out + w.B * w.C_out * HWo)
+    return contraction, sampling, elems * es
+
+
+def label2d(w):
+    return "%s B%d Cin%d Cout%d %dx%d k%dx%d s%s p%s d%s groups%d G%d%s %s" % (
+        w.name, w.B, w.C_in, w.C_out, w.H, w.W, w.kh, w.kw, w.stride, w.padding, w.dilation, w.groups, w.G,
+        " mask" if w.modulated else "", w.dtype)
+
+
+def run2d(w, steps, warmup, check=True, baseline=True):
+    """Time the 2D forward; check whole images of the first and last batch
+    against the oracle, whose run on one image is also the CPU baseline."""
+    import torch
+    from deformable_convolution_amd import dc1d, inputs
+
+    dev = torch.device("cuda:0")
+    t = inputs.make_inputs2d(w, seed=0)
+    g = {k: (v.to(dev) if v is not None else None) for k, v in t.items()}
+    kw = dict(stride=w.stride, padding=w.padding, dilation=w.dilation, groups=w.groups)
+    kern = dc1d.plan2d(g["x"], g["offsets"], g["weight"], g["bias"], g["mask"], **kw)
+    nws = dc1d.workspace_bytes2d(g["x"], g["offsets"], g["weight"], g["bias"], g["mask"], **kw)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev) if nws else None
+    out = torch.empty((w.B, w.C_out, w.Ho, w.Wo), dtype=g["x"].dtype, device=dev)
+
+    def step():
+        dc1d.forward2d(g["x"], g["offsets"], g["weight"], g["bias"], g["mask"], out=out, workspace=ws, **kw)
+
+    step()
+    torch.cuda.synchronize()
+    parity = cpu = None
+    if check or baseline:
+        import oracle
+        cores = len(os.sched_getaffinity(0))
+        os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+        worst, el = 0.0, 0.0
+        for b in (0, w.B - 1):
+            sl = {k: (v[b:b + 1] if v is not None and k in ("x", "offsets", "mask") else v) for k, v in t.items()}
+            t0 = time.perf_counter()
+            ref = oracle.forward2d(sl["x"], sl["offsets"], sl["weight"], sl["bias"], sl["mask"], **kw)
+            el = time.perf_counter() - t0
+            a = out[b:b + 1].double().cpu().numpy()
+            rms = math.sqrt(float(np.mean(ref ** 2)))
+            if w.dtype == "f32":
+                tol = 1e-5 * math.sqrt(w.C_in // w.groups * w.kh * w.kw) * max(rms, 1.0)
+                worst = max(worst, float(np.abs(a - ref).max()) / tol)
+            else:
+                worst = max(worst, float((np.abs(a - ref) / (2e-2 * np.maximum(np.abs(ref), rms))).max()))
+        parity = {"images": 2, "max_err_over_tol": worst, "ok": bool(worst <= 1.0)}
+        if not parity["ok"]:
+            raise SystemExit("2D parity check failed: %r" % parity)
+        c1, s1, _ = work2d(w.with_batch(1))
+        cpu = {"value": (c1 + s1) / el / 1e9, "unit": "GFLOP/s",
+               "cores": min(int(os.environ["OMP_NUM_THREADS"]), cores), "kind": "oracle",
+               "sample": "1 image of the batch (all its %d outputs), %.1f s, on %s" % (w.C_out * w.Ho * w.Wo, el,
+                                                                                     cpu_model())}
+    tm = timed(step, steps, warmup, dev)
+    return {"kernel": kern, "region_ms": tm["region_ms"], "launch_ms": tm["launch_ms"], "parity": parity, "cpu": cpu}
+
+
+def main2d(args, w):
+    r = run2d(w, args.steps, args.warmup, baseline=not args.no_cpu_baseline)
+    contraction, sampling, nbytes = work2d(w)
+    ms = r["region_ms"] / args.steps
+    peak = PEAK["mfma_f32_TFLOPs"] if w.dtype == "f32" else PEAK["mfma_bf16_TFLOPs"]
+    achieved = contraction / (ms * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": read_traffic(w.name, r["kernel"], kernel_hash()),
+            "kernel": r["kernel"], "kernel_ms": round(ms, 5)}
+    es = 4 if w.dtype == "f32" else 2
+    s_bytes = 2 * w.B * (w.C_in // w.groups) * w.kh * w.kw * w.Ho * w.Wo * es  # the sampled matrix, out and back
+    line = {
+        "metric": "Deformable conv2d (DCNv2) fwd GFLOP/s",
+        "value": round((contraction + sampling) / (ms * 1e-3) / 1e9, 1),
+        "unit": "GFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic, seeded (deformable_convolution_amd/inputs.py; no dataset)",
+        "config": {"workload": label2d(w), "gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                   "hbm_frac_with_sampled_matrix": round((nbytes + s_bytes) / (ms * 1e-3) / 1e9 / PEAK["hbm_GBps"], 4),
+                   "parity": r["parity"], "forward_ms": {"warm": pct(r["launch_ms"])}},
+        "roofline": roof,
+    }
+    if r["cpu"] is not None:
+        line["cpu_baseline"] = r["cpu"]
+    print(json.dumps(line), flush=True)
+
+
 def pct(v):
     """median, p10, p90 of a list of times (ms)."""
     if not v:
@@ -504,6 +600,14 @@ def main():
         print("copied %d bytes" % n, flush=True)
         return
 
+    if args.workload in inputs.WORKLOADS_2D:
+        w = inputs.WORKLOADS_2D[args.workload]
+        if args.profile_run:
+            r = run2d(w, args.steps, args.warmup, check=False, baseline=False)
+            print("profile run: %s %s, %d timed launches" % (w.name, r["kernel"], args.steps), flush=True)
+            return
+        main2d(args, w)
+        return
     if args.workload in inputs.PACKED_WORKLOADS:
         w = inputs.PACKED_WORKLOADS[args.workload]
         if args.profile_run:
@@ -620,7 +724,7 @@ def summarize_profile(d, workload):
 
     from deformable_convolution_amd import inputs
 
-    w = inputs.PACKED_WORKLOADS[workload] if workload in inputs.PACKED_WORKLOADS else inputs.WORKLOADS[workload]
+    w = (inputs.PACKED_WORKLOADS.get(workload) or inputs.WORKLOADS_2D.get(workload) or inputs.WORKLOADS[workload])
 
     def csvs(sub, pattern):
         out = []
@@ -671,15 +775,19 @@ def summarize_profile(d, workload):
 
 def write_profile_md(d, workload, kernel):
     stats, rows_k, total_bytes, (cf_v, cw_v, f_scale, w_scale), w = summarize_profile(d, workload)
+    is2d = workload in __import__("deformable_convolution_amd.inputs", fromlist=["x"]).WORKLOADS_2D
     if kernel == "packed":
         contraction, alg_bytes, _ = work_packed(w)
+    elif is2d:
+        contraction, sampling, alg_bytes = work2d(w)
     else:
         contraction, sampling, alg_bytes = work_backward(w) if kernel == "backward" else work(w)
     # launches in the trace run: the fewest calls of any of our kernels
     n_launch = min((int(r["Calls"]) for r in stats), default=1)
     fwd_ns = sum(float(r["TotalDurationNs"]) for r in stats) / max(n_launch, 1)
     out = []
-    out.append("# %s -- %s" % (packed_label(w) if kernel == "packed" else workload_label(w), kernel))
+    out.append("# %s -- %s" % (packed_label(w) if kernel == "packed" else (label2d(w) if is2d else workload_label(w)),
+                               kernel))
     out.append("")
     out.append("<!-- kernel=%s -->" % kernel)
     out.append("<!-- kernel_sources=%s -->" % kernel_hash())

@@ -1,5 +1,6 @@
 """MI355X-native 1D deformable convolution (DeformConv1d): forward, backward, and
-the packed layer whose offsets (and mask) are generated from its input.
+the packed layer whose offsets (and mask) are generated from its input, and
+2D modulated deformable convolution (DCNv2).
 
 The compute lives in ``libdc1d.so`` (HIP kernels for gfx950 behind a C ABI
 declared in ``include/dc1d.h``); ``deformable_convolution_amd.dc1d`` is the
@@ -13,13 +14,16 @@ from .dc1d import (  # noqa: F401
     backward_workspace_bytes,
     debug_positions,
     forward,
+    forward2d,
     library_path,
     load_library,
     output_length,
     packed_forward,
     packed_workspace_bytes,
     plan,
+    plan2d,
     resolve_padding,
     status_string,
     workspace_bytes,
+    workspace_bytes2d,
 )

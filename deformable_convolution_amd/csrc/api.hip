@@ -629,6 +629,138 @@ int dc1d_packed_forward(const dc1d_tensor *x, const dc1d_tensor *trunk_weight,
     return e == hipSuccess ? DC1D_OK : DC1D_ERR_LAUNCH;
 }
 
+}  // extern "C"
+
+namespace {
+
+int validate2d(const dc1d_tensor *x, const dc1d_tensor *off, const dc1d_tensor *mask, const dc1d_tensor *w,
+               const dc1d_tensor *bias, const dc1d_tensor *out, int64_t sh, int64_t sw, int64_t ph, int64_t pw,
+               int64_t dh, int64_t dw, int64_t groups, int64_t offset_groups, Params2 *p) {
+    if (!x || !off || !w) return DC1D_ERR_NULL_PTR;
+    if (sh < 1 || sw < 1 || ph < 0 || pw < 0 || dh < 1 || dw < 1 || groups < 1 || offset_groups < 1)
+        return DC1D_ERR_BAD_ARG;
+    if (x->ndim != 4 || w->ndim != 4 || off->ndim != 4) return DC1D_ERR_BAD_SHAPE;
+    const int dt = x->dtype;
+    if (dt != DC1D_F32 && dt != DC1D_BF16) return DC1D_ERR_BAD_DTYPE;
+    if (off->dtype != dt || w->dtype != dt || (mask && mask->dtype != dt) || (bias && bias->dtype != dt) ||
+        (out && out->dtype != dt))
+        return DC1D_ERR_BAD_DTYPE;
+    const int64_t B = x->shape[0], C_in = x->shape[1], H = x->shape[2], W = x->shape[3];
+    const int64_t C_out = w->shape[0], kh = w->shape[2], kw = w->shape[3];
+    if (B < 0 || C_in < 1 || H < 0 || W < 0 || C_out < 1 || kh < 1 || kw < 1) return DC1D_ERR_BAD_SHAPE;
+    if (C_in % groups || C_out % groups || C_in % offset_groups) return DC1D_ERR_BAD_ARG;
+    if (w->shape[1] != C_in / groups) return DC1D_ERR_BAD_SHAPE;
+    const int64_t T = kh * kw;
+    if (H + ph > kMaxPos || W + pw > kMaxPos || dh * (kh - 1) > kMaxPos || dw * (kw - 1) > kMaxPos ||
+        H * W >= ((int64_t)1 << 31) || C_in / groups * T > ((int64_t)1 << 30) || C_out > ((int64_t)1 << 30) ||
+        offset_groups * T > ((int64_t)1 << 24) || B > 65535)
+        return DC1D_ERR_BAD_SHAPE;
+    const int64_t Ho = dc1d_output_length(H, kh, sh, ph, dh), Wo = dc1d_output_length(W, kw, sw, pw, dw);
+    if (Ho < 1 || Wo < 1 || Ho * sh > ((int64_t)1 << 30) || Wo * sw > ((int64_t)1 << 30) ||
+        B * Ho * Wo >= ((int64_t)1 << 31))
+        return DC1D_ERR_BAD_SHAPE;
+    const int64_t so[4] = {B, 2 * offset_groups * T, Ho, Wo};
+    if (!shape_is(off, 4, so)) return DC1D_ERR_BAD_SHAPE;
+    const int64_t sm[4] = {B, offset_groups * T, Ho, Wo};
+    if (mask && !shape_is(mask, 4, sm)) return DC1D_ERR_BAD_SHAPE;
+    const int64_t sb[1] = {C_out};
+    if (bias && !shape_is(bias, 1, sb)) return DC1D_ERR_BAD_SHAPE;
+    const int64_t sout[4] = {B, C_out, Ho, Wo};
+    if (out && !shape_is(out, 4, sout)) return DC1D_ERR_BAD_SHAPE;
+    memset(p, 0, sizeof(*p));
+    p->x = x->data;
+    p->off = off->data;
+    p->mask = mask ? mask->data : nullptr;
+    p->w = w->data;
+    p->bias = bias ? bias->data : nullptr;
+    p->out = out ? out->data : nullptr;
+    p->dtype = dt;
+    p->B = (int)B;
+    p->C_in = (int)C_in;
+    p->C_out = (int)C_out;
+    p->H = (int)H;
+    p->W = (int)W;
+    p->Ho = (int)Ho;
+    p->Wo = (int)Wo;
+    p->kh = (int)kh;
+    p->kw = (int)kw;
+    p->sh = (int)sh;
+    p->sw = (int)sw;
+    p->ph = (int)ph;
+    p->pw = (int)pw;
+    p->dh = (int)dh;
+    p->dw = (int)dw;
+    p->groups = (int)groups;
+    p->G = (int)offset_groups;
+    p->cpg = (int)(C_in / groups);
+    p->opg = (int)(C_out / groups);
+    p->cpo = (int)(C_in / offset_groups);
+    p->T = (int)T;
+    p->Kred = (int)(C_in / groups * T);
+    return DC1D_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dc2d_workspace_bytes(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_tensor *mask_or_null,
+                         const dc1d_tensor *weight, const dc1d_tensor *bias_or_null, int64_t stride_h,
+                         int64_t stride_w, int64_t pad_h, int64_t pad_w, int64_t dil_h, int64_t dil_w,
+                         int64_t groups, int64_t offset_groups, size_t *bytes_out) {
+    if (!bytes_out) return DC1D_ERR_NULL_PTR;
+    Params2 p;
+    int st = validate2d(x, offsets, mask_or_null, weight, bias_or_null, nullptr, stride_h, stride_w, pad_h, pad_w,
+                        dil_h, dil_w, groups, offset_groups, &p);
+    if (st) return st;
+    DeviceInfo dev;
+    if ((st = current_device(&dev))) return st;
+    *bytes_out = dc2d_workspace(p, dev.num_cus);
+    return DC1D_OK;
+}
+
+int dc2d_plan(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_tensor *mask_or_null,
+              const dc1d_tensor *weight, const dc1d_tensor *bias_or_null, int64_t stride_h, int64_t stride_w,
+              int64_t pad_h, int64_t pad_w, int64_t dil_h, int64_t dil_w, int64_t groups, int64_t offset_groups,
+              const char **kernel_name) {
+    Params2 p;
+    int st = validate2d(x, offsets, mask_or_null, weight, bias_or_null, nullptr, stride_h, stride_w, pad_h, pad_w,
+                        dil_h, dil_w, groups, offset_groups, &p);
+    if (st) return st;
+    if (kernel_name) *kernel_name = dc2d_kernel_name(p);
+    return DC1D_OK;
+}
+
+int dc2d_forward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_tensor *mask_or_null,
+                 const dc1d_tensor *weight, const dc1d_tensor *bias_or_null, const dc1d_tensor *out, int64_t stride_h,
+                 int64_t stride_w, int64_t pad_h, int64_t pad_w, int64_t dil_h, int64_t dil_w, int64_t groups,
+                 int64_t offset_groups, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!out) return DC1D_ERR_NULL_PTR;
+    Params2 p;
+    int st = validate2d(x, offsets, mask_or_null, weight, bias_or_null, out, stride_h, stride_w, pad_h, pad_w, dil_h,
+                        dil_w, groups, offset_groups, &p);
+    if (st) return st;
+    const dc1d_tensor *all[6] = {x, offsets, mask_or_null, weight, bias_or_null, out};
+    for (const dc1d_tensor *t : all)
+        if (t && numel(t) > 0 && !t->data) return DC1D_ERR_NULL_PTR;
+    const size_t es = elem_size(p.dtype);
+    const size_t out_bytes = (size_t)numel(out) * es;
+    for (int i = 0; i < 5; ++i)
+        if (all[i] && overlaps(out->data, out_bytes, all[i]->data, (size_t)numel(all[i]) * es)) return DC1D_ERR_ALIAS;
+    DeviceInfo dev;
+    if ((st = current_device(&dev))) return st;
+    const size_t need = dc2d_workspace(p, dev.num_cus);
+    if (need > 0 && p.B > 0) {
+        if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255)) return DC1D_ERR_WORKSPACE;
+        for (int i = 0; i < 6; ++i)
+            if (all[i] && overlaps(workspace, need, all[i]->data, (size_t)numel(all[i]) * es)) return DC1D_ERR_ALIAS;
+    }
+    p.ws = workspace;
+    p.ws_bytes = workspace_bytes;
+    const hipError_t e = launch_dc2d(p, dev.num_cus, (hipStream_t)stream);
+    return e == hipSuccess ? DC1D_OK : DC1D_ERR_LAUNCH;
+}
+
 int dc1d_debug_positions(const dc1d_tensor *offsets, int64_t L_in, int64_t stride, int64_t padding,
                          int64_t dilation, int32_t *i0, float *frac, uint8_t *valid, void *stream) {
     if (!offsets) return DC1D_ERR_NULL_PTR;

@@ -183,6 +183,10 @@ struct BwdParams {
 size_t gemm_workspace_bytes(const Params &q, int out_mode, int num_cus);
 hipError_t launch_gemm_f32(const Params &q, int64_t brow, int64_t bbatch, int out_mode, int num_cus,
                            hipStream_t stream);
+// The same GEMM on bf16 operands (A = q.w, B from q.x, both bf16; fp32
+// accumulation; C stored in bf16, RNE), out_mode 0 only.
+hipError_t launch_gemm_bf16(const Params &q, int64_t brow, int64_t bbatch, int num_cus, hipStream_t stream);
+size_t gemm_bf16_workspace_bytes(const Params &q, int num_cus);
 // The packed layer's trunk (fp32 storage): t[b,c,l] = tb[c] +
 // sum_k tw[c,k] * x~[b,c, l*stride - padding + k*dilation], t [B][C][L_out].
 struct TrunkArgs {
@@ -196,6 +200,30 @@ hipError_t launch_trunk(const TrunkArgs &a, hipStream_t stream);
 // zeros): the packed layer's two heads stacked for one GEMM.
 hipError_t launch_stack_heads(const float *ow, const float *ob, const float *mw, const float *mb, int GK, int C,
                               float *wcat, float *bcat, hipStream_t stream);
+// ---- 2D modulated deformable convolution ---------------------------------
+//
+// x [B][C_in][H][W]; offsets [B][2*G*T][Ho][Wo] (T = kh*kw taps; channel
+// 2*((g*kh + i)*kw + j) the row offset of tap (i, j) of group g, the next its
+// column offset); mask [B][G*T][Ho][Wo] or null; weight
+// [C_out][C_in/groups][kh][kw]; out [B][C_out][Ho][Wo].
+struct Params2 {
+    const void *x, *off, *mask, *w, *bias;
+    void *out;
+    int dtype;
+    int B, C_in, C_out, H, W, Ho, Wo, kh, kw, sh, sw, ph, pw, dh, dw, groups, G;
+    int cpg, opg, cpo, T, Kred;  // C_in/groups, C_out/groups, C_in/G, kh*kw, cpg*T
+    void *ws;
+    size_t ws_bytes;
+};
+// Workspace of the dense (groups == 1) path: the sampled matrix
+// S [B][C_in*T][Ho*Wo] in the storage dtype, then the GEMM's split partials;
+// 0 for the direct path.
+size_t dc2d_workspace(const Params2 &p, int num_cus);
+// Dense path (sampling kernel, then the MFMA GEMM) when groups == 1 and
+// C_out >= 32, else one thread per output.
+hipError_t launch_dc2d(const Params2 &p, int num_cus, hipStream_t stream);
+const char *dc2d_kernel_name(const Params2 &p);
+
 size_t backward_workspace_bytes(const Params &p, bool want_weight, int num_cus);
 hipError_t launch_backward(BwdParams a, int num_cus, hipStream_t stream);
 

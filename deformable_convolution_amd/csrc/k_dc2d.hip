@@ -1,0 +1,218 @@
+// k_dc2d.hip -- 2D modulated deformable convolution (DCNv2).
+//
+// The deformable convolution article (section Deformable Convolution) moves
+// every tap p0 + pn of a 2D kernel by a learned offset and samples the input
+// there by bilinear interpolation between the four surrounding pixels (Step
+// 2), then weighs the samples with the kernel (Step 3); the modulation mask
+// multiplies each sample.  Offsets come in the layout of torchvision's
+// deform_conv2d, which its documentation issue settles as: per offset group
+// g, kernel row i, kernel column j, the pair (row offset, column offset) --
+// channel 2*((g*kh + i)*kw + j) and the next.
+//
+// Tap (i, j) of output (oh, ow) samples row oh*sh - ph + i*dh + dy and column
+// ow*sw - pw + j*dw + dx.  Each axis is split like the 1D position
+// (split_position: exact integer grid term plus the floor of the offset);
+// neighbours outside the image read zero.
+//
+// Dense layers (groups == 1, C_out >= 32) run in two kernels:
+//   k_im2col2d  the sampled matrix S [B][C_in*T][Ho*Wo] (row ci*T + tap) in
+//               the storage dtype -- a thread takes one (b, g, tap, output
+//               position) and a run of the group's channels, splits the
+//               position and forms the four bilinear weights once, then
+//               gathers and blends each channel, storing coalesced along the
+//               output positions;
+//   k_gemm      out = W S on the MFMA kernel's plain-GEMM form (M = C_out,
+//               N = B*Ho*Wo, Kred = C_in*T), the bias in its epilogue.
+// Other layers use k_direct2d, one thread per output.
+#include "dc1d_internal.h"
+
+namespace dc1d {
+namespace {
+
+constexpr int kChanRun = 32;  // channels per im2col thread
+constexpr int kUnroll = 8;    // channels whose gathers are in flight together
+
+// The four bilinear neighbours of one (tap, output position): element
+// offsets inside a channel plane and their weights (0 outside the image).
+struct Corners {
+    int idx[4];
+    float wt[4];
+};
+
+__device__ __forceinline__ Corners corners(const Params2 &p, float dy, float dx, int oh, int ow, int i, int j) {
+    int r0, c0;
+    float fy, fx;
+    split_position(dy, oh * p.sh - p.ph + i * p.dh, r0, fy);
+    split_position(dx, ow * p.sw - p.pw + j * p.dw, c0, fx);
+    const bool vr0 = (unsigned)r0 < (unsigned)p.H, vr1 = (unsigned)(r0 + 1) < (unsigned)p.H;
+    const bool vc0 = (unsigned)c0 < (unsigned)p.W, vc1 = (unsigned)(c0 + 1) < (unsigned)p.W;
+    Corners c;
+    c.wt[0] = (vr0 && vc0) ? (1.0f - fy) * (1.0f - fx) : 0.0f;
+    c.wt[1] = (vr0 && vc1) ? (1.0f - fy) * fx : 0.0f;
+    c.wt[2] = (vr1 && vc0) ? fy * (1.0f - fx) : 0.0f;
+    c.wt[3] = (vr1 && vc1) ? fy * fx : 0.0f;
+    // clamped indices: a zero-weight neighbour still reads inside the plane
+    const int ra = min(max(r0, 0), p.H - 1), rb = min(max(r0 + 1, 0), p.H - 1);
+    const int ca = min(max(c0, 0), p.W - 1), cb = min(max(c0 + 1, 0), p.W - 1);
+    c.idx[0] = ra * p.W + ca;
+    c.idx[1] = ra * p.W + cb;
+    c.idx[2] = rb * p.W + ca;
+    c.idx[3] = rb * p.W + cb;
+    return c;
+}
+
+template <class D>
+__device__ __forceinline__ float blend(const typename D::T *plane, const Corners &c) {
+    float v = c.wt[0] * D::ld(plane, c.idx[0]);
+    v = fmaf(c.wt[1], D::ld(plane, c.idx[1]), v);
+    v = fmaf(c.wt[2], D::ld(plane, c.idx[2]), v);
+    return fmaf(c.wt[3], D::ld(plane, c.idx[3]), v);
+}
+
+// grid: (ceil(Ho*Wo / 256), G*T*ceil(cpo / kChanRun), B)
+template <class D, bool MASK>
+__global__ void __launch_bounds__(256) k_im2col2d(Params2 p, int runs) {
+    using T = typename D::T;
+    const int HWo = p.Ho * p.Wo;
+    const int q = blockIdx.x * 256 + threadIdx.x;
+    if (q >= HWo) return;
+    const int run = blockIdx.y % runs;
+    const int gt = blockIdx.y / runs;  // g*T + tap
+    const int g = gt / p.T, tap = gt - g * p.T;
+    const int i = tap / p.kw, j = tap - i * p.kw;
+    const int b = blockIdx.z;
+    const int oh = q / p.Wo, ow = q - oh * p.Wo;
+    const T *__restrict__ off = (const T *)p.off + ((int64_t)b * 2 * p.G * p.T + 2 * gt) * HWo + q;
+    const Corners c = corners(p, D::ld(off, 0), D::ld(off, HWo), oh, ow, i, j);
+    const float m = MASK ? D::ld((const T *)p.mask, ((int64_t)b * p.G * p.T + gt) * HWo + q) : 1.0f;
+    const int c_lo = g * p.cpo + run * kChanRun, c_hi = min(c_lo + kChanRun, (g + 1) * p.cpo);
+    const T *__restrict__ x = (const T *)p.x;
+    T *__restrict__ S = (T *)p.ws;
+    const int64_t plane = (int64_t)p.H * p.W;
+    // kUnroll channels at a time: all their gathers issued before the blends
+    for (int c0 = c_lo; c0 < c_hi; c0 += kUnroll) {
+        float xv[kUnroll][4];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const T *xp = x + ((int64_t)b * p.C_in + min(c0 + u, c_hi - 1)) * plane;
+#pragma unroll
+            for (int z = 0; z < 4; ++z) xv[u][z] = D::ld(xp, c.idx[z]);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (c0 + u >= c_hi) break;
+            float v = c.wt[0] * xv[u][0];
+            v = fmaf(c.wt[1], xv[u][1], v);
+            v = fmaf(c.wt[2], xv[u][2], v);
+            v = fmaf(c.wt[3], xv[u][3], v);
+            if (MASK) v *= m;
+            D::st(S, (((int64_t)b * p.C_in + c0 + u) * p.T + tap) * HWo + q, v);
+        }
+    }
+}
+
+// One thread per output (b, co, oh, ow): the group's channels and taps in
+// ascending order.
+template <class D, bool MASK>
+__global__ void __launch_bounds__(256) k_direct2d(Params2 p) {
+    using T = typename D::T;
+    const int HWo = p.Ho * p.Wo;
+    const int64_t total = (int64_t)p.B * p.C_out * HWo;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= total) return;
+    const int q = (int)(e % HWo);
+    const int64_t bc = e / HWo;
+    const int co = (int)(bc % p.C_out), b = (int)(bc / p.C_out);
+    const int oh = q / p.Wo, ow = q - oh * p.Wo;
+    const int grp = co / p.opg;
+    const T *__restrict__ x = (const T *)p.x;
+    const T *__restrict__ w = (const T *)p.w + (int64_t)co * p.Kred;
+    const int64_t plane = (int64_t)p.H * p.W;
+    float acc = 0.0f;
+    for (int cl = 0; cl < p.cpg; ++cl) {
+        const int ci = grp * p.cpg + cl;
+        const int g = ci / p.cpo;
+        const T *xp = x + ((int64_t)b * p.C_in + ci) * plane;
+        for (int tap = 0; tap < p.T; ++tap) {
+            const int gt = g * p.T + tap;
+            const int i = tap / p.kw, j = tap - i * p.kw;
+            const T *off = (const T *)p.off + ((int64_t)b * 2 * p.G * p.T + 2 * gt) * HWo + q;
+            const Corners c = corners(p, D::ld(off, 0), D::ld(off, HWo), oh, ow, i, j);
+            float v = blend<D>(xp, c);
+            if (MASK) v *= D::ld((const T *)p.mask, ((int64_t)b * p.G * p.T + gt) * HWo + q);
+            acc = fmaf(D::ld(w, cl * p.T + tap), v, acc);
+        }
+    }
+    if (p.bias) acc += D::ld((const T *)p.bias, co);
+    D::st((T *)p.out, e, acc);
+}
+
+bool dense(const Params2 &p) { return p.groups == 1 && p.C_out >= 32 && p.Kred >= 16; }
+
+// The contraction's GEMM arguments: A = weight [C_out][Kred], B(k, n) =
+// S[b][k][q], C = out [B][C_out][Ho*Wo].
+Params gemm_args(const Params2 &p, void *part) {
+    Params q = {};
+    q.dtype = p.dtype;
+    q.w = p.w;
+    q.x = p.ws;
+    q.out = p.out;
+    q.bias = p.bias;
+    q.B = p.B;
+    q.C_out = p.C_out;
+    q.Kred = p.Kred;
+    q.L_out = p.Ho * p.Wo;
+    q.ws = part;
+    return q;
+}
+
+size_t s_bytes(const Params2 &p) {
+    const size_t es = p.dtype == kF32 ? 4 : 2;
+    return ((size_t)p.B * p.Kred * p.Ho * p.Wo * es + 255) & ~(size_t)255;
+}
+
+template <class D, bool MASK>
+hipError_t launch_typed(const Params2 &p, int num_cus, hipStream_t stream) {
+    const int64_t HWo = (int64_t)p.Ho * p.Wo;
+    if (dense(p)) {
+        const int runs = (p.cpo + kChanRun - 1) / kChanRun;
+        const int64_t gy = (int64_t)p.G * p.T * runs;
+        if (gy > 65535 || p.B > 65535) return hipErrorInvalidValue;
+        const dim3 grid((unsigned)((HWo + 255) / 256), (unsigned)gy, (unsigned)p.B);
+        hipLaunchKernelGGL((k_im2col2d<D, MASK>), grid, dim3(256), 0, stream, p, runs);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const Params q = gemm_args(p, (char *)p.ws + s_bytes(p));
+        const int64_t brow = HWo, bbatch = (int64_t)p.Kred * HWo;
+        return p.dtype == kF32 ? launch_gemm_f32(q, brow, bbatch, 0, num_cus, stream)
+                               : launch_gemm_bf16(q, brow, bbatch, num_cus, stream);
+    }
+    const int64_t total = (int64_t)p.B * p.C_out * HWo;
+    const int64_t blocks = (total + 255) / 256;
+    if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_direct2d<D, MASK>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t dc2d_workspace(const Params2 &p, int num_cus) {
+    if (!dense(p)) return 0;
+    const Params q = gemm_args(p, nullptr);
+    const size_t part = p.dtype == kF32 ? gemm_workspace_bytes(q, 0, num_cus) : gemm_bf16_workspace_bytes(q, num_cus);
+    return s_bytes(p) + part;
+}
+
+const char *dc2d_kernel_name(const Params2 &p) {
+    if (!dense(p)) return "direct2d";
+    return p.dtype == kF32 ? "im2col2d_gemm_f32" : "im2col2d_gemm_bf16";
+}
+
+hipError_t launch_dc2d(const Params2 &p, int num_cus, hipStream_t stream) {
+    if (p.B == 0) return hipSuccess;
+    if (p.dtype == kF32) return p.mask ? launch_typed<F32, true>(p, num_cus, stream)
+                                       : launch_typed<F32, false>(p, num_cus, stream);
+    return p.mask ? launch_typed<BF16, true>(p, num_cus, stream) : launch_typed<BF16, false>(p, num_cus, stream);
+}
+
+}  // namespace dc1d

@@ -229,13 +229,14 @@ hipError_t launch_gemm_t(const Params &q, int64_t brow, int64_t bbatch, int num_
     a.splits = pl.splits;
     a.chunks = pl.chunks;
     a.N = N;
-    a.vec_w = (q.Kred % 4 == 0) && (((uintptr_t)q.w & 15) == 0);
+    constexpr int EPW = 16 / (int)sizeof(typename Tr::T);  // elements per 16-byte weight word
+    a.vec_w = (q.Kred % EPW == 0) && (((uintptr_t)q.w & 15) == 0);
     a.off_w = 0;
-    a.off_s = 2 * BM * BK * 4;
+    a.off_s = 2 * BM * BK * (int)sizeof(typename Tr::T);
     a.partials = pl.splits > 1 ? (float *)q.ws : nullptr;
     a.brow = brow;
     a.bbatch = bbatch;
-    size_t lds = (size_t)a.off_s + 2 * (size_t)BN * Tr::SLD * 4;
+    size_t lds = (size_t)a.off_s + 2 * (size_t)BN * Tr::SLD * sizeof(typename Tr::T);
     if (OUT != 0) {
         if (BN + 1 != kHeadLd || q.K < 1 || (int64_t)BN * q.K >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
         lds = std::max(lds, (size_t)BM * (kHeadLd + 1) * 4);  // the staged head tile and its biases
@@ -251,6 +252,12 @@ hipError_t launch_gemm_t(const Params &q, int64_t brow, int64_t bbatch, int num_
     }
     return hipGetLastError();
 }
+
+hipError_t launch_gemm_bf16(const Params &q, int64_t brow, int64_t bbatch, int num_cus, hipStream_t stream) {
+    return launch_gemm_t<TrBF16, 0>(q, brow, bbatch, num_cus, stream);
+}
+
+size_t gemm_bf16_workspace_bytes(const Params &q, int num_cus) { return gemm_ws<TrBF16>(q, num_cus); }
 
 size_t gemm_workspace_bytes(const Params &q, int out_mode, int num_cus) {
     return out_mode == 0 ? gemm_ws<TrF32>(q, num_cus) : gemm_ws<TrF32H>(q, num_cus);

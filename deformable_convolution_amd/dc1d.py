@@ -84,6 +84,12 @@ def load_library():
             lib.dc1d_packed_workspace_bytes.argtypes = [T] * 5 + [i64] * 4 + [ctypes.POINTER(ctypes.c_size_t)]
             lib.dc1d_packed_forward.restype = ctypes.c_int
             lib.dc1d_packed_forward.argtypes = [T] * 12 + [i64] * 4 + [p, ctypes.c_size_t, p]
+            lib.dc2d_workspace_bytes.restype = ctypes.c_int
+            lib.dc2d_workspace_bytes.argtypes = [T] * 5 + [i64] * 8 + [ctypes.POINTER(ctypes.c_size_t)]
+            lib.dc2d_forward.restype = ctypes.c_int
+            lib.dc2d_forward.argtypes = [T] * 6 + [i64] * 8 + [p, ctypes.c_size_t, p]
+            lib.dc2d_plan.restype = ctypes.c_int
+            lib.dc2d_plan.argtypes = [T] * 5 + [i64] * 8 + [ctypes.POINTER(ctypes.c_char_p)]
             lib.dc1d_status_string.restype = ctypes.c_char_p
             lib.dc1d_status_string.argtypes = [ctypes.c_int]
             _lib = lib
@@ -365,6 +371,68 @@ def packed_workspace_bytes(x, trunk_weight, off_weight, weight, mask_weight=None
         _check(load_library().dc1d_packed_workspace_bytes(*[_ref(t) for t in d], stride, padding, dilation, groups,
                                                           ctypes.byref(n)), "dc1d_packed_workspace_bytes")
     return int(n.value)
+
+
+def _pair(v):
+    return (int(v[0]), int(v[1])) if isinstance(v, (tuple, list)) else (int(v), int(v))
+
+
+def _args2d(x, offsets, weight, stride, padding, dilation):
+    kh, kw = (weight.shape[2], weight.shape[3]) if weight.dim() == 4 else (1, 1)
+    G = offsets.shape[1] // (2 * kh * kw) if offsets.dim() == 4 else 0
+    return _pair(stride), _pair(padding), _pair(dilation), G
+
+
+def workspace_bytes2d(x, offsets, weight, bias=None, mask=None, stride=1, padding=0, dilation=1, groups=1) -> int:
+    """Device workspace (bytes) a 2D forward call with these arguments needs."""
+    s, p, d, G = _args2d(x, offsets, weight, stride, padding, dilation)
+    n = ctypes.c_size_t(0)
+    dx, do, dm, dw, db = map(_desc, (x, offsets, mask, weight, bias))
+    with _device_ctx(x.device):
+        _check(load_library().dc2d_workspace_bytes(_ref(dx), _ref(do), _ref(dm), _ref(dw), _ref(db), s[0], s[1], p[0],
+                                                   p[1], d[0], d[1], groups, G, ctypes.byref(n)),
+               "dc2d_workspace_bytes")
+    return int(n.value)
+
+
+def plan2d(x, offsets, weight, bias=None, mask=None, stride=1, padding=0, dilation=1, groups=1) -> str:
+    s, p, d, G = _args2d(x, offsets, weight, stride, padding, dilation)
+    name = ctypes.c_char_p()
+    dx, do, dm, dw, db = map(_desc, (x, offsets, mask, weight, bias))
+    _check(load_library().dc2d_plan(_ref(dx), _ref(do), _ref(dm), _ref(dw), _ref(db), s[0], s[1], p[0], p[1], d[0],
+                                    d[1], groups, G, ctypes.byref(name)), "dc2d_plan")
+    return name.value.decode()
+
+
+def forward2d(x, offsets, weight, bias=None, mask=None, stride=1, padding=0, dilation=1, groups=1, out=None,
+              workspace=None):
+    """2D modulated deformable convolution on the GPU (torchvision's offset
+    layout: [B, 2*G*kh*kw, H_out, W_out], (row, column) per tap).  stride,
+    padding, dilation: an int or a (row, column) pair.  Returns out
+    [B, C_out, H_out, W_out] (allocated unless given), enqueued on torch's
+    current stream."""
+    lib = load_library()
+    x, offsets, weight, bias, mask = (_contig(t, n) for t, n in ((x, "x"), (offsets, "offsets"), (weight, "weight"),
+                                                                   (bias, "bias"), (mask, "mask")))
+    s, p, d, G = _args2d(x, offsets, weight, stride, padding, dilation)
+    if out is None:
+        if x.dim() != 4 or weight.dim() != 4:
+            raise Dc1dValueError(ERR_BAD_SHAPE, "dc2d_forward")
+        Ho = output_length(x.shape[2], weight.shape[2], s[0], p[0], d[0])
+        Wo = output_length(x.shape[3], weight.shape[3], s[1], p[1], d[1])
+        if Ho < 1 or Wo < 1:
+            raise Dc1dValueError(ERR_BAD_SHAPE, "dc2d_forward")
+        out = torch.empty((x.shape[0], weight.shape[0], Ho, Wo), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        workspace = _workspace(workspace_bytes2d(x, offsets, weight, bias, mask, s, p, d, groups), x.device)
+    ws_ptr = None if workspace is None else workspace.data_ptr()
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    dx, do, dm, dw, db, dout = map(_desc, (x, offsets, mask, weight, bias, out))
+    with _device_ctx(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        _check(lib.dc2d_forward(_ref(dx), _ref(do), _ref(dm), _ref(dw), _ref(db), _ref(dout), s[0], s[1], p[0], p[1],
+                                d[0], d[1], groups, G, ws_ptr, ws_len, stream), "dc2d_forward")
+    return out
 
 
 def debug_positions(offsets, L_in, stride=1, padding=0, dilation=1):

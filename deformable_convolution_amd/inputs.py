@@ -180,3 +180,67 @@ def packed_custom(name="packed_custom", *, B, C_in, C_out, L_in, K, stride=1, pa
     """A packed-layer workload of arbitrary shape (L_out supplied by the caller)."""
     return PackedWorkload(name, B, C_in, C_out, L_in, K, stride, padding, dilation, groups, G, L_out, modulated,
                           off_var)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload2D:
+    """2D modulated deformable convolution (offsets in torchvision's layout)."""
+    name: str
+    B: int
+    C_in: int
+    C_out: int
+    H: int
+    W: int
+    kh: int
+    kw: int
+    stride: Tuple[int, int]
+    padding: Tuple[int, int]
+    dilation: Tuple[int, int]
+    groups: int
+    G: int
+    Ho: int
+    Wo: int
+    dtype: str
+    modulated: bool
+    off_var: float = 1.0
+
+    def with_batch(self, B: int) -> "Workload2D":
+        return dataclasses.replace(self, B=B, name="%s[B=%d]" % (self.name, B))
+
+
+# The deformable convolution article's torchvision example (input
+# [1, 64, 28, 28], a 3x3 deformable conv 64 -> 128 with padding 1, offsets
+# from a plain conv), modulated here, and a DCNv2 layer of a detection
+# backbone's size for measurement, in fp32 and bf16.
+WORKLOADS_2D = {
+    "dcn2d_article": Workload2D("dcn2d_article", 1, 64, 128, 28, 28, 3, 3, (1, 1), (1, 1), (1, 1), 1, 1, 28, 28,
+                                "f32", True),
+    "dcn2d": Workload2D("dcn2d", 8, 256, 256, 64, 64, 3, 3, (1, 1), (1, 1), (1, 1), 1, 1, 64, 64, "f32", True),
+    "dcn2d_bf16": Workload2D("dcn2d_bf16", 8, 256, 256, 64, 64, 3, 3, (1, 1), (1, 1), (1, 1), 1, 1, 64, 64, "bf16",
+                             True),
+}
+
+
+def make_inputs2d(w: Workload2D, seed: int = 0) -> dict:
+    """CPU tensors x, offsets, mask (or None), weight, bias, drawn in that
+    order in float32 and cast to the storage dtype: x ~ N(0, 1); offsets ~
+    N(0, off_var) (row and column alike); mask ~ sigmoid(N(0, 1)); weight ~
+    N(0, 1/((C_in/groups)*kh*kw)); bias ~ N(0, 0.1)."""
+    gen = torch.Generator().manual_seed(seed)
+    dt = torch_dtype(w.dtype)
+    T = w.kh * w.kw
+    n = lambda shape, var: torch.randn(shape, generator=gen, dtype=torch.float32) * math.sqrt(var)
+    x = n((w.B, w.C_in, w.H, w.W), 1.0)
+    off = n((w.B, 2 * w.G * T, w.Ho, w.Wo), w.off_var)
+    mask = torch.sigmoid(n((w.B, w.G * T, w.Ho, w.Wo), 1.0)) if w.modulated else None
+    weight = n((w.C_out, w.C_in // w.groups, w.kh, w.kw), 1.0 / ((w.C_in // w.groups) * T))
+    bias = n((w.C_out,), 0.1)
+    cast = lambda t: None if t is None else t.to(dt).contiguous()
+    return {"x": cast(x), "offsets": cast(off), "mask": cast(mask), "weight": cast(weight), "bias": cast(bias)}
+
+
+def custom2d(name="custom2d", *, B, C_in, C_out, H, W, kh, kw, stride=(1, 1), padding=(0, 0), dilation=(1, 1),
+             groups=1, G=1, Ho, Wo, dtype="f32", modulated=False, off_var=1.0) -> Workload2D:
+    """A 2D workload of arbitrary shape (Ho, Wo supplied by the caller)."""
+    return Workload2D(name, B, C_in, C_out, H, W, kh, kw, tuple(stride), tuple(padding), tuple(dilation), groups, G,
+                      Ho, Wo, dtype, modulated, off_var)

@@ -275,6 +275,57 @@ int dc1d_backward_constrained(const dc1d_tensor *x, const dc1d_tensor *offsets,
                               int64_t offset_groups, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * 2D modulated deformable convolution (DCNv2), the variant the deformable
+ * convolution article describes (section Deformable Convolution: every tap
+ * of a 2D kernel moved by its own offset, Step 2 bilinear sampling between
+ * the four surrounding pixels, Step 3 the weighted sum), with the offset
+ * layout of torchvision's deform_conv2d as its documentation issue settles
+ * it:
+ *
+ *   x        [B, C_in, H, W]
+ *   offsets  [B, 2*G*kh*kw, H_out, W_out]: channel 2*((g*kh + i)*kw + j) is
+ *            the row (height) offset of kernel tap (i, j) for offset group g,
+ *            the next channel its column (width) offset
+ *   mask     [B, G*kh*kw, H_out, W_out] or NULL (channel (g*kh + i)*kw + j),
+ *            multiplied as given
+ *   weight   [C_out, C_in/groups, kh, kw];  bias [C_out] or NULL
+ *   out      [B, C_out, H_out, W_out], overwritten
+ *
+ *   out[b,co,oh,ow] = bias[co] + sum over the group's ci and taps (i, j) of
+ *       weight[co,ci_local,i,j] * m * bilinear(x[b,ci], oh*stride_h - pad_h +
+ *       i*dil_h + dy, ow*stride_w - pad_w + j*dil_w + dx)
+ *
+ * with channel ci in offset group ci / (C_in/G); each coordinate split as
+ * in the 1D forward (integer grid term plus the floor of the offset);
+ * bilinear weights (1-fy)(1-fx), (1-fy)fx, fy(1-fx), fy fx on the four
+ * neighbours, a neighbour outside the image reading 0.  H_out and W_out
+ * follow dc1d_output_length per axis.  Storage fp32 or bf16 (one dtype per
+ * call; fp32 arithmetic, bf16 samples rounded once for the bf16 MFMA).
+ * Limits (DC1D_ERR_BAD_SHAPE beyond them): H*W < 2^31, B <= 65535,
+ * B*H_out*W_out < 2^31, G*kh*kw <= 2^24, and the 1D position limits per
+ * axis.  workspace: at least dc2d_workspace_bytes() bytes, 256-byte aligned,
+ * when that is not 0 (the sampled matrix [B, C_in*kh*kw, H_out*W_out] in the
+ * storage dtype and split partial sums; dense layers only); no
+ * initialisation; nothing kept.  Errors as dc1d_forward.
+ */
+int dc2d_workspace_bytes(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_tensor *mask_or_null,
+                         const dc1d_tensor *weight, const dc1d_tensor *bias_or_null, int64_t stride_h,
+                         int64_t stride_w, int64_t pad_h, int64_t pad_w, int64_t dil_h, int64_t dil_w,
+                         int64_t groups, int64_t offset_groups, size_t *bytes_out);
+
+int dc2d_forward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_tensor *mask_or_null,
+                 const dc1d_tensor *weight, const dc1d_tensor *bias_or_null, const dc1d_tensor *out,
+                 int64_t stride_h, int64_t stride_w, int64_t pad_h, int64_t pad_w, int64_t dil_h, int64_t dil_w,
+                 int64_t groups, int64_t offset_groups, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Which path dc2d_forward takes ("im2col2d_gemm_f32", "im2col2d_gemm_bf16",
+ * "direct2d"); same validation as dc2d_workspace_bytes, no device query. */
+int dc2d_plan(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_tensor *mask_or_null,
+              const dc1d_tensor *weight, const dc1d_tensor *bias_or_null, int64_t stride_h, int64_t stride_w,
+              int64_t pad_h, int64_t pad_w, int64_t dil_h, int64_t dil_w, int64_t groups, int64_t offset_groups,
+              const char **kernel_name);
+
+/*
  * Test aid: the sampling positions the forward kernels use, from the same
  * device function.  For every (b, g, l, k) of offsets [B, G, L_out, K]
  * (K = offsets->shape[3]; L_out must equal dc1d_output_length(L_in, K, ...)):
