@@ -291,7 +291,8 @@ DxPlan plan_dx(const Params &p) {
     return pl;
 }
 
-// Depthwise shapes (one input channel per group and per output channel):
+// Depthwise shapes (one input channel per group and per output channel)
+// whose gather arrays do not fit in LDS (k_bwd_dwg below serves the others):
 // every gradient in one pass, nothing materialised.  A block takes 512
 // consecutive outputs l of one (b, c); thread t owns outputs l0 + 2t, +1 and
 // all their taps.  dS = w[c,k] * dout[b,c,l] is formed on the fly; x comes
@@ -461,6 +462,309 @@ __global__ void __launch_bounds__(256) k_bwd_dw(BwdParams a, int WIN, int tiles_
     }
 }
 
+// The same depthwise pass with grad_x gathered instead of scattered: LDS
+// float atomics (two per sample) are the slow part of k_bwd_dw, so here each
+// block OWNS a run of input positions -- tile t of a row owns
+// [t*LT*s - p, (t+1)*LT*s - p), the first tile from 0, the last to L_in --
+// and computes their gradient itself, with plain stores (deterministic):
+//   phase 1: every sample that could land in the owned run (the tile's
+//            outputs and a halo of outputs on both sides, for floor(offset)
+//            within kDwgR) puts its left neighbour i0 and its two weighted
+//            contributions dS*m*(1-f), dS*m*f into LDS ([tap][output]);
+//            the tile's own samples also produce their offset / mask /
+//            weight gradients as in k_bwd_dw;
+//   phase 2: owned position i sums, per tap, the samples whose i0 is i or
+//            i - 1 -- only outputs within R (the block's largest
+//            |floor(offset)|) of the tap's grid position can be among them.
+// Samples with |floor(offset)| > kDwgR are left to k_bwd_dwg_fix (global
+// atomics after this kernel), which runs only if one was seen (*flag).
+constexpr int kDwgT = 512;      // threads per block (one output each: twice the waves of k_bwd_dw per block)
+constexpr int kDwgOpt = 1;      // outputs per thread
+constexpr int kDwgLT = kDwgT * kDwgOpt;
+constexpr int kDwgR = 16;       // largest |floor(offset)| gathered
+constexpr int kDwgMargin = 24;  // x window margin (>= kDwgR + 2)
+constexpr int kIrregular = INT_MIN / 2;
+
+__device__ __forceinline__ int floor_div(int a, int b) {
+    if (b == 1) return a;
+    return a >= 0 ? a / b : -((-a + b - 1) / b);
+}
+
+struct DwgGeo {
+    int l0, lh0, lh1, i_lo, i_hi;
+};
+
+__device__ __forceinline__ DwgGeo dwg_geo(const Params &p, int tile, int tiles_l) {
+    constexpr int LT = kDwgLT;
+    DwgGeo g;
+    g.l0 = tile * LT;
+    g.i_lo = tile == 0 ? 0 : max(0, g.l0 * p.stride - p.padding);
+    g.i_hi = tile == tiles_l - 1 ? p.L_in : min(p.L_in, (g.l0 + LT) * p.stride - p.padding);
+    // outputs whose taps can reach [i_lo - 1, i_hi) with |floor(offset)| <= kDwgR
+    g.lh0 = max(0, -floor_div(-(g.i_lo - 1 + p.padding - (p.K - 1) * p.dilation - kDwgR), p.stride));
+    g.lh1 = min(p.L_out, floor_div(g.i_hi - 1 + p.padding + kDwgR, p.stride) + 1);
+    g.lh0 = min(g.lh0, g.l0);
+    g.lh1 = max(g.lh1, min(g.l0 + LT, p.L_out));
+    return g;
+}
+
+template <int KT>
+__global__ void __launch_bounds__(kDwgT, 4) k_bwd_dwg(BwdParams a, int WIN, int NHP, int tiles_l, int *flag) {
+    const Params &p = a.p;
+    extern __shared__ float smem[];
+    float *xs = smem;                          // [WIN]
+    int *I0 = (int *)(smem + WIN);             // [KT][NHP]
+    float *WL = smem + WIN + KT * NHP;         // [KT][NHP]
+    float *WR = smem + WIN + 2 * KT * NHP;     // [KT][NHP]
+    __shared__ float wred[KT];
+    __shared__ int s_R, s_irr;
+    const int L_in = p.L_in, L_out = p.L_out;
+    const int tile = blockIdx.x % tiles_l;
+    const int row = blockIdx.x / tiles_l;  // b * C_in + c
+    const int c = row % p.C_in, b = row / p.C_in;
+    const int g = c / p.cpo;
+    const DwgGeo geo = dwg_geo(p, tile, tiles_l);
+    const int l0 = geo.l0, lh0 = geo.lh0;
+    const int lo = l0 * p.stride - p.padding - kDwgMargin;
+    const float *__restrict__ xrow = (const float *)p.x + (int64_t)row * L_in;
+    for (int j = threadIdx.x; j < WIN; j += kDwgT) {
+        const int pos = lo + j;
+        xs[j] = (pos >= 0 && pos < L_in) ? xrow[pos] : 0.0f;
+    }
+    if (threadIdx.x < KT) wred[threadIdx.x] = 0.0f;
+    if (threadIdx.x == 0) {
+        s_R = 0;
+        s_irr = 0;
+    }
+    __syncthreads();
+    const float *__restrict__ off = (const float *)p.off;
+    const float *__restrict__ mask = (const float *)p.mask;
+    const float *__restrict__ w = (const float *)p.w + (int64_t)c * KT;
+    const float *__restrict__ dout = a.dout + (int64_t)row * L_out;
+    const int64_t orow = ((int64_t)b * p.G + g) * L_out;  // offsets row of (b, g)
+    const bool om_atomic = p.cpo > 1;
+    float wk[KT], wacc[KT];
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+        wk[k] = w[k];
+        wacc[k] = 0.0f;
+    }
+    int rmax = 0;
+    bool irregular = false;
+    // ---- phase 1a: the tile's own samples (two outputs x KT taps per thread)
+    constexpr int NV = kDwgOpt * KT;
+    const int lt = l0 + kDwgOpt * threadIdx.x;
+    const int nvalid = min(kDwgOpt, L_out - lt);
+    const int64_t e0 = (orow + lt) * KT;
+    const bool vec = NV % 2 == 0 && nvalid == kDwgOpt && ((((uintptr_t)(off + e0)) & 7) == 0) &&
+                     (!mask || (((uintptr_t)(mask + e0)) & 7) == 0);
+    float ov[NV], mv[NV], dv[kDwgOpt];
+    if (nvalid > 0) {
+        if (vec) {
+#pragma unroll
+            for (int q = 0; q < NV; q += 2) {
+                const float2 t = *(const float2 *)(off + e0 + q);
+                ov[q] = t.x;
+                ov[q + 1] = t.y;
+                if (mask) {
+                    const float2 u = *(const float2 *)(mask + e0 + q);
+                    mv[q] = u.x;
+                    mv[q + 1] = u.y;
+                } else {
+                    mv[q] = mv[q + 1] = 1.0f;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < NV; ++q) {
+                const bool ok = q < nvalid * KT;
+                ov[q] = ok ? off[e0 + q] : 0.0f;
+                mv[q] = (ok && mask) ? mask[e0 + q] : 1.0f;
+            }
+        }
+#pragma unroll
+        for (int o = 0; o < kDwgOpt; ++o) dv[o] = o < nvalid ? dout[lt + o] : 0.0f;
+    }
+    float go[NV], gm[NV];
+#pragma unroll
+    for (int o = 0; o < kDwgOpt; ++o) {
+        const int l = lt + o;
+        const int base0 = l * p.stride - p.padding;
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+            const int q = o * KT + k;
+            go[q] = gm[q] = 0.0f;
+            if (o >= nvalid) continue;
+            int i0;
+            float f;
+            const TapRange r = tap_range(p, k);
+            const int base = base0 + k * p.dilation;
+            split_position(ov[q], base, r, i0, f);
+            const float m = mv[q];
+            const int j = i0 - lo;
+            float x0, x1;
+            if ((unsigned)j < (unsigned)(WIN - 1)) {
+                x0 = xs[j];
+                x1 = xs[j + 1];
+            } else {
+                x0 = (i0 >= 0 && i0 < L_in) ? xrow[i0] : 0.0f;
+                x1 = (i0 + 1 >= 0 && i0 + 1 < L_in) ? xrow[i0 + 1] : 0.0f;
+            }
+            const float d = dv[o];
+            const float ds = wk[k] * d;
+            const float lerp = fmaf(f, x1 - x0, x0);
+            wacc[k] = fmaf(d, lerp * m, wacc[k]);
+            go[q] = tap_moves(p, ov[q], r) ? ds * m * (x1 - x0) : 0.0f;
+            gm[q] = ds * lerp;
+            const int fl = i0 - base;
+            const bool reg = fl >= -kDwgR && fl <= kDwgR;
+            irregular |= !reg;
+            if (reg) rmax = max(rmax, abs(fl));
+            const int h = l - lh0;
+            const float dm = ds * m;
+            I0[k * NHP + h] = reg ? i0 : kIrregular;
+            WL[k * NHP + h] = dm * (1.0f - f);
+            WR[k * NHP + h] = dm * f;
+        }
+    }
+    // offset and mask gradients of the two outputs
+    if (nvalid > 0 && (a.goff || a.gmask)) {
+        if (om_atomic) {
+#pragma unroll
+            for (int q = 0; q < NV; ++q)
+                if (q < nvalid * KT) {
+                    if (a.goff) unsafeAtomicAdd(a.goff + e0 + q, go[q]);
+                    if (a.gmask) unsafeAtomicAdd(a.gmask + e0 + q, gm[q]);
+                }
+        } else if (vec) {
+#pragma unroll
+            for (int q = 0; q < NV; q += 2) {
+                if (a.goff) *(float2 *)(a.goff + e0 + q) = float2{go[q], go[q + 1]};
+                if (a.gmask) *(float2 *)(a.gmask + e0 + q) = float2{gm[q], gm[q + 1]};
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < NV; ++q)
+                if (q < nvalid * KT) {
+                    if (a.goff) a.goff[e0 + q] = go[q];
+                    if (a.gmask) a.gmask[e0 + q] = gm[q];
+                }
+        }
+    }
+    // ---- phase 1b: halo samples (outputs outside the tile that can reach the owned run)
+    {
+        const int nleft = l0 - lh0, nright = geo.lh1 - min(l0 + kDwgLT, L_out);
+        const int nh = (nleft + nright) * KT;
+        for (int e = threadIdx.x; e < nh; e += kDwgT) {
+            const int hk = e / KT, k = e - hk * KT;
+            const int l = hk < nleft ? lh0 + hk : min(l0 + kDwgLT, L_out) + (hk - nleft);
+            const int64_t oi = (orow + l) * KT + k;
+            int i0;
+            float f;
+            const TapRange r = tap_range(p, k);
+            const int base = l * p.stride - p.padding + k * p.dilation;
+            split_position(off[oi], base, r, i0, f);
+            const float dm = w[k] * dout[l] * (mask ? mask[oi] : 1.0f);
+            const int fl = i0 - base;
+            const bool reg = fl >= -kDwgR && fl <= kDwgR;
+            if (reg) rmax = max(rmax, abs(fl));
+            const int h = l - lh0;
+            I0[k * NHP + h] = reg ? i0 : kIrregular;
+            WL[k * NHP + h] = dm * (1.0f - f);
+            WR[k * NHP + h] = dm * f;
+        }
+    }
+    // weight gradient partials: wave sums, then LDS, then one atomic per tap
+    if (a.gw) {
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+            float v = wacc[k];
+            for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+            if ((threadIdx.x & 63) == 0) atomicAdd(wred + k, v);
+        }
+    }
+    for (int o = 32; o > 0; o >>= 1) rmax = max(rmax, __shfl_xor(rmax, o));
+    const bool irr_w = __any(irregular);
+    if ((threadIdx.x & 63) == 0) {
+        atomicMax(&s_R, rmax);
+        if (irr_w) s_irr = 1;
+    }
+    __syncthreads();
+    if (a.gw && threadIdx.x < KT) unsafeAtomicAdd(a.gw + (int64_t)c * KT + threadIdx.x, wred[threadIdx.x]);
+    if (threadIdx.x == 0 && s_irr) atomicOr(flag, 1);
+    if (!a.gx) return;
+    // ---- phase 2: the owned positions, gathered
+    const int R = s_R;
+    const int nhl = geo.lh1 - lh0;
+    float *__restrict__ gxr = a.gx + (int64_t)row * L_in;
+    // candidates per tap: outputs l with l*s in [t - 1 - R, t + R]; a uniform
+    // trip count (the largest any lane has) in groups of four, so that the
+    // LDS reads of a group are in flight together
+    const int ncand = (2 * R + 1) / p.stride + 2;
+    for (int i = geo.i_lo + threadIdx.x; i < geo.i_hi; i += kDwgT) {
+        float acc = 0.0f;
+#pragma unroll 1
+        for (int k = 0; k < KT; ++k) {
+            const int t = i + p.padding - k * p.dilation;  // l*s for i0 == i with floor(offset) 0
+            const int hmin = -floor_div(-(t - 1 - R), p.stride) - lh0;
+            const int hmax = min(floor_div(t + R, p.stride) - lh0, nhl - 1);
+            const int *__restrict__ i0k = I0 + k * NHP;
+            const float *__restrict__ wlk = WL + k * NHP, *__restrict__ wrk = WR + k * NHP;
+            for (int m0 = 0; m0 < ncand; m0 += 4) {
+                int v[4];
+                float wl[4], wr[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int h = hmin + m0 + u;
+                    const bool ok = h >= 0 && h <= hmax;
+                    const int hc = ok ? h : 0;
+                    v[u] = ok ? i0k[hc] : kIrregular;
+                    wl[u] = wlk[hc];
+                    wr[u] = wrk[hc];
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    acc += v[u] == i ? wl[u] : 0.0f;
+                    acc += v[u] == i - 1 ? wr[u] : 0.0f;
+                }
+            }
+        }
+        gxr[i] = acc;
+    }
+}
+
+// The samples k_bwd_dwg left out (|floor(offset)| > kDwgR), added to grad_x
+// with global atomics once every owned run is stored.  Runs only if one was
+// seen.
+template <int KT>
+__global__ void __launch_bounds__(256) k_bwd_dwg_fix(BwdParams a, int tiles_l, const int *flag) {
+    if (*flag == 0) return;
+    const Params &p = a.p;
+    const int tile = blockIdx.x % tiles_l;
+    const int row = blockIdx.x / tiles_l;
+    const int c = row % p.C_in, b = row / p.C_in;
+    const int g = c / p.cpo;
+    const int64_t orow = ((int64_t)b * p.G + g) * p.L_out;
+    const float *__restrict__ w = (const float *)p.w + (int64_t)c * KT;
+    float *__restrict__ gxr = a.gx + (int64_t)row * p.L_in;
+    const int l1 = min((tile + 1) * kDwgLT, p.L_out);
+    for (int l = tile * kDwgLT + threadIdx.x; l < l1; l += 256) {
+        const float d = a.dout[(int64_t)row * p.L_out + l];
+        for (int k = 0; k < KT; ++k) {
+            const int64_t oi = (orow + l) * KT + k;
+            int i0;
+            float f;
+            const int base = l * p.stride - p.padding + k * p.dilation;
+            split_position(((const float *)p.off)[oi], base, tap_range(p, k), i0, f);
+            const int fl = i0 - base;
+            if (fl >= -kDwgR && fl <= kDwgR) continue;
+            const float dm = w[k] * d * (p.mask ? ((const float *)p.mask)[oi] : 1.0f);
+            if (i0 >= 0 && i0 < p.L_in) unsafeAtomicAdd(gxr + i0, dm * (1.0f - f));
+            if (i0 + 1 >= 0 && i0 + 1 < p.L_in) unsafeAtomicAdd(gxr + i0 + 1, dm * f);
+        }
+    }
+}
+
 // out[c][r] = in[r][c] for a rows x cols matrix (32 x 32 tiles through LDS).
 __global__ void __launch_bounds__(256) k_transpose(const float *__restrict__ in, float *__restrict__ out, int rows,
                                                    int cols) {
@@ -548,9 +852,33 @@ bool depthwise_path(const Params &p) {
            (int64_t)p.B * p.C_in * ((p.L_out + 256 * kDwbOpt - 1) / (256 * kDwbOpt)) < ((int64_t)1 << 31);
 }
 
+// LDS of the gather pass (k_bwd_dwg) for this shape: the x window and the
+// [K][NHP] sample arrays, or 0 when they exceed kDwgLds (then the
+// scattering k_bwd_dw runs).
+constexpr size_t kDwgLds = 64 * 1024;
+struct DwgPlan {
+    int win, nhp;
+    size_t lds;
+};
+DwgPlan plan_dwg(const Params &p) {
+    const int64_t LT = kDwgLT, s = p.stride;
+    const int64_t span = (int64_t)(p.K - 1) * p.dilation;
+    int64_t win = (LT - 1) * s + span + kDwgR + kDwgMargin + 4;
+    win = (win + 63) / 64 * 64;
+    const int64_t nh = LT + (span + kDwgR + 1 + s - 1) / s + kDwgR / s + 2;
+    const int64_t nhp = (nh + 31) / 32 * 32 + 1;  // pitch = 1 (mod 32): taps on distinct banks
+    DwgPlan pl = {0, 0, 0};
+    const size_t lds = ((size_t)win + 3 * (size_t)p.K * nhp) * 4;
+    if (lds <= kDwgLds && win >= 2) pl = {(int)win, (int)nhp, lds};
+    return pl;
+}
+
 BwdLayout layout(const Params &p, bool want_weight, int num_cus) {
     BwdLayout L = {};
-    if (depthwise_path(p)) return L;  // nothing materialised
+    if (depthwise_path(p)) {  // nothing materialised; the gather pass's flag
+        L.total = plan_dwg(p).lds > 0 ? 256 : 0;
+        return L;
+    }
     const size_t nds = (size_t)p.B * p.C_in * p.K * p.L_out * 4;
     size_t o = 0;
     L.dS = o;
@@ -582,10 +910,16 @@ size_t backward_workspace_bytes(const Params &p, bool want_weight, int num_cus) 
     return layout(p, want_weight, num_cus).total;
 }
 
-hipError_t launch_backward_dw(BwdParams a, hipStream_t stream) {
+hipError_t launch_backward_dw(BwdParams a, int *flag, hipStream_t stream) {
     const Params &p = a.p;
     const int LT = 256 * kDwbOpt;
     const int tiles_l = (p.L_out + LT - 1) / LT;
+    const DwgPlan g = plan_dwg(p);
+    const bool gather = g.lds > 0 && flag != nullptr;
+    if (a.gx && !gather) {  // the scattering pass accumulates into grad_x
+        const int64_t nx = (int64_t)p.B * p.C_in * p.L_in;
+        hipLaunchKernelGGL(k_bwd_zero, dim3(grid_for(nx)), dim3(256), 0, stream, a.gx, nx);
+    }
     int64_t win = (int64_t)(LT - 1) * p.stride + (int64_t)(p.K - 1) * p.dilation + 2 + 2 * kDwbMargin;
     win = (win + 63) / 64 * 64;
     if (win > 6144) win = 0;  // wider spans: global memory only
@@ -600,6 +934,28 @@ hipError_t launch_backward_dw(BwdParams a, hipStream_t stream) {
         hipLaunchKernelGGL(k_bwd_zero, dim3(grid_for(nw)), dim3(256), 0, stream, a.gw, nw);
     }
     const dim3 grid((unsigned)((int64_t)p.B * p.C_in * tiles_l));
+    if (gather) {
+        const int tiles_g = (p.L_out + kDwgLT - 1) / kDwgLT;
+        const dim3 grid((unsigned)((int64_t)p.B * p.C_in * tiles_g));
+        hipLaunchKernelGGL(k_bwd_zero, dim3(1), dim3(256), 0, stream, (float *)flag, (int64_t)1);
+        switch (p.K) {
+#define DC1D_BDWG(KK)                                                                                              \
+    case KK:                                                                                                       \
+        hipLaunchKernelGGL((k_bwd_dwg<KK>), grid, dim3(kDwgT), g.lds, stream, a, g.win, g.nhp, tiles_g, flag);    \
+        if (a.gx) hipLaunchKernelGGL((k_bwd_dwg_fix<KK>), grid, dim3(256), 0, stream, a, tiles_g, (const int *)flag); \
+        break;
+            DC1D_BDWG(1)
+            DC1D_BDWG(2)
+            DC1D_BDWG(3)
+            DC1D_BDWG(4)
+            DC1D_BDWG(5)
+            DC1D_BDWG(7)
+            DC1D_BDWG(9)
+#undef DC1D_BDWG
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     switch (p.K) {
 #define DC1D_BDW(KK) \
     case KK: hipLaunchKernelGGL((k_bwd_dw<KK>), grid, dim3(256), lds, stream, a, (int)win, tiles_l); break;
@@ -622,6 +978,12 @@ hipError_t launch_backward(BwdParams a, int num_cus, hipStream_t stream) {
     char *ws = (char *)a.dS;  // the workspace base
     const BwdLayout L = layout(p, a.gw != nullptr, num_cus);
     const DxPlan dx = plan_dx(p);
+    const bool want_dx = a.gx || a.goff || a.gmask;
+    if (n > 0 && (want_dx || a.gw) && depthwise_path(p)) {
+        const hipError_t e = launch_backward_dw(a, L.total > 0 ? (int *)ws : nullptr, stream);
+        if (e != hipSuccess) return e;
+        return launch_bias(a, stream);
+    }
     if (a.gx) {
         const int64_t nx = (int64_t)p.B * p.C_in * p.L_in;
         hipLaunchKernelGGL(k_bwd_zero, dim3(grid_for(nx)), dim3(256), 0, stream, a.gx, nx);
@@ -630,12 +992,6 @@ hipError_t launch_backward(BwdParams a, int num_cus, hipStream_t stream) {
     if (dx.atomic_om && n > 0) {  // offset and mask gradients are accumulated
         if (a.goff) hipLaunchKernelGGL(k_bwd_zero, dim3(grid_for(no)), dim3(256), 0, stream, a.goff, no);
         if (a.gmask) hipLaunchKernelGGL(k_bwd_zero, dim3(grid_for(no)), dim3(256), 0, stream, a.gmask, no);
-    }
-    const bool want_dx = a.gx || a.goff || a.gmask;
-    if (n > 0 && (want_dx || a.gw) && depthwise_path(p)) {
-        const hipError_t e = launch_backward_dw(a, stream);
-        if (e != hipSuccess) return e;
-        return launch_bias(a, stream);
     }
     const int64_t dx_blocks = (int64_t)p.B * dx.ngrp_blocks * dx.tiles_l;
     if (dx_blocks >= ((int64_t)1 << 31) || (int64_t)p.C_out * p.cpg * p.K >= ((int64_t)1 << 31))

@@ -70,6 +70,9 @@ def fp32_shapes():
         (2, 24, 24, 100, 5, 1, 2, 2, 24, 24, True, 4.0),
         (2, 8, 24, 90, 3, 2, 1, 1, 8, 2, False, 3.0),
         (1, 6, 6, 500, 3, 1, 1, 1, 6, 6, False, 200.0),
+        (2, 16, 16, 300, 3, 2, 1, 1, 16, 16, True, 3.0),     # depthwise, strided (gathered grad_x)
+        (1, 8, 8, 700, 9, 1, 4, 24, 8, 8, True, 5.0),       # depthwise, wide dilation (scattered grad_x)
+        (1, 4, 4, 1500, 5, 1, 2, 2, 4, 4, False, 20.0),     # depthwise, some samples moved > 16 (fix pass)
     ]
     for i, (B, C_in, C_out, L_in, K, s, p, d, groups, G, mask, sc) in enumerate(spec):
         L_out = oracle.output_length(L_in, K, s, p, d)
