@@ -111,6 +111,129 @@ __global__ void __launch_bounds__(256) k_im2col2d(Params2 p, int runs) {
     }
 }
 
+// The same matrix with the input staged in LDS: a block takes 256
+// consecutive output positions of one batch and a run of one offset group's
+// channels; each thread splits its position's TT taps once (registers), and
+// for every channel the block stages the band of input rows those positions
+// can reach -- their rows' span plus kBandR rows of offset on each side,
+// zero outside the image -- in LDS (double-buffered, one barrier per
+// channel, the next channel's band loaded while this one is sampled), so
+// that every tap's four neighbours are LDS reads.  Taps moved beyond the
+// band read global memory.
+constexpr int kBandR = 4;
+constexpr int kBandRun = 8;  // channels per block (more, smaller blocks keep more waves resident)
+constexpr int kBandPer = 8;  // band elements per thread (the band holds at most 256 * kBandPer)
+constexpr size_t kBandLds = 48 * 1024;
+
+template <class D, bool MASK, int TT>
+__global__ void __launch_bounds__(256) k_im2col2d_band(Params2 p, int runs, int band_cap) {
+    using T = typename D::T;
+    extern __shared__ float s_band[];  // [2][band_cap]
+    const int HWo = p.Ho * p.Wo;
+    const int q0 = blockIdx.x * 256;
+    const int q = q0 + threadIdx.x;
+    const bool valid = q < HWo;
+    const int run = blockIdx.y % runs;
+    const int g = blockIdx.y / runs;
+    const int b = blockIdx.z;
+    const int qq = valid ? q : HWo - 1;
+    const int oh = qq / p.Wo, ow = qq - oh * p.Wo;
+    const int oh_a = q0 / p.Wo, oh_b = min(q0 + 255, HWo - 1) / p.Wo;
+    const int r_lo = oh_a * p.sh - p.ph - kBandR;
+    const int nrows = (oh_b - oh_a) * p.sh + (p.kh - 1) * p.dh + 2 * kBandR + 2;
+    const int W = p.W;
+    // this position's taps, once: band-relative indices of the left
+    // neighbours in the two rows, column weights, and row weights with the
+    // mask folded in; ia = -1 marks a tap moved beyond the band
+    int ia[TT], ib[TT];
+    float wx0[TT], wx1[TT], wt[TT], wb[TT];
+    const T *__restrict__ off = (const T *)p.off + ((int64_t)b * 2 * p.G + 2 * g) * TT * HWo + qq;
+    const T *__restrict__ msk = MASK ? (const T *)p.mask + ((int64_t)b * p.G + g) * TT * HWo + qq : nullptr;
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        const int i = t / p.kw, j = t - i * p.kw;
+        int r0, c0;
+        float fy, fx;
+        split_position(D::ld(off, (int64_t)2 * t * HWo), oh * p.sh - p.ph + i * p.dh, r0, fy);
+        split_position(D::ld(off, (int64_t)(2 * t + 1) * HWo), ow * p.sw - p.pw + j * p.dw, c0, fx);
+        const float m = MASK ? D::ld(msk, (int64_t)t * HWo) : 1.0f;
+        const bool vc0 = (unsigned)c0 < (unsigned)W, vc1 = (unsigned)(c0 + 1) < (unsigned)W;
+        const int ca = min(max(c0, 0), W - 1), cb = min(max(c0 + 1, 0), W - 1);
+        const int rb = r0 - r_lo;
+        const bool inband = (unsigned)rb <= (unsigned)(nrows - 2);
+        ia[t] = inband ? rb * W + ca : -1;
+        ib[t] = inband ? rb * W + cb : 0;
+        wx0[t] = vc0 ? 1.0f - fx : 0.0f;
+        wx1[t] = vc1 ? fx : 0.0f;
+        wt[t] = (1.0f - fy) * m;
+        wb[t] = fy * m;
+    }
+    const int c_lo = g * p.cpo + run * kBandRun, c_hi = min(c_lo + kBandRun, (g + 1) * p.cpo);
+    const T *__restrict__ x = (const T *)p.x;
+    const int64_t plane = (int64_t)p.H * W;
+    const int nband = nrows * W;
+    // the band of channel ci + 1 is loaded into registers before channel
+    // ci's samples are stored, so waiting for those loads never waits for
+    // the stores (one memory counter tracks both)
+    float xv[kBandPer];
+    auto fetch = [&](int ci) {
+        const T *__restrict__ xp = x + ((int64_t)b * p.C_in + ci) * plane;
+#pragma unroll
+        for (int u = 0; u < kBandPer; ++u) {
+            const int e = threadIdx.x + 256 * u;
+            const int rr = e / W, col = e - rr * W, r = r_lo + rr;
+            xv[u] = (e < nband && r >= 0 && r < p.H) ? D::ld(xp, (int64_t)r * W + col) : 0.0f;
+        }
+    };
+    auto put = [&](float *band) {
+#pragma unroll
+        for (int u = 0; u < kBandPer; ++u) {
+            const int e = threadIdx.x + 256 * u;
+            if (e < nband) band[e] = xv[u];
+        }
+    };
+    if (c_lo < c_hi) {
+        fetch(c_lo);
+        put(s_band);
+    }
+    __syncthreads();
+    for (int ci = c_lo; ci < c_hi; ++ci) {
+        float *band = s_band + ((ci - c_lo) & 1) * band_cap;
+        const T *__restrict__ xp = x + ((int64_t)b * p.C_in + ci) * plane;
+        const bool more = ci + 1 < c_hi;
+        if (more) fetch(ci + 1);
+        if (valid) {
+            T *__restrict__ st = (T *)p.ws + ((int64_t)b * p.C_in + ci) * TT * HWo + q;
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
+                float v;
+                if (ia[t] >= 0) {
+                    const float top = fmaf(wx1[t], band[ib[t]], wx0[t] * band[ia[t]]);
+                    const float bot = fmaf(wx1[t], band[ib[t] + W], wx0[t] * band[ia[t] + W]);
+                    v = fmaf(wb[t], bot, wt[t] * top);
+                } else {  // moved beyond the band: the neighbours from global memory
+                    const int i = t / p.kw, j = t - i * p.kw;
+                    int r0, c0;
+                    float fy, fx;
+                    split_position(D::ld(off, (int64_t)2 * t * HWo), oh * p.sh - p.ph + i * p.dh, r0, fy);
+                    split_position(D::ld(off, (int64_t)(2 * t + 1) * HWo), ow * p.sw - p.pw + j * p.dw, c0, fx);
+                    const int ca = min(max(c0, 0), W - 1), cb = min(max(c0 + 1, 0), W - 1);
+                    const int ra = min(max(r0, 0), p.H - 1), rc = min(max(r0 + 1, 0), p.H - 1);
+                    const bool vr0 = (unsigned)r0 < (unsigned)p.H, vr1 = (unsigned)(r0 + 1) < (unsigned)p.H;
+                    const float top = vr0 ? fmaf(wx1[t], D::ld(xp, (int64_t)ra * W + cb), wx0[t] * D::ld(xp, (int64_t)ra * W + ca))
+                                          : 0.0f;
+                    const float bot = vr1 ? fmaf(wx1[t], D::ld(xp, (int64_t)rc * W + cb), wx0[t] * D::ld(xp, (int64_t)rc * W + ca))
+                                          : 0.0f;
+                    v = fmaf(wb[t], bot, wt[t] * top);
+                }
+                D::st(st, (int64_t)t * HWo, v);
+            }
+        }
+        if (more) put(s_band + ((ci + 1 - c_lo) & 1) * band_cap);
+        __syncthreads();
+    }
+}
+
 // One thread per output (b, co, oh, ow): the group's channels and taps in
 // ascending order.
 template <class D, bool MASK>
@@ -149,6 +272,17 @@ __global__ void __launch_bounds__(256) k_direct2d(Params2 p) {
 
 bool dense(const Params2 &p) { return p.groups == 1 && p.C_out >= 32 && p.Kred >= 16; }
 
+// The banded sampler's LDS band (floats per buffer), or 0 when it does not
+// serve this shape (taps other than 1x1, 2x2, 3x3 square counts 1, 4, 9 with
+// kw matching, or a band beyond kBandLds).
+int band_cap(const Params2 &p) {
+    if (p.T != 1 && p.T != 4 && p.T != 9) return 0;
+    const int64_t dr = 255 / p.Wo + 1;  // output rows a block of 256 positions spans, minus one (at most)
+    const int64_t nrows = dr * p.sh + (int64_t)(p.kh - 1) * p.dh + 2 * kBandR + 2;
+    const int64_t cap = nrows * p.W;
+    return cap <= 256 * kBandPer && 2 * cap * 4 <= (int64_t)kBandLds ? (int)cap : 0;
+}
+
 // The contraction's GEMM arguments: A = weight [C_out][Kred], B(k, n) =
 // S[b][k][q], C = out [B][C_out][Ho*Wo].
 Params gemm_args(const Params2 &p, void *part) {
@@ -176,10 +310,25 @@ hipError_t launch_typed(const Params2 &p, int num_cus, hipStream_t stream) {
     const int64_t HWo = (int64_t)p.Ho * p.Wo;
     if (dense(p)) {
         const int runs = (p.cpo + kChanRun - 1) / kChanRun;
-        const int64_t gy = (int64_t)p.G * p.T * runs;
-        if (gy > 65535 || p.B > 65535) return hipErrorInvalidValue;
-        const dim3 grid((unsigned)((HWo + 255) / 256), (unsigned)gy, (unsigned)p.B);
-        hipLaunchKernelGGL((k_im2col2d<D, MASK>), grid, dim3(256), 0, stream, p, runs);
+        const int cap = band_cap(p);
+        if (cap > 0) {
+            const int runs_b = (p.cpo + kBandRun - 1) / kBandRun;
+            const int64_t gy = (int64_t)p.G * runs_b;
+            if (gy > 65535 || p.B > 65535) return hipErrorInvalidValue;
+            const dim3 grid((unsigned)((HWo + 255) / 256), (unsigned)gy, (unsigned)p.B);
+            const size_t lds = 2 * (size_t)cap * 4;
+            switch (p.T) {
+            case 1: hipLaunchKernelGGL((k_im2col2d_band<D, MASK, 1>), grid, dim3(256), lds, stream, p, runs_b, cap); break;
+            case 4: hipLaunchKernelGGL((k_im2col2d_band<D, MASK, 4>), grid, dim3(256), lds, stream, p, runs_b, cap); break;
+            case 9: hipLaunchKernelGGL((k_im2col2d_band<D, MASK, 9>), grid, dim3(256), lds, stream, p, runs_b, cap); break;
+            default: return hipErrorInvalidValue;
+            }
+        } else {
+            const int64_t gy = (int64_t)p.G * p.T * runs;
+            if (gy > 65535 || p.B > 65535) return hipErrorInvalidValue;
+            const dim3 grid((unsigned)((HWo + 255) / 256), (unsigned)gy, (unsigned)p.B);
+            hipLaunchKernelGGL((k_im2col2d<D, MASK>), grid, dim3(256), 0, stream, p, runs);
+        }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const Params q = gemm_args(p, (char *)p.ws + s_bytes(p));
