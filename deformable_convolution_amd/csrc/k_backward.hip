@@ -627,30 +627,6 @@ __global__ void __launch_bounds__(kDwgT, 4) k_bwd_dwg(BwdParams a, int WIN, int 
             WR[k * NHP + h] = dm * f;
         }
     }
-    // offset and mask gradients of the two outputs
-    if (nvalid > 0 && (a.goff || a.gmask)) {
-        if (om_atomic) {
-#pragma unroll
-            for (int q = 0; q < NV; ++q)
-                if (q < nvalid * KT) {
-                    if (a.goff) unsafeAtomicAdd(a.goff + e0 + q, go[q]);
-                    if (a.gmask) unsafeAtomicAdd(a.gmask + e0 + q, gm[q]);
-                }
-        } else if (vec) {
-#pragma unroll
-            for (int q = 0; q < NV; q += 2) {
-                if (a.goff) *(float2 *)(a.goff + e0 + q) = float2{go[q], go[q + 1]};
-                if (a.gmask) *(float2 *)(a.gmask + e0 + q) = float2{gm[q], gm[q + 1]};
-            }
-        } else {
-#pragma unroll
-            for (int q = 0; q < NV; ++q)
-                if (q < nvalid * KT) {
-                    if (a.goff) a.goff[e0 + q] = go[q];
-                    if (a.gmask) a.gmask[e0 + q] = gm[q];
-                }
-        }
-    }
     // ---- phase 1b: halo samples (outputs outside the tile that can reach the owned run)
     {
         const int nleft = l0 - lh0, nright = geo.lh1 - min(l0 + kDwgLT, L_out);
@@ -672,6 +648,31 @@ __global__ void __launch_bounds__(kDwgT, 4) k_bwd_dwg(BwdParams a, int WIN, int 
             I0[k * NHP + h] = reg ? i0 : kIrregular;
             WL[k * NHP + h] = dm * (1.0f - f);
             WR[k * NHP + h] = dm * f;
+        }
+    }
+    // offset and mask gradients of the tile's outputs (stored after the halo's
+    // loads: waiting for a load also waits for the stores issued before it)
+    if (nvalid > 0 && (a.goff || a.gmask)) {
+        if (om_atomic) {
+#pragma unroll
+            for (int q = 0; q < NV; ++q)
+                if (q < nvalid * KT) {
+                    if (a.goff) unsafeAtomicAdd(a.goff + e0 + q, go[q]);
+                    if (a.gmask) unsafeAtomicAdd(a.gmask + e0 + q, gm[q]);
+                }
+        } else if (vec) {
+#pragma unroll
+            for (int q = 0; q < NV; q += 2) {
+                if (a.goff) *(float2 *)(a.goff + e0 + q) = float2{go[q], go[q + 1]};
+                if (a.gmask) *(float2 *)(a.gmask + e0 + q) = float2{gm[q], gm[q + 1]};
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < NV; ++q)
+                if (q < nvalid * KT) {
+                    if (a.goff) a.goff[e0 + q] = go[q];
+                    if (a.gmask) a.gmask[e0 + q] = gm[q];
+                }
         }
     }
     // weight gradient partials: wave sums, then LDS, then one atomic per tap
