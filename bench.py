@@ -102,19 +102,36 @@ def read_traffic(name, kernel, khash):
 
 
 def timed(step, steps, warmup, dev, graph=False):
-    """Run `warmup` untimed steps, then time `steps` of them on the launch
-    stream: one HIP event on the stream before each step and one after the
-    last; step i lasts ev[i] -> ev[i+1] (its kernels run back to back on
-    that stream).  With graph=True the step is also captured once into a HIP
-    graph (torch.cuda.CUDAGraph) and the timed figures are its replays (on
-    this machine eager launches keep the GPU busy and time slightly faster,
-    so the bench uses eager launches); the eager times are always
-    returned."""
+    """Run `warmup` untimed steps (then more, untimed, until 0.2 s have
+    passed), then time `steps` of them on the launch stream, twice: step by
+    step (an event between consecutive steps, for the
+    spread of single steps), then the region (one HIP event on the stream
+    before the first step and one after the last, synchronised on both
+    sides; the figure the bench reports).  With graph=True the step is also captured
+    once into a HIP graph (torch.cuda.CUDAGraph) and the step-by-step
+    figures are its replays."""
     import torch
 
     stream = torch.cuda.current_stream(dev)
     for _ in range(warmup):
         step()
+    # and until the GPU has been busy for a while (its clocks ramp up under
+    # load; a few warm-up steps of a fraction of a millisecond do not)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.2:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+
+    def region(run):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(steps):
+            run()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
 
     def chain(run):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
@@ -126,9 +143,10 @@ def timed(step, steps, warmup, dev, graph=False):
         torch.cuda.synchronize()
         return ev[0].elapsed_time(ev[steps]), [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
 
-    eager_region, eager_ms = chain(step)
+    _, eager_ms = chain(step)
+    region_ms = region(step)
     if not graph:
-        return {"region_ms": eager_region, "launch_ms": eager_ms, "eager_ms": eager_ms, "graph": False}
+        return {"region_ms": region_ms, "launch_ms": eager_ms, "eager_ms": eager_ms, "graph": False}
     side = torch.cuda.Stream(dev)
     side.wait_stream(stream)
     with torch.cuda.stream(side):
@@ -285,17 +303,18 @@ def main_backward(args, w):
     r = run_backward(w, args.steps, args.warmup, baseline=not args.no_cpu_baseline)
     contraction, sampling, nbytes = work_backward(w)
     ms = r["region_ms"] / args.steps
+    kern_ms = float(np.mean(r["launch_ms"]))  # per-launch events, as the kernel trace sees them
     if w.groups == 1:
-        achieved = contraction / (ms * 1e-3) / 1e12
+        achieved = contraction / (kern_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK["mfma_f32_TFLOPs"], "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK["mfma_f32_TFLOPs"], 4)}
     else:
-        achieved = nbytes / (ms * 1e-3) / 1e9
+        achieved = nbytes / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm_GBps"], "unit": "GB/s",
                 "frac": round(achieved / PEAK["hbm_GBps"], 4)}
     roof["traffic"] = read_traffic(w.name, "backward", kernel_hash())
     roof["kernel"] = "backward"
-    roof["kernel_ms"] = round(ms, 5)
+    roof["kernel_ms"] = round(kern_ms, 5)
     line = {
         "metric": "DeformConv1d bwd GFLOP/s (all five gradients)",
         "value": round((contraction + sampling) / (ms * 1e-3) / 1e9, 1),
@@ -397,10 +416,11 @@ def main_packed(args, w):
     r = run_packed(w, args.steps, args.warmup, baseline=not args.no_cpu_baseline)
     flops, pipeline, compulsory = work_packed(w)
     ms = r["region_ms"] / args.steps
-    achieved = pipeline / (ms * 1e-3) / 1e9
+    kern_ms = float(np.mean(r["launch_ms"]))  # per-launch events, as the kernel trace sees them
+    achieved = pipeline / (kern_ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm_GBps"], "unit": "GB/s",
             "frac": round(achieved / PEAK["hbm_GBps"], 4), "traffic": read_traffic(w.name, "packed", kernel_hash()),
-            "kernel": "packed", "kernel_ms": round(ms, 5)}
+            "kernel": "packed", "kernel_ms": round(kern_ms, 5)}
     line = {
         "metric": "Packed DeformConv1d fwd GFLOP/s (offset/mask generator + forward)",
         "value": round(flops / (ms * 1e-3) / 1e9, 1),
@@ -491,11 +511,12 @@ def main2d(args, w):
     r = run2d(w, args.steps, args.warmup, baseline=not args.no_cpu_baseline)
     contraction, sampling, nbytes = work2d(w)
     ms = r["region_ms"] / args.steps
+    kern_ms = float(np.mean(r["launch_ms"]))  # per-launch events, as the kernel trace sees them
     peak = PEAK["mfma_f32_TFLOPs"] if w.dtype == "f32" else PEAK["mfma_bf16_TFLOPs"]
-    achieved = contraction / (ms * 1e-3) / 1e12
+    achieved = contraction / (kern_ms * 1e-3) / 1e12
     roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": read_traffic(w.name, r["kernel"], kernel_hash()),
-            "kernel": r["kernel"], "kernel_ms": round(ms, 5)}
+            "kernel": r["kernel"], "kernel_ms": round(kern_ms, 5)}
     es = 4 if w.dtype == "f32" else 2
     s_bytes = 2 * w.B * (w.C_in // w.groups) * w.kh * w.kw * w.Ho * w.Wo * es  # the sampled matrix, out and back
     line = {

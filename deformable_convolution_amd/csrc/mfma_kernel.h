@@ -370,6 +370,9 @@ __device__ __forceinline__ void mfma_role(const MfmaArgs &a, const Tile &tl, typ
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[mb][nb][q] = 0.0f;
+    // issue priority over the other role's wave on the same SIMD, so that
+    // the matrix unit is fed first and the other role fills the gaps
+    __builtin_amdgcn_s_setprio(2);
 
     if (tl.c_begin < tl.c_end) {
         fetch_w(tl.c_begin);
