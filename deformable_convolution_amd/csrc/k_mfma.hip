@@ -77,8 +77,12 @@ void plan_for(const Params &p, int num_cus, MfmaPlan &pl) {
     // a margin for the offsets' spread.
     const int64_t seg_possible =
         (p.L_out % BN == 0) ? 1 : std::min<int64_t>(NSEG, (BN - 1) / p.L_out + 2);
+    // (+ 2 words per segment: windows staged in 16-byte words start and end
+    // on whole words)
+    constexpr int V = 16 / (int)sizeof(T);
+    const bool vx = p.L_in % V == 0;
     const int64_t want = (int64_t)(std::min<int64_t>(BN, N) - 1) * p.stride +
-                         seg_possible * ((int64_t)(p.K - 1) * p.dilation + 2 + 32);
+                         seg_possible * ((int64_t)(p.K - 1) * p.dilation + 2 + 32 + (vx ? 2 * V : 0));
 
     // ---- channel-block order (preferred): the block size with the fewest
     // padded taps, then the largest whose window fits in LDS
@@ -91,7 +95,9 @@ void plan_for(const Params &p, int num_cus, MfmaPlan &pl) {
             const int nkb = (p.K + tpc - 1) / tpc;
             const int waste = nkb * tpc - p.K;
             if (fixed + 2 * (size_t)cb * slot * NTS * sizeof(T) > lds_cap) continue;
-            const int need = (cb * slot + nkb - 1) / nkb;
+            // staging lines per part: the block's window over its chunks, and
+            // whole words per thread when staging in words
+            const int need = std::max((cb * slot + nkb - 1) / nkb, vx ? V : 1);
             int pick = -1;
             for (int i = 0; i < kNumCbCombos; ++i)
                 if (!kCbCombos[i].dw && kCbCombos[i].cb == cb && kCbCombos[i].slot == slot &&

@@ -90,6 +90,8 @@ struct MfmaArgs {
     float *partials;  // split partial tiles [splits][tiles][BM*BN], or null
     int wt_max;       // window capacity per channel row (elements); 0: always gather
     int vec_w;        // weight rows can be read in aligned 16-byte words
+    int vec_x;        // channel-block order: x rows can be staged in aligned 16-byte words
+                      // (L_in a multiple of the word, x aligned); windows then start on a word
     int off_mask, off_w, off_s, off_x;  // byte offsets of the LDS regions
     // channel-block order only: the reduction runs over ncb blocks of CB
     // input channels (outer) and nkb groups of 32/CB taps (inner); wb holds
@@ -154,6 +156,7 @@ struct TrF32 {
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[j], b.v[j], acc, 0, 0, 0);
     }
+    static __device__ __forceinline__ void st1(float *dst, float v) { *dst = v; }
 };
 
 // fp32 with half the rows per MFMA wave (a 128 x 128 tile): the packed
@@ -196,6 +199,10 @@ struct TrBF16 {
         for (int s = 0; s < 2; ++s)
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf8, a.v[s]),
                                                           __builtin_bit_cast(bf8, b.v[s]), acc, 0, 0, 0);
+    }
+    // one output element, rounded to nearest even by the conversion instruction
+    static __device__ __forceinline__ void st1(uint16_t *dst, float v) {
+        *dst = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xffffu);
     }
 };
 
@@ -432,6 +439,68 @@ __device__ __forceinline__ void mfma_role(const MfmaArgs &a, const Tile &tl, typ
             }
         return;
     }
+    // The bias of this thread's rows is loaded before the first store: a
+    // wait for a load also waits for every store issued before it, so bias
+    // loads between the stores would serialise them on the write latency.
+    float bq[MB][16];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int row = tl.m0 + row0 + 32 * mb + 8 * (q >> 2) + 4 * lh + (q & 3);
+            bq[mb][q] = bias ? D::ld(bias, min(row, M - 1)) : 0.0f;
+        }
+    if (L_out % EPW == 0 && ((uintptr_t)out & 15) == 0) {
+        // Whole 16-byte words of output rows.  A word never straddles a
+        // batch (L_out is a multiple of the word) nor the end of N (nor is
+        // N).  The wave stages each 32-row block of its tile (bias added) in
+        // the LDS that the main loop used, then every lane writes EPW
+        // consecutive columns of one row: 32 / RPI stores per block instead
+        // of one per element.
+        constexpr int WC = 32 * NB, PITCH = WC + 8;  // staging row (floats): rows 4 apart land 32 banks apart
+        constexpr int LPR = WC / EPW, RPI = 64 / LPR;  // lanes per row, rows per store
+        static_assert(NWM * 32 * PITCH * 4 <= 2 * BM * BK * sizeof(T) + 2 * BN * SLD * sizeof(T),
+                      "staging fits in the weight and sample tiles");
+        float *stg = (float *)s_w + wv * 32 * PITCH;
+        const int rl = lane / LPR, cl = (lane % LPR) * EPW;
+        const int col = (int)tl.n0 + col0 + cl;
+        const bool col_ok = col < a.N;
+        const int b = (int)fdiv((uint32_t)(col_ok ? col : 0), a.fd_Lout);
+        T *ob = out + (int64_t)b * M * L_out + (col - b * L_out);
+        // LDS is shared by the wave's lanes only here; fences order each
+        // lane's accesses around the exchange
+        auto wave_sync = [] {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        };
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            wave_sync();  // the previous block's reads are done
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    stg[(8 * (q >> 2) + 4 * lh + (q & 3)) * PITCH + 32 * nb + li] = acc[mb][nb][q] + bq[mb][q];
+            wave_sync();
+#pragma unroll
+            for (int it = 0; it < 32 / RPI; ++it) {
+                const int r = it * RPI + rl;
+                const int row = tl.m0 + row0 + 32 * mb + r;
+                const float *src = stg + r * PITCH + cl;
+                u4 word;
+                if constexpr (EPW == 4) {
+                    word = __builtin_bit_cast(u4, *(const f4 *)src);
+                } else {
+                    const f4 v0 = *(const f4 *)src, v1 = *(const f4 *)(src + 4);
+                    word = u4{pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]), pack_bf16x2(v1[0], v1[1]),
+                              pack_bf16x2(v1[2], v1[3])};
+                }
+                if (col_ok && (m_full || row < M)) *(u4 *)(ob + (int64_t)row * L_out) = word;
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const int col = (int)tl.n0 + col0 + 32 * nb + li;
@@ -444,7 +513,7 @@ __device__ __forceinline__ void mfma_role(const MfmaArgs &a, const Tile &tl, typ
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
                 const int row = tl.m0 + row0 + 32 * mb + 8 * (q >> 2) + 4 * lh + (q & 3);
-                if (row < M) D::st(ob, (int64_t)row * L_out, acc[mb][nb][q] + (bias ? D::ld(bias, row) : 0.0f));
+                if (m_full || row < M) Tr::st1(ob + (int64_t)row * L_out, acc[mb][nb][q] + bq[mb][q]);
             }
     }
 }
@@ -753,10 +822,18 @@ __device__ __forceinline__ void setup_tile(const MfmaArgs &a, Tile &tl, Pos *s_t
     }
     __syncthreads();
     if (t == 0) {
+        constexpr int V = 16 / sizeof(T);  // elements per 16-byte word
         int base = 0;
         for (int z = 0; z < (win ? tl.nseg : 0); ++z) {
+            int len;
+            if (a.vec_x) {  // segments start and end on whole words of x and of the window row
+                s_lo[z] &= -V;
+                len = (s_hi[z] + 2 - s_lo[z] + V - 1) & -V;
+            } else {
+                len = s_hi[z] + 2 - s_lo[z];
+            }
             s_base[z] = base;
-            base += s_hi[z] + 2 - s_lo[z];
+            base += len;
         }
         s_base[win ? tl.nseg : 0] = base;
         // two elements of slack past the last window position (paired reads)
@@ -821,7 +898,7 @@ __global__ void __launch_bounds__(NTT) k_mfma(MfmaArgs a) {
 // the end of one iteration and written to LDS at the end of the next, after
 // its samples, so their latency hides behind a barrier and a sampling pass.
 // Windows are double-buffered by block parity.
-template <class Tr, bool MASK, bool WIN, int CB, int SLOT, int LPP>
+template <class Tr, bool MASK, bool WIN, int CB, int SLOT, int LPP, bool VX = false>
 __device__ __forceinline__ void sampler_cb(const MfmaArgs &a, const Tile &tl, const Pos *s_tab,
                                            const float *s_m, typename Tr::T *s_S, typename Tr::T *s_x,
                                            const int *s_lo, const int *s_base) {
@@ -870,29 +947,70 @@ __device__ __forceinline__ void sampler_cb(const MfmaArgs &a, const Tile &tl, co
     const int colg = (int)tl.n0 + col;
     const T *xcol = x + (colg < a.N ? (int64_t)fdiv((uint32_t)colg, a.fd_Lout) * C_in * L_in : 0);
 
+    // Word staging (VX): a window row is VPR 16-byte words of V elements;
+    // thread ts stages word vv of rows vr, vr + RSTEP, ... of each part.  A
+    // word starts on a multiple of V in x, and L_in is a multiple of V, so it
+    // lies wholly inside [0, L_in) or wholly outside (then zeros).
+    constexpr int V = 16 / sizeof(T);
+    constexpr int VPR = WTM / V;          // words per window row
+    constexpr int RSTEP = NTS / VPR;      // rows between one thread's words
+    constexpr int VPT = VX ? LPP / V : 1;  // words per thread per part
+    static_assert(!VX || (LPP % V == 0 && NTS % VPR == 0), "a part is whole words for every thread");
+    const int vv = ts % VPR, vr = ts / VPR;
+    int64_t vxoff = 0;
+    bool vval = false;
+    if (VX && WIN && vv * V < tl.WT) {
+        const int jj = vv * V;
+        int sg = 0;
+        while (sg + 1 < tl.nseg && s_base[sg + 1] <= jj) ++sg;
+        const int pos = s_lo[sg] + (jj - s_base[sg]);
+        vval = pos >= 0 && pos < L_in;
+        vxoff = (int64_t)(tl.b_first + sg) * C_in * L_in + (vval ? pos : 0);
+    }
+
     // ---- window staging
-    T xreg[LPP];
+    T xreg[VX ? 1 : LPP];
+    u4 vreg[VPT];
     int pend_blk = 0, pend_l0 = NL;  // pending part: lines pend_l0 .. +LPP of block pend_blk
     auto load_part = [&](int blk, int part) {
         pend_blk = blk;
         pend_l0 = part * LPP;
         if (pend_l0 < NL) {  // uniform
             const int ib = pend_l0 / SLOT;
+            if constexpr (VX) {
 #pragma unroll
-            for (int n = 0; n < LPP; ++n) {
-                const int ci = min(blk * CB + ib + n / SLOT, C_in - 1);
-                xreg[n] = x[xoff[n % SLOT] + (int64_t)ci * L_in];
+                for (int n = 0; n < VPT; ++n) {
+                    const int ci = min(blk * CB + ib + vr + RSTEP * n, C_in - 1);
+                    vreg[n] = *(const u4 *)(x + vxoff + (int64_t)ci * L_in);
+                }
+            } else {
+#pragma unroll
+                for (int n = 0; n < LPP; ++n) {
+                    const int ci = min(blk * CB + ib + n / SLOT, C_in - 1);
+                    xreg[n] = x[xoff[n % SLOT] + (int64_t)ci * L_in];
+                }
             }
         }
     };
     auto commit_part = [&]() {
         if (pend_l0 < NL) {  // uniform
-            T *dx = s_x + (pend_blk & 1) * XBUF + (pend_l0 / SLOT) * WTM + ts;
-            const int cib = pend_blk * CB + pend_l0 / SLOT;
+            const int ib = pend_l0 / SLOT;
+            if constexpr (VX) {
+                T *dx = s_x + (pend_blk & 1) * XBUF + vv * V;
 #pragma unroll
-            for (int n = 0; n < LPP; ++n) {
-                const int q = n % SLOT;
-                dx[(n / SLOT) * WTM + NTS * q] = (xval[q] && cib + n / SLOT < C_in) ? xreg[n] : (T)0;
+                for (int n = 0; n < VPT; ++n) {
+                    const int row = ib + vr + RSTEP * n;
+                    const bool ok = vval && pend_blk * CB + row < C_in;
+                    *(u4 *)(dx + row * WTM) = ok ? vreg[n] : u4{0, 0, 0, 0};
+                }
+            } else {
+                T *dx = s_x + (pend_blk & 1) * XBUF + ib * WTM + ts;
+                const int cib = pend_blk * CB + ib;
+#pragma unroll
+                for (int n = 0; n < LPP; ++n) {
+                    const int q = n % SLOT;
+                    dx[(n / SLOT) * WTM + NTS * q] = (xval[q] && cib + n / SLOT < C_in) ? xreg[n] : (T)0;
+                }
             }
         }
         pend_l0 = NL;
@@ -1034,6 +1152,12 @@ __global__ void __launch_bounds__(NTT) k_mfma_cb(MfmaArgs a) {
     if (threadIdx.x < NTM) {
         mfma_role<Tr, DW ? 2 : 1>(a, tl, s_w, s_S);
     } else if (tl.win) {
+        if constexpr (LPP % (16 / sizeof(T)) == 0) {
+            if (a.vec_x) {
+                sampler_cb<Tr, MASK, true, CB, SLOT, LPP, true>(a, tl, s_tab, s_m, s_S, s_x, s_lo, s_base);
+                return;
+            }
+        }
         sampler_cb<Tr, MASK, true, CB, SLOT, LPP>(a, tl, s_tab, s_m, s_S, s_x, s_lo, s_base);
     } else {
         sampler_cb<Tr, MASK, false, CB, 1, 4>(a, tl, s_tab, s_m, s_S, s_x, s_lo, s_base);
@@ -1181,14 +1305,17 @@ __global__ void __launch_bounds__(256) k_split_reduce(MfmaArgs a) {
     const int l = col - b * L_out;
     const T *__restrict__ bias = (const T *)p.bias;
     T *ob = (T *)p.out + (int64_t)b * M * L_out + l;
+    const int row_q = tm * BM + Geo<Tr>::row0(wv) + 32 * mb + 8 * (qq >> 2) + 4 * lh;  // rows row_q + z
+    float bz[4];
+#pragma unroll
+    for (int z = 0; z < 4; ++z) bz[z] = bias ? D::ld(bias, min(row_q + z, M - 1)) : 0.0f;  // before any store
 #pragma unroll
     for (int z = 0; z < 4; ++z) {
-        const int q = qq + z;
-        const int row = tm * BM + Geo<Tr>::row0(wv) + 32 * mb + 8 * (q >> 2) + 4 * lh + (q & 3);
+        const int row = row_q + z;
         if (row >= M) continue;
-        const float val = tot[z] + (bias ? D::ld(bias, row) : 0.0f);
+        const float val = tot[z] + bz[z];
         if constexpr (OUT == 0)
-            D::st(ob, (int64_t)row * L_out, val);
+            Tr::st1(ob + (int64_t)row * L_out, val);
         else
             store_head<Tr, OUT>(p, b, l, row, val);
     }
@@ -1264,6 +1391,7 @@ hipError_t launch_for(const Params &p, const MfmaPlan &pl, hipStream_t stream) {
     a.off_x = pl.off_x;
     const int vec_elems = 16 / (int)sizeof(T);
     a.vec_w = (p.Kred % vec_elems == 0) && (((uintptr_t)p.w & 15) == 0);
+    a.vec_x = pl.blocked && (p.L_in % vec_elems == 0) && (((uintptr_t)p.x & 15) == 0);
     a.wb = nullptr;
     a.ncb = pl.ncb;
     a.nkb = pl.nkb;

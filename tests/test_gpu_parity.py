@@ -114,6 +114,11 @@ def _shape_cases():
         (1, 48, 40, 700, 5, 1, 2, 1, 1, 6, "bf16", False, 3.0),     # bf16 channel blocks of 16
         (3, 100, 72, 150, 3, 2, 1, 1, 1, 1, "f32", True, 2.5),      # C_in not a multiple of the block
         (1, 64, 64, 600, 3, 1, 1, 1, 1, 1, "f32", False, 2.0),      # f32 K=3, long rows
+        # rows staged in 16-byte words (L_in a multiple of the word): tiles over
+        # several batches, ragged channel blocks, windows past both ends
+        (3, 40, 64, 96, 3, 1, 1, 1, 1, 1, "bf16", True, 5.0),       # bf16 blocks of 16, 40 channels
+        (2, 64, 96, 1024, 3, 2, 1, 1, 1, 2, "bf16", True, 8.0),     # bf16 stride 2, two-slot window
+        (4, 24, 40, 52, 4, 1, 2, 2, 1, 1, "f32", False, 6.0),       # f32, 50 columns per batch
     ]
     for i, (B, C_in, C_out, L_in, K, s, p, d, groups, G, dt, mask, sc) in enumerate(spec):
         L_out = oracle.output_length(L_in, K, s, p, d)
