@@ -291,12 +291,14 @@ __device__ __forceinline__ void mfma_role(const MfmaArgs &a, const Tile &tl, typ
     const T *__restrict__ w = (const T *)p.w;
     const bool m_full = tl.m0 + BM <= M;  // no rows past C_out in this tile
 
-    // The weight tile of chunk c+1 is loaded into registers at the start of
-    // iteration c and written to LDS after chunk c's MFMAs, so its load
-    // latency hides under them.  Loads never wait on a bounds test: words
-    // outside the matrix load a clamped address and are zeroed in commit_w.
-    u4 wreg[WV];
-    auto fetch_w = [&](int cw) {
+    // The weight tile of chunk c+1 is written to LDS after chunk c's MFMAs.
+    // With two register sets (W2: the bf16 tile's 4 words per thread) its
+    // loads were issued an iteration earlier, so their latency hides under
+    // two chunks of MFMAs; fp32 tiles (8 words) load at the start of
+    // iteration c.  Loads never wait on a bounds test: words outside the
+    // matrix load a clamped address and are zeroed in commit_w.
+    constexpr bool W2 = WV <= 4;
+    auto fetch_w = [&](int cw, u4 (&wreg)[WV]) {
         const int r0 = cw * BK;
         if (WL == 1) {
             const int cb = (int)fdiv((uint32_t)cw, a.fd_nkb), kb = cw - cb * a.nkb;
@@ -346,7 +348,7 @@ __device__ __forceinline__ void mfma_role(const MfmaArgs &a, const Tile &tl, typ
     };
     // registers -> LDS (swizzled words).  Tiles wholly inside the matrix
     // store without tests.
-    auto commit_w = [&](int cw) {
+    auto commit_w = [&](int cw, const u4 (&wreg)[WV]) {
         T *dw = s_w + (cw & 1) * BM * BK;
         const int r0 = cw * BK;
         const int cb = WL == 2 ? (int)fdiv((uint32_t)cw, a.fd_nkb) : 0;
@@ -381,16 +383,22 @@ __device__ __forceinline__ void mfma_role(const MfmaArgs &a, const Tile &tl, typ
     // the matrix unit is fed first and the other role fills the gaps
     __builtin_amdgcn_s_setprio(2);
 
+    u4 wA[WV], wB[WV];
     if (tl.c_begin < tl.c_end) {
-        fetch_w(tl.c_begin);
-        commit_w(tl.c_begin);
+        fetch_w(tl.c_begin, wA);
+        commit_w(tl.c_begin, wA);
     }
+    if (W2 && tl.c_begin + 1 < tl.c_end) fetch_w(tl.c_begin + 1, wA);
     // prologue barriers shared with the sampler role: staging done, first sample tile done
     __syncthreads();
     __syncthreads();
-    for (int c = tl.c_begin; c < tl.c_end; ++c) {
-        const bool more = c + 1 < tl.c_end;
-        if (more) fetch_w(c + 1);
+    // chunk c: `cur` holds (W2) or receives chunk c+1's weights, `nxt` receives chunk c+2's (W2)
+    auto step = [&](int c, u4 (&cur)[WV], u4 (&nxt)[WV]) {
+        if constexpr (W2) {
+            if (c + 2 < tl.c_end) fetch_w(c + 2, nxt);
+        } else {
+            if (c + 1 < tl.c_end) fetch_w(c + 1, cur);
+        }
         const T *tile = s_w + (c & 1) * BM * BK;
         const T *st = s_S + (c & 1) * BN * SLD;
         Frag bf[NB];
@@ -403,8 +411,16 @@ __device__ __forceinline__ void mfma_role(const MfmaArgs &a, const Tile &tl, typ
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) Tr::mma(af, bf[nb], acc[mb][nb]);
         }
-        if (more) commit_w(c + 1);
+        if (c + 1 < tl.c_end) commit_w(c + 1, cur);
         __syncthreads();
+    };
+    if constexpr (W2) {
+        for (int c = tl.c_begin; c < tl.c_end; c += 2) {
+            step(c, wA, wB);
+            if (c + 1 < tl.c_end) step(c + 1, wB, wA);
+        }
+    } else {
+        for (int c = tl.c_begin; c < tl.c_end; ++c) step(c, wA, wA);
     }
 
     // ---- epilogue
@@ -969,56 +985,70 @@ __device__ __forceinline__ void sampler_cb(const MfmaArgs &a, const Tile &tl, co
     }
 
     // ---- window staging
-    T xreg[VX ? 1 : LPP];
-    u4 vreg[VPT];
-    int pend_blk = 0, pend_l0 = NL;  // pending part: lines pend_l0 .. +LPP of block pend_blk
-    auto load_part = [&](int blk, int part) {
-        pend_blk = blk;
-        pend_l0 = part * LPP;
-        if (pend_l0 < NL) {  // uniform
-            const int ib = pend_l0 / SLOT;
+    // A part in flight: lines l0 .. l0+LPP-1 of block blk (l0 >= NL: none),
+    // loaded into registers and written to LDS later by commit_part.
+    struct Part {
+        int blk, l0;
+        T xr[VX ? 1 : LPP];
+        u4 v[VPT];
+    };
+    auto load_part = [&](Part &q, int blk, int part) {
+        q.blk = blk;
+        q.l0 = part * LPP;
+        if (q.l0 < NL) {  // uniform
+            const int ib = q.l0 / SLOT;
             if constexpr (VX) {
 #pragma unroll
                 for (int n = 0; n < VPT; ++n) {
                     const int ci = min(blk * CB + ib + vr + RSTEP * n, C_in - 1);
-                    vreg[n] = *(const u4 *)(x + vxoff + (int64_t)ci * L_in);
+                    q.v[n] = *(const u4 *)(x + vxoff + (int64_t)ci * L_in);
                 }
             } else {
 #pragma unroll
                 for (int n = 0; n < LPP; ++n) {
                     const int ci = min(blk * CB + ib + n / SLOT, C_in - 1);
-                    xreg[n] = x[xoff[n % SLOT] + (int64_t)ci * L_in];
+                    q.xr[n] = x[xoff[n % SLOT] + (int64_t)ci * L_in];
                 }
             }
         }
     };
-    auto commit_part = [&]() {
-        if (pend_l0 < NL) {  // uniform
-            const int ib = pend_l0 / SLOT;
+    auto commit_part = [&](Part &q) {
+        if (q.l0 < NL) {  // uniform
+            const int ib = q.l0 / SLOT;
             if constexpr (VX) {
-                T *dx = s_x + (pend_blk & 1) * XBUF + vv * V;
+                T *dx = s_x + (q.blk & 1) * XBUF + vv * V;
 #pragma unroll
                 for (int n = 0; n < VPT; ++n) {
                     const int row = ib + vr + RSTEP * n;
-                    const bool ok = vval && pend_blk * CB + row < C_in;
-                    *(u4 *)(dx + row * WTM) = ok ? vreg[n] : u4{0, 0, 0, 0};
+                    const bool ok = vval && q.blk * CB + row < C_in;
+                    *(u4 *)(dx + row * WTM) = ok ? q.v[n] : u4{0, 0, 0, 0};
                 }
             } else {
-                T *dx = s_x + (pend_blk & 1) * XBUF + ib * WTM + ts;
-                const int cib = pend_blk * CB + ib;
+                T *dx = s_x + (q.blk & 1) * XBUF + ib * WTM + ts;
+                const int cib = q.blk * CB + ib;
 #pragma unroll
                 for (int n = 0; n < LPP; ++n) {
-                    const int q = n % SLOT;
-                    dx[(n / SLOT) * WTM + NTS * q] = (xval[q] && cib + n / SLOT < C_in) ? xreg[n] : (T)0;
+                    const int qq = n % SLOT;
+                    dx[(n / SLOT) * WTM + NTS * qq] = (xval[qq] && cib + n / SLOT < C_in) ? q.xr[n] : (T)0;
                 }
             }
         }
-        pend_l0 = NL;
+        q.l0 = NL;
     };
+    Part q0, q1;  // the parts of the next two chunks (see the main loop)
+    q0.blk = q1.blk = 0;
+    q0.l0 = q1.l0 = NL;
     auto stage_block = [&](int blk) {
         for (int part = 0; part * LPP < NL; ++part) {
-            load_part(blk, part);
-            commit_part();
+            load_part(q0, blk, part);
+            commit_part(q0);
+        }
+    };
+    // part kb(u) of the block after chunk u's, if this workgroup uses that block
+    auto load_for = [&](Part &q, int u) {
+        if (u < tl.c_end) {
+            const int bu = (int)fdiv((uint32_t)u, a.fd_nkb);
+            if ((bu + 1) * nkb < tl.c_end) load_part(q, bu + 1, u - bu * nkb);
         }
     };
 
@@ -1097,9 +1127,14 @@ __device__ __forceinline__ void sampler_cb(const MfmaArgs &a, const Tile &tl, co
     };
 
     const int c0 = tl.c_begin, c1 = tl.c_end;
+    // Staging schedule: the part P(u) (part kb(u) of the block after chunk
+    // u's) is loaded into registers in iteration u-3 and written to LDS in
+    // iteration u-1, after that iteration's samples: its loads have two
+    // iterations to arrive.  The two parts in flight alternate between q0
+    // and q1 (P(u) in q[(u - c0) & 1]).
     // Prologue: the windows of the blocks of chunks c0 and c0+1 in LDS; the
     // parts of the following block that the steady state would already have
-    // staged, in LDS, and its next part loaded into registers.
+    // written, in LDS; P(c0+1) and P(c0+2) in flight.
     if (WIN && c0 < c1) {
         const int b0 = (int)fdiv((uint32_t)c0, a.fd_nkb);
         stage_block(b0);
@@ -1108,31 +1143,29 @@ __device__ __forceinline__ void sampler_cb(const MfmaArgs &a, const Tile &tl, co
             if (b1 != b0) stage_block(b1);
             if ((b1 + 1) * nkb < c1) {
                 for (int part = 0; part < k1; ++part) {
-                    load_part(b1 + 1, part);
-                    commit_part();
+                    load_part(q0, b1 + 1, part);
+                    commit_part(q0);
                 }
-                load_part(b1 + 1, k1);
             }
+            load_for(q1, c0 + 1);
+            load_for(q0, c0 + 2);
         }
     }
     __syncthreads();
     if (c0 < c1) sample(c0);
     __syncthreads();
-    for (int c = c0; c < c1; ++c) {
+    // iteration c: the samples of chunk c+1, then P(c+1) to LDS and P(c+3) loaded, both in q
+    auto iter = [&](int c, Part &q) {
         if (c + 1 < c1) sample(c + 1);
         if (WIN) {
-            // The part loaded in the previous iteration (for the block after
-            // chunk c+1's) goes to LDS only now, after this iteration's
-            // samples, so its loads had a whole iteration to arrive.  Then
-            // part kb(c+2) of the block after chunk c+2's, if this workgroup
-            // uses it.
-            commit_part();
-            if (c + 2 < c1) {
-                const int b2 = (int)fdiv((uint32_t)(c + 2), a.fd_nkb);
-                if ((b2 + 1) * nkb < c1) load_part(b2 + 1, c + 2 - b2 * nkb);
-            }
+            commit_part(q);
+            load_for(q, c + 3);
         }
         __syncthreads();
+    };
+    for (int c = c0; c < c1; c += 2) {
+        iter(c, q1);
+        if (c + 1 < c1) iter(c + 1, q0);
     }
 }
 
