@@ -233,7 +233,9 @@ struct Tile {
 // [0, G*K) as OUT 1 and rows G*K + g*K + k to the mask tensor (p.mask, same
 // shape) through the logistic sigmoid.  OUT 0 is the convolution's
 // [B][M][L_out].
-__device__ __forceinline__ float sigmoid(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// (the reciprocal instruction, within an ulp, instead of a full division:
+// the write-out of the mask head is arithmetic-bound otherwise)
+__device__ __forceinline__ float sigmoid(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // Destination row (b, g) of the run of L_out*K elements that holds head
 // group gg (offset group gg, or mask group gg - G), and whether it is a

@@ -8,7 +8,8 @@ Tolerances, elementwise, derived from the arithmetic:
 * mask = sigmoid(z), z like an offset: tol_m = tol_o / 4 + 2^-20 (the
   sigmoid's slope is at most 1/4; the GPU's exponential, exp2 of z*log2(e),
   is off by about (|z| + 2) * 2^-24 relatively, which the sigmoid scales by
-  s(1 - s) <= 1/4, plus the final add and divide);
+  s(1 - s) <= 1/4, plus the final add and the reciprocal instruction,
+  within an ulp);
 * out: the forward's tolerance 1e-5 * sqrt(cpg*K) * max(rms(out), 1) plus
   the effect of the generated inputs' errors through the interpolation,
   which is Lipschitz in the position with constant |x(i0+1) - x(i0)| <= 2 max|x|:
@@ -79,6 +80,10 @@ def shapes():
         (1, 512, 32, 64, 3, 1, 1, 1, 1, 8, True),      # long head reduction: split head GEMM
         (2, 24, 48, 300, 7, 3, 5, 1, 24, 6, True),     # depthwise multiplier, G < C_in
         (5, 40, 40, 129, 4, 1, 0, 3, 40, 40, False),   # ragged tiles, even K
+        # more head tiles than CUs (the persistent head GEMM walks several per
+        # workgroup): ragged columns; two row blocks with a ragged second
+        (3, 32, 32, 12001, 3, 1, 1, 1, 32, 16, True),
+        (2, 50, 50, 9000, 3, 1, 1, 1, 50, 25, True),
     ]
     out = []
     for i, (B, C_in, C_out, L_in, K, s, p, d, groups, G, mod) in enumerate(spec):
