@@ -483,6 +483,8 @@ constexpr int kDwgOpt = 1;      // outputs per thread
 constexpr int kDwgLT = kDwgT * kDwgOpt;
 constexpr int kDwgR = 16;       // largest |floor(offset)| gathered
 constexpr int kDwgMargin = 24;  // x window margin (>= kDwgR + 2)
+constexpr int kDwgTail = 2 * kDwgR + 4;  // sentinel entries after each tap's filled outputs (phase 2
+                                         // reads up to (2 kDwgR + 2) + 2 candidates from the last one)
 constexpr int kIrregular = INT_MIN / 2;
 
 __device__ __forceinline__ int floor_div(int a, int b) {
@@ -530,6 +532,13 @@ __global__ void __launch_bounds__(kDwgT, 4) k_bwd_dwg(BwdParams a, int WIN, int 
     for (int j = threadIdx.x; j < WIN; j += kDwgT) {
         const int pos = lo + j;
         xs[j] = (pos >= 0 && pos < L_in) ? xrow[pos] : 0.0f;
+    }
+    {  // entries past the filled outputs match no position
+        const int nhl = geo.lh1 - lh0;
+        for (int e = threadIdx.x; e < KT * NHP; e += kDwgT) {
+            const int k = e / NHP, h = e - k * NHP;
+            if (h >= nhl) I0[e] = kIrregular;
+        }
     }
     if (threadIdx.x < KT) wred[threadIdx.x] = 0.0f;
     if (threadIdx.x == 0) {
@@ -698,39 +707,41 @@ __global__ void __launch_bounds__(kDwgT, 4) k_bwd_dwg(BwdParams a, int WIN, int 
     const int R = s_R;
     const int nhl = geo.lh1 - lh0;
     float *__restrict__ gxr = a.gx + (int64_t)row * L_in;
-    // candidates per tap: outputs l with l*s in [t - 1 - R, t + R]; a uniform
-    // trip count (the largest any lane has) in groups of four, so that the
-    // LDS reads of a group are in flight together
-    const int ncand = (2 * R + 1) / p.stride + 2;
-    for (int i = geo.i_lo + threadIdx.x; i < geo.i_hi; i += kDwgT) {
-        float acc = 0.0f;
+    // A thread owns two consecutive positions i, i+1.  Candidates per tap:
+    // outputs l with l*s in [t - 1 - R, t + 1 + R] (a sample whose left
+    // neighbour is i - 1, i or i + 1 with |floor(offset)| <= R has its grid
+    // position in that range), at most (2R + 2)/s + 1 of them; a uniform
+    // trip count (the largest any lane has) in pairs, so that the LDS reads
+    // of a pair are in flight together.  The run read starts at the range's
+    // first output clamped to [0, filled outputs]: outputs outside the range
+    // cannot match, and past the filled ones sit sentinels (kDwgTail of
+    // them), so no read needs a bounds test.  Each position's terms are
+    // added in the same order as one position per thread would (taps, then
+    // outputs).
+    const int ncand = (2 * R + 2) / p.stride + 1;
+    for (int i = geo.i_lo + 2 * threadIdx.x; i < geo.i_hi; i += 2 * kDwgT) {
+        float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll 1
         for (int k = 0; k < KT; ++k) {
             const int t = i + p.padding - k * p.dilation;  // l*s for i0 == i with floor(offset) 0
-            const int hmin = -floor_div(-(t - 1 - R), p.stride) - lh0;
-            const int hmax = min(floor_div(t + R, p.stride) - lh0, nhl - 1);
-            const int *__restrict__ i0k = I0 + k * NHP;
-            const float *__restrict__ wlk = WL + k * NHP, *__restrict__ wrk = WR + k * NHP;
-            for (int m0 = 0; m0 < ncand; m0 += 4) {
-                int v[4];
-                float wl[4], wr[4];
+            const int h0 = min(max(-floor_div(-(t - 1 - R), p.stride) - lh0, 0), nhl);
+            const int *__restrict__ i0k = I0 + k * NHP + h0;
+            const float *__restrict__ wlk = WL + k * NHP + h0, *__restrict__ wrk = WR + k * NHP + h0;
+            for (int m0 = 0; m0 < ncand; m0 += 2) {
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int h = hmin + m0 + u;
-                    const bool ok = h >= 0 && h <= hmax;
-                    const int hc = ok ? h : 0;
-                    v[u] = ok ? i0k[hc] : kIrregular;
-                    wl[u] = wlk[hc];
-                    wr[u] = wrk[hc];
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    acc += v[u] == i ? wl[u] : 0.0f;
-                    acc += v[u] == i - 1 ? wr[u] : 0.0f;
+                for (int u = 0; u < 2; ++u) {
+                    const int v = i0k[m0 + u];
+                    const float wl = wlk[m0 + u], wr = wrk[m0 + u];
+                    const bool e0 = v == i;
+                    acc0 += e0 ? wl : 0.0f;
+                    acc0 += v == i - 1 ? wr : 0.0f;
+                    acc1 += v == i + 1 ? wl : 0.0f;
+                    acc1 += e0 ? wr : 0.0f;
                 }
             }
         }
-        gxr[i] = acc;
+        gxr[i] = acc0;
+        if (i + 1 < geo.i_hi) gxr[i + 1] = acc1;
     }
 }
 
@@ -867,7 +878,8 @@ DwgPlan plan_dwg(const Params &p) {
     int64_t win = (LT - 1) * s + span + kDwgR + kDwgMargin + 4;
     win = (win + 63) / 64 * 64;
     const int64_t nh = LT + (span + kDwgR + 1 + s - 1) / s + kDwgR / s + 2;
-    const int64_t nhp = (nh + 31) / 32 * 32 + 1;  // pitch = 1 (mod 32): taps on distinct banks
+    // pitch = 1 (mod 32): taps on distinct banks; room for the sentinels
+    const int64_t nhp = (nh + kDwgTail + 31) / 32 * 32 + 1;
     DwgPlan pl = {0, 0, 0};
     const size_t lds = ((size_t)win + 3 * (size_t)p.K * nhp) * 4;
     if (lds <= kDwgLds && win >= 2) pl = {(int)win, (int)nhp, lds};

@@ -73,6 +73,8 @@ def fp32_shapes():
         (2, 16, 16, 300, 3, 2, 1, 1, 16, 16, True, 3.0),     # depthwise, strided (gathered grad_x)
         (1, 8, 8, 700, 9, 1, 4, 24, 8, 8, True, 5.0),       # depthwise, wide dilation (scattered grad_x)
         (1, 4, 4, 1500, 5, 1, 2, 2, 4, 4, False, 20.0),     # depthwise, some samples moved > 16 (fix pass)
+        (2, 16, 16, 1100, 7, 1, 9, 3, 16, 16, True, 6.0),   # depthwise, wide padding, three gather tiles
+        (2, 12, 12, 905, 4, 3, 5, 2, 12, 4, False, 7.0),    # depthwise, stride 3, offsets shared by 3 channels
     ]
     for i, (B, C_in, C_out, L_in, K, s, p, d, groups, G, mask, sc) in enumerate(spec):
         L_out = oracle.output_length(L_in, K, s, p, d)
