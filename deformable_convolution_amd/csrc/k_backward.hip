@@ -732,11 +732,10 @@ __global__ void __launch_bounds__(kDwgT, 4) k_bwd_dwg(BwdParams a, int WIN, int 
                 for (int u = 0; u < 2; ++u) {
                     const int v = i0k[m0 + u];
                     const float wl = wlk[m0 + u], wr = wrk[m0 + u];
+                    // at most one of a position's two terms is nonzero
                     const bool e0 = v == i;
-                    acc0 += e0 ? wl : 0.0f;
-                    acc0 += v == i - 1 ? wr : 0.0f;
-                    acc1 += v == i + 1 ? wl : 0.0f;
-                    acc1 += e0 ? wr : 0.0f;
+                    acc0 += e0 ? wl : (v == i - 1 ? wr : 0.0f);
+                    acc1 += e0 ? wr : (v == i + 1 ? wl : 0.0f);
                 }
             }
         }
