@@ -24,7 +24,8 @@
 //                    k_bwd_samples (a loop over the group's output channels);
 //                    dS is [B][C_in][K][L_out] in the workspace;
 //   samples          for the weight gradient: k_bwd_samples_t writes them in
-//                    the weight GEMM's layout [(b, l)][C_in*K] (dense), or
+//                    the weight GEMM's layout [(b, l)][C_in*K] (dense, one
+//                    workgroup per row), or
 //                    k_bwd_samples beside dS as [B][C_in][K][L_out];
 //   k_bwd_dx         grad_x, grad_offsets, grad_mask from dS (tiled, LDS
 //                    windows);
@@ -123,31 +124,33 @@ __global__ void __launch_bounds__(256) k_bwd_bias(BwdParams a) {
 
 // Dense path (groups == 1): dS = W^T dout and grad_weight = dout S^T are
 // two plain GEMMs on the MFMA kernel.  This kernel writes the samples for
-// the weight gradient in the GEMM's layout [(b, l)][ci*K + k] (one thread
-// per element, (ci, k) fastest).
-__global__ void __launch_bounds__(256) k_bwd_samples_t(BwdParams a) {
+// the weight gradient in the GEMM's layout [(b, l)][ci*K + k]: a workgroup
+// per row (b, l) (grid-stride), (ci, k) fastest, 32-bit index arithmetic
+// inside a row.
+__global__ void __launch_bounds__(256) k_bwd_samples_t(BwdParams a, FastDiv fd_K, FastDiv fd_cpo) {
     const Params &p = a.p;
-    const float *__restrict__ x = (const float *)p.x;
     const float *__restrict__ off = (const float *)p.off;
     const float *__restrict__ mask = (const float *)p.mask;
-    const int CK = p.C_in * p.K;
-    const int64_t n = (int64_t)p.B * p.L_out * CK;
-    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
-        const int r = (int)(e % CK);
-        const int64_t bl = e / CK;
-        const int l = (int)(bl % p.L_out);
-        const int b = (int)(bl / p.L_out);
-        const int ci = r / p.K, k = r - ci * p.K, g = ci / p.cpo;
-        const int64_t oi = (((int64_t)b * p.G + g) * p.L_out + l) * p.K + k;
-        int i0;
-        float f;
-        split_position(off[oi], l * p.stride - p.padding + k * p.dilation, tap_range(p, k), i0, f);
-        const float m = mask ? mask[oi] : 1.0f;
-        const float *xrow = x + ((int64_t)b * p.C_in + ci) * p.L_in;
-        const bool v0 = i0 >= 0 && i0 < p.L_in, v1 = i0 + 1 >= 0 && i0 + 1 < p.L_in;
-        if (a.S) {
-            const float x0 = v0 ? xrow[i0] : 0.0f, x1 = v1 ? xrow[i0 + 1] : 0.0f;
-            a.S[e] = fmaf(f, x1 - x0, x0) * m;
+    const int K = p.K, CK = p.C_in * K, L_in = p.L_in;
+    const int64_t rows = (int64_t)p.B * p.L_out;
+    for (int64_t bl = blockIdx.x; bl < rows; bl += gridDim.x) {
+        const int b = (int)(bl / p.L_out), l = (int)(bl - (int64_t)b * p.L_out);
+        const float *__restrict__ xb = (const float *)p.x + (int64_t)b * p.C_in * L_in;
+        const int64_t orow = (int64_t)b * p.G * p.L_out + l;  // offsets row (b, g = 0) at l
+        const int base0 = l * p.stride - p.padding;
+        float *__restrict__ dst = a.S + bl * CK;
+        for (int r = threadIdx.x; r < CK; r += 256) {
+            const int ci = (int)fdiv((uint32_t)r, fd_K), k = r - ci * K;
+            const int g = (int)fdiv((uint32_t)ci, fd_cpo);
+            const int64_t oi = (orow + (int64_t)g * p.L_out) * K + k;
+            int i0;
+            float f;
+            split_position(off[oi], base0 + k * p.dilation, tap_range(p, k), i0, f);
+            const float m = mask ? mask[oi] : 1.0f;
+            const float *__restrict__ xrow = xb + (int64_t)ci * L_in;
+            const float x0 = (i0 >= 0 && i0 < L_in) ? xrow[i0] : 0.0f;
+            const float x1 = (i0 + 1 >= 0 && i0 + 1 < L_in) ? xrow[i0 + 1] : 0.0f;
+            dst[r] = fmaf(f, x1 - x0, x0) * m;
         }
     }
 }
@@ -1021,7 +1024,9 @@ hipError_t launch_backward(BwdParams a, int num_cus, hipStream_t stream) {
             const hipError_t e = launch_gemm_f32(gemm_ds(p, wt, a.dout, a.dS, ws + L.part), p.L_out,
                                                  (int64_t)p.C_out * p.L_out, 0, num_cus, stream);
             if (e != hipSuccess) return e;
-            if (s.S) hipLaunchKernelGGL(k_bwd_samples_t, dim3(grid_for(n)), dim3(256), 0, stream, s);
+            if (s.S && (int64_t)p.B * p.L_out > 0)
+                hipLaunchKernelGGL(k_bwd_samples_t, dim3((unsigned)std::min<int64_t>((int64_t)p.B * p.L_out, 1 << 20)),
+                                   dim3(256), 0, stream, s, make_fastdiv((uint32_t)p.K), make_fastdiv((uint32_t)p.cpo));
         } else {
             hipLaunchKernelGGL(k_bwd_samples, dim3(grid_for(n)), dim3(256), 0, stream, s);
         }
