@@ -166,6 +166,41 @@ def test_weights_read_in_place_or_rearranged():
     check(w, gpu_forward(w, dict(g, weight=wv)), ref, "misaligned weights")
 
 
+def _misaligned_copy(t):
+    """The same values at a device address that is not 16-byte aligned."""
+    buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=DEV)
+    v = buf[1:].view(t.shape)
+    v.copy_(t)
+    assert v.data_ptr() % 16 != 0
+    return v
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_unaligned_input_and_output_take_the_element_paths(dtype):
+    """x rows are staged in 16-byte words and the output written in 16-byte
+    words only when the pointers allow; a misaligned x (element staging) and
+    a misaligned output (element stores) give the same bits."""
+    # enough column tiles to fill the GPU without a split reduction (the
+    # direct epilogue)
+    w = inputs.custom("align_" + dtype, B=4, C_in=64, C_out=96, L_in=8192, K=3, padding=1, G=2, L_out=8192,
+                      dtype=dtype, off_dist=("uniform", -5.0, 5.0), mask_dist=("sigmoid_normal", 0.0, 1.0))
+    t = inputs.make_inputs(w, seed=8)
+    g = to_dev(t)
+    kw = dict(stride=w.stride, padding=w.padding, dilation=w.dilation, groups=w.groups)
+    pl = dc1d.plan(g["x"], g["offsets"], g["weight"], g["bias"], g["mask"], **kw)
+    assert pl["kernel"].startswith("mfma_") and pl["splits"] == 1, pl
+    ref = oracle_forward(w, t)
+    a = gpu_forward(w, g)
+    xm = _misaligned_copy(g["x"])
+    b = gpu_forward(w, dict(g, x=xm))
+    om = _misaligned_copy(torch.zeros_like(a))
+    dc1d.forward(g["x"], g["offsets"], g["weight"], g["bias"], g["mask"], out=om, **kw)
+    torch.cuda.synchronize()
+    check(w, a, ref, "aligned")
+    assert torch.equal(a, b), "misaligned x"
+    assert torch.equal(a, om), "misaligned out"
+
+
 # ---- positions: bit-exact ---------------------------------------------------
 
 def _adversarial_offsets(shape, seed):
