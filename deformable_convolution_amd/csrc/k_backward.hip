@@ -514,7 +514,8 @@ __device__ __forceinline__ DwgGeo dwg_geo(const Params &p, int tile, int tiles_l
 }
 
 template <int KT>
-__global__ void __launch_bounds__(kDwgT, 4) k_bwd_dwg(BwdParams a, int WIN, int NHP, int tiles_l, int *flag) {
+__global__ void __launch_bounds__(kDwgT, 4) k_bwd_dwg(BwdParams a, int WIN, int NHP, int tiles_l, int *flag,
+                                                      bool bias_here) {
     const Params &p = a.p;
     extern __shared__ float smem[];
     float *xs = smem;                          // [WIN]
@@ -522,6 +523,7 @@ __global__ void __launch_bounds__(kDwgT, 4) k_bwd_dwg(BwdParams a, int WIN, int 
     float *WL = smem + WIN + KT * NHP;         // [KT][NHP]
     float *WR = smem + WIN + 2 * KT * NHP;     // [KT][NHP]
     __shared__ float wred[KT];
+    __shared__ float s_bsum;  // the block's share of grad_bias (bias_here)
     __shared__ int s_R, s_irr;
     const int L_in = p.L_in, L_out = p.L_out;
     const int tile = blockIdx.x % tiles_l;
@@ -544,6 +546,7 @@ __global__ void __launch_bounds__(kDwgT, 4) k_bwd_dwg(BwdParams a, int WIN, int 
         }
     }
     if (threadIdx.x < KT) wred[threadIdx.x] = 0.0f;
+    if (threadIdx.x == 0) s_bsum = 0.0f;
     if (threadIdx.x == 0) {
         s_R = 0;
         s_irr = 0;
@@ -696,6 +699,13 @@ __global__ void __launch_bounds__(kDwgT, 4) k_bwd_dwg(BwdParams a, int WIN, int 
             if ((threadIdx.x & 63) == 0) atomicAdd(wred + k, v);
         }
     }
+    if (bias_here) {  // grad_bias[c]: this block's outputs' dout, summed
+        float v = 0.0f;
+#pragma unroll
+        for (int o = 0; o < kDwgOpt; ++o) v += (o < nvalid) ? dv[o] : 0.0f;
+        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+        if ((threadIdx.x & 63) == 0) atomicAdd(&s_bsum, v);
+    }
     for (int o = 32; o > 0; o >>= 1) rmax = max(rmax, __shfl_xor(rmax, o));
     const bool irr_w = __any(irregular);
     if ((threadIdx.x & 63) == 0) {
@@ -704,6 +714,7 @@ __global__ void __launch_bounds__(kDwgT, 4) k_bwd_dwg(BwdParams a, int WIN, int 
     }
     __syncthreads();
     if (a.gw && threadIdx.x < KT) unsafeAtomicAdd(a.gw + (int64_t)c * KT + threadIdx.x, wred[threadIdx.x]);
+    if (bias_here && threadIdx.x == 0) unsafeAtomicAdd(a.gb + c, s_bsum);
     if (threadIdx.x == 0 && s_irr) atomicOr(flag, 1);
     if (!a.gx) return;
     // ---- phase 2: the owned positions, gathered
@@ -925,7 +936,8 @@ size_t backward_workspace_bytes(const Params &p, bool want_weight, int num_cus) 
     return layout(p, want_weight, num_cus).total;
 }
 
-hipError_t launch_backward_dw(BwdParams a, int *flag, hipStream_t stream) {
+hipError_t launch_backward_dw(BwdParams a, int *flag, hipStream_t stream, bool *bias_done) {
+    if (bias_done) *bias_done = false;
     const Params &p = a.p;
     const int LT = 256 * kDwbOpt;
     const int tiles_l = (p.L_out + LT - 1) / LT;
@@ -953,10 +965,15 @@ hipError_t launch_backward_dw(BwdParams a, int *flag, hipStream_t stream) {
         const int tiles_g = (p.L_out + kDwgLT - 1) / kDwgLT;
         const dim3 grid((unsigned)((int64_t)p.B * p.C_in * tiles_g));
         hipLaunchKernelGGL(k_bwd_zero, dim3(1), dim3(256), 0, stream, (float *)flag, (int64_t)1);
+        // grad_bias from the dout the pass reads anyway (C_out == C_in here)
+        const bool bias_here = a.gb != nullptr;
+        if (bias_here) hipLaunchKernelGGL(k_bwd_zero, dim3(grid_for(p.C_out)), dim3(256), 0, stream, a.gb, (int64_t)p.C_out);
+        if (bias_done) *bias_done = bias_here;
         switch (p.K) {
 #define DC1D_BDWG(KK)                                                                                              \
     case KK:                                                                                                       \
-        hipLaunchKernelGGL((k_bwd_dwg<KK>), grid, dim3(kDwgT), g.lds, stream, a, g.win, g.nhp, tiles_g, flag);    \
+        hipLaunchKernelGGL((k_bwd_dwg<KK>), grid, dim3(kDwgT), g.lds, stream, a, g.win, g.nhp, tiles_g, flag,     \
+                           bias_here);                                                                             \
         if (a.gx) hipLaunchKernelGGL((k_bwd_dwg_fix<KK>), grid, dim3(256), 0, stream, a, tiles_g, (const int *)flag); \
         break;
             DC1D_BDWG(1)
@@ -995,9 +1012,10 @@ hipError_t launch_backward(BwdParams a, int num_cus, hipStream_t stream) {
     const DxPlan dx = plan_dx(p);
     const bool want_dx = a.gx || a.goff || a.gmask;
     if (n > 0 && (want_dx || a.gw) && depthwise_path(p)) {
-        const hipError_t e = launch_backward_dw(a, L.total > 0 ? (int *)ws : nullptr, stream);
+        bool bias_done = false;
+        const hipError_t e = launch_backward_dw(a, L.total > 0 ? (int *)ws : nullptr, stream, &bias_done);
         if (e != hipSuccess) return e;
-        return launch_bias(a, stream);
+        return bias_done ? hipGetLastError() : launch_bias(a, stream);
     }
     if (a.gx) {
         const int64_t nx = (int64_t)p.B * p.C_in * p.L_in;
