@@ -499,8 +499,7 @@ struct DwgGeo {
     int l0, lh0, lh1, i_lo, i_hi;
 };
 
-__device__ __forceinline__ DwgGeo dwg_geo(const Params &p, int tile, int tiles_l) {
-    constexpr int LT = kDwgLT;
+__device__ __forceinline__ DwgGeo dwg_geo(const Params &p, int tile, int tiles_l, int LT = kDwgLT) {
     DwgGeo g;
     g.l0 = tile * LT;
     g.i_lo = tile == 0 ? 0 : max(0, g.l0 * p.stride - p.padding);
@@ -758,6 +757,199 @@ __global__ void __launch_bounds__(kDwgT, 4) k_bwd_dwg(BwdParams a, int WIN, int 
     }
 }
 
+// grad_x gathered from a materialised dS ([B][C_in][K][L_out]: dense and
+// grouped shapes) -- the same ownership as k_bwd_dwg, without LDS atomics:
+// a block takes one batch, a block of cbx channels of one offset group and
+// the input positions owned by a tile of lt outputs.  Phase 1 stores, per
+// (tap, output) of the tile and its halo, the left neighbour and the two
+// interpolation weights times the mask (shared by the block's channels).
+// Phase 2: a thread owns two consecutive positions of CPT channels and
+// sums, per tap, over the candidate outputs (as in k_bwd_dwg) the products
+// dS * weight, reading dS from global memory (the CPT channels' values of
+// one candidate are one load each, their weights computed once).  Samples
+// moved further than kDwgR are added afterwards by k_bwd_dxg_fix.
+struct DxgPlan {
+    int lt, nhp, tiles_l, cbx, cblocks, cpt;
+    size_t lds;  // 0: not served (the scattering k_bwd_dx computes grad_x)
+};
+
+template <int CPT>
+__global__ void __launch_bounds__(256) k_bwd_dxg(BwdParams a, DxgPlan pl, int *flag) {
+    const Params &p = a.p;
+    extern __shared__ float smem[];
+    const int K = p.K, NHP = pl.nhp, L_in = p.L_in, L_out = p.L_out;
+    int *I0 = (int *)smem;       // [K][NHP]
+    float *ML = smem + K * NHP;  // [K][NHP]: m * (1 - f)
+    float *MR = smem + 2 * K * NHP;  // [K][NHP]: m * f
+    __shared__ int s_R, s_irr;
+    int blk = blockIdx.x;
+    const int tile = blk % pl.tiles_l;
+    blk /= pl.tiles_l;
+    const int cblk = blk % pl.cblocks;
+    const int b = blk / pl.cblocks;
+    const int ci0 = cblk * pl.cbx, g = ci0 / p.cpo;
+    const DwgGeo geo = dwg_geo(p, tile, pl.tiles_l, pl.lt);
+    const int lh0 = geo.lh0, nhl = geo.lh1 - lh0;
+    if (threadIdx.x == 0) {
+        s_R = 0;
+        s_irr = 0;
+    }
+    __syncthreads();
+    // ---- phase 1: positions of the tile's and the halo's samples (sentinels past them)
+    const float *__restrict__ off = (const float *)p.off;
+    const float *__restrict__ mask = (const float *)p.mask;
+    const int64_t orow = ((int64_t)b * p.G + g) * L_out;
+    int rmax = 0;
+    bool irregular = false;
+    for (int e = threadIdx.x; e < K * NHP; e += 256) {
+        const int k = e / NHP, h = e - k * NHP;
+        int v = kIrregular;
+        float ml = 0.0f, mr = 0.0f;
+        if (h < nhl) {
+            const int l = lh0 + h;
+            const int64_t oi = (orow + l) * K + k;
+            const int base = l * p.stride - p.padding + k * p.dilation;
+            int i0;
+            float f;
+            split_position(off[oi], base, tap_range(p, k), i0, f);
+            const float m = mask ? mask[oi] : 1.0f;
+            const int fl = i0 - base;
+            if (fl >= -kDwgR && fl <= kDwgR) {
+                v = i0;
+                rmax = max(rmax, abs(fl));
+            } else {
+                irregular = true;
+            }
+            ml = m * (1.0f - f);
+            mr = m * f;
+        }
+        I0[e] = v;
+        ML[e] = ml;
+        MR[e] = mr;
+    }
+    for (int o = 32; o > 0; o >>= 1) rmax = max(rmax, __shfl_xor(rmax, o));
+    const bool irr_w = __any(irregular);
+    if ((threadIdx.x & 63) == 0) {
+        atomicMax(&s_R, rmax);
+        if (irr_w) s_irr = 1;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0 && s_irr) atomicOr(flag, 1);
+    // ---- phase 2: (position pair, channel group) tasks, consecutive threads on consecutive pairs
+    const int R = s_R;
+    const int ncand = (2 * R + 2) / p.stride + 1;
+    const int npairs = (geo.i_hi - geo.i_lo + 1) / 2;
+    const int ntask = npairs * (pl.cbx / CPT);
+    const int64_t cs = (int64_t)K * L_out;  // dS channel stride
+    const float *__restrict__ dsb = a.dS + ((int64_t)b * p.C_in + ci0) * cs;
+    float *__restrict__ gxb = a.gx + ((int64_t)b * p.C_in + ci0) * L_in;
+    for (int task = threadIdx.x; task < ntask; task += 256) {
+        const int q = task % npairs, cq = task / npairs;
+        const int i = geo.i_lo + 2 * q;
+        float acc0[CPT], acc1[CPT];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) acc0[c] = acc1[c] = 0.0f;
+        const float *__restrict__ dsc = dsb + (int64_t)cq * CPT * cs;
+#pragma unroll 1
+        for (int k = 0; k < K; ++k) {
+            const int t = i + p.padding - k * p.dilation;  // l*s for i0 == i with floor(offset) 0
+            const int h0 = min(max(-floor_div(-(t - 1 - R), p.stride) - lh0, 0), nhl);
+            const int *__restrict__ i0k = I0 + k * NHP + h0;
+            const float *__restrict__ mlk = ML + k * NHP + h0, *__restrict__ mrk = MR + k * NHP + h0;
+            const float *__restrict__ dsk = dsc + (int64_t)k * L_out + lh0 + h0;
+            const int last = nhl - 1 - h0;  // candidates past the filled outputs read the last one's dS
+            for (int m0 = 0; m0 < ncand; m0 += 2) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int v = i0k[m0 + u];
+                    const float ml = mlk[m0 + u], mr = mrk[m0 + u];
+                    // at most one of a position's two terms is nonzero
+                    const bool e0 = v == i;
+                    const float w0 = e0 ? ml : (v == i - 1 ? mr : 0.0f);
+                    const float w1 = e0 ? mr : (v == i + 1 ? ml : 0.0f);
+                    const int hd = min(m0 + u, last);
+#pragma unroll
+                    for (int c = 0; c < CPT; ++c) {
+                        const float ds = dsk[c * cs + hd];
+                        acc0[c] = fmaf(ds, w0, acc0[c]);
+                        acc1[c] = fmaf(ds, w1, acc1[c]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            float *gr = gxb + (int64_t)(cq * CPT + c) * L_in;
+            gr[i] = acc0[c];
+            if (i + 1 < geo.i_hi) gr[i + 1] = acc1[c];
+        }
+    }
+}
+
+// The samples k_bwd_dxg left out (|floor(offset)| > kDwgR), added to grad_x
+// for every channel of their offset group with global atomics once every
+// owned run is stored.  Runs only if one was seen.
+__global__ void __launch_bounds__(256) k_bwd_dxg_fix(BwdParams a, const int *flag) {
+    if (*flag == 0) return;
+    const Params &p = a.p;
+    const float *__restrict__ off = (const float *)p.off;
+    const float *__restrict__ mask = (const float *)p.mask;
+    const int K = p.K, L_out = p.L_out, L_in = p.L_in;
+    const int64_t n = (int64_t)p.B * p.G * L_out * K;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+        const int k = (int)(e % K);
+        const int64_t r = e / K;
+        const int l = (int)(r % L_out);
+        const int64_t bg = r / L_out;
+        const int g = (int)(bg % p.G), b = (int)(bg / p.G);
+        const int base = l * p.stride - p.padding + k * p.dilation;
+        int i0;
+        float f;
+        split_position(off[e], base, tap_range(p, k), i0, f);
+        const int fl = i0 - base;
+        if (fl >= -kDwgR && fl <= kDwgR) continue;
+        const float m = mask ? mask[e] : 1.0f;
+        const bool v0 = i0 >= 0 && i0 < L_in, v1 = i0 + 1 >= 0 && i0 + 1 < L_in;
+        if (!v0 && !v1) continue;
+        for (int ci = g * p.cpo; ci < (g + 1) * p.cpo; ++ci) {
+            const float dm = a.dS[(((int64_t)b * p.C_in + ci) * K + k) * L_out + l] * m;
+            float *gr = a.gx + ((int64_t)b * p.C_in + ci) * L_in;
+            if (v0) unsafeAtomicAdd(gr + i0, dm * (1.0f - f));
+            if (v1) unsafeAtomicAdd(gr + i0 + 1, dm * f);
+        }
+    }
+}
+
+DxgPlan plan_dxg(const Params &p) {
+    DxgPlan pl = {};
+    const int64_t s = p.stride, span = (int64_t)(p.K - 1) * p.dilation;
+    const int64_t halo = (span + kDwgR + 1 + s - 1) / s + kDwgR / s + 2;
+    // the largest tile (a multiple of 32 outputs, at most 512) whose arrays fit in 64 KB
+    for (int64_t lt = std::min<int64_t>(512, ((int64_t)p.L_out + 31) / 32 * 32); lt >= 32; lt /= 2) {
+        const int64_t nh = std::min<int64_t>(lt, p.L_out) + halo;
+        const int64_t nhp = (nh + kDwgTail + 31) / 32 * 32 + 1;
+        const size_t lds = 3 * (size_t)p.K * (size_t)nhp * 4;
+        if (lds <= 64 * 1024) {
+            pl.lt = (int)lt;
+            pl.nhp = (int)nhp;
+            pl.lds = lds;
+            break;
+        }
+    }
+    if (pl.lds == 0) return pl;
+    pl.tiles_l = (p.L_out + pl.lt - 1) / pl.lt;
+    pl.cbx = 1;  // the largest divisor of the offset group's channel count up to 32
+    for (int c = 32; c >= 1; --c)
+        if (p.cpo % c == 0) {
+            pl.cbx = c;
+            break;
+        }
+    pl.cpt = pl.cbx % 4 == 0 ? 4 : 1;
+    pl.cblocks = p.C_in / pl.cbx;
+    if ((int64_t)p.B * pl.cblocks * pl.tiles_l >= ((int64_t)1 << 31)) pl.lds = 0;
+    return pl;
+}
+
 // The samples k_bwd_dwg left out (|floor(offset)| > kDwgR), added to grad_x
 // with global atomics once every owned run is stored.  Runs only if one was
 // seen.
@@ -857,7 +1049,7 @@ Params gemm_dw(const Params &p, const float *A, const float *S, float *gw, void 
 }
 
 struct BwdLayout {
-    size_t dS, wt, S, A, part, total;
+    size_t dS, wt, S, A, part, flag, total;
 };
 
 hipError_t launch_bias(const BwdParams &a, hipStream_t stream) {
@@ -926,6 +1118,8 @@ BwdLayout layout(const Params &p, bool want_weight, int num_cus) {
         L.S = o;
         o += align256(nds);
     }
+    L.flag = o;  // the grad_x gather's flag
+    o += 256;
     L.total = o;
     return L;
 }
@@ -1017,7 +1211,9 @@ hipError_t launch_backward(BwdParams a, int num_cus, hipStream_t stream) {
         if (e != hipSuccess) return e;
         return bias_done ? hipGetLastError() : launch_bias(a, stream);
     }
-    if (a.gx) {
+    const DxgPlan xg = plan_dxg(p);
+    const bool gather_x = a.gx && xg.lds > 0;  // grad_x gathered (no clear, no atomics) or scattered
+    if (a.gx && !gather_x) {
         const int64_t nx = (int64_t)p.B * p.C_in * p.L_in;
         hipLaunchKernelGGL(k_bwd_zero, dim3(grid_for(nx)), dim3(256), 0, stream, a.gx, nx);
     }
@@ -1048,8 +1244,20 @@ hipError_t launch_backward(BwdParams a, int num_cus, hipStream_t stream) {
         } else {
             hipLaunchKernelGGL(k_bwd_samples, dim3(grid_for(n)), dim3(256), 0, stream, s);
         }
-        if (want_dx && dx_blocks > 0)
-            hipLaunchKernelGGL(k_bwd_dx, dim3((unsigned)dx_blocks), dim3(256), dx.lds, stream, a, dx);
+        BwdParams ad = a;  // the offset and mask gradients (and grad_x when not gathered)
+        if (gather_x) ad.gx = nullptr;
+        if ((ad.gx || ad.goff || ad.gmask) && dx_blocks > 0)
+            hipLaunchKernelGGL(k_bwd_dx, dim3((unsigned)dx_blocks), dim3(256), dx.lds, stream, ad, dx);
+        if (gather_x) {
+            int *flag = (int *)(ws + L.flag);
+            hipLaunchKernelGGL(k_bwd_zero, dim3(1), dim3(256), 0, stream, (float *)flag, (int64_t)1);
+            const dim3 grid((unsigned)((int64_t)p.B * xg.cblocks * xg.tiles_l));
+            if (xg.cpt == 4)
+                hipLaunchKernelGGL((k_bwd_dxg<4>), grid, dim3(256), xg.lds, stream, a, xg, flag);
+            else
+                hipLaunchKernelGGL((k_bwd_dxg<1>), grid, dim3(256), xg.lds, stream, a, xg, flag);
+            hipLaunchKernelGGL(k_bwd_dxg_fix, dim3(grid_for(no)), dim3(256), 0, stream, a, (const int *)flag);
+        }
         if (a.gw) {
             if (dense) {
                 float *A = (float *)(ws + L.A);
