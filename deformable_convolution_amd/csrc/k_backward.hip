@@ -17,8 +17,9 @@
 // integer offsets).
 //
 // Kernels, in order on the caller's stream:
-//   k_bwd_zero       clears grad_x (and the offset / mask gradients when they
-//                    are accumulated over several channel blocks);
+//   k_bwd_zero       clears grad_x when it is scattered (and the offset /
+//                    mask gradients when they are accumulated over several
+//                    channel blocks);
 //   dS               dense shapes (groups == 1): k_transpose W -> W^T, then
 //                    k_gemm dS = W^T dout on the MFMA kernel; other shapes:
 //                    k_bwd_samples (a loop over the group's output channels);
@@ -27,8 +28,10 @@
 //                    the weight GEMM's layout [(b, l)][C_in*K] (dense, one
 //                    workgroup per row), or
 //                    k_bwd_samples beside dS as [B][C_in][K][L_out];
-//   k_bwd_dx         grad_x, grad_offsets, grad_mask from dS (tiled, LDS
-//                    windows);
+//   k_bwd_dx         grad_offsets, grad_mask from dS (tiled, LDS windows),
+//                    and grad_x (LDS atomics) when the gather does not fit;
+//   k_bwd_dxg        grad_x gathered from dS (no clear, no atomics), then
+//                    k_bwd_dxg_fix for samples moved beyond its reach;
 //   weight gradient  dense: k_restride_dout then k_gemm grad_weight =
 //                    dout S^T; other shapes: k_bwd_weight;
 //   k_bwd_bias       one workgroup per (output channel, batch), atomics.
