@@ -69,9 +69,34 @@ def work(w):
     return contraction, sampling, elems * es
 
 
-def kernel_hash():
+# The sources each measured kernel family is built from (a summary's counters
+# stay valid while these are unchanged).  Every family includes the shared
+# header and the C ABI's launch code.
+_COMMON = ["dc1d_internal.h", "api.hip"]
+_MFMA = ["mfma_kernel.h", "k_mfma.hip", "k_mfma_f32.hip", "k_mfma_f32_mask.hip", "k_mfma_bf16.hip",
+         "k_mfma_bf16_mask.hip"]
+_FAMILY_SOURCES = [
+    ("mfma_", _MFMA),
+    ("depthwise", ["k_direct.hip"]),
+    ("direct2d", ["k_dc2d.hip"]),
+    ("direct", ["k_direct.hip"]),
+    ("backward", ["k_backward.hip"] + _MFMA),
+    ("packed", ["k_packed.hip", "k_direct.hip"] + _MFMA),
+    ("im2col2d", ["k_dc2d.hip"] + _MFMA),
+]
+
+
+def kernel_sources(kernel=None):
+    """The source files behind `kernel` (all of them when it is unknown)."""
+    for prefix, files in _FAMILY_SOURCES:
+        if kernel is not None and kernel.startswith(prefix):
+            return sorted(os.path.join(CSRC, f) for f in set(files + _COMMON))
+    return KERNEL_SOURCES
+
+
+def kernel_hash(kernel=None):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in kernel_sources(kernel):
         h.update(open(os.path.join(ROOT, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -312,7 +337,7 @@ def main_backward(args, w):
         achieved = nbytes / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm_GBps"], "unit": "GB/s",
                 "frac": round(achieved / PEAK["hbm_GBps"], 4)}
-    roof["traffic"] = read_traffic(w.name, "backward", kernel_hash())
+    roof["traffic"] = read_traffic(w.name, "backward", kernel_hash("backward"))
     roof["kernel"] = "backward"
     roof["kernel_ms"] = round(kern_ms, 5)
     line = {
@@ -419,7 +444,7 @@ def main_packed(args, w):
     kern_ms = float(np.mean(r["launch_ms"]))  # per-launch events, as the kernel trace sees them
     achieved = pipeline / (kern_ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm_GBps"], "unit": "GB/s",
-            "frac": round(achieved / PEAK["hbm_GBps"], 4), "traffic": read_traffic(w.name, "packed", kernel_hash()),
+            "frac": round(achieved / PEAK["hbm_GBps"], 4), "traffic": read_traffic(w.name, "packed", kernel_hash("packed")),
             "kernel": "packed", "kernel_ms": round(kern_ms, 5)}
     line = {
         "metric": "Packed DeformConv1d fwd GFLOP/s (offset/mask generator + forward)",
@@ -515,7 +540,7 @@ def main2d(args, w):
     peak = PEAK["mfma_f32_TFLOPs"] if w.dtype == "f32" else PEAK["mfma_bf16_TFLOPs"]
     achieved = contraction / (kern_ms * 1e-3) / 1e12
     roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4), "traffic": read_traffic(w.name, r["kernel"], kernel_hash()),
+            "frac": round(achieved / peak, 4), "traffic": read_traffic(w.name, r["kernel"], kernel_hash(r["kernel"])),
             "kernel": r["kernel"], "kernel_ms": round(kern_ms, 5)}
     es = 4 if w.dtype == "f32" else 2
     s_bytes = 2 * w.B * (w.C_in // w.groups) * w.kh * w.kw * w.Ho * w.Wo * es  # the sampled matrix, out and back
@@ -669,7 +694,7 @@ def main():
         achieved = nbytes / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm_GBps"], "unit": "GB/s",
                 "frac": round(achieved / PEAK["hbm_GBps"], 4)}
-    traffic = read_traffic(w.name, kern + ("_constrained" if args.constrained else ""), kernel_hash())
+    traffic = read_traffic(w.name, kern + ("_constrained" if args.constrained else ""), kernel_hash(kern))
     roof["traffic"] = traffic
     roof["kernel"] = kern
     roof["kernel_ms"] = round(kern_ms, 5)
@@ -811,7 +836,7 @@ def write_profile_md(d, workload, kernel):
                                kernel))
     out.append("")
     out.append("<!-- kernel=%s -->" % kernel)
-    out.append("<!-- kernel_sources=%s -->" % kernel_hash())
+    out.append("<!-- kernel_sources=%s -->" % kernel_hash(kernel))
     if rows_k and f_scale and w_scale:
         out.append("<!-- hbm_bytes_per_launch=%.0f -->" % total_bytes)
     out.append("")
