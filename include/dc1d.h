@@ -188,16 +188,21 @@ int dc1d_forward_constrained(const dc1d_tensor *x, const dc1d_tensor *offsets,
  * checks their gradient against a finite difference, section Demo
  * notebook).  The offset gradient is that of the interpolation formula with
  * i0 held fixed, i.e. the right derivative at integer offsets.  Every
- * requested gradient is overwritten.  grad_x and grad_bias (and, for some
- * shapes, the others) are cleared and then accumulated with atomics, so
- * their last bits may differ between runs.  grad_mask needs a mask.
- * Gradients must not overlap the inputs, each other or the workspace.
+ * requested gradient is overwritten.  grad_x is gathered (each position's
+ * sum formed by one thread in a fixed order) when the shape's gather arrays
+ * fit in LDS, samples moved more than 16 positions then added with atomics;
+ * otherwise it is cleared and accumulated with atomics.  grad_bias and, for
+ * some shapes, the other gradients are accumulated with atomics.  Where
+ * atomics are used the last bits may differ between runs.  grad_mask needs
+ * a mask.  Gradients must not overlap the inputs, each other or the
+ * workspace.
  *
  * workspace: at least dc1d_backward_workspace_bytes() bytes, 256-byte
  * aligned, when that is not 0 (it holds dS = the gradient of the samples,
- * the transposed weight and the samples for the weight gradient, and split
- * partial sums, depending on the shape; depthwise shapes need none); no
- * initialisation; nothing kept.
+ * the transposed weight and the samples for the weight gradient, split
+ * partial sums, and the grad_x gather's flag, depending on the shape;
+ * depthwise shapes need only the flag, or nothing); no initialisation;
+ * nothing kept.
  */
 int dc1d_backward_workspace_bytes(const dc1d_tensor *x, const dc1d_tensor *offsets,
                                   const dc1d_tensor *mask_or_null, const dc1d_tensor *weight,
