@@ -57,12 +57,13 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f) {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// float -> bfloat16, round to nearest even (NaN stays a quiet NaN).
+// float -> bfloat16, round to nearest even (NaN stays a quiet NaN): the
+// conversion instruction, on a pair whose second half is dropped.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+    const bf2_t r = __builtin_convertvector(f2_t{f, 0.0f}, bf2_t);
+    return (uint16_t)(__builtin_bit_cast(uint32_t, r) & 0xffffu);
 }
 
 struct F32 {
