@@ -175,15 +175,20 @@ __global__ void __launch_bounds__(256) k_im2col2d_band(Params2 p, int runs, int 
     // the band of channel ci + 1 is loaded into registers before channel
     // ci's samples are stored, so waiting for those loads never waits for
     // the stores (one memory counter tracks both)
+    // this thread's band elements e = t + 256u: their offset in a channel's
+    // plane (-1: outside the image or past the band), the same for every channel
+    int boff[kBandPer];
+#pragma unroll
+    for (int u = 0; u < kBandPer; ++u) {
+        const int e = threadIdx.x + 256 * u;
+        const int rr = e / W, col = e - rr * W, r = r_lo + rr;
+        boff[u] = (e < nband && r >= 0 && r < p.H) ? r * W + col : -1;
+    }
     float xv[kBandPer];
     auto fetch = [&](int ci) {
         const T *__restrict__ xp = x + ((int64_t)b * p.C_in + ci) * plane;
 #pragma unroll
-        for (int u = 0; u < kBandPer; ++u) {
-            const int e = threadIdx.x + 256 * u;
-            const int rr = e / W, col = e - rr * W, r = r_lo + rr;
-            xv[u] = (e < nband && r >= 0 && r < p.H) ? D::ld(xp, (int64_t)r * W + col) : 0.0f;
-        }
+        for (int u = 0; u < kBandPer; ++u) xv[u] = boff[u] >= 0 ? D::ld(xp, boff[u]) : 0.0f;
     };
     auto put = [&](float *band) {
 #pragma unroll
