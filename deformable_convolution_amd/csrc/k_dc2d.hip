@@ -121,7 +121,7 @@ __global__ void __launch_bounds__(256) k_im2col2d(Params2 p, int runs) {
 // that every tap's four neighbours are LDS reads.  Taps moved beyond the
 // band read global memory.
 constexpr int kBandR = 4;
-constexpr int kBandRun = 8;  // channels per block (more, smaller blocks keep more waves resident)
+constexpr int kBandRun = 16;  // channels per block (measured: 8 and 32 were slower on the 64 x 64 workloads)
 constexpr int kBandPer = 8;  // band elements per thread (the band holds at most 256 * kBandPer)
 constexpr size_t kBandLds = 48 * 1024;
 
