@@ -84,6 +84,10 @@ def shapes():
         # workgroup): ragged columns; two row blocks with a ragged second
         (3, 32, 32, 12001, 3, 1, 1, 1, 32, 16, True),
         (2, 50, 50, 9000, 3, 1, 1, 1, 50, 25, True),
+        # depthwise with one offset group per channel (heads and forward
+        # fused): strided and dilated, ragged tiles; unmodulated
+        (3, 16, 16, 777, 5, 2, 3, 2, 16, 16, True),
+        (2, 32, 32, 1000, 3, 1, 1, 1, 32, 32, False),
     ]
     out = []
     for i, (B, C_in, C_out, L_in, K, s, p, d, groups, G, mod) in enumerate(spec):
