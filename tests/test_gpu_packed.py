@@ -84,8 +84,8 @@ def shapes():
         # workgroup): ragged columns; two row blocks with a ragged second
         (3, 32, 32, 12001, 3, 1, 1, 1, 32, 16, True),
         (2, 50, 50, 9000, 3, 1, 1, 1, 50, 25, True),
-        # depthwise with one offset group per channel (heads and forward
-        # fused): strided and dilated, ragged tiles; unmodulated
+        # depthwise with one offset group per channel: strided and dilated,
+        # ragged tiles; unmodulated
         (3, 16, 16, 777, 5, 2, 3, 2, 16, 16, True),
         (2, 32, 32, 1000, 3, 1, 1, 1, 32, 32, False),
     ]
