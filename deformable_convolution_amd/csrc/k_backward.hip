@@ -17,9 +17,9 @@
 // integer offsets).
 //
 // Kernels, in order on the caller's stream:
-//   k_bwd_zero       clears grad_x when it is scattered (and the offset /
-//                    mask gradients when they are accumulated over several
-//                    channel blocks);
+//   k_bwd_zero_set   clears, in one launch, grad_x when it is scattered, the
+//                    offset / mask gradients when they are accumulated over
+//                    several channel blocks, and the gather's flag;
 //   dS               dense shapes (groups == 1): k_transpose W -> W^T, then
 //                    k_gemm dS = W^T dout on the MFMA kernel; other shapes:
 //                    k_bwd_samples (a loop over the group's output channels);
@@ -45,6 +45,29 @@ namespace {
 
 __global__ void __launch_bounds__(256) k_bwd_zero(float *__restrict__ p, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.0f;
+}
+
+// Up to six buffers cleared in one launch (the clears a backward call
+// needs before its accumulating kernels; one launch instead of several).
+struct ZeroSet {
+    float *p[6];
+    int64_t n[6];
+    int count;
+    int64_t most;
+    void add(float *q, int64_t m) {
+        if (q && m > 0) {
+            p[count] = q;
+            n[count] = m;
+            ++count;
+            if (m > most) most = m;
+        }
+    }
+};
+
+__global__ void __launch_bounds__(256) k_bwd_zero_set(ZeroSet z) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int b = 0; b < z.count; ++b)
+        for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < z.n[b]; i += stride) z.p[b][i] = 0.0f;
 }
 
 __global__ void __launch_bounds__(256) k_bwd_samples(BwdParams a) {
@@ -1140,31 +1163,27 @@ hipError_t launch_backward_dw(BwdParams a, int *flag, hipStream_t stream, bool *
     const int tiles_l = (p.L_out + LT - 1) / LT;
     const DwgPlan g = plan_dwg(p);
     const bool gather = g.lds > 0 && flag != nullptr;
-    if (a.gx && !gather) {  // the scattering pass accumulates into grad_x
-        const int64_t nx = (int64_t)p.B * p.C_in * p.L_in;
-        hipLaunchKernelGGL(k_bwd_zero, dim3(grid_for(nx)), dim3(256), 0, stream, a.gx, nx);
-    }
+    // grad_bias from the dout the gather pass reads anyway (C_out == C_in here)
+    const bool bias_here = gather && a.gb != nullptr;
+    ZeroSet z = {};
+    if (!gather) z.add(a.gx, (int64_t)p.B * p.C_in * p.L_in);  // the scattering pass accumulates into grad_x
     int64_t win = (int64_t)(LT - 1) * p.stride + (int64_t)(p.K - 1) * p.dilation + 2 + 2 * kDwbMargin;
     win = (win + 63) / 64 * 64;
     if (win > 6144) win = 0;  // wider spans: global memory only
     const size_t lds = 2 * (size_t)win * 4;
     const int64_t no = (int64_t)p.B * p.G * p.L_out * p.K;
     if (p.cpo > 1) {
-        if (a.goff) hipLaunchKernelGGL(k_bwd_zero, dim3(grid_for(no)), dim3(256), 0, stream, a.goff, no);
-        if (a.gmask) hipLaunchKernelGGL(k_bwd_zero, dim3(grid_for(no)), dim3(256), 0, stream, a.gmask, no);
+        z.add(a.goff, no);
+        z.add(a.gmask, no);
     }
-    if (a.gw) {
-        const int64_t nw = (int64_t)p.C_out * p.K;
-        hipLaunchKernelGGL(k_bwd_zero, dim3(grid_for(nw)), dim3(256), 0, stream, a.gw, nw);
-    }
+    z.add(a.gw, (int64_t)p.C_out * p.K);
+    if (gather) z.add((float *)flag, 1);
+    if (bias_here) z.add(a.gb, p.C_out);
+    if (z.count > 0) hipLaunchKernelGGL(k_bwd_zero_set, dim3(grid_for(z.most)), dim3(256), 0, stream, z);
     const dim3 grid((unsigned)((int64_t)p.B * p.C_in * tiles_l));
     if (gather) {
         const int tiles_g = (p.L_out + kDwgLT - 1) / kDwgLT;
         const dim3 grid((unsigned)((int64_t)p.B * p.C_in * tiles_g));
-        hipLaunchKernelGGL(k_bwd_zero, dim3(1), dim3(256), 0, stream, (float *)flag, (int64_t)1);
-        // grad_bias from the dout the pass reads anyway (C_out == C_in here)
-        const bool bias_here = a.gb != nullptr;
-        if (bias_here) hipLaunchKernelGGL(k_bwd_zero, dim3(grid_for(p.C_out)), dim3(256), 0, stream, a.gb, (int64_t)p.C_out);
         if (bias_done) *bias_done = bias_here;
         switch (p.K) {
 #define DC1D_BDWG(KK)                                                                                              \
@@ -1216,15 +1235,16 @@ hipError_t launch_backward(BwdParams a, int num_cus, hipStream_t stream) {
     }
     const DxgPlan xg = plan_dxg(p);
     const bool gather_x = a.gx && xg.lds > 0;  // grad_x gathered (no clear, no atomics) or scattered
-    if (a.gx && !gather_x) {
-        const int64_t nx = (int64_t)p.B * p.C_in * p.L_in;
-        hipLaunchKernelGGL(k_bwd_zero, dim3(grid_for(nx)), dim3(256), 0, stream, a.gx, nx);
-    }
+    ZeroSet z = {};
+    if (!gather_x) z.add(a.gx, (int64_t)p.B * p.C_in * p.L_in);
     const int64_t no = (int64_t)p.B * p.G * p.L_out * p.K;
     if (dx.atomic_om && n > 0) {  // offset and mask gradients are accumulated
-        if (a.goff) hipLaunchKernelGGL(k_bwd_zero, dim3(grid_for(no)), dim3(256), 0, stream, a.goff, no);
-        if (a.gmask) hipLaunchKernelGGL(k_bwd_zero, dim3(grid_for(no)), dim3(256), 0, stream, a.gmask, no);
+        z.add(a.goff, no);
+        z.add(a.gmask, no);
     }
+    int *flag = (int *)(ws + L.flag);
+    if (gather_x && n > 0) z.add((float *)flag, 1);
+    if (z.count > 0) hipLaunchKernelGGL(k_bwd_zero_set, dim3(grid_for(z.most)), dim3(256), 0, stream, z);
     const int64_t dx_blocks = (int64_t)p.B * dx.ngrp_blocks * dx.tiles_l;
     if (dx_blocks >= ((int64_t)1 << 31) || (int64_t)p.C_out * p.cpg * p.K >= ((int64_t)1 << 31))
         return hipErrorInvalidValue;  // grids beyond the launch limits
@@ -1252,8 +1272,6 @@ hipError_t launch_backward(BwdParams a, int num_cus, hipStream_t stream) {
         if ((ad.gx || ad.goff || ad.gmask) && dx_blocks > 0)
             hipLaunchKernelGGL(k_bwd_dx, dim3((unsigned)dx_blocks), dim3(256), dx.lds, stream, ad, dx);
         if (gather_x) {
-            int *flag = (int *)(ws + L.flag);
-            hipLaunchKernelGGL(k_bwd_zero, dim3(1), dim3(256), 0, stream, (float *)flag, (int64_t)1);
             const dim3 grid((unsigned)((int64_t)p.B * xg.cblocks * xg.tiles_l));
             if (xg.cpt == 4)
                 hipLaunchKernelGGL((k_bwd_dxg<4>), grid, dim3(256), xg.lds, stream, a, xg, flag);
