@@ -549,14 +549,18 @@ int dc1d_packed_workspace_bytes(const dc1d_tensor *x, const dc1d_tensor *trunk_w
     return DC1D_OK;
 }
 
-int dc1d_packed_forward(const dc1d_tensor *x, const dc1d_tensor *trunk_weight,
+}  // extern "C"
+
+namespace {
+
+int packed_forward_impl(const dc1d_tensor *x, const dc1d_tensor *trunk_weight,
                         const dc1d_tensor *trunk_bias_or_null, const dc1d_tensor *off_weight,
                         const dc1d_tensor *off_bias_or_null, const dc1d_tensor *mask_weight_or_null,
                         const dc1d_tensor *mask_bias_or_null, const dc1d_tensor *weight,
                         const dc1d_tensor *bias_or_null, const dc1d_tensor *out,
                         const dc1d_tensor *offsets_out_or_null, const dc1d_tensor *mask_out_or_null,
                         int64_t stride, int64_t padding, int64_t dilation, int64_t groups, void *workspace,
-                        size_t workspace_bytes, void *stream) {
+                        size_t workspace_bytes, void *stream, int constrained) {
     if (!out) return DC1D_ERR_NULL_PTR;
     DeviceInfo dev;
     int st = current_device(&dev);
@@ -566,6 +570,10 @@ int dc1d_packed_forward(const dc1d_tensor *x, const dc1d_tensor *trunk_weight,
                          mask_bias_or_null, weight, bias_or_null, out, offsets_out_or_null, mask_out_or_null,
                          stride, padding, dilation, groups, &dev, &pk);
     if (st) return st;
+    // the forward's taps clamped to their windows; the generated offsets
+    // (and the offsets output) are the heads' own
+    if (constrained && !constrained_ok(pk.fwd)) return DC1D_ERR_BAD_ARG;
+    pk.fwd.constrained = constrained;
     const dc1d_tensor *ins[9] = {x, trunk_weight, trunk_bias_or_null, off_weight, off_bias_or_null,
                                  mask_weight_or_null, mask_bias_or_null, weight, bias_or_null};
     const dc1d_tensor *outs[3] = {out, offsets_out_or_null, mask_out_or_null};
@@ -627,6 +635,38 @@ int dc1d_packed_forward(const dc1d_tensor *x, const dc1d_tensor *trunk_weight,
     default: e = launch_direct(p, s); break;
     }
     return e == hipSuccess ? DC1D_OK : DC1D_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dc1d_packed_forward(const dc1d_tensor *x, const dc1d_tensor *trunk_weight,
+                        const dc1d_tensor *trunk_bias_or_null, const dc1d_tensor *off_weight,
+                        const dc1d_tensor *off_bias_or_null, const dc1d_tensor *mask_weight_or_null,
+                        const dc1d_tensor *mask_bias_or_null, const dc1d_tensor *weight,
+                        const dc1d_tensor *bias_or_null, const dc1d_tensor *out,
+                        const dc1d_tensor *offsets_out_or_null, const dc1d_tensor *mask_out_or_null,
+                        int64_t stride, int64_t padding, int64_t dilation, int64_t groups, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    return packed_forward_impl(x, trunk_weight, trunk_bias_or_null, off_weight, off_bias_or_null,
+                               mask_weight_or_null, mask_bias_or_null, weight, bias_or_null, out,
+                               offsets_out_or_null, mask_out_or_null, stride, padding, dilation, groups, workspace,
+                               workspace_bytes, stream, 0);
+}
+
+int dc1d_packed_forward_constrained(const dc1d_tensor *x, const dc1d_tensor *trunk_weight,
+                                    const dc1d_tensor *trunk_bias_or_null, const dc1d_tensor *off_weight,
+                                    const dc1d_tensor *off_bias_or_null, const dc1d_tensor *mask_weight_or_null,
+                                    const dc1d_tensor *mask_bias_or_null, const dc1d_tensor *weight,
+                                    const dc1d_tensor *bias_or_null, const dc1d_tensor *out,
+                                    const dc1d_tensor *offsets_out_or_null, const dc1d_tensor *mask_out_or_null,
+                                    int64_t stride, int64_t padding, int64_t dilation, int64_t groups,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+    return packed_forward_impl(x, trunk_weight, trunk_bias_or_null, off_weight, off_bias_or_null,
+                               mask_weight_or_null, mask_bias_or_null, weight, bias_or_null, out,
+                               offsets_out_or_null, mask_out_or_null, stride, padding, dilation, groups, workspace,
+                               workspace_bytes, stream, 1);
 }
 
 }  // extern "C"

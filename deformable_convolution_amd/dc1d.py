@@ -84,6 +84,8 @@ def load_library():
             lib.dc1d_packed_workspace_bytes.argtypes = [T] * 5 + [i64] * 4 + [ctypes.POINTER(ctypes.c_size_t)]
             lib.dc1d_packed_forward.restype = ctypes.c_int
             lib.dc1d_packed_forward.argtypes = [T] * 12 + [i64] * 4 + [p, ctypes.c_size_t, p]
+            lib.dc1d_packed_forward_constrained.restype = ctypes.c_int
+            lib.dc1d_packed_forward_constrained.argtypes = lib.dc1d_packed_forward.argtypes
             lib.dc2d_workspace_bytes.restype = ctypes.c_int
             lib.dc2d_workspace_bytes.argtypes = [T] * 5 + [i64] * 8 + [ctypes.POINTER(ctypes.c_size_t)]
             lib.dc2d_forward.restype = ctypes.c_int
@@ -301,13 +303,14 @@ def backward(x, offsets, weight, grad_out, mask=None, stride=1, padding=0, dilat
 
 def packed_forward(x, trunk_weight, trunk_bias, off_weight, off_bias, weight, bias=None, mask_weight=None,
                    mask_bias=None, stride=1, padding=0, dilation=1, groups=1, with_offsets=False, out=None,
-                   workspace=None):
+                   workspace=None, constrained=False):
     """The packed layer on the GPU (fp32): offsets (and, with mask_weight, the
     mask) generated from x by the depthwise trunk and pointwise heads, then
-    the deformable forward.  trunk_weight [C_in, 1, K], off_weight and
-    mask_weight [G*K, C_in, 1].  Returns out (allocated unless given), or
-    with with_offsets (out, offsets) / (out, (offsets, mask)).  Enqueued on
-    torch's current stream."""
+    the deformable forward (constrained=True: in the constrained mode, the
+    generated offsets returned as generated).  trunk_weight [C_in, 1, K],
+    off_weight and mask_weight [G*K, C_in, 1].  Returns out (allocated unless
+    given), or with with_offsets (out, offsets) / (out, (offsets, mask)).
+    Enqueued on torch's current stream."""
     lib = load_library()
     names = ("x", "trunk_weight", "trunk_bias", "off_weight", "off_bias", "weight", "bias", "mask_weight",
              "mask_bias")
@@ -340,8 +343,9 @@ def packed_forward(x, trunk_weight, trunk_bias, off_weight, off_bias, weight, bi
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
     with torch.cuda.device(x.device):
         stream = torch.cuda.current_stream(x.device).cuda_stream
-        _check(lib.dc1d_packed_forward(*[_ref(t) for t in d], stride, padding, dilation, groups, ws_ptr, ws_len,
-                                       stream), "dc1d_packed_forward")
+        fn = lib.dc1d_packed_forward_constrained if constrained else lib.dc1d_packed_forward
+        _check(fn(*[_ref(t) for t in d], stride, padding, dilation, groups, ws_ptr, ws_len, stream),
+               "dc1d_packed_forward")
     if not with_offsets:
         return out
     return (out, (offs, msk)) if mw is not None else (out, offs)

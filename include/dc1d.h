@@ -265,6 +265,23 @@ int dc1d_packed_forward(const dc1d_tensor *x, const dc1d_tensor *trunk_weight,
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * dc1d_packed_forward_constrained: the packed layer with the forward in the
+ * constrained mode of dc1d_forward_constrained (each tap's offset clamped
+ * to its window before the split).  The generated offsets, and the offsets
+ * output, are the heads' own (unclamped).  Same arguments, workspace and
+ * errors as dc1d_packed_forward, plus DC1D_ERR_BAD_ARG when
+ * (K-1)*dilation >= 2^24.
+ */
+int dc1d_packed_forward_constrained(const dc1d_tensor *x, const dc1d_tensor *trunk_weight,
+                        const dc1d_tensor *trunk_bias_or_null, const dc1d_tensor *off_weight,
+                        const dc1d_tensor *off_bias_or_null, const dc1d_tensor *mask_weight_or_null,
+                        const dc1d_tensor *mask_bias_or_null, const dc1d_tensor *weight,
+                        const dc1d_tensor *bias_or_null, const dc1d_tensor *out,
+                        const dc1d_tensor *offsets_out_or_null, const dc1d_tensor *mask_out_or_null,
+                        int64_t stride, int64_t padding, int64_t dilation, int64_t groups,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Backward of dc1d_forward_constrained: the gradients above at the clamped
  * offsets, with grad_offsets multiplied by the clamp's right derivative
  * (1 for an offset in [-k*dilation, (K-1-k)*dilation), 0 otherwise: a tap

@@ -268,12 +268,14 @@ def packed_heads(x, trunk_weight, trunk_bias, off_weight, off_bias, mask_weight=
 
 
 def packed_forward(x, trunk_weight, trunk_bias, off_weight, off_bias, weight, bias=None, mask_weight=None,
-                   mask_bias=None, stride=1, padding=0, dilation=1, groups=1, lib=None):
+                   mask_bias=None, stride=1, padding=0, dilation=1, groups=1, lib=None, constrained=False):
     """The packed layer: its generator's offsets (and mask), then the
-    deformable forward.  Returns (out, offsets, mask)."""
+    deformable forward (constrained=True: in the constrained mode; the
+    returned offsets are the generator's, unclamped).  Returns (out,
+    offsets, mask)."""
     off, mask = packed_heads(x, trunk_weight, trunk_bias, off_weight, off_bias, mask_weight, mask_bias,
                              stride, padding, dilation, lib)
-    out = forward(x, off, weight, bias, mask, stride, padding, dilation, groups, lib)
+    out = forward(x, off, weight, bias, mask, stride, padding, dilation, groups, lib, constrained=constrained)
     return out, off, mask
 
 

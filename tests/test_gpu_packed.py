@@ -33,19 +33,20 @@ def rms(a):
     return math.sqrt(float(np.mean(a ** 2))) if a.size else 0.0
 
 
-def run_packed(w, seed=0, check_out=True):
-    print("packed case", w, "seed", seed, flush=True)
+def run_packed(w, seed=0, check_out=True, constrained=False):
+    print("packed case", w, "seed", seed, "constrained", constrained, flush=True)
     t = inputs.make_packed_inputs(w, seed=seed)
     g = {k: (v.to(DEV) if v is not None else None) for k, v in t.items()}
     kw = dict(stride=w.stride, padding=w.padding, dilation=w.dilation)
     got = dc1d.packed_forward(g["x"], g["trunk_weight"], g["trunk_bias"], g["off_weight"], g["off_bias"], g["weight"],
-                              g["bias"], g["mask_weight"], g["mask_bias"], groups=w.groups, with_offsets=True, **kw)
+                              g["bias"], g["mask_weight"], g["mask_bias"], groups=w.groups, with_offsets=True,
+                              constrained=constrained, **kw)
     torch.cuda.synchronize()
     out, gen = got
     off, mask = gen if w.modulated else (gen, None)
     r_out, r_off, r_mask = oracle.packed_forward(t["x"], t["trunk_weight"], t["trunk_bias"], t["off_weight"],
                                                  t["off_bias"], t["weight"], t["bias"], t["mask_weight"],
-                                                 t["mask_bias"], groups=w.groups, **kw)
+                                                 t["mask_bias"], groups=w.groups, constrained=constrained, **kw)
     a_off = off.double().cpu().numpy()
     assert a_off.shape == r_off.shape
     tol_o = 1e-5 * math.sqrt(w.C_in) * max(rms(r_off), 1.0)
@@ -105,6 +106,19 @@ def test_packed_page_layer(name):
 @pytest.mark.parametrize("w", shapes(), ids=lambda w: w.name)
 def test_packed_ragged_shapes(w):
     run_packed(w, seed=3)
+
+
+@pytest.mark.parametrize("i", [0, 1, 2, 5, 6, 9])
+def test_packed_constrained_shapes(i):
+    """The constrained mode on generated offsets: the clamp to the receptive
+    field moves a position by no more than the offset's own error, so the
+    tolerances are the unconstrained ones; the offsets come back as
+    generated."""
+    run_packed(shapes()[i], seed=5, constrained=True)
+
+
+def test_packed_constrained_page_layer():
+    run_packed(inputs.PACKED_WORKLOADS["packed_page_modulated"], seed=6, constrained=True)
 
 
 def test_packed_full_size_workload():

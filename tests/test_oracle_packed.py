@@ -133,6 +133,35 @@ def test_bias_only_offset_head_places_each_channel():
             assert np.all(off[:, g, :, k] == g * K + k + 0.25)
 
 
+@pytest.mark.parametrize("shape", SHAPES)
+def test_constrained_packed_is_constrained_forward_of_the_generated_offsets(shape):
+    """The constrained packed layer: the unconstrained generator's offsets,
+    fed to the constrained forward (pinned on its own); with the offsets
+    scaled up most taps leave their receptive field, so the two modes
+    differ."""
+    c = make_case(shape, seed=27, scale=4.0)
+    out, off, mask = oracle.packed_forward(c["x"], c["tw"], c["tb"], c["ow"], c["ob"], c["w"], c["b"], c["mw"],
+                                           c["mb"], groups=c["groups"], constrained=True, **c["kw"])
+    off0, mask0 = heads(c)
+    assert np.array_equal(off, off0)
+    ref = oracle.forward(c["x"], off0, c["w"], c["b"], mask0, groups=c["groups"], constrained=True, **c["kw"])
+    assert np.array_equal(out, ref)
+    free, _, _ = run(c)
+    assert np.abs(out - free).max() > 1e-6
+
+
+def test_constrained_packed_with_zero_offset_head_is_plain_conv1d():
+    c = make_case(SHAPES[2], seed=28)
+    c["ow"] = np.zeros_like(c["ow"])
+    c["ob"] = np.zeros_like(c["ob"])
+    c["mw"], c["mb"] = None, None
+    out, _, _ = oracle.packed_forward(c["x"], c["tw"], c["tb"], c["ow"], c["ob"], c["w"], c["b"], None, None,
+                                      groups=c["groups"], constrained=True, **c["kw"])
+    ref = F.conv1d(torch.tensor(c["x"]), torch.tensor(c["w"]), torch.tensor(c["b"]), groups=c["groups"],
+                   **c["kw"]).numpy()
+    close(out, ref)
+
+
 def test_sigmoid_values():
     c = make_case(SHAPES[0], seed=25)
     c["mw"] = np.zeros_like(c["mw"])
