@@ -20,10 +20,10 @@ namespace dc1d {
 namespace {
 
 constexpr int kTrThreads = 256;
-constexpr int kTrOpt = 4;
+constexpr int kTrOpt = 8;
 constexpr int kTrLT = kTrThreads * kTrOpt;  // outputs per block
 constexpr int kTrWinMax = 16384;            // largest LDS window (floats)
-constexpr int kTrFill = 5;                  // window loads per thread in flight together
+constexpr int kTrFill = 9;                  // window loads per thread in flight together
 
 // win: the LDS window's capacity in floats (the span of a full tile), or 0
 // when that would exceed kTrWinMax (every tap then reads global memory).

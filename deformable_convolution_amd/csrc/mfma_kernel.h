@@ -551,6 +551,48 @@ __device__ __forceinline__ void head_writeout(const MfmaArgs &a, const Tile &tl,
     const int ncol = (int)min((int64_t)BN, a.N - tl.n0);
     const int g_first = (int)fdiv((uint32_t)tl.m0, a.fd_K);
     const int ng = (int)fdiv((uint32_t)(tl.m0 + rows - 1), a.fd_K) - g_first + 1;
+    if constexpr (sizeof(typename Tr::T) == 4) {
+        // In 16-byte words when the tile's columns lie in one batch and every
+        // run (l0 .. l0+ncol-1 times K taps of one group) starts on a word:
+        // the (group, word) pairs spread over all the workgroup's threads.  A
+        // word holding taps of rows outside this tile (the first or last
+        // group, when BM is not a multiple of K) stores only its own elements.
+        const int b0 = (int)fdiv((uint32_t)tl.n0, a.fd_Lout);
+        const int l0 = (int)(tl.n0 - (int64_t)b0 * L_out);
+        const bool aligned = ((uintptr_t)p.out & 15) == 0 && (OUT != 2 || ((uintptr_t)p.mask & 15) == 0);
+        if (aligned && l0 + ncol <= L_out && ((int64_t)L_out * K) % 4 == 0 && ((int64_t)l0 * K) % 4 == 0 &&
+            (ncol * K) % 4 == 0) {
+            const int wpr = ncol * K / 4;  // words per run
+            for (int idx = threadIdx.x; idx < ng * wpr; idx += NTT) {
+                const int gi = idx / wpr, e0 = 4 * (idx - gi * wpr);
+                const int g = g_first + gi;
+                int c = (int)fdiv((uint32_t)e0, a.fd_K), k = e0 - c * K;
+                bool is_mask;
+                float *dst = (float *)head_run<Tr, OUT>(p, b0, g, is_mask) + ((int64_t)l0 * K + e0);
+                float v[4];
+                bool own[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int rl = g * K + k - tl.m0;
+                    own[q] = rl >= 0 && rl < rows;
+                    v[q] = own[q] ? s_out[rl * kHeadLd + c] + s_bias[rl] : 0.0f;
+                    if (is_mask) v[q] = sigmoid(v[q]);
+                    if (++k == K) {
+                        k = 0;
+                        ++c;
+                    }
+                }
+                if (own[0] && own[1] && own[2] && own[3]) {
+                    *(f4 *)dst = f4{v[0], v[1], v[2], v[3]};
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (own[q]) dst[q] = v[q];
+                }
+            }
+            return;
+        }
+    }
     for (int j = threadIdx.x; j < BN * K; j += NTT) {
         const int c = (int)fdiv((uint32_t)j, a.fd_K);
         const int k = j - c * K;
