@@ -608,16 +608,22 @@ int packed_forward_impl(const dc1d_tensor *x, const dc1d_tensor *trunk_weight,
     void *shared = cat + pk.cat_bytes;
     hipStream_t s = (hipStream_t)stream;
     pk.trunk.t = t;
+    // with a mask: one GEMM for both heads, their weights and biases stacked
+    // by the trunk's launch
+    const int GK = pk.G * pk.K;
+    float *wcat = pk.mw ? (float *)cat : nullptr;
+    float *bcat = pk.mw ? (float *)(cat + round256((size_t)2 * GK * pk.fwd.C_in * 4)) : nullptr;
+    pk.trunk.ow = pk.ow;
+    pk.trunk.ob = pk.ob;
+    pk.trunk.mw = pk.mw;
+    pk.trunk.mb = pk.mb;
+    pk.trunk.wcat = wcat;
+    pk.trunk.bcat = bcat;
+    pk.trunk.GK = GK;
     hipError_t e = launch_trunk(pk.trunk, s);
     if (e != hipSuccess) return DC1D_ERR_LAUNCH;
     const int64_t brow = pk.fwd.L_out, bbatch = (int64_t)pk.fwd.C_in * pk.fwd.L_out;
     if (pk.mw) {
-        // one GEMM for both heads: their weights and biases stacked
-        const int GK = pk.G * pk.K;
-        float *wcat = (float *)cat;
-        float *bcat = (float *)(cat + round256((size_t)2 * GK * pk.fwd.C_in * 4));
-        e = launch_stack_heads(pk.ow, pk.ob, pk.mw, pk.mb, GK, pk.fwd.C_in, wcat, bcat, s);
-        if (e != hipSuccess) return DC1D_ERR_LAUNCH;
         e = launch_gemm_f32(head_gemm(pk, wcat, bcat, off, mask, shared), brow, bbatch, 2, dev.num_cus, s);
     } else {
         e = launch_gemm_f32(head_gemm(pk, pk.ow, pk.ob, off, nullptr, shared), brow, bbatch, 1, dev.num_cus, s);

@@ -195,12 +195,14 @@ struct TrunkArgs {
     const float *tw, *tb;  // [C][K], [C] or null
     float *t;
     int dtype, B, C, L_in, L_out, K, stride, padding, dilation;
+    // With wcat non-null the same launch also stacks the packed layer's two
+    // heads for one GEMM: wcat = [ow; mw] ([2*GK][C] row-major), bcat =
+    // [ob; mb] (null biases as zeros).
+    const float *ow, *ob, *mw, *mb;
+    float *wcat, *bcat;
+    int GK;
 };
 hipError_t launch_trunk(const TrunkArgs &a, hipStream_t stream);
-// wcat = [ow; mw] ([2*GK][C] row-major), bcat = [ob; mb] (null biases as
-// zeros): the packed layer's two heads stacked for one GEMM.
-hipError_t launch_stack_heads(const float *ow, const float *ob, const float *mw, const float *mb, int GK, int C,
-                              float *wcat, float *bcat, hipStream_t stream);
 // ---- 2D modulated deformable convolution ---------------------------------
 //
 // x [B][C_in][H][W]; offsets [B][2*G*T][Ho][Wo] (T = kh*kw taps; channel

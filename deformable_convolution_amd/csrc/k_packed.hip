@@ -7,7 +7,8 @@
 //     t[b,c,l] = tb[c] + sum_k tw[c,k] * x~[b,c, l*s - p + k*d]
 // (x~ zero outside [0, L_in)).  The pointwise heads that follow are the
 // MFMA GEMM (k_gemm with a head epilogue) and the deformable forward is the
-// library's own; this file holds only the trunk.
+// library's own; this file holds only the trunk (whose launch also stacks
+// the two heads' weights for that GEMM when the layer is modulated).
 //
 // One block takes kTrLT consecutive outputs of one (b, c) row.  The row's
 // input span for those outputs is staged in LDS, sized to the span, when it
@@ -36,6 +37,19 @@ __global__ void __launch_bounds__(kTrThreads) k_trunk(TrunkArgs a, int tiles_l, 
     const int tile = (int)(blk - row * tiles_l);
     const int c = (int)(row % a.C);
     const int l0 = tile * kTrLT;
+    if (a.wcat) {  // the heads' stacking, spread over the grid
+        const int64_t nw = (int64_t)a.GK * a.C, n = nw > a.GK ? nw : a.GK;
+        for (int64_t i = blk * kTrThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kTrThreads) {
+            if (i < nw) {
+                a.wcat[i] = a.ow[i];
+                a.wcat[nw + i] = a.mw[i];
+            }
+            if (i < a.GK) {
+                a.bcat[i] = a.ob ? a.ob[i] : 0.0f;
+                a.bcat[a.GK + i] = a.mb ? a.mb[i] : 0.0f;
+            }
+        }
+    }
     const T *__restrict__ xr = (const T *)a.x + row * a.L_in;
     const int K = a.K, s = a.stride, d = a.dilation;
     const int lo = l0 * s - a.padding;
@@ -82,31 +96,7 @@ __global__ void __launch_bounds__(kTrThreads) k_trunk(TrunkArgs a, int tiles_l, 
     }
 }
 
-__global__ void __launch_bounds__(256) k_stack_heads(const float *__restrict__ ow, const float *__restrict__ ob,
-                                                     const float *__restrict__ mw, const float *__restrict__ mb,
-                                                     int64_t nw, int GK, float *__restrict__ wcat,
-                                                     float *__restrict__ bcat) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < nw) {
-        wcat[i] = ow[i];
-        wcat[nw + i] = mw[i];
-    }
-    if (i < GK) {
-        bcat[i] = ob ? ob[i] : 0.0f;
-        bcat[GK + i] = mb ? mb[i] : 0.0f;
-    }
-}
-
 }  // namespace
-
-hipError_t launch_stack_heads(const float *ow, const float *ob, const float *mw, const float *mb, int GK, int C,
-                              float *wcat, float *bcat, hipStream_t stream) {
-    const int64_t nw = (int64_t)GK * C;
-    const int64_t n = nw > GK ? nw : GK;
-    hipLaunchKernelGGL(k_stack_heads, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, ow, ob, mw, mb, nw,
-                       GK, wcat, bcat);
-    return hipGetLastError();
-}
 
 hipError_t launch_trunk(const TrunkArgs &a, hipStream_t stream) {
     if (a.B == 0 || a.L_out == 0) return hipSuccess;
