@@ -624,7 +624,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; the forward shards by batch or output channel "
+        print("bench.py: measures one GPU only; the forward shards by batch or output channel "
               "with no exchange, and no multi-GPU figure is produced.", file=sys.stderr)
         raise SystemExit(2)
     if args.summarize_profile:
@@ -646,6 +646,8 @@ def main():
         print("copied %d bytes" % n, flush=True)
         return
 
+    if args.constrained and (args.workload in inputs.WORKLOADS_2D or args.workload in inputs.PACKED_WORKLOADS):
+        raise SystemExit("--constrained times the 1D forward workloads (%s)" % ", ".join(sorted(inputs.WORKLOADS)))
     if args.workload in inputs.WORKLOADS_2D:
         w = inputs.WORKLOADS_2D[args.workload]
         if args.profile_run:
