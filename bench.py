@@ -740,7 +740,7 @@ def main():
 
 
 PROFILE_COMMANDS = """\
-cd /tmp && export TMPDIR=/tmp; R=<repo root>; P=$R/gpurun_out/prof/{wl}{suffix}
+cd /tmp && export TMPDIR=/tmp; R=<repo root>; P=<output dir>/{wl}{suffix}
 rocprofv3 --kernel-trace --stats --output-format csv -d $P/trace -o run -- \\
     python3 $R/bench.py --workload {wl}{flag} --profile-run --steps 20 --warmup 3
 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $P/fetch -o run -- \\

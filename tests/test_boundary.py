@@ -110,7 +110,7 @@ def good(B=2, C=8, L=20, K=3, G=2, C_out=6, groups=1, addr0=FAKE):
 
 def test_valid_call_reaches_device_check(lib):
     # everything host-checkable is fine, so the only failure left is the
-    # missing gfx950 device in this container (or OK/other on a GPU machine)
+    # missing gfx950 device on a host without one (or OK/other with one)
     st = call(lib, *good())
     assert st in (dc1d.ERR_DEVICE, dc1d.ERR_WORKSPACE, dc1d.OK)
 
