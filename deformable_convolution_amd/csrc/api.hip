@@ -74,7 +74,9 @@ int validate(const dc1d_tensor *x, const dc1d_tensor *off, const dc1d_tensor *ma
         return DC1D_ERR_BAD_DTYPE;
     const int64_t B = x->shape[0], C_in = x->shape[1], L_in = x->shape[2];
     const int64_t C_out = w->shape[0], K = w->shape[2];
-    if (B < 0 || C_in < 1 || L_in < 0 || C_out < 1 || K < 1) return DC1D_ERR_BAD_SHAPE;
+    // an empty input sequence has nothing to sample (conv1d rejects it too),
+    // and the kernels' samplers assume at least one element per row
+    if (B < 0 || C_in < 1 || L_in < 1 || C_out < 1 || K < 1) return DC1D_ERR_BAD_SHAPE;
     if (C_in % groups || C_out % groups || C_in % offset_groups) return DC1D_ERR_BAD_ARG;
     if (off->shape[1] != offset_groups) return DC1D_ERR_BAD_ARG;
     if (w->shape[1] != C_in / groups) return DC1D_ERR_BAD_SHAPE;
@@ -466,7 +468,7 @@ int validate_packed(const dc1d_tensor *x, const dc1d_tensor *tw, const dc1d_tens
                     const dc1d_tensor *ob, const dc1d_tensor *mw, const dc1d_tensor *mb, const dc1d_tensor *w,
                     const dc1d_tensor *bias, const dc1d_tensor *out, const dc1d_tensor *off_out,
                     const dc1d_tensor *mask_out, int64_t stride, int64_t padding, int64_t dilation,
-                    int64_t groups, const DeviceInfo *dev, Packed *pk) {
+                    int64_t groups, Packed *pk) {
     if (!x || !tw || !ow || !w) return DC1D_ERR_NULL_PTR;
     if (stride < 1 || padding < 0 || dilation < 1 || groups < 1) return DC1D_ERR_BAD_ARG;
     if (!mw && (mb || mask_out)) return DC1D_ERR_BAD_ARG;
@@ -521,12 +523,18 @@ int validate_packed(const dc1d_tensor *x, const dc1d_tensor *tw, const dc1d_tens
     pk->off_bytes = round256(n_off);
     pk->mask_bytes = mw ? round256(n_off) : 0;
     pk->cat_bytes = mw ? round256((size_t)2 * G * K * C_in * 4) + round256((size_t)2 * G * K * 4) : 0;
+    pk->shared_bytes = pk->total = 0;
+    return DC1D_OK;
+}
+
+// The part of the workspace that depends on the device (the head GEMM's and
+// the forward's plans); after validate_packed.
+void size_packed(const DeviceInfo &dev, Packed *pk) {
     const size_t gemm =
-        gemm_workspace_bytes(head_gemm(*pk, nullptr, nullptr, nullptr, nullptr, nullptr), 1, dev->num_cus);
-    const size_t fwd = make_plan(pk->fwd, *dev).ws_bytes;
+        gemm_workspace_bytes(head_gemm(*pk, nullptr, nullptr, nullptr, nullptr, nullptr), 1, dev.num_cus);
+    const size_t fwd = make_plan(pk->fwd, dev).ws_bytes;
     pk->shared_bytes = round256(gemm > fwd ? gemm : fwd);
     pk->total = pk->t_bytes + pk->off_bytes + pk->mask_bytes + pk->cat_bytes + pk->shared_bytes;
-    return DC1D_OK;
 }
 
 }  // namespace
@@ -538,13 +546,13 @@ int dc1d_packed_workspace_bytes(const dc1d_tensor *x, const dc1d_tensor *trunk_w
                                 const dc1d_tensor *weight, int64_t stride, int64_t padding, int64_t dilation,
                                 int64_t groups, size_t *bytes_out) {
     if (!bytes_out) return DC1D_ERR_NULL_PTR;
-    DeviceInfo dev;
-    int st = current_device(&dev);
-    if (st) return st;
     Packed pk;
-    st = validate_packed(x, trunk_weight, nullptr, off_weight, nullptr, mask_weight_or_null, nullptr, weight,
-                         nullptr, nullptr, nullptr, nullptr, stride, padding, dilation, groups, &dev, &pk);
+    int st = validate_packed(x, trunk_weight, nullptr, off_weight, nullptr, mask_weight_or_null, nullptr, weight,
+                             nullptr, nullptr, nullptr, nullptr, stride, padding, dilation, groups, &pk);
     if (st) return st;
+    DeviceInfo dev;
+    if ((st = current_device(&dev))) return st;
+    size_packed(dev, &pk);
     *bytes_out = pk.total;
     return DC1D_OK;
 }
@@ -562,13 +570,10 @@ int packed_forward_impl(const dc1d_tensor *x, const dc1d_tensor *trunk_weight,
                         int64_t stride, int64_t padding, int64_t dilation, int64_t groups, void *workspace,
                         size_t workspace_bytes, void *stream, int constrained) {
     if (!out) return DC1D_ERR_NULL_PTR;
-    DeviceInfo dev;
-    int st = current_device(&dev);
-    if (st) return st;
     Packed pk;
-    st = validate_packed(x, trunk_weight, trunk_bias_or_null, off_weight, off_bias_or_null, mask_weight_or_null,
-                         mask_bias_or_null, weight, bias_or_null, out, offsets_out_or_null, mask_out_or_null,
-                         stride, padding, dilation, groups, &dev, &pk);
+    int st = validate_packed(x, trunk_weight, trunk_bias_or_null, off_weight, off_bias_or_null,
+                             mask_weight_or_null, mask_bias_or_null, weight, bias_or_null, out, offsets_out_or_null,
+                             mask_out_or_null, stride, padding, dilation, groups, &pk);
     if (st) return st;
     // the forward's taps clamped to their windows; the generated offsets
     // (and the offsets output) are the heads' own
@@ -590,6 +595,9 @@ int packed_forward_impl(const dc1d_tensor *x, const dc1d_tensor *trunk_weight,
         for (int j = i + 1; j < 3; ++j)
             if (outs[j] && overlaps(o->data, ob, outs[j]->data, (size_t)numel(outs[j]) * 4)) return DC1D_ERR_ALIAS;
     }
+    DeviceInfo dev;
+    if ((st = current_device(&dev))) return st;
+    size_packed(dev, &pk);
     if (pk.total > 0) {
         if (!workspace || workspace_bytes < pk.total || ((uintptr_t)workspace & 255)) return DC1D_ERR_WORKSPACE;
         for (const dc1d_tensor *t : ins)
@@ -693,7 +701,8 @@ int validate2d(const dc1d_tensor *x, const dc1d_tensor *off, const dc1d_tensor *
         return DC1D_ERR_BAD_DTYPE;
     const int64_t B = x->shape[0], C_in = x->shape[1], H = x->shape[2], W = x->shape[3];
     const int64_t C_out = w->shape[0], kh = w->shape[2], kw = w->shape[3];
-    if (B < 0 || C_in < 1 || H < 0 || W < 0 || C_out < 1 || kh < 1 || kw < 1) return DC1D_ERR_BAD_SHAPE;
+    // an empty image has nothing to sample; the samplers assume H, W >= 1
+    if (B < 0 || C_in < 1 || H < 1 || W < 1 || C_out < 1 || kh < 1 || kw < 1) return DC1D_ERR_BAD_SHAPE;
     if (C_in % groups || C_out % groups || C_in % offset_groups) return DC1D_ERR_BAD_ARG;
     if (w->shape[1] != C_in / groups) return DC1D_ERR_BAD_SHAPE;
     const int64_t T = kh * kw;

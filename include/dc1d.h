@@ -138,6 +138,9 @@ int dc1d_workspace_bytes(const dc1d_tensor *x, const dc1d_tensor *offsets,
  * initialisation and holds nothing between calls.  Calls in flight at the
  * same time must not share a workspace.
  *
+ * An empty input sequence (L_in == 0) is rejected with DC1D_ERR_BAD_SHAPE
+ * even when the padding would give L_out >= 1 (as conv1d rejects it).
+ *
  * Limits (DC1D_ERR_BAD_SHAPE beyond them): L_in + padding <= 2^29,
  * dilation*(K-1) <= 2^29, L_out*stride <= 2^30, C_in*K <= 2^30,
  * C_out <= 2^30.  Offsets whose magnitude exceeds 2^29 are clamped to
@@ -323,7 +326,8 @@ int dc1d_backward_constrained(const dc1d_tensor *x, const dc1d_tensor *offsets,
  * neighbours, a neighbour outside the image reading 0.  H_out and W_out
  * follow dc1d_output_length per axis.  Storage fp32 or bf16 (one dtype per
  * call; fp32 arithmetic, bf16 samples rounded once for the bf16 MFMA).
- * Limits (DC1D_ERR_BAD_SHAPE beyond them): H*W < 2^31, B <= 65535,
+ * Limits (DC1D_ERR_BAD_SHAPE beyond them): H >= 1 and W >= 1 (an empty
+ * image is rejected even when the padding would give outputs), H*W < 2^31, B <= 65535,
  * B*H_out*W_out < 2^31, G*kh*kw <= 2^24, and the 1D position limits per
  * axis.  workspace: at least dc2d_workspace_bytes() bytes, 256-byte aligned,
  * when that is not 0 (the sampled matrix [B, C_in*kh*kw, H_out*W_out] in the

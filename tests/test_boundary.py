@@ -225,3 +225,45 @@ def test_backward_validation(lib):
     # no gradient on an input or on another gradient
     assert bcall(lib, x, off, mask, w, gout, gx=T([2, 8, 20], addr=x.data)) == dc1d.ERR_ALIAS
     assert bcall(lib, x, off, mask, w, gout, gx=gx, gw=T([6, 8, 3], addr=gx.data + 16)) == dc1d.ERR_ALIAS
+
+
+# ---- empty input sequences -----------------------------------------------------
+
+def test_empty_sequence_rejected(lib):
+    # L_in == 0 with enough padding gives L_out >= 1 by the closed form, but
+    # there is nothing to sample: rejected before any device work
+    L_out = dc1d.output_length(0, 3, 1, 2, 1)
+    assert L_out == 2
+    w = T([6, 8, 3], addr=FAKE + (3 << 24))
+    st = call(lib, T([2, 8, 0], addr=None), T([2, 2, L_out, 3], addr=FAKE + (1 << 24)), None, w, None,
+              T([2, 6, L_out], addr=FAKE + (5 << 24)), p=2)
+    assert st == dc1d.ERR_BAD_SHAPE
+    n = ctypes.c_size_t(0)
+    r = ctypes.byref
+    assert lib.dc1d_workspace_bytes(r(T([2, 8, 0], addr=None)), r(T([2, 2, L_out, 3])), None, r(w), None,
+                                    1, 2, 1, 1, 2, r(n)) == dc1d.ERR_BAD_SHAPE
+    # the backward validates the same way
+    gout = T([2, 6, L_out], addr=FAKE + (6 << 24))
+    assert lib.dc1d_backward(r(T([2, 8, 0], addr=None)), r(T([2, 2, L_out, 3], addr=FAKE + (1 << 24))), None,
+                             r(w), r(gout), None, None, None, None, None, 1, 2, 1, 1, 2, None, 0,
+                             None) == dc1d.ERR_BAD_SHAPE
+    # and the packed layer (its forward's validation)
+    tw, ow = T([8, 1, 3], addr=FAKE + (7 << 24)), T([6, 8, 1], addr=FAKE + (8 << 24))
+    assert lib.dc1d_packed_workspace_bytes(r(T([2, 8, 0], addr=None)), r(tw), r(ow), None, r(w), 1, 2, 1, 1,
+                                           r(n)) == dc1d.ERR_BAD_SHAPE
+
+
+def test_empty_image_rejected(lib):
+    r = ctypes.byref
+    w = T([6, 4, 3, 3], addr=FAKE + (3 << 24))
+    n = ctypes.c_size_t(0)
+    for H, W in ((0, 5), (5, 0), (0, 0)):
+        Ho = dc1d.output_length(H, 3, 1, 2, 1)
+        Wo = dc1d.output_length(W, 3, 1, 2, 1)
+        x = T([1, 4, H, W], addr=None)
+        off = T([1, 18, Ho, Wo], addr=FAKE + (1 << 24))
+        out = T([1, 6, Ho, Wo], addr=FAKE + (5 << 24))
+        assert lib.dc2d_forward(r(x), r(off), None, r(w), None, r(out), 1, 1, 2, 2, 1, 1, 1, 1, None, 0,
+                                None) == dc1d.ERR_BAD_SHAPE
+        assert lib.dc2d_workspace_bytes(r(x), r(off), None, r(w), None, 1, 1, 2, 2, 1, 1, 1, 1,
+                                        r(n)) == dc1d.ERR_BAD_SHAPE
