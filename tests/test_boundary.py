@@ -108,11 +108,21 @@ def good(B=2, C=8, L=20, K=3, G=2, C_out=6, groups=1, addr0=FAKE):
     return x, off, mask, w, bias, out
 
 
+def _device_visible():
+    # counting devices does not initialise the runtime
+    import torch
+    return torch.cuda.device_count() > 0
+
+
 def test_valid_call_reaches_device_check(lib):
     # everything host-checkable is fine, so the only failure left is the
-    # missing gfx950 device on a host without one (or OK/other with one)
+    # missing gfx950 device.  The descriptors hold fake addresses: where a
+    # device is visible this call would pass the device check and launch on
+    # them, so it is made only on hosts without one.
+    if _device_visible():
+        pytest.skip("a device is visible: a valid call would launch on the fake addresses")
     st = call(lib, *good())
-    assert st in (dc1d.ERR_DEVICE, dc1d.ERR_WORKSPACE, dc1d.OK)
+    assert st == dc1d.ERR_DEVICE
 
 
 def test_null_pointers(lib):
@@ -206,9 +216,10 @@ def test_backward_validation(lib):
     x, off, mask, w, bias, out = good()
     gout = out  # grad_out has the output's shape
     gx, goff, gmask, gw, gb = grads_like(x, off, mask, w)
-    # everything host-checkable is fine
-    assert bcall(lib, x, off, mask, w, gout, gx, goff, gmask, gw, gb) in (dc1d.ERR_DEVICE, dc1d.ERR_WORKSPACE,
-                                                                         dc1d.OK)
+    # everything host-checkable is fine (made only without a device: with one
+    # the call would launch on the fake addresses)
+    if not _device_visible():
+        assert bcall(lib, x, off, mask, w, gout, gx, goff, gmask, gw, gb) == dc1d.ERR_DEVICE
     assert bcall(lib, x, off, mask, w, None, gx) == dc1d.ERR_NULL_PTR
     # fp32 only
     xb = T([2, 8, 20], dtype=1, addr=x.data)
