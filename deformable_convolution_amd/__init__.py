@@ -14,6 +14,7 @@ from .dc1d import (  # noqa: F401
     backward_workspace_bytes,
     debug_positions,
     forward,
+    forward_noalloc,
     forward2d,
     library_path,
     load_library,

@@ -223,10 +223,33 @@ namespace {
 // The constrained mode's tap bounds -k*d and (K-1-k)*d must be exact floats.
 bool constrained_ok(const Params &p) { return (int64_t)(p.K - 1) * p.dilation < ((int64_t)1 << 24); }
 
+// The allocation-free entry's workspace: one fixed array per device, in
+// device memory for the life of the process.  Host code never uses the
+// array's name as an address (on the host it is only a stand-in for the
+// symbol): the device address is looked up once per device and kept.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+std::once_flag g_scratch_once[kMaxDevices];
+void *g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address (nullptr if the lookup failed).
+void *scratch_address(int dev) {
+    std::call_once(g_scratch_once[dev], [dev]() {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) {
+            (void)hipGetLastError();
+            ptr = nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    });
+    return g_scratch_ptr[dev];
+}
+
 int forward_impl(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_tensor *mask_or_null,
                  const dc1d_tensor *weight, const dc1d_tensor *bias_or_null, const dc1d_tensor *out,
                  int64_t stride, int64_t padding, int64_t dilation, int64_t groups, int64_t offset_groups,
-                 void *workspace, size_t workspace_bytes, void *stream, int constrained) {
+                 void *workspace, size_t workspace_bytes, void *stream, int constrained,
+                 bool use_scratch = false) {
     if (!out) return DC1D_ERR_NULL_PTR;
     Params p;
     int st = validate(x, offsets, mask_or_null, weight, bias_or_null, out, stride, padding, dilation, groups,
@@ -247,6 +270,14 @@ int forward_impl(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_te
     DeviceInfo dev;
     if ((st = current_device(&dev))) return st;
     const Plan pl = make_plan(p, dev);
+    if (use_scratch) {
+        if (pl.ws_bytes > kScratchBytes) return DC1D_ERR_WORKSPACE;
+        int d = -1;
+        if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= kMaxDevices) return DC1D_ERR_DEVICE;
+        workspace = pl.ws_bytes > 0 ? scratch_address(d) : nullptr;
+        if (pl.ws_bytes > 0 && !workspace) return DC1D_ERR_DEVICE;
+        workspace_bytes = pl.ws_bytes > 0 ? kScratchBytes : 0;
+    }
     if (pl.ws_bytes > 0) {
         if (!workspace || workspace_bytes < pl.ws_bytes || ((uintptr_t)workspace & 255))
             return DC1D_ERR_WORKSPACE;
@@ -279,6 +310,16 @@ int dc1d_forward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_te
     return forward_impl(x, offsets, mask_or_null, weight, bias_or_null, out, stride, padding, dilation, groups,
                         offset_groups, workspace, workspace_bytes, stream, 0);
 }
+
+int dc1d_forward_noalloc(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_tensor *mask_or_null,
+                         const dc1d_tensor *weight, const dc1d_tensor *bias_or_null, const dc1d_tensor *out,
+                         int64_t stride, int64_t padding, int64_t dilation, int64_t groups, int64_t offset_groups,
+                         void *stream) {
+    return forward_impl(x, offsets, mask_or_null, weight, bias_or_null, out, stride, padding, dilation, groups,
+                        offset_groups, nullptr, 0, stream, 0, true);
+}
+
+size_t dc1d_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 int dc1d_forward_constrained(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_tensor *mask_or_null,
                              const dc1d_tensor *weight, const dc1d_tensor *bias_or_null, const dc1d_tensor *out,

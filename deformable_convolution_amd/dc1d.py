@@ -76,6 +76,10 @@ def load_library():
                 ctypes.POINTER(ctypes.c_size_t)]
             lib.dc1d_backward.restype = ctypes.c_int
             lib.dc1d_backward.argtypes = [T] * 10 + [i64] * 5 + [p, ctypes.c_size_t, p]
+            lib.dc1d_forward_noalloc.restype = ctypes.c_int
+            lib.dc1d_forward_noalloc.argtypes = [T] * 6 + [i64] * 5 + [p]
+            lib.dc1d_noalloc_scratch_bytes.restype = ctypes.c_size_t
+            lib.dc1d_noalloc_scratch_bytes.argtypes = []
             lib.dc1d_forward_constrained.restype = ctypes.c_int
             lib.dc1d_forward_constrained.argtypes = lib.dc1d_forward.argtypes
             lib.dc1d_backward_constrained.restype = ctypes.c_int
@@ -216,6 +220,29 @@ def plan(x, offsets, weight, bias=None, mask=None, stride=1, padding=0, dilation
                                     dilation, groups, G, ctypes.byref(name), ctypes.byref(grid),
                                     ctypes.byref(block), ctypes.byref(splits)), "dc1d_plan")
     return {"kernel": name.value.decode(), "grid": grid.value, "block": block.value, "splits": splits.value}
+
+
+def forward_noalloc(x, offsets, weight, bias=None, mask=None, stride=1, padding=0, dilation=1, groups=1,
+                    *, out):
+    """dc1d_forward_noalloc: the forward with its workspace in the library's
+    per-device scratch array (no device allocation in the call, none here
+    either: ``out`` must be given).  Calls that may overlap on one device
+    race on the scratch.  Enqueued on torch's current stream."""
+    lib = load_library()
+    x, offsets, weight, bias, mask, out = (_contig(t, n) for t, n in ((x, "x"), (offsets, "offsets"),
+                                                                        (weight, "weight"), (bias, "bias"),
+                                                                        (mask, "mask"), (out, "out")))
+    padding, G = _args(x, offsets, weight, bias, mask, stride, padding, dilation, groups)
+    dx, do, dm, dw, db, dout = map(_desc, (x, offsets, mask, weight, bias, out))
+    with _device_ctx(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        _check(lib.dc1d_forward_noalloc(_ref(dx), _ref(do), _ref(dm), _ref(dw), _ref(db), _ref(dout), stride,
+                                        padding, dilation, groups, G, stream), "dc1d_forward_noalloc")
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(load_library().dc1d_noalloc_scratch_bytes())
 
 
 def forward(x, offsets, weight, bias=None, mask=None, stride=1, padding=0, dilation=1, groups=1,

@@ -156,6 +156,31 @@ int dc1d_forward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_te
                  int64_t offset_groups, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * forward as dc1d_forward (same kernels, same results bit for bit), with
+ * its workspace taken from a scratch array that the library keeps in device
+ * memory, one per device, of dc1d_noalloc_scratch_bytes() bytes (64 MiB),
+ * held from the library's first use on that device until the process ends.
+ * The call allocates nothing (no hipMalloc, no allocating library routine);
+ * the caller still passes inputs and out.  Returns DC1D_ERR_WORKSPACE,
+ * before any device work, when dc1d_workspace_bytes() for these arguments
+ * exceeds the scratch size; DC1D_ERR_DEVICE if the scratch address cannot
+ * be looked up.  Every call on one device shares that device's scratch
+ * (it needs no initialisation and holds nothing useful between calls):
+ * calls that may run at the same time on one device (different streams
+ * without an ordering between them) race on it and must be serialised by
+ * the caller.  Other arguments and errors as dc1d_forward.
+ */
+int dc1d_forward_noalloc(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_tensor *mask_or_null,
+                         const dc1d_tensor *weight, const dc1d_tensor *bias_or_null, const dc1d_tensor *out,
+                         int64_t stride, int64_t padding, int64_t dilation, int64_t groups,
+                         int64_t offset_groups, void *stream);
+
+/* Size in bytes of the per-device scratch array dc1d_forward_noalloc uses. */
+size_t dc1d_noalloc_scratch_bytes(void);
+
+/*
  * Constrained mode: dc1d_forward with every tap kept inside its receptive
  * field (the dc1d page's default, section Usage / DeformConv1d: each kernel
  * tap is constrained to its own receptive field unless the layer is made
