@@ -156,6 +156,10 @@ struct MfmaPlan {
     int blocked, cb, slot, lpp, ncb, nkb;
     int variant_dw;  // the same shape reading the weights directly when they are 16-byte aligned (-1: none)
     size_t wb_bytes;
+    // bf16 blocks of 32 channels at one tap per chunk: window positions of the
+    // position-major kernel (k_mfma_cbt), taken when x is 16-byte aligned
+    // (0: not planned; `variant` is then, or otherwise, the kernel)
+    int tpos;
 };
 MfmaPlan plan_mfma(const Params &p, int num_cus);
 hipError_t launch_mfma(const Params &p, const MfmaPlan &pl, hipStream_t stream);

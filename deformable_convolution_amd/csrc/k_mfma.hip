@@ -134,6 +134,20 @@ void plan_for(const Params &p, int num_cus, MfmaPlan &pl) {
                     kCbCombos[i].lpp == pl.lpp)
                     pl.variant_dw = i;
         pl.wb_bytes = ((size_t)pl.nkb * p.C_out * pl.ncb * BK * sizeof(T) + 255) & ~(size_t)255;
+        // bf16, blocks of 32 channels at one tap per chunk, rows staged in
+        // words: the position-major window (k_mfma_cbt) when one of its
+        // compiled sizes holds the expected extent and fits
+        pl.tpos = 0;
+        if (sizeof(T) == 2 && pl.cb == 32 && pl.nkb >= 2 && vx) {
+            for (int i = 0; i < kNumTpos; ++i) {
+                const size_t xw = 2 * (size_t)kTposOpts[i] * kTPitch * sizeof(T);
+                if (kTposOpts[i] >= want + 2 && fixed + xw <= lds_cap) {
+                    pl.tpos = kTposOpts[i];  // (wt_max stays the channel-major fallback's capacity)
+                    pl.lds_bytes = std::max(pl.lds_bytes, fixed + xw);
+                    break;
+                }
+            }
+        }
         plan_splits(tiles, pl.chunks, num_cus, pl);
         pl.ws_bytes = pl.wb_bytes + (pl.splits > 1 ? (size_t)tiles * pl.splits * BM * BN * 4 : 0);
         return;
@@ -194,7 +208,7 @@ MfmaPlan plan_mfma(const Params &p, int num_cus) {
     if (pl.blocked) {
         static const char *const names[2][3] = {{"mfma_f32_cb8", "mfma_f32_cb16", "mfma_f32_cb32"},
                                                 {"mfma_bf16_cb8", "mfma_bf16_cb16", "mfma_bf16_cb32"}};
-        pl.name = names[p.dtype == kF32 ? 0 : 1][pl.cb == 8 ? 0 : (pl.cb == 16 ? 1 : 2)];
+        pl.name = pl.tpos ? "mfma_bf16_cb32t" : names[p.dtype == kF32 ? 0 : 1][pl.cb == 8 ? 0 : (pl.cb == 16 ? 1 : 2)];
     }
     return pl;
 }

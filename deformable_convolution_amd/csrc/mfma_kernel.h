@@ -300,9 +300,30 @@ __device__ __forceinline__ void mfma_role(const MfmaArgs &a, const Tile &tl, typ
     // iteration c.  Loads never wait on a bounds test: words outside the
     // matrix load a clamped address and are zeroed in commit_w.
     constexpr bool W2 = WV <= 4;
+    // Word v of this thread is row prow + RV*v, 16-byte word ppart of the
+    // row, for every chunk; in tiles wholly inside C_out the loads are a
+    // per-thread base plus a wave-uniform stride (no clamps in the loop).
+    constexpr int RV = NTM / WPR;  // rows between one thread's words
+    static_assert(RV % 8 == 0, "the word swizzle is the same for all of a thread's rows");
+    const int prow = t / WPR, ppart = t % WPR;
+    const T *wfast = w;
+    int64_t vstride = 0;
+    if (WL == 1) {
+        wfast = (const T *)a.wb + (int64_t)(tl.m0 + prow) * a.ncb * BK + ppart * EPW;
+        vstride = (int64_t)RV * a.ncb * BK;
+    } else if (WL == 2) {
+        wfast = w + (int64_t)(tl.m0 + prow) * C_in * p.K;
+        vstride = (int64_t)RV * C_in * p.K;
+    }
     auto fetch_w = [&](int cw, u4 (&wreg)[WV]) {
         const int r0 = cw * BK;
-        if (WL == 1) {
+        if ((WL == 1 || WL == 2) && m_full) {
+            const int cb = (int)fdiv((uint32_t)cw, a.fd_nkb), kb = cw - cb * a.nkb;
+            const T *base = WL == 1 ? wfast + ((int64_t)kb * M * a.ncb + cb) * BK
+                                    : wfast + (int64_t)min(cb * (BK / 4) + ppart, C_in - 1) * p.K + 4 * kb;
+#pragma unroll
+            for (int v = 0; v < WV; ++v) wreg[v] = *(const u4 *)(base + v * vstride);
+        } else if (WL == 1) {
             const int cb = (int)fdiv((uint32_t)cw, a.fd_nkb), kb = cw - cb * a.nkb;
             const T *wb = (const T *)a.wb + ((int64_t)kb * M * a.ncb + cb) * BK;
 #pragma unroll
@@ -350,18 +371,16 @@ __device__ __forceinline__ void mfma_role(const MfmaArgs &a, const Tile &tl, typ
     };
     // registers -> LDS (swizzled words).  Tiles wholly inside the matrix
     // store without tests.
+    T *const wdst = s_w + prow * BK + EPW * Tr::swz(prow, ppart);  // word 0 of this thread, buffer 0
     auto commit_w = [&](int cw, const u4 (&wreg)[WV]) {
         T *dw = s_w + (cw & 1) * BM * BK;
         const int r0 = cw * BK;
         const int cb = WL == 2 ? (int)fdiv((uint32_t)cw, a.fd_nkb) : 0;
         const bool full = m_full && (WL == 1 || (WL == 2 ? (cb + 1) * (BK / 4) <= C_in : r0 + BK <= Kred));
         if (full) {
+            T *d0 = wdst + (cw & 1) * BM * BK;
 #pragma unroll
-            for (int v = 0; v < WV; ++v) {
-                const int e = t + NTM * v;
-                const int row = e / WPR, part = e % WPR;
-                *(u4 *)(dw + row * BK + EPW * Tr::swz(row, part)) = wreg[v];
-            }
+            for (int v = 0; v < WV; ++v) *(u4 *)(d0 + v * RV * BK) = wreg[v];
         } else {
 #pragma unroll
             for (int v = 0; v < WV; ++v) {
@@ -386,19 +405,28 @@ __device__ __forceinline__ void mfma_role(const MfmaArgs &a, const Tile &tl, typ
     __builtin_amdgcn_s_setprio(2);
 
     u4 wA[WV], wB[WV];
+    const int c_last = max(tl.c_end - 1, 0);
     if (tl.c_begin < tl.c_end) {
         fetch_w(tl.c_begin, wA);
         commit_w(tl.c_begin, wA);
     }
-    if (W2 && tl.c_begin + 1 < tl.c_end) fetch_w(tl.c_begin + 1, wA);
+    if (W2) fetch_w(min(tl.c_begin + 1, c_last), wA);
     // prologue barriers shared with the sampler role: staging done, first sample tile done
     __syncthreads();
     __syncthreads();
-    // chunk c: `cur` holds (W2) or receives chunk c+1's weights, `nxt` receives chunk c+2's (W2)
+    // Chunk c: `cur` holds (W2) or receives chunk c+1's weights, `nxt`
+    // receives chunk c+2's (W2).  The loads are issued after the first row
+    // block's MFMAs and the LDS commit before the last block's, so that both
+    // run while the matrix unit is busy (scheduling barriers keep them
+    // there).  Both happen on every step, past the range on the last chunk's
+    // words (unused; the buffer written is not read again): with branches
+    // around them the compiler's wait for `cur` also waited for the loads
+    // just issued.
+    // (the plain fp32 GEMM's single register set keeps the loads at the top
+    // of the step and the commit at its end: held across the MFMAs it spills)
+    constexpr bool MID = WL != 0 || W2;
     auto step = [&](int c, u4 (&cur)[WV], u4 (&nxt)[WV]) {
-        if constexpr (W2) {
-            if (c + 2 < tl.c_end) fetch_w(c + 2, nxt);
-        } else {
+        if constexpr (!MID) {
             if (c + 1 < tl.c_end) fetch_w(c + 1, cur);
         }
         const T *tile = s_w + (c & 1) * BM * BK;
@@ -406,14 +434,32 @@ __device__ __forceinline__ void mfma_role(const MfmaArgs &a, const Tile &tl, typ
         Frag bf[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) Tr::lds_b(st + (col0 + 32 * nb + li) * SLD + 16 * lh, bf[nb]);
+        // weight fragments double-buffered: block mb+1's reads are in flight
+        // while block mb's MFMAs run
+        Frag af[2];
+        Tr::lds_a(tile, row0 + li, lh, af[0]);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            Frag af;
-            Tr::lds_a(tile, row0 + 32 * mb + li, lh, af);
+            if (mb + 1 < MB) Tr::lds_a(tile, row0 + 32 * (mb + 1) + li, lh, af[(mb + 1) & 1]);
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) Tr::mma(af, bf[nb], acc[mb][nb]);
+            for (int nb = 0; nb < NB; ++nb) Tr::mma(af[mb & 1], bf[nb], acc[mb][nb]);
+            if (MID && mb == 0) {
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (W2)
+                    fetch_w(min(c + 2, c_last), nxt);
+                else
+                    fetch_w(min(c + 1, c_last), cur);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (MID && (mb == MB - 2 || (MB == 1 && mb == 0))) {
+                __builtin_amdgcn_sched_barrier(0);
+                commit_w(c + 1, cur);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-        if (c + 1 < tl.c_end) commit_w(c + 1, cur);
+        if constexpr (!MID) {
+            if (c + 1 < tl.c_end) commit_w(c + 1, cur);
+        }
         __syncthreads();
     };
     if constexpr (W2) {
@@ -1213,6 +1259,186 @@ __device__ __forceinline__ void sampler_cb(const MfmaArgs &a, const Tile &tl, co
     }
 }
 
+// ---- channel-block order, bf16: windows stored position-major --------------------
+//
+// With bfloat16 storage and blocks of 32 channels at one tap per chunk, the
+// window of a channel block can be kept position-major: row j holds the
+// block's 32 channels at window position j (kTPitch elements; the 16-byte
+// pad puts consecutive rows on different banks).  A sampler thread's 16
+// channels at one position are then two 16-byte words, so the two
+// neighbours of its 16 samples are four 16-byte LDS reads, where the
+// channel-major window takes two 4-byte reads per sample.  The
+// interpolation is the same instruction sequence as sampler_cb's, so both
+// give the same bits.
+//
+// Staging transposes in registers: item (position word pw, channel octet
+// co) is one thread's; it loads positions 8pw .. 8pw+7 of its 8 channels
+// (eight 16-byte words of x; window segments start on words, so a word lies
+// wholly inside [0, L_in) or wholly outside) and writes 8 words, one per
+// position, of its 8 channels.  Block B's window is loaded into registers in
+// iteration B*nkb - 4 and written to LDS in iteration B*nkb - 2, after that
+// iteration's samples (its buffer's previous block is finished by then and
+// the block's first chunk is sampled in the next iteration); the first two
+// blocks of the workgroup's range are staged before the main loop.  Needs
+// nkb >= 2 (a block's window serves at least two chunks).
+constexpr int kTPitch = 40;  // bf16 elements per window row: 32 channels + 8 pad (80 bytes)
+
+template <bool MASK, int NPOS>
+__device__ __forceinline__ void sampler_cbt(const MfmaArgs &a, const Tile &tl, const Pos *s_tab,
+                                            const float *s_m, uint16_t *s_S, uint16_t *s_x, const int *s_lo,
+                                            const int *s_base) {
+    using Tr = TrBF16;
+    using T = uint16_t;
+    constexpr int BN = Geo<Tr>::BN, SLD = Tr::SLD, CB = 32;
+    constexpr int XBUF = NPOS * kTPitch;           // window buffer (elements)
+    constexpr int NITEM = (NPOS / 8) * (CB / 8);   // staging items per block
+    static_assert(NPOS % 8 == 0 && NITEM <= NTS, "at most one staging item per thread");
+    const Params &p = a.p;
+    const int ts = threadIdx.x - NTM;  // 0 .. NTS-1
+    const int lane = ts % 64;
+    const int sw = __builtin_amdgcn_readfirstlane(ts / 64);
+    const int h = sw & 1;
+    const int col = 64 * (sw >> 1) + lane;
+    const int K = p.K, L_in = p.L_in, C_in = p.C_in;
+    const int nkb = a.nkb;
+    const T *__restrict__ x = (const T *)p.x;
+    const int ic = 16 * h;  // this thread's first channel in a block
+
+    // ---- staging item of this thread
+    const bool has_item = ts < NITEM;
+    const int pw = ts >> 2, co = ts & 3;
+    int64_t ixoff = 0;
+    bool ival = false;
+    if (has_item && pw * 8 < tl.WT) {
+        const int jj = pw * 8;
+        int sg = 0;
+        while (sg + 1 < tl.nseg && s_base[sg + 1] <= jj) ++sg;
+        const int pos = s_lo[sg] + (jj - s_base[sg]);
+        ival = pos >= 0 && pos < L_in;
+        ixoff = (int64_t)(tl.b_first + sg) * C_in * L_in + (ival ? pos : 0);
+    }
+    u4 xr[8];
+    auto load_blk = [&](int blk) {
+        if (!has_item) return;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int ci = min(blk * CB + co * 8 + c, C_in - 1);
+            xr[c] = *(const u4 *)(x + ixoff + (int64_t)ci * L_in);
+        }
+    };
+    auto commit_blk = [&](int blk) {
+        if (!has_item) return;
+        uint32_t keep[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) keep[c] = (ival && blk * CB + co * 8 + c < C_in) ? 0xffffffffu : 0u;
+        T *dst = s_x + (blk & 1) * XBUF + pw * 8 * kTPitch + co * 8;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {  // positions 2q, 2q+1: dword q of every channel's word
+            u4 ev, od;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {  // channels 2i, 2i+1
+                const uint32_t lo = xr[2 * i][q] & keep[2 * i], hi = xr[2 * i + 1][q] & keep[2 * i + 1];
+                ev[i] = (lo & 0xffffu) | (hi << 16);
+                od[i] = (lo >> 16) | (hi & 0xffff0000u);
+            }
+            *(u4 *)(dst + (2 * q) * kTPitch) = ev;
+            *(u4 *)(dst + (2 * q + 1) * kTPitch) = od;
+        }
+    };
+
+    // ---- the 16 samples (channels ic .. ic+15 of the block, one tap) of this lane's column for chunk u.
+    // The chunk's position pair (and mask value) is read at the end of the
+    // previous chunk's samples, so that its LDS latency passes in the barrier.
+    Pos ps;
+    float mk;
+    auto fetch_pos = [&](int u) {
+        const int cb = (int)fdiv((uint32_t)u, a.fd_nkb), k = u - cb * nkb;  // one tap per chunk: kb is the tap
+        const int g = (int)fdiv((uint32_t)min(cb * CB + ic, C_in - 1), a.fd_cpo);
+        const int te = (g * K + k) * BN + col;
+        ps = s_tab[te];
+        mk = MASK ? s_m[te] : 1.0f;
+    };
+    auto sample = [&](int u) {
+        const int cb = (int)fdiv((uint32_t)u, a.fd_nkb);
+        const T *xw = s_x + (cb & 1) * XBUF + __umul24((uint32_t)ps.j, kTPitch) + ic;
+        const u4 a0 = *(const u4 *)xw, a1 = *(const u4 *)(xw + 8);
+        const u4 b0 = *(const u4 *)(xw + kTPitch), b1 = *(const u4 *)(xw + kTPitch + 8);
+        float x0[16], x1[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x0[2 * i] = __uint_as_float(a0[i] << 16);
+            x0[2 * i + 1] = __uint_as_float(a0[i] & 0xffff0000u);
+            x0[8 + 2 * i] = __uint_as_float(a1[i] << 16);
+            x0[8 + 2 * i + 1] = __uint_as_float(a1[i] & 0xffff0000u);
+            x1[2 * i] = __uint_as_float(b0[i] << 16);
+            x1[2 * i + 1] = __uint_as_float(b0[i] & 0xffff0000u);
+            x1[8 + 2 * i] = __uint_as_float(b1[i] << 16);
+            x1[8 + 2 * i + 1] = __uint_as_float(b1[i] & 0xffff0000u);
+        }
+        float v[16];
+#pragma unroll
+        for (int s2 = 0; s2 < 16; ++s2) {
+            float val = fmaf(ps.f, x1[s2] - x0[s2], x0[s2]);
+            if (MASK) val *= mk;
+            v[s2] = val;
+        }
+        Tr::store_b(s_S + (u & 1) * BN * SLD + col * SLD + 16 * h, v);
+        fetch_pos(min(u + 1, tl.c_end - 1));
+    };
+
+    const int c0 = tl.c_begin, c1 = tl.c_end;
+    const int b0 = c0 < c1 ? (int)fdiv((uint32_t)c0, a.fd_nkb) : 0;
+    fetch_pos(max(min(c0, c1 - 1), 0));
+    // prologue: blocks b0 and b0+1 in LDS; block b0+2 in registers when its
+    // regular load iteration lies before c0
+    if (c0 < c1) {
+        load_blk(b0);
+        commit_blk(b0);
+        if ((b0 + 1) * nkb < c1) {
+            load_blk(b0 + 1);
+            commit_blk(b0 + 1);
+        }
+        if ((b0 + 2) * nkb < c1 && (b0 + 2) * nkb - 4 < c0) load_blk(b0 + 2);
+    }
+    __syncthreads();
+    if (c0 < c1) sample(c0);
+    __syncthreads();
+    for (int c = c0; c < c1; ++c) {
+        if (c + 1 < c1) sample(c + 1);
+        // block (c+2)/nkb to LDS, then block (c+4)/nkb into registers (blocks
+        // from b0+2 on whose first chunk is inside the range)
+        const int bc = (int)fdiv((uint32_t)(c + 2), a.fd_nkb);
+        if (bc * nkb == c + 2 && bc >= b0 + 2 && c + 2 < c1) commit_blk(bc);
+        const int bl = (int)fdiv((uint32_t)(c + 4), a.fd_nkb);
+        if (bl * nkb == c + 4 && bl >= b0 + 2 && c + 4 < c1) load_blk(bl);
+        __syncthreads();
+    }
+}
+
+// The bf16 channel-block kernel with position-major windows (sampler_cbt);
+// tiles whose offsets spread wider than the window gather with sampler_cb.
+template <bool MASK, int NPOS>
+__global__ void __launch_bounds__(NTT) k_mfma_cbt(MfmaArgs a) {
+    using Tr = TrBF16;
+    using T = uint16_t;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    Pos *s_tab = (Pos *)smem;                   // [G*K][BN]
+    float *s_m = (float *)(smem + a.off_mask);  // [G*K][BN] if MASK
+    T *s_w = (T *)(smem + a.off_w);             // [2][BM][BK], swizzled
+    T *s_S = (T *)(smem + a.off_s);             // [2][BN][SLD]
+    T *s_x = (T *)(smem + a.off_x);             // [2][NPOS][kTPitch]
+    __shared__ int s_lo[NSEG], s_hi[NSEG], s_base[NSEG + 1];
+    __shared__ int s_win;
+    Tile tl;
+    setup_tile<Tr, MASK>(a, tl, s_tab, s_m, s_lo, s_hi, s_base, &s_win);
+    if (threadIdx.x < NTM)
+        mfma_role<Tr, 1>(a, tl, s_w, s_S);
+    else if (tl.win)
+        sampler_cbt<MASK, NPOS>(a, tl, s_tab, s_m, s_S, s_x, s_lo, s_base);
+    else
+        sampler_cb<Tr, MASK, false, 32, 1, 4>(a, tl, s_tab, s_m, s_S, s_x, s_lo, s_base);
+}
+
 template <class Tr, bool MASK, int CB, int SLOT, int LPP, bool DW>
 __global__ void __launch_bounds__(NTT) k_mfma_cb(MfmaArgs a) {
     using T = typename Tr::T;
@@ -1448,6 +1674,20 @@ void launch_cb_combo(int idx, const MfmaArgs &a, dim3 grid, size_t lds, hipStrea
     }
 }
 
+// Window sizes (positions) the position-major bf16 kernel is compiled for.
+constexpr int kTposOpts[] = {256, 320, 384, 512};
+constexpr int kNumTpos = sizeof(kTposOpts) / sizeof(kTposOpts[0]);
+
+template <bool MASK, int I>
+void launch_cbt(int npos, const MfmaArgs &a, dim3 grid, size_t lds, hipStream_t stream) {
+    if constexpr (I < kNumTpos) {
+        if (npos == kTposOpts[I])
+            hipLaunchKernelGGL((k_mfma_cbt<MASK, kTposOpts[I]>), grid, dim3(NTT), lds, stream, a);
+        else
+            launch_cbt<MASK, I + 1>(npos, a, grid, lds, stream);
+    }
+}
+
 template <class Tr, bool MASK>
 hipError_t launch_for(const Params &p, const MfmaPlan &pl, hipStream_t stream) {
     using T = typename Tr::T;
@@ -1479,7 +1719,8 @@ hipError_t launch_for(const Params &p, const MfmaPlan &pl, hipStream_t stream) {
         int variant = pl.variant;
         if (pl.variant_dw >= 0 && ((uintptr_t)p.w & 15) == 0) variant = pl.variant_dw;
         if (variant < 0 || variant >= kNumCbCombos) return hipErrorInvalidValue;
-        if (!kCbCombos[variant].dw) {
+        const bool cbt = std::is_same<Tr, TrBF16>::value && pl.tpos > 0 && a.vec_x;
+        if (cbt || !kCbCombos[variant].dw) {
             T *wb = (T *)p.ws;
             a.wb = wb;
             int tpc_log2 = 0;
@@ -1489,7 +1730,16 @@ hipError_t launch_for(const Params &p, const MfmaPlan &pl, hipStream_t stream) {
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
-        launch_cb_combo<Tr, MASK, 0>(variant, a, grid, pl.lds_bytes, stream);
+        if constexpr (std::is_same<Tr, TrBF16>::value) {
+            if (cbt) {
+                a.wt_max = pl.tpos;
+                launch_cbt<MASK, 0>(pl.tpos, a, grid, pl.lds_bytes, stream);
+            } else {
+                launch_cb_combo<Tr, MASK, 0>(variant, a, grid, pl.lds_bytes, stream);
+            }
+        } else {
+            launch_cb_combo<Tr, MASK, 0>(variant, a, grid, pl.lds_bytes, stream);
+        }
     } else {
         if (pl.variant < 0 || pl.variant >= kNumCombos) return hipErrorInvalidValue;
         launch_combo<Tr, MASK, 0>(pl.variant, a, grid, pl.lds_bytes, stream);

@@ -119,6 +119,13 @@ def _shape_cases():
         (3, 40, 64, 96, 3, 1, 1, 1, 1, 1, "bf16", True, 5.0),       # bf16 blocks of 16, 40 channels
         (2, 64, 96, 1024, 3, 2, 1, 1, 1, 2, "bf16", True, 8.0),     # bf16 stride 2, two-slot window
         (4, 24, 40, 52, 4, 1, 2, 2, 1, 1, "f32", False, 6.0),       # f32, 50 columns per batch
+        # bf16 blocks of 32 channels with position-major windows
+        (3, 64, 96, 96, 3, 1, 1, 1, 1, 2, "bf16", True, 5.0),       # tiles over three batches
+        (2, 96, 64, 256, 2, 1, 0, 1, 1, 1, "bf16", False, 3.0),     # two chunks per block (K = 2)
+        (1, 512, 64, 64, 3, 1, 0, 1, 1, 1, "bf16", True, 2.0),      # split reduction, ranges start mid-block
+        (1, 64, 64, 2048, 3, 1, 1, 1, 1, 2, "bf16", False, 200.0),  # offsets too wide: gathered tiles
+        (2, 80, 64, 160, 3, 1, 1, 1, 1, 5, "bf16", True, 3.0),      # a partial last block (80 channels)
+        (2, 64, 64, 800, 5, 2, 2, 2, 1, 1, "bf16", False, 6.0),     # stride 2, dilation 2: wider window
     ]
     for i, (B, C_in, C_out, L_in, K, s, p, d, groups, G, dt, mask, sc) in enumerate(spec):
         L_out = oracle.output_length(L_in, K, s, p, d)
@@ -145,7 +152,7 @@ def test_ragged_shapes_reach_every_kernel():
     # (fp32 blocks of 32 channels need more LDS than a workgroup has next to
     # the fp32 weight and sample tiles, so the planner never picks them)
     want = {"direct", "depthwise", "mfma_f32", "mfma_bf16", "mfma_f32_cb8", "mfma_f32_cb16", "mfma_bf16_cb8",
-            "mfma_bf16_cb16", "mfma_bf16_cb32"}
+            "mfma_bf16_cb16", "mfma_bf16_cb32", "mfma_bf16_cb32t"}
     assert want <= names, sorted(want - names)
 
 
