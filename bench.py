@@ -1,6 +1,6 @@
 """Benchmark of the DeformConv1d forward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--all]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--only]
 
 One step is one forward (the whole hot path: position split, interpolation,
 modulation, contraction, bias) over one batch of seeded synthetic inputs
@@ -9,16 +9,19 @@ dc1d page's layer shape (B16, C512 -> 512, K16, dilation 3, "valid", L128,
 fp32).  Prints ONE JSON line (rank 0, one GPU):
 
   value      contraction + sampling GFLOP per step / seconds per step
-  roofline   the achieved rate of one launch (one forward call: its
-             dominant kernel and any small kernels it enqueues, back to
-             back) against the dominant kernel's roofline peak, from HIP
-             events between consecutive forwards on the launch stream
+  roofline   the dominant kernel's achieved rate against its roofline peak:
+             algorithmic flops (MFMA-bound) or bytes (HBM-bound) of one
+             launch over that kernel's mean duration, from HIP events the
+             library records on the launch stream right before and after
+             its launch (kernel_ms); call_ms is the whole forward call
+             (the small kernels it also enqueues included)
   cpu_baseline  the CPU oracle timed on the host cores (reported baseline)
 
-Parity is checked in the same run (sampled outputs against the oracle)
-before timing; a mismatch aborts the bench.
-
---all additionally writes one JSON line per named workload to stderr.
+Parity is checked in the same run: every output of the GPU's forward
+against the oracle's (the CPU baseline's own last run); a mismatch aborts
+the bench.  Unless --only is given, each of the other named workloads is
+also timed and checked (every output against the oracle) and written as one
+JSON record to stderr, before the headline line.
 --profile-run runs only the warmup + timed launches (no oracle, no JSON),
 for rocprofv3; --copy-calibration MB runs one device-to-device copy of that
 size (the reference kernel for scaling the HBM byte counters).
@@ -187,12 +190,54 @@ def timed(step, steps, warmup, dev, graph=False):
     return {"region_ms": region, "launch_ms": launch, "eager_ms": eager_ms, "graph": True}
 
 
-def run_gpu(w, steps, warmup, check=True, cold_reps=0, constrained=False):
+def kernel_times(step, steps, dev):
+    """The dominant kernel's duration (ms) in each of `steps` steps, from HIP
+    events that the library records on the launch stream right before and
+    right after that kernel's launch (dc1d_set_kernel_events): the fused
+    sampling + MFMA kernel without the weight rearrangement before it and
+    the split reduction after it, or the depthwise / direct kernel."""
+    import torch
+    from deformable_convolution_amd import dc1d
+
+    stream = torch.cuda.current_stream(dev)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    for e in evs:
+        e.record(stream)  # creates the HIP events
+    torch.cuda.synchronize()
+    try:
+        for i in range(steps):
+            dc1d.set_kernel_events(evs[2 * i], evs[2 * i + 1])
+            step()
+    finally:
+        dc1d.set_kernel_events(None, None)
+    torch.cuda.synchronize()
+    return [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(steps)]
+
+
+def parity_of(w, got, ref):
+    """Elementwise comparison of GPU outputs with the oracle's (float64
+    arrays of the same elements): fp32 max|err| <= 1e-5 sqrt(C_in K / groups);
+    bf16 |err| <= 2e-2 max(|ref|, rms(ref)) elementwise."""
+    n = int(ref.size)
+    if w.dtype == "f32":
+        err = float(np.abs(got - ref).max())
+        tol = 1e-5 * math.sqrt(w.C_in * w.K / w.groups)
+        return {"elements": n, "max_err": err, "tol": tol, "ok": bool(err <= tol)}
+    rms = math.sqrt(float(np.mean(ref ** 2)))
+    worst = float((np.abs(got - ref) / (2e-2 * np.maximum(np.abs(ref), rms))).max())
+    return {"elements": n, "max_err_over_tol": worst, "tol": "2e-2*max(|ref|, rms(ref)) elementwise",
+            "ok": bool(worst <= 1.0)}
+
+
+def run_gpu(w, steps, warmup, cold_reps=0, constrained=False, t=None):
+    """Time the forward on the GPU.  Returns the plan, the timings and the
+    output of the first (untimed) call, for the parity check."""
     import torch
     from deformable_convolution_amd import dc1d, inputs
 
     dev = torch.device("cuda:0")
-    t = inputs.make_inputs(w, seed=0)
+    if t is None:
+        t = inputs.make_inputs(w, seed=0)
     g = {k: (v.to(dev) if v is not None else None) for k, v in t.items()}
     kw = dict(stride=w.stride, padding=w.padding, dilation=w.dilation, groups=w.groups)
     plan = dc1d.plan(g["x"], g["offsets"], g["weight"], g["bias"], g["mask"], **kw)
@@ -206,33 +251,12 @@ def run_gpu(w, steps, warmup, check=True, cold_reps=0, constrained=False):
 
     step()
     torch.cuda.synchronize()
-    parity = None
-    if check:
-        import oracle
-        rng = np.random.default_rng(1)
-        n = 512
-        pts = np.stack([rng.integers(0, w.B, n), rng.integers(0, w.C_out, n), rng.integers(0, w.L_out, n)], 1)
-        ref = oracle.forward_points(t["x"], t["offsets"], t["weight"], pts, t["bias"], t["mask"],
-                                    constrained=constrained, **kw)
-        got = out[pts[:, 0], pts[:, 1], pts[:, 2]].double().cpu().numpy()
-        if w.dtype == "f32":
-            err = float(np.abs(got - ref).max())
-            tol = 1e-5 * math.sqrt(w.C_in * w.K / w.groups)
-            ok = err <= tol
-        else:
-            rms = math.sqrt(float(np.mean(ref ** 2)))
-            err = float((np.abs(got - ref) / np.maximum(np.abs(ref), rms)).max())
-            tol = 2e-2
-            ok = err <= tol
-        parity = {"points": n, "max_err": err, "tol": tol, "ok": bool(ok)}
-        if not ok:
-            raise SystemExit("bench parity check failed: %r" % parity)
-
-    # Timed region: one HIP event on the launch stream before each forward and
-    # one after the last; forward i lasts ev[i] -> ev[i+1] (its kernels run
-    # back to back on that stream), the region ev[0] -> ev[steps].
+    first = out.clone()
+    # The timed region: one HIP event on the launch stream before each
+    # forward and one after the last; forward i lasts ev[i] -> ev[i+1] (its
+    # kernels run back to back on that stream), the region ev[0] -> ev[steps].
     tm = timed(step, steps, warmup, dev)
-    launch_ms, region_ms = tm["launch_ms"], tm["region_ms"]
+    kern = kernel_times(step, steps, dev)
     stream = torch.cuda.current_stream(dev)
     cold_ms = []
     if cold_reps:
@@ -248,8 +272,62 @@ def run_gpu(w, steps, warmup, check=True, cold_reps=0, constrained=False):
             torch.cuda.synchronize()
             cold_ms.append(a.elapsed_time(b))
         del flush
-    return {"plan": plan, "region_ms": region_ms, "launch_ms": launch_ms, "cold_ms": cold_ms, "parity": parity,
-            "eager_ms": tm["eager_ms"], "graph": tm["graph"]}
+    return {"plan": plan, "region_ms": tm["region_ms"], "launch_ms": tm["launch_ms"], "kernel_ms": kern,
+            "cold_ms": cold_ms, "eager_ms": tm["eager_ms"], "graph": tm["graph"], "out": first}
+
+
+def roofline_of(w, kern, kernel_ms, call_ms, constrained=False):
+    """The roofline object for a forward: algorithmic work of one launch over
+    the dominant kernel's mean duration (events around its launch), against
+    its peak (MFMA for the fused kernels, HBM otherwise)."""
+    contraction, _, nbytes = work(w)
+    if kern.startswith("mfma"):
+        peak = PEAK["mfma_f32_TFLOPs"] if w.dtype == "f32" else PEAK["mfma_bf16_TFLOPs"]
+        achieved = contraction / (kernel_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4)}
+    else:
+        achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm_GBps"], "unit": "GB/s",
+                "frac": round(achieved / PEAK["hbm_GBps"], 4)}
+    roof["traffic"] = read_traffic(w.name, kern + ("_constrained" if constrained else ""), kernel_hash(kern))
+    roof["kernel"] = kern
+    roof["kernel_ms"] = round(kernel_ms, 5)  # the dominant kernel alone (events around its launch)
+    roof["call_ms"] = round(call_ms, 5)      # the whole forward call (every kernel it enqueues)
+    return roof
+
+
+def oracle_reference(w, t, constrained=False):
+    """Every output of the workload from the oracle, and the seconds it took."""
+    import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+    kw = dict(stride=w.stride, padding=w.padding, dilation=w.dilation, groups=w.groups)
+    t0 = time.perf_counter()
+    ref = oracle.forward(t["x"], t["offsets"], t["weight"], t["bias"], t["mask"], constrained=constrained, **kw)
+    return ref, time.perf_counter() - t0
+
+
+def workload_line(w, steps, warmup):
+    """One stderr record: a workload's timing, roofline and full-output parity
+    against the oracle."""
+    from deformable_convolution_amd import inputs
+
+    t = inputs.make_inputs(w, seed=0)
+    r = run_gpu(w, steps, warmup, t=t)
+    ref, el = oracle_reference(w, t)
+    parity = parity_of(w, r["out"].double().cpu().numpy(), ref)
+    if not parity["ok"]:
+        raise SystemExit("bench parity check failed for %s: %r" % (w.name, parity))
+    contraction, sampling, nbytes = work(w)
+    ms = r["region_ms"] / steps
+    kern = r["plan"]["kernel"]
+    return {"workload": workload_label(w), "kernel": kern, "plan": r["plan"], "steps": steps,
+            "ms_per_step": round(ms, 5), "GFLOP/s": round((contraction + sampling) / (ms * 1e-3) / 1e9, 1),
+            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1), "parity": parity,
+            "roofline": roofline_of(w, kern, float(np.mean(r["kernel_ms"])), float(np.mean(r["launch_ms"]))),
+            "oracle_s": round(el, 2)}
 
 
 def work_backward(w):
@@ -338,8 +416,8 @@ def main_backward(args, w):
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm_GBps"], "unit": "GB/s",
                 "frac": round(achieved / PEAK["hbm_GBps"], 4)}
     roof["traffic"] = read_traffic(w.name, "backward", kernel_hash("backward"))
-    roof["kernel"] = "backward"
-    roof["kernel_ms"] = round(kern_ms, 5)
+    roof["kernel"] = "backward"  # the whole backward call (all its kernels)
+    roof["call_ms"] = round(kern_ms, 5)
     line = {
         "metric": "DeformConv1d bwd GFLOP/s (all five gradients)",
         "value": round((contraction + sampling) / (ms * 1e-3) / 1e9, 1),
@@ -445,7 +523,7 @@ def main_packed(args, w):
     achieved = pipeline / (kern_ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm_GBps"], "unit": "GB/s",
             "frac": round(achieved / PEAK["hbm_GBps"], 4), "traffic": read_traffic(w.name, "packed", kernel_hash("packed")),
-            "kernel": "packed", "kernel_ms": round(kern_ms, 5)}
+            "kernel": "packed", "call_ms": round(kern_ms, 5)}  # the whole layer call (all its kernels)
     line = {
         "metric": "Packed DeformConv1d fwd GFLOP/s (offset/mask generator + forward)",
         "value": round(flops / (ms * 1e-3) / 1e9, 1),
@@ -541,7 +619,7 @@ def main2d(args, w):
     achieved = contraction / (kern_ms * 1e-3) / 1e12
     roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": read_traffic(w.name, r["kernel"], kernel_hash(r["kernel"])),
-            "kernel": r["kernel"], "kernel_ms": round(kern_ms, 5)}
+            "kernel": r["kernel"], "call_ms": round(kern_ms, 5)}  # the whole call (sampler and GEMM)
     es = 4 if w.dtype == "f32" else 2
     s_bytes = 2 * w.B * (w.C_in // w.groups) * w.kh * w.kw * w.Ho * w.Wo * es  # the sampled matrix, out and back
     line = {
@@ -581,7 +659,9 @@ def cpu_model():
 
 def cpu_baseline(w, budget_s=12.0, max_reps=200, constrained=False):
     """The oracle, untouched, on this host's cores: full forwards of the same
-    workload repeated until about budget_s seconds have passed."""
+    workload repeated until about budget_s seconds have passed.  Returns the
+    baseline record and the last forward's output (every element, for the
+    parity check of the GPU's output)."""
     import oracle
     from deformable_convolution_amd import inputs
 
@@ -594,7 +674,8 @@ def cpu_baseline(w, budget_s=12.0, max_reps=200, constrained=False):
                    **kw)  # warm (untimed)
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.forward(t["x"], t["offsets"], t["weight"], t["bias"], t["mask"], constrained=constrained, **kw)
+        ref = oracle.forward(t["x"], t["offsets"], t["weight"], t["bias"], t["mask"], constrained=constrained,
+                             **kw)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= max_reps:
@@ -603,7 +684,7 @@ def cpu_baseline(w, budget_s=12.0, max_reps=200, constrained=False):
     return {"value": (contraction + sampling) * reps / el / 1e9, "unit": "GFLOP/s", "cores": min(threads, cores),
             "kind": "oracle",
             "sample": "%d full forward(s) of the same workload (all %d outputs each), %.1f s, on %s" % (
-                reps, w.B * w.C_out * w.L_out, el, cpu_model())}
+                reps, w.B * w.C_out * w.L_out, el, cpu_model())}, ref
 
 
 def main():
@@ -612,7 +693,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="dc1d_layer")
-    ap.add_argument("--all", action="store_true")
+    ap.add_argument("--only", action="store_true",
+                    help="time the named workload alone (no stderr records of the other workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--backward", action="store_true", help="time the backward (fp32 workloads) instead")
@@ -677,29 +759,37 @@ def main():
         main_backward(args, w)
         return
     if args.profile_run:
-        r = run_gpu(w, args.steps, args.warmup, check=False, constrained=args.constrained)
+        r = run_gpu(w, args.steps, args.warmup, constrained=args.constrained)
         print("profile run: %s %s, %d timed launches, %.4f ms/launch" % (
             w.name, r["plan"]["kernel"], args.steps, float(np.mean(r["launch_ms"]))), flush=True)
         return
 
-    r = run_gpu(w, args.steps, args.warmup, cold_reps=20, constrained=args.constrained)
+    # The other workloads first, one JSON record each on stderr (timing,
+    # roofline, full-output parity against the oracle), then the headline.
+    if not args.only:
+        for name in inputs.WORKLOAD_ORDER:
+            if name == w.name:
+                continue
+            rec = workload_line(inputs.WORKLOADS[name], max(10, args.steps // 2), args.warmup)
+            print(json.dumps(rec), file=sys.stderr, flush=True)
+
+    t = inputs.make_inputs(w, seed=0)
+    r = run_gpu(w, args.steps, args.warmup, cold_reps=20, constrained=args.constrained, t=t)
     contraction, sampling, nbytes = work(w)
     ms = r["region_ms"] / args.steps
-    kern_ms = float(np.mean(r["launch_ms"]))
     kern = r["plan"]["kernel"]
-    if kern.startswith("mfma"):
-        peak = PEAK["mfma_f32_TFLOPs"] if w.dtype == "f32" else PEAK["mfma_bf16_TFLOPs"]
-        achieved = contraction / (kern_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4)}
+    roof = roofline_of(w, kern, float(np.mean(r["kernel_ms"])), float(np.mean(r["launch_ms"])),
+                       constrained=args.constrained)
+    # parity: every output against the oracle's, from the CPU baseline's own
+    # run (or a run of its own when the baseline is not taken)
+    if args.no_cpu_baseline:
+        base = None
+        ref, _ = oracle_reference(w, t, constrained=args.constrained)
     else:
-        achieved = nbytes / (kern_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm_GBps"], "unit": "GB/s",
-                "frac": round(achieved / PEAK["hbm_GBps"], 4)}
-    traffic = read_traffic(w.name, kern + ("_constrained" if args.constrained else ""), kernel_hash(kern))
-    roof["traffic"] = traffic
-    roof["kernel"] = kern
-    roof["kernel_ms"] = round(kern_ms, 5)
+        base, ref = cpu_baseline(w, constrained=args.constrained)
+    parity = parity_of(w, r["out"].double().cpu().numpy(), ref)
+    if not parity["ok"]:
+        raise SystemExit("bench parity check failed: %r" % parity)
     line = {
         "metric": METRIC,
         "value": round((contraction + sampling) / (ms * 1e-3) / 1e9, 1),
@@ -714,28 +804,14 @@ def main():
         "dtype": "f32" if w.dtype == "f32" else "bf16",
         "data": "synthetic, seeded (deformable_convolution_amd/inputs.py; no dataset)",
         "config": {"workload": workload_label(w) + (" constrained" if args.constrained else ""), "plan": r["plan"],
-                   "gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "parity": r["parity"],
+                   "gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "parity": parity,
                    "timing": "graph replay" if r["graph"] else "eager",
-                   "forward_ms": {"warm": pct(r["launch_ms"]), "cold": pct(r["cold_ms"]),
-                                  "eager": pct(r["eager_ms"])}},
+                   "forward_ms": {"warm": pct(r["launch_ms"]), "kernel": pct(r["kernel_ms"]),
+                                  "cold": pct(r["cold_ms"]), "eager": pct(r["eager_ms"])}},
         "roofline": roof,
     }
-    if args.all:
-        for name in inputs.WORKLOAD_ORDER:
-            ww = inputs.WORKLOADS[name]
-            rr = run_gpu(ww, max(10, args.steps // 2), args.warmup)
-            c2, s2, b2 = work(ww)
-            m2 = float(np.mean(rr["launch_ms"]))
-            rec = {"workload": workload_label(ww), "kernel": rr["plan"]["kernel"], "plan": rr["plan"],
-                   "ms": round(m2, 5), "GFLOP/s": round((c2 + s2) / (m2 * 1e-3) / 1e9, 1),
-                   "GB/s": round(b2 / (m2 * 1e-3) / 1e9, 1), "parity": rr["parity"]}
-            if rr["plan"]["kernel"].startswith("mfma"):
-                pk = PEAK["mfma_f32_TFLOPs"] if ww.dtype == "f32" else PEAK["mfma_bf16_TFLOPs"]
-                rec["mfma_frac"] = round(c2 / (m2 * 1e-3) / 1e12 / pk, 4)
-            rec["hbm_frac"] = round(b2 / (m2 * 1e-3) / 1e9 / PEAK["hbm_GBps"], 4)
-            print(json.dumps(rec), file=sys.stderr, flush=True)
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, constrained=args.constrained)
+    if base is not None:
+        line["cpu_baseline"] = base
     print(json.dumps(line), flush=True)
 
 

@@ -22,6 +22,9 @@ struct DeviceInfo {
 std::once_flag g_dev_once[kMaxDevices];
 DeviceInfo g_dev[kMaxDevices];
 
+// Profiling hook (dc1d_set_kernel_events): per calling thread.
+thread_local void *t_ev_start = nullptr, *t_ev_stop = nullptr;
+
 // The current device's capability, probed once per device.
 int current_device(DeviceInfo *info) {
     int dev = -1;
@@ -289,12 +292,22 @@ int forward_impl(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_te
     if (p.B == 0) return DC1D_OK;
     p.ws = workspace;
     p.ws_bytes = workspace_bytes;
+    p.ev_start = t_ev_start;
+    p.ev_stop = t_ev_stop;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     switch (pl.kernel) {
     case kMfma: e = launch_mfma(p, pl.mfma, s); break;
-    case kDepthwise: e = launch_depthwise(p, pl.dw, s); break;
-    default: e = launch_direct(p, s); break;
+    case kDepthwise:
+        mark_event(p.ev_start, s);
+        e = launch_depthwise(p, pl.dw, s);
+        mark_event(p.ev_stop, s);
+        break;
+    default:
+        mark_event(p.ev_start, s);
+        e = launch_direct(p, s);
+        mark_event(p.ev_stop, s);
+        break;
     }
     return e == hipSuccess ? DC1D_OK : DC1D_ERR_LAUNCH;
 }
@@ -320,6 +333,13 @@ int dc1d_forward_noalloc(const dc1d_tensor *x, const dc1d_tensor *offsets, const
 }
 
 size_t dc1d_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int dc1d_set_kernel_events(void *start_event, void *stop_event) {
+    if ((start_event == nullptr) != (stop_event == nullptr)) return DC1D_ERR_NULL_PTR;
+    t_ev_start = start_event;
+    t_ev_stop = stop_event;
+    return DC1D_OK;
+}
 
 int dc1d_forward_constrained(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_tensor *mask_or_null,
                              const dc1d_tensor *weight, const dc1d_tensor *bias_or_null, const dc1d_tensor *out,

@@ -30,7 +30,15 @@ struct Params {
     int constrained;  // taps kept inside the undeformed kernel window (tap_range)
     void *ws;
     size_t ws_bytes;
+    // profiling: HIP events recorded on the launch stream right before and
+    // right after the call's dominant kernel (null: none)
+    void *ev_start, *ev_stop;
 };
+
+// Records a profiling event (see Params::ev_start) when one is set.
+inline void mark_event(void *ev, hipStream_t stream) {
+    if (ev) (void)hipEventRecord((hipEvent_t)ev, stream);
+}
 
 // Division by a run-time invariant d >= 1 for numerators n < 2^31:
 // q = (umulhi(n, mul) + n) >> shift, with 2^shift >= d and

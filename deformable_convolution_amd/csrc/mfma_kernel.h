@@ -1730,6 +1730,7 @@ hipError_t launch_for(const Params &p, const MfmaPlan &pl, hipStream_t stream) {
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
+        mark_event(p.ev_start, stream);
         if constexpr (std::is_same<Tr, TrBF16>::value) {
             if (cbt) {
                 a.wt_max = pl.tpos;
@@ -1740,9 +1741,12 @@ hipError_t launch_for(const Params &p, const MfmaPlan &pl, hipStream_t stream) {
         } else {
             launch_cb_combo<Tr, MASK, 0>(variant, a, grid, pl.lds_bytes, stream);
         }
+        mark_event(p.ev_stop, stream);
     } else {
         if (pl.variant < 0 || pl.variant >= kNumCombos) return hipErrorInvalidValue;
+        mark_event(p.ev_start, stream);
         launch_combo<Tr, MASK, 0>(pl.variant, a, grid, pl.lds_bytes, stream);
+        mark_event(p.ev_stop, stream);
     }
     if (pl.splits > 1) {
         const hipError_t e = hipGetLastError();

@@ -80,6 +80,8 @@ def load_library():
             lib.dc1d_forward_noalloc.argtypes = [T] * 6 + [i64] * 5 + [p]
             lib.dc1d_noalloc_scratch_bytes.restype = ctypes.c_size_t
             lib.dc1d_noalloc_scratch_bytes.argtypes = []
+            lib.dc1d_set_kernel_events.restype = ctypes.c_int
+            lib.dc1d_set_kernel_events.argtypes = [p, p]
             lib.dc1d_forward_constrained.restype = ctypes.c_int
             lib.dc1d_forward_constrained.argtypes = lib.dc1d_forward.argtypes
             lib.dc1d_backward_constrained.restype = ctypes.c_int
@@ -239,6 +241,13 @@ def forward_noalloc(x, offsets, weight, bias=None, mask=None, stride=1, padding=
         _check(lib.dc1d_forward_noalloc(_ref(dx), _ref(do), _ref(dm), _ref(dw), _ref(db), _ref(dout), stride,
                                         padding, dilation, groups, G, stream), "dc1d_forward_noalloc")
     return out
+
+
+def set_kernel_events(start=None, stop=None):
+    """dc1d_set_kernel_events for this thread: torch.cuda.Event objects (already
+    recorded once, so that their HIP events exist), or None, None."""
+    h = (lambda e: None if e is None else ctypes.c_void_p(e.cuda_event))
+    _check(load_library().dc1d_set_kernel_events(h(start), h(stop)), "dc1d_set_kernel_events")
 
 
 def noalloc_scratch_bytes() -> int:

@@ -181,6 +181,21 @@ int dc1d_forward_noalloc(const dc1d_tensor *x, const dc1d_tensor *offsets, const
 size_t dc1d_noalloc_scratch_bytes(void);
 
 /*
+ * Profiling aid.  While set, every forward call made on the calling thread
+ * (dc1d_forward, dc1d_forward_constrained, dc1d_forward_noalloc) records
+ * start_event on its stream immediately before it launches its dominant
+ * kernel (the fused sampling + MFMA kernel, or the depthwise or direct
+ * kernel) and stop_event immediately after, so that the elapsed time
+ * between them is that kernel's alone, without the small kernels the call
+ * may also enqueue (the weight rearrangement before it, the split
+ * reduction after it).  Both are hipEvent_t handles owned by the caller,
+ * passed as void*; (NULL, NULL) turns the hook off.  The setting is
+ * per thread and changes no result.  Returns DC1D_ERR_NULL_PTR when exactly
+ * one of the two is NULL.
+ */
+int dc1d_set_kernel_events(void *start_event, void *stop_event);
+
+/*
  * Constrained mode: dc1d_forward with every tap kept inside its receptive
  * field (the dc1d page's default, section Usage / DeformConv1d: each kernel
  * tap is constrained to its own receptive field unless the layer is made

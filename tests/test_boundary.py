@@ -278,3 +278,10 @@ def test_empty_image_rejected(lib):
                                 None) == dc1d.ERR_BAD_SHAPE
         assert lib.dc2d_workspace_bytes(r(x), r(off), None, r(w), None, 1, 1, 2, 2, 1, 1, 1, 1,
                                         r(n)) == dc1d.ERR_BAD_SHAPE
+
+
+def test_kernel_events_arguments(lib):
+    # both events or neither (no device needed: only the per-thread setting)
+    assert lib.dc1d_set_kernel_events(None, ctypes.c_void_p(FAKE)) == dc1d.ERR_NULL_PTR
+    assert lib.dc1d_set_kernel_events(ctypes.c_void_p(FAKE), None) == dc1d.ERR_NULL_PTR
+    assert lib.dc1d_set_kernel_events(None, None) == dc1d.OK

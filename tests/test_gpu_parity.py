@@ -357,3 +357,27 @@ def test_full_size_sampled(name):
         rms = math.sqrt(float(np.mean(ref ** 2)))
         assert (np.abs(gv - ref) <= 2e-2 * np.maximum(np.abs(ref), rms)).all()
     assert torch.isfinite(got).all()
+
+
+@pytest.mark.parametrize("name", ["dc1d_layer", "dcnv2_bf16", "depthwise"])
+def test_kernel_events_bracket_the_dominant_kernel(name):
+    """dc1d_set_kernel_events: the events a forward records around its
+    dominant kernel lie inside the call and change no result."""
+    w = inputs.WORKLOADS[name].with_batch(2)
+    g = to_dev(inputs.make_inputs(w, seed=2))
+    ref = gpu_forward(w, g)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    dc1d.set_kernel_events(ev[1], ev[2])
+    try:
+        ev[0].record()
+        out = gpu_forward(w, g)
+        ev[3].record()
+    finally:
+        dc1d.set_kernel_events(None, None)
+    torch.cuda.synchronize()
+    kernel, call = ev[1].elapsed_time(ev[2]), ev[0].elapsed_time(ev[3])
+    assert 0.0 < kernel <= call, (kernel, call)
+    assert torch.equal(out, ref)
