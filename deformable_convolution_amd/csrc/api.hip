@@ -2,6 +2,8 @@
 // kernel choice, and launch.  No allocation, no synchronisation, no
 // exceptions across the boundary.
 #include <mutex>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "dc1d.h"
@@ -25,6 +27,18 @@ DeviceInfo g_dev[kMaxDevices];
 // Profiling hook (dc1d_set_kernel_events): per calling thread.
 thread_local void *t_ev_start = nullptr, *t_ev_stop = nullptr;
 
+// Dispatch log: with the environment variable DC1D_LOG set to a non-zero
+// value when the library first looks, every call that launches work writes
+// one line to stderr (entry, shapes, dtype, the kernel chosen, its grid and
+// split count, workspace bytes).  Read once.
+bool log_on() {
+    static const bool on = [] {
+        const char *v = getenv("DC1D_LOG");
+        return v && v[0] && strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
 // The current device's capability, probed once per device.
 int current_device(DeviceInfo *info) {
     int dev = -1;
@@ -47,11 +61,24 @@ int current_device(DeviceInfo *info) {
     return info->gfx950 ? DC1D_OK : DC1D_ERR_DEVICE;
 }
 
-int64_t numel(const dc1d_tensor *t) {
+// The element count of a tensor, or -1 when its rank is outside 0..4, a
+// dimension is negative, or the count exceeds kMaxElems; each product is
+// checked before it is formed, so no arithmetic overflows.
+constexpr int64_t kMaxElems = (int64_t)1 << 48;
+int64_t numel_checked(const dc1d_tensor *t) {
+    if (t->ndim < 0 || t->ndim > 4) return -1;
     int64_t n = 1;
-    for (int i = 0; i < t->ndim; ++i) n *= t->shape[i];
+    for (int i = 0; i < t->ndim; ++i) {
+        const int64_t s = t->shape[i];
+        if (s < 0) return -1;
+        if (s > 0 && n > kMaxElems / s) return -1;
+        n *= s;
+    }
     return n;
 }
+
+// The element count of a tensor that validation has accepted.
+int64_t numel(const dc1d_tensor *t) { return numel_checked(t); }
 
 size_t elem_size(int dtype) { return dtype == DC1D_F32 ? 4 : 2; }
 
@@ -80,15 +107,26 @@ int validate(const dc1d_tensor *x, const dc1d_tensor *off, const dc1d_tensor *ma
     // an empty input sequence has nothing to sample (conv1d rejects it too),
     // and the kernels' samplers assume at least one element per row
     if (B < 0 || C_in < 1 || L_in < 1 || C_out < 1 || K < 1) return DC1D_ERR_BAD_SHAPE;
+    // every size bounded on its own before any product of two is formed
+    const int64_t lim30 = (int64_t)1 << 30;
+    if (L_in > kMaxPos || padding > kMaxPos || K > kMaxPos || dilation > kMaxPos || stride > lim30 ||
+        C_in > lim30 || C_out > lim30 || B > lim30 || offset_groups > lim30)
+        return DC1D_ERR_BAD_SHAPE;
     if (C_in % groups || C_out % groups || C_in % offset_groups) return DC1D_ERR_BAD_ARG;
     if (off->shape[1] != offset_groups) return DC1D_ERR_BAD_ARG;
     if (w->shape[1] != C_in / groups) return DC1D_ERR_BAD_SHAPE;
     // size limits that keep all position arithmetic inside int32
-    if (L_in + padding > kMaxPos || dilation * (K - 1) > kMaxPos || C_in * K > ((int64_t)1 << 30) ||
-        C_out > ((int64_t)1 << 30) || B > ((int64_t)1 << 30) || offset_groups * K > ((int64_t)1 << 30))
+    if (L_in + padding > kMaxPos || dilation * (K - 1) > kMaxPos || C_in * K > lim30 ||
+        offset_groups * K > lim30)
         return DC1D_ERR_BAD_SHAPE;
     const int64_t L_out = dc1d_output_length(L_in, K, stride, padding, dilation);
-    if (L_out < 1 || L_out * stride > ((int64_t)1 << 30)) return DC1D_ERR_BAD_SHAPE;
+    if (L_out < 1 || L_out * stride > lim30) return DC1D_ERR_BAD_SHAPE;
+    // the sampled tensor [B, C_in, K, L_out] (the backward's workspace holds
+    // it) and every operand stay countable
+    if (B > 0 && C_in * K * B > kMaxElems / L_out) return DC1D_ERR_BAD_SHAPE;
+    const dc1d_tensor *ts[6] = {x, off, mask, w, bias, out};
+    for (const dc1d_tensor *t : ts)
+        if (t && numel_checked(t) < 0) return DC1D_ERR_BAD_SHAPE;
     const int64_t so[4] = {B, offset_groups, L_out, K};
     if (!shape_is(off, 4, so)) return DC1D_ERR_BAD_SHAPE;
     if (mask && !shape_is(mask, 4, so)) return DC1D_ERR_BAD_SHAPE;
@@ -290,6 +328,13 @@ int forward_impl(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_te
                 return DC1D_ERR_ALIAS;
     }
     if (p.B == 0) return DC1D_OK;
+    if (log_on())
+        fprintf(stderr,
+                "dc1d: %s B=%d C_in=%d C_out=%d L_in=%d L_out=%d K=%d s=%d p=%d d=%d groups=%d G=%d mask=%d %s "
+                "-> %s grid=%lld block=%d splits=%d ws=%zu\n",
+                use_scratch ? "forward_noalloc" : (constrained ? "forward_constrained" : "forward"), p.B, p.C_in,
+                p.C_out, p.L_in, p.L_out, p.K, p.stride, p.padding, p.dilation, p.groups, p.G, p.mask != nullptr,
+                p.dtype == DC1D_F32 ? "f32" : "bf16", pl.name, (long long)pl.grid, pl.block, pl.splits, pl.ws_bytes);
     p.ws = workspace;
     p.ws_bytes = workspace_bytes;
     p.ev_start = t_ev_start;
@@ -445,6 +490,14 @@ int backward_impl(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_t
         for (const dc1d_tensor *t : ins)
             if (t && overlaps(workspace, need, t->data, (size_t)numel(t) * 4)) return DC1D_ERR_ALIAS;
     }
+    if (log_on())
+        fprintf(stderr,
+                "dc1d: %s B=%d C_in=%d C_out=%d L_in=%d L_out=%d K=%d s=%d p=%d d=%d groups=%d G=%d mask=%d f32 "
+                "grads=%s%s%s%s%s ws=%zu\n",
+                constrained ? "backward_constrained" : "backward", p.B, p.C_in, p.C_out, p.L_in, p.L_out, p.K,
+                p.stride, p.padding, p.dilation, p.groups, p.G, p.mask != nullptr, grad_x_or_null ? "x," : "",
+                grad_offsets_or_null ? "offsets," : "", grad_mask_or_null ? "mask," : "",
+                grad_weight_or_null ? "weight," : "", grad_bias_or_null ? "bias" : "", need);
     BwdParams a;
     a.p = p;
     a.dout = (const float *)grad_out->data;
@@ -555,6 +608,11 @@ int validate_packed(const dc1d_tensor *x, const dc1d_tensor *tw, const dc1d_tens
     if (off_out && !shape_is(off_out, 4, offT.shape)) return DC1D_ERR_BAD_SHAPE;
     if (mask_out && !shape_is(mask_out, 4, offT.shape)) return DC1D_ERR_BAD_SHAPE;
     if (B * L_out >= ((int64_t)1 << 31)) return DC1D_ERR_BAD_SHAPE;
+    // the trunk [B, C_in, L_out] stays countable (B*L_out < 2^31, C_in <= 2^30)
+    if (C_in * (B * L_out) > kMaxElems) return DC1D_ERR_BAD_SHAPE;
+    const dc1d_tensor *ps[6] = {tw, tb, ow, ob, mw, mb};
+    for (const dc1d_tensor *t : ps)
+        if (t && numel_checked(t) < 0) return DC1D_ERR_BAD_SHAPE;
     pk->G = (int)G;
     pk->K = (int)K;
     pk->ow = (const float *)ow->data;
@@ -666,6 +724,12 @@ int packed_forward_impl(const dc1d_tensor *x, const dc1d_tensor *trunk_weight,
         for (const dc1d_tensor *t : outs)
             if (t && overlaps(workspace, pk.total, t->data, (size_t)numel(t) * 4)) return DC1D_ERR_ALIAS;
     }
+    if (log_on())
+        fprintf(stderr, "dc1d: %s B=%d C_in=%d C_out=%d L_in=%d L_out=%d K=%d s=%d p=%d d=%d groups=%d G=%d mask=%d "
+                        "f32 -> trunk, heads GEMM, %s ws=%zu\n",
+                constrained ? "packed_forward_constrained" : "packed_forward", pk.fwd.B, pk.fwd.C_in, pk.fwd.C_out,
+                pk.fwd.L_in, pk.fwd.L_out, pk.K, pk.fwd.stride, pk.fwd.padding, pk.fwd.dilation, pk.fwd.groups,
+                pk.G, pk.mw != nullptr, make_plan(pk.fwd, dev).name, pk.total);
     if (pk.fwd.B == 0) return DC1D_OK;
 
     char *ws = (char *)workspace;
@@ -764,17 +828,26 @@ int validate2d(const dc1d_tensor *x, const dc1d_tensor *off, const dc1d_tensor *
     const int64_t C_out = w->shape[0], kh = w->shape[2], kw = w->shape[3];
     // an empty image has nothing to sample; the samplers assume H, W >= 1
     if (B < 0 || C_in < 1 || H < 1 || W < 1 || C_out < 1 || kh < 1 || kw < 1) return DC1D_ERR_BAD_SHAPE;
+    // every size bounded on its own before any product of two is formed
+    const int64_t lim30 = (int64_t)1 << 30;
+    if (H > kMaxPos || W > kMaxPos || ph > kMaxPos || pw > kMaxPos || kh > kMaxPos || kw > kMaxPos ||
+        dh > kMaxPos || dw > kMaxPos || sh > lim30 || sw > lim30 || C_in > lim30 || C_out > lim30 || B > 65535 ||
+        offset_groups > ((int64_t)1 << 24))
+        return DC1D_ERR_BAD_SHAPE;
     if (C_in % groups || C_out % groups || C_in % offset_groups) return DC1D_ERR_BAD_ARG;
     if (w->shape[1] != C_in / groups) return DC1D_ERR_BAD_SHAPE;
+    if (kh * kw > lim30) return DC1D_ERR_BAD_SHAPE;
     const int64_t T = kh * kw;
     if (H + ph > kMaxPos || W + pw > kMaxPos || dh * (kh - 1) > kMaxPos || dw * (kw - 1) > kMaxPos ||
-        H * W >= ((int64_t)1 << 31) || C_in / groups * T > ((int64_t)1 << 30) || C_out > ((int64_t)1 << 30) ||
-        offset_groups * T > ((int64_t)1 << 24) || B > 65535)
+        H * W >= ((int64_t)1 << 31) || C_in / groups * T > lim30 || offset_groups * T > ((int64_t)1 << 24))
         return DC1D_ERR_BAD_SHAPE;
     const int64_t Ho = dc1d_output_length(H, kh, sh, ph, dh), Wo = dc1d_output_length(W, kw, sw, pw, dw);
-    if (Ho < 1 || Wo < 1 || Ho * sh > ((int64_t)1 << 30) || Wo * sw > ((int64_t)1 << 30) ||
+    if (Ho < 1 || Wo < 1 || Ho * sh > lim30 || Wo * sw > lim30 || Ho * Wo >= ((int64_t)1 << 31) ||
         B * Ho * Wo >= ((int64_t)1 << 31))
         return DC1D_ERR_BAD_SHAPE;
+    const dc1d_tensor *ts[6] = {x, off, mask, w, bias, out};
+    for (const dc1d_tensor *t : ts)
+        if (t && numel_checked(t) < 0) return DC1D_ERR_BAD_SHAPE;
     const int64_t so[4] = {B, 2 * offset_groups * T, Ho, Wo};
     if (!shape_is(off, 4, so)) return DC1D_ERR_BAD_SHAPE;
     const int64_t sm[4] = {B, offset_groups * T, Ho, Wo};
@@ -871,6 +944,11 @@ int dc2d_forward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_te
         for (int i = 0; i < 6; ++i)
             if (all[i] && overlaps(workspace, need, all[i]->data, (size_t)numel(all[i]) * es)) return DC1D_ERR_ALIAS;
     }
+    if (log_on())
+        fprintf(stderr, "dc1d: dc2d_forward B=%d C_in=%d C_out=%d %dx%d -> %dx%d k=%dx%d groups=%d G=%d mask=%d %s "
+                        "-> %s ws=%zu\n",
+                p.B, p.C_in, p.C_out, p.H, p.W, p.Ho, p.Wo, p.kh, p.kw, p.groups, p.G, p.mask != nullptr,
+                p.dtype == DC1D_F32 ? "f32" : "bf16", dc2d_kernel_name(p), need);
     p.ws = workspace;
     p.ws_bytes = workspace_bytes;
     const hipError_t e = launch_dc2d(p, dev.num_cus, (hipStream_t)stream);
@@ -884,11 +962,15 @@ int dc1d_debug_positions(const dc1d_tensor *offsets, int64_t L_in, int64_t strid
     if (offsets->ndim != 4) return DC1D_ERR_BAD_SHAPE;
     if (offsets->dtype != DC1D_F32 && offsets->dtype != DC1D_BF16) return DC1D_ERR_BAD_DTYPE;
     const int64_t K = offsets->shape[3];
-    if (K < 1 || L_in + padding > kMaxPos || dilation * (K - 1) > kMaxPos) return DC1D_ERR_BAD_SHAPE;
-    const int64_t L_out = dc1d_output_length(L_in, K, stride, padding, dilation);
-    if (L_out < 1 || offsets->shape[2] != L_out || offsets->shape[0] < 0 || offsets->shape[1] < 1)
+    if (K < 1 || K > kMaxPos || L_in > kMaxPos || padding > kMaxPos || dilation > kMaxPos ||
+        L_in + padding > kMaxPos || dilation * (K - 1) > kMaxPos)
         return DC1D_ERR_BAD_SHAPE;
-    const int64_t n = numel(offsets);
+    const int64_t L_out = dc1d_output_length(L_in, K, stride, padding, dilation);
+    if (L_out < 1 || L_out * (stride > kMaxPos ? kMaxPos : stride) > ((int64_t)1 << 30) ||
+        offsets->shape[2] != L_out || offsets->shape[0] < 0 || offsets->shape[1] < 1)
+        return DC1D_ERR_BAD_SHAPE;
+    const int64_t n = numel_checked(offsets);
+    if (n < 0 || n >= ((int64_t)1 << 40)) return DC1D_ERR_BAD_SHAPE;
     if (n > 0 && (!offsets->data || !i0 || !frac || !valid)) return DC1D_ERR_NULL_PTR;
     DeviceInfo dev;
     int st = current_device(&dev);

@@ -980,30 +980,36 @@ DxgPlan plan_dxg(const Params &p) {
 // with global atomics once every owned run is stored.  Runs only if one was
 // seen.
 template <int KT>
+// A small grid strides over the (row, tile) units: when no sample moved that
+// far (the usual case) the pass costs one flag read per block.
 __global__ void __launch_bounds__(256) k_bwd_dwg_fix(BwdParams a, int tiles_l, const int *flag) {
     if (*flag == 0) return;
     const Params &p = a.p;
-    const int tile = blockIdx.x % tiles_l;
-    const int row = blockIdx.x / tiles_l;
-    const int c = row % p.C_in, b = row / p.C_in;
-    const int g = c / p.cpo;
-    const int64_t orow = ((int64_t)b * p.G + g) * p.L_out;
-    const float *__restrict__ w = (const float *)p.w + (int64_t)c * KT;
-    float *__restrict__ gxr = a.gx + (int64_t)row * p.L_in;
-    const int l1 = min((tile + 1) * kDwgLT, p.L_out);
-    for (int l = tile * kDwgLT + threadIdx.x; l < l1; l += 256) {
-        const float d = a.dout[(int64_t)row * p.L_out + l];
-        for (int k = 0; k < KT; ++k) {
-            const int64_t oi = (orow + l) * KT + k;
-            int i0;
-            float f;
-            const int base = l * p.stride - p.padding + k * p.dilation;
-            split_position(((const float *)p.off)[oi], base, tap_range(p, k), i0, f);
-            const int fl = i0 - base;
-            if (fl >= -kDwgR && fl <= kDwgR) continue;
-            const float dm = w[k] * d * (p.mask ? ((const float *)p.mask)[oi] : 1.0f);
-            if (i0 >= 0 && i0 < p.L_in) unsafeAtomicAdd(gxr + i0, dm * (1.0f - f));
-            if (i0 + 1 >= 0 && i0 + 1 < p.L_in) unsafeAtomicAdd(gxr + i0 + 1, dm * f);
+    const int64_t units = (int64_t)p.B * p.C_in * tiles_l;
+    for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+        const int tile = (int)(u % tiles_l);
+        const int64_t row = u / tiles_l;
+        const int c = (int)(row % p.C_in);
+        const int64_t b = row / p.C_in;
+        const int g = c / p.cpo;
+        const int64_t orow = (b * p.G + g) * p.L_out;
+        const float *__restrict__ w = (const float *)p.w + (int64_t)c * KT;
+        float *__restrict__ gxr = a.gx + row * p.L_in;
+        const int l1 = min((tile + 1) * kDwgLT, p.L_out);
+        for (int l = tile * kDwgLT + threadIdx.x; l < l1; l += 256) {
+            const float d = a.dout[row * p.L_out + l];
+            for (int k = 0; k < KT; ++k) {
+                const int64_t oi = (orow + l) * KT + k;
+                int i0;
+                float f;
+                const int base = l * p.stride - p.padding + k * p.dilation;
+                split_position(((const float *)p.off)[oi], base, tap_range(p, k), i0, f);
+                const int fl = i0 - base;
+                if (fl >= -kDwgR && fl <= kDwgR) continue;
+                const float dm = w[k] * d * (p.mask ? ((const float *)p.mask)[oi] : 1.0f);
+                if (i0 >= 0 && i0 < p.L_in) unsafeAtomicAdd(gxr + i0, dm * (1.0f - f));
+                if (i0 + 1 >= 0 && i0 + 1 < p.L_in) unsafeAtomicAdd(gxr + i0 + 1, dm * f);
+            }
         }
     }
 }
@@ -1038,6 +1044,11 @@ unsigned grid_for(int64_t n) {
     const int64_t b = (n + 255) / 256;
     return (unsigned)(b < (1 << 20) ? (b > 0 ? b : 1) : (1 << 20));
 }
+
+// Grid of the flagged fix passes (grid-stride kernels that usually return at
+// once): small, so that the no-op case costs a few microseconds.
+constexpr int64_t kFixBlocks = 512;
+unsigned fix_grid(int64_t units) { return (unsigned)std::max<int64_t>(1, std::min<int64_t>(units, kFixBlocks)); }
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
@@ -1190,7 +1201,9 @@ hipError_t launch_backward_dw(BwdParams a, int *flag, hipStream_t stream, bool *
     case KK:                                                                                                       \
         hipLaunchKernelGGL((k_bwd_dwg<KK>), grid, dim3(kDwgT), g.lds, stream, a, g.win, g.nhp, tiles_g, flag,     \
                            bias_here);                                                                             \
-        if (a.gx) hipLaunchKernelGGL((k_bwd_dwg_fix<KK>), grid, dim3(256), 0, stream, a, tiles_g, (const int *)flag); \
+        if (a.gx)                                                                                                  \
+            hipLaunchKernelGGL((k_bwd_dwg_fix<KK>), dim3(fix_grid((int64_t)p.B * p.C_in * tiles_g)), dim3(256), 0,  \
+                               stream, a, tiles_g, (const int *)flag);                                             \
         break;
             DC1D_BDWG(1)
             DC1D_BDWG(2)
@@ -1277,7 +1290,8 @@ hipError_t launch_backward(BwdParams a, int num_cus, hipStream_t stream) {
                 hipLaunchKernelGGL((k_bwd_dxg<4>), grid, dim3(256), xg.lds, stream, a, xg, flag);
             else
                 hipLaunchKernelGGL((k_bwd_dxg<1>), grid, dim3(256), xg.lds, stream, a, xg, flag);
-            hipLaunchKernelGGL(k_bwd_dxg_fix, dim3(grid_for(no)), dim3(256), 0, stream, a, (const int *)flag);
+            hipLaunchKernelGGL(k_bwd_dxg_fix, dim3(fix_grid((no + 255) / 256)), dim3(256), 0, stream, a,
+                               (const int *)flag);
         }
         if (a.gw) {
             if (dense) {

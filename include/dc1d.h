@@ -48,6 +48,11 @@
  * stream's work is done.  Calls are re-entrant; calls that share a workspace
  * must be ordered on one stream.
  *
+ * Logging: with the environment variable DC1D_LOG set to a non-zero value
+ * (read once, at the first call that launches work), each such call writes
+ * one line to stderr naming the entry, the shapes, the dtype, the kernel
+ * chosen, its grid and split count and the workspace bytes.
+ *
  * Errors: every entry returns a dc1d_status.  Errors detected on the host
  * return before any device work and write nothing.  Faults inside a kernel
  * surface at the caller's next synchronisation.  No C++ exception crosses
