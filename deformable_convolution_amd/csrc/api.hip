@@ -408,20 +408,60 @@ int validate_backward(const dc1d_tensor *x, const dc1d_tensor *off, const dc1d_t
     if (!gout) return DC1D_ERR_NULL_PTR;
     int st = validate(x, off, mask, w, nullptr, gout, stride, padding, dilation, groups, offset_groups, p);
     if (st) return st;
-    if (p->dtype != DC1D_F32) return DC1D_ERR_BAD_DTYPE;
     if (gmask && !mask) return DC1D_ERR_BAD_ARG;
+    // every gradient has its input's dtype
     const dc1d_tensor *pairs[4][2] = {{gx, x}, {goff, off}, {gmask, mask}, {gw, w}};
     for (auto &pr : pairs) {
         if (!pr[0]) continue;
-        if (pr[0]->dtype != DC1D_F32) return DC1D_ERR_BAD_DTYPE;
+        if (pr[0]->dtype != p->dtype) return DC1D_ERR_BAD_DTYPE;
         if (!shape_is(pr[0], pr[1]->ndim, pr[1]->shape)) return DC1D_ERR_BAD_SHAPE;
     }
     if (gb) {
         const int64_t sb[1] = {p->C_out};
-        if (gb->dtype != DC1D_F32) return DC1D_ERR_BAD_DTYPE;
+        if (gb->dtype != p->dtype) return DC1D_ERR_BAD_DTYPE;
         if (!shape_is(gb, 1, sb)) return DC1D_ERR_BAD_SHAPE;
     }
     return DC1D_OK;
+}
+
+// A bf16 backward runs the fp32 kernels on fp32 copies of its inputs and
+// rounds each gradient once into the caller's bf16 buffer.  The copies and
+// the fp32 gradients sit at the start of the workspace (byte offsets below),
+// the fp32 backward's own workspace after them.
+struct Bf16Bwd {
+    size_t x, off, mask, w, dout, gx, goff, gmask, gw, gb, total;
+};
+
+Bf16Bwd bf16_backward_layout(const Params &p) {
+    Bf16Bwd L = {};
+    size_t o = 0;
+    auto take = [&](int64_t n) {
+        const size_t at = o;
+        o += ((size_t)n * 4 + 255) & ~(size_t)255;
+        return at;
+    };
+    const int64_t nx = (int64_t)p.B * p.C_in * p.L_in, no = (int64_t)p.B * p.G * p.L_out * p.K;
+    const int64_t nw = (int64_t)p.C_out * p.cpg * p.K, nd = (int64_t)p.B * p.C_out * p.L_out;
+    L.x = take(nx);
+    L.off = take(no);
+    L.mask = p.mask ? take(no) : 0;
+    L.w = take(nw);
+    L.dout = take(nd);
+    L.gx = take(nx);
+    L.goff = take(no);
+    L.gmask = p.mask ? take(no) : 0;
+    L.gw = take(nw);
+    L.gb = take(p.C_out);
+    L.total = o;
+    return L;
+}
+
+// Workspace of a backward call: the fp32 backward's, plus the copies of a bf16 call.
+size_t backward_ws(const Params &p, bool want_weight, int num_cus) {
+    if (p.dtype != DC1D_BF16) return backward_workspace_bytes(p, want_weight, num_cus);
+    Params q = p;
+    q.dtype = DC1D_F32;
+    return bf16_backward_layout(p).total + backward_workspace_bytes(q, want_weight, num_cus);
 }
 
 }  // namespace
@@ -440,7 +480,7 @@ int dc1d_backward_workspace_bytes(const dc1d_tensor *x, const dc1d_tensor *offse
     if (st) return st;
     DeviceInfo dev;
     if ((st = current_device(&dev))) return st;
-    *bytes_out = backward_workspace_bytes(p, want_grad_weight != 0, dev.num_cus);
+    *bytes_out = backward_ws(p, want_grad_weight != 0, dev.num_cus);
     return DC1D_OK;
 }
 
@@ -469,26 +509,28 @@ int backward_impl(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_t
     for (const dc1d_tensor *t : outs)
         if (t && numel(t) > 0 && !t->data) return DC1D_ERR_NULL_PTR;
     // no gradient may overlap an input or another gradient
+    const size_t es = elem_size(p.dtype);
     for (int i = 0; i < 5; ++i) {
         const dc1d_tensor *o = outs[i];
         if (!o) continue;
-        const size_t ob = (size_t)numel(o) * 4;
+        const size_t ob = (size_t)numel(o) * es;
         for (const dc1d_tensor *t : ins)
-            if (t && overlaps(o->data, ob, t->data, (size_t)numel(t) * 4)) return DC1D_ERR_ALIAS;
+            if (t && overlaps(o->data, ob, t->data, (size_t)numel(t) * es)) return DC1D_ERR_ALIAS;
         for (int j = i + 1; j < 5; ++j)
-            if (outs[j] && overlaps(o->data, ob, outs[j]->data, (size_t)numel(outs[j]) * 4)) return DC1D_ERR_ALIAS;
+            if (outs[j] && overlaps(o->data, ob, outs[j]->data, (size_t)numel(outs[j]) * es)) return DC1D_ERR_ALIAS;
     }
     DeviceInfo dev;
     if ((st = current_device(&dev))) return st;
     // ... nor the workspace
-    const size_t need = backward_workspace_bytes(p, grad_weight_or_null != nullptr, dev.num_cus);
+    const size_t need = backward_ws(p, grad_weight_or_null != nullptr, dev.num_cus);
     for (const dc1d_tensor *o : outs)
-        if (o && workspace && overlaps(o->data, (size_t)numel(o) * 4, workspace, need)) return DC1D_ERR_ALIAS;
+        if (o && workspace && overlaps(o->data, (size_t)numel(o) * es, workspace, need)) return DC1D_ERR_ALIAS;
     const bool want_ds = grad_x_or_null || grad_offsets_or_null || grad_mask_or_null || grad_weight_or_null;
-    if (want_ds && need > 0 && (int64_t)p.B * p.C_in * p.K * p.L_out > 0) {
+    const bool bf16 = p.dtype == DC1D_BF16;  // the copies need the workspace whatever the shape
+    if ((want_ds && need > 0 && (int64_t)p.B * p.C_in * p.K * p.L_out > 0) || (bf16 && need > 0)) {
         if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255)) return DC1D_ERR_WORKSPACE;
         for (const dc1d_tensor *t : ins)
-            if (t && overlaps(workspace, need, t->data, (size_t)numel(t) * 4)) return DC1D_ERR_ALIAS;
+            if (t && overlaps(workspace, need, t->data, (size_t)numel(t) * es)) return DC1D_ERR_ALIAS;
     }
     if (log_on())
         fprintf(stderr,
@@ -508,7 +550,48 @@ int backward_impl(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_t
     a.gb = grad_bias_or_null ? (float *)grad_bias_or_null->data : nullptr;
     a.dS = (float *)workspace;  // the workspace base; launch_backward lays it out
     a.S = nullptr;
-    const hipError_t e = launch_backward(a, dev.num_cus, (hipStream_t)stream);
+    hipStream_t s = (hipStream_t)stream;
+    if (!bf16) {
+        const hipError_t e = launch_backward(a, dev.num_cus, s);
+        return e == hipSuccess ? DC1D_OK : DC1D_ERR_LAUNCH;
+    }
+    // bf16: widen the inputs into the workspace, run the fp32 backward on
+    // them into fp32 gradients there, round each gradient into its buffer
+    const Bf16Bwd L = bf16_backward_layout(p);
+    char *ws = (char *)workspace;
+    const int64_t nx = (int64_t)p.B * p.C_in * p.L_in, no = (int64_t)p.B * p.G * p.L_out * p.K;
+    const int64_t nw = (int64_t)p.C_out * p.cpg * p.K, nd = (int64_t)p.B * p.C_out * p.L_out;
+    hipError_t e = hipSuccess;
+    auto widen = [&](const void *src, size_t at, int64_t n) {
+        if (e == hipSuccess) e = launch_convert(src, kBF16, ws + at, kF32, n, s);
+    };
+    widen(p.x, L.x, nx);
+    widen(p.off, L.off, no);
+    if (p.mask) widen(p.mask, L.mask, no);
+    widen(p.w, L.w, nw);
+    widen(grad_out->data, L.dout, nd);
+    BwdParams b = a;
+    b.p.dtype = kF32;
+    b.p.x = ws + L.x;
+    b.p.off = ws + L.off;
+    b.p.mask = p.mask ? ws + L.mask : nullptr;
+    b.p.w = ws + L.w;
+    b.dout = (const float *)(ws + L.dout);
+    b.gx = a.gx ? (float *)(ws + L.gx) : nullptr;
+    b.goff = a.goff ? (float *)(ws + L.goff) : nullptr;
+    b.gmask = a.gmask ? (float *)(ws + L.gmask) : nullptr;
+    b.gw = a.gw ? (float *)(ws + L.gw) : nullptr;
+    b.gb = a.gb ? (float *)(ws + L.gb) : nullptr;
+    b.dS = (float *)(ws + L.total);
+    if (e == hipSuccess) e = launch_backward(b, dev.num_cus, s);
+    auto narrow = [&](const float *src, void *dst, int64_t n) {
+        if (e == hipSuccess && dst) e = launch_convert(src, kF32, dst, kBF16, n, s);
+    };
+    narrow(b.gx, a.gx, nx);
+    narrow(b.goff, a.goff, no);
+    narrow(b.gmask, a.gmask, no);
+    narrow(b.gw, a.gw, nw);
+    narrow(b.gb, a.gb, p.C_out);
     return e == hipSuccess ? DC1D_OK : DC1D_ERR_LAUNCH;
 }
 
@@ -553,6 +636,10 @@ struct Packed {
     int G, K;
     bool given_off, given_mask;
     size_t t_bytes, off_bytes, mask_bytes, cat_bytes, shared_bytes, total;
+    // bf16 storage: fp32 copies of the generator's parameters and the bf16
+    // offsets / mask the forward reads (conv_bytes of the workspace)
+    int dtype;
+    size_t conv_bytes;
 };
 
 size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -587,8 +674,9 @@ int validate_packed(const dc1d_tensor *x, const dc1d_tensor *tw, const dc1d_tens
     if (stride < 1 || padding < 0 || dilation < 1 || groups < 1) return DC1D_ERR_BAD_ARG;
     if (!mw && (mb || mask_out)) return DC1D_ERR_BAD_ARG;
     const dc1d_tensor *all[12] = {x, tw, tb, ow, ob, mw, mb, w, bias, out, off_out, mask_out};
+    if (x->dtype != DC1D_F32 && x->dtype != DC1D_BF16) return DC1D_ERR_BAD_DTYPE;
     for (const dc1d_tensor *t : all)
-        if (t && t->dtype != DC1D_F32) return DC1D_ERR_BAD_DTYPE;
+        if (t && t->dtype != x->dtype) return DC1D_ERR_BAD_DTYPE;
     if (x->ndim != 3 || tw->ndim != 3 || ow->ndim != 3) return DC1D_ERR_BAD_SHAPE;
     const int64_t B = x->shape[0], C_in = x->shape[1], L_in = x->shape[2], K = tw->shape[2];
     if (C_in < 1 || K < 1 || tw->shape[0] != C_in || tw->shape[1] != 1) return DC1D_ERR_BAD_SHAPE;
@@ -601,7 +689,7 @@ int validate_packed(const dc1d_tensor *x, const dc1d_tensor *tw, const dc1d_tens
     if ((ob && !shape_is(ob, 1, sh)) || (mb && !shape_is(mb, 1, sh))) return DC1D_ERR_BAD_SHAPE;
     const int64_t L_out = dc1d_output_length(L_in, K, stride, padding, dilation);
     if (L_out < 1) return DC1D_ERR_BAD_SHAPE;
-    dc1d_tensor offT = {nullptr, DC1D_F32, 4, {B, G, L_out, K}};
+    dc1d_tensor offT = {nullptr, x->dtype, 4, {B, G, L_out, K}};
     int st = validate(x, &offT, mw ? &offT : nullptr, w, bias, out, stride, padding, dilation, groups, G,
                       &pk->fwd);
     if (st) return st;
@@ -642,6 +730,16 @@ int validate_packed(const dc1d_tensor *x, const dc1d_tensor *tw, const dc1d_tens
     pk->off_bytes = round256(n_off);
     pk->mask_bytes = mw ? round256(n_off) : 0;
     pk->cat_bytes = mw ? round256((size_t)2 * G * K * C_in * 4) + round256((size_t)2 * G * K * 4) : 0;
+    pk->dtype = x->dtype;
+    pk->conv_bytes = 0;
+    if (x->dtype == DC1D_BF16) {
+        // fp32 copies of trunk_weight, trunk_bias, off_weight, off_bias (and
+        // the mask head's), then the offsets (and mask) in bf16
+        const size_t gk = (size_t)G * K, heads = mw ? 2 : 1;
+        pk->conv_bytes = round256((size_t)C_in * K * 4) + round256((size_t)C_in * 4) +
+                         heads * (round256(gk * C_in * 4) + round256(gk * 4)) +
+                         (mw ? 2 : 1) * round256((size_t)B * G * L_out * K * 2);
+    }
     pk->shared_bytes = pk->total = 0;
     return DC1D_OK;
 }
@@ -653,7 +751,7 @@ void size_packed(const DeviceInfo &dev, Packed *pk) {
         gemm_workspace_bytes(head_gemm(*pk, nullptr, nullptr, nullptr, nullptr, nullptr), 1, dev.num_cus);
     const size_t fwd = make_plan(pk->fwd, dev).ws_bytes;
     pk->shared_bytes = round256(gemm > fwd ? gemm : fwd);
-    pk->total = pk->t_bytes + pk->off_bytes + pk->mask_bytes + pk->cat_bytes + pk->shared_bytes;
+    pk->total = pk->t_bytes + pk->off_bytes + pk->mask_bytes + pk->cat_bytes + pk->conv_bytes + pk->shared_bytes;
 }
 
 }  // namespace
@@ -705,14 +803,15 @@ int packed_forward_impl(const dc1d_tensor *x, const dc1d_tensor *trunk_weight,
         if (t && numel(t) > 0 && !t->data) return DC1D_ERR_NULL_PTR;
     for (const dc1d_tensor *t : outs)
         if (t && numel(t) > 0 && !t->data) return DC1D_ERR_NULL_PTR;
+    const size_t es = elem_size(pk.dtype);
     for (int i = 0; i < 3; ++i) {
         const dc1d_tensor *o = outs[i];
         if (!o) continue;
-        const size_t ob = (size_t)numel(o) * 4;
+        const size_t ob = (size_t)numel(o) * es;
         for (const dc1d_tensor *t : ins)
-            if (t && overlaps(o->data, ob, t->data, (size_t)numel(t) * 4)) return DC1D_ERR_ALIAS;
+            if (t && overlaps(o->data, ob, t->data, (size_t)numel(t) * es)) return DC1D_ERR_ALIAS;
         for (int j = i + 1; j < 3; ++j)
-            if (outs[j] && overlaps(o->data, ob, outs[j]->data, (size_t)numel(outs[j]) * 4)) return DC1D_ERR_ALIAS;
+            if (outs[j] && overlaps(o->data, ob, outs[j]->data, (size_t)numel(outs[j]) * es)) return DC1D_ERR_ALIAS;
     }
     DeviceInfo dev;
     if ((st = current_device(&dev))) return st;
@@ -720,30 +819,65 @@ int packed_forward_impl(const dc1d_tensor *x, const dc1d_tensor *trunk_weight,
     if (pk.total > 0) {
         if (!workspace || workspace_bytes < pk.total || ((uintptr_t)workspace & 255)) return DC1D_ERR_WORKSPACE;
         for (const dc1d_tensor *t : ins)
-            if (t && overlaps(workspace, pk.total, t->data, (size_t)numel(t) * 4)) return DC1D_ERR_ALIAS;
+            if (t && overlaps(workspace, pk.total, t->data, (size_t)numel(t) * es)) return DC1D_ERR_ALIAS;
         for (const dc1d_tensor *t : outs)
-            if (t && overlaps(workspace, pk.total, t->data, (size_t)numel(t) * 4)) return DC1D_ERR_ALIAS;
+            if (t && overlaps(workspace, pk.total, t->data, (size_t)numel(t) * es)) return DC1D_ERR_ALIAS;
     }
     if (log_on())
         fprintf(stderr, "dc1d: %s B=%d C_in=%d C_out=%d L_in=%d L_out=%d K=%d s=%d p=%d d=%d groups=%d G=%d mask=%d "
-                        "f32 -> trunk, heads GEMM, %s ws=%zu\n",
+                        "%s -> trunk, heads GEMM, %s ws=%zu\n",
                 constrained ? "packed_forward_constrained" : "packed_forward", pk.fwd.B, pk.fwd.C_in, pk.fwd.C_out,
                 pk.fwd.L_in, pk.fwd.L_out, pk.K, pk.fwd.stride, pk.fwd.padding, pk.fwd.dilation, pk.fwd.groups,
-                pk.G, pk.mw != nullptr, make_plan(pk.fwd, dev).name, pk.total);
+                pk.G, pk.mw != nullptr, pk.dtype == DC1D_F32 ? "f32" : "bf16", make_plan(pk.fwd, dev).name,
+                pk.total);
     if (pk.fwd.B == 0) return DC1D_OK;
 
     char *ws = (char *)workspace;
     float *t = (float *)ws;
-    void *off = pk.given_off ? offsets_out_or_null->data : (void *)(ws + pk.t_bytes);
-    void *mask = pk.mw ? (pk.given_mask ? mask_out_or_null->data : (void *)(ws + pk.t_bytes + pk.off_bytes))
+    const bool bf16 = pk.dtype == DC1D_BF16;
+    // the heads write fp32: straight into the caller's buffers for fp32
+    // storage, into the workspace for bf16 (rounded into the bf16 tensors
+    // the forward reads afterwards)
+    void *off = (pk.given_off && !bf16) ? offsets_out_or_null->data : (void *)(ws + pk.t_bytes);
+    void *mask = pk.mw ? ((pk.given_mask && !bf16) ? mask_out_or_null->data
+                                                   : (void *)(ws + pk.t_bytes + pk.off_bytes))
                        : nullptr;
     char *cat = ws + pk.t_bytes + pk.off_bytes + pk.mask_bytes;
-    void *shared = cat + pk.cat_bytes;
+    char *conv = cat + pk.cat_bytes;
+    void *shared = conv + pk.conv_bytes;
     hipStream_t s = (hipStream_t)stream;
     pk.trunk.t = t;
+    pk.trunk.dtype = pk.dtype;
+    const int GK = pk.G * pk.K;
+    void *off16 = nullptr, *mask16 = nullptr;
+    if (bf16) {
+        // the generator's parameters widened to fp32 (exact)
+        const int64_t C = pk.fwd.C_in;
+        char *c = conv;
+        hipError_t e = hipSuccess;
+        auto widen = [&](const float *&dst_ptr, const void *src, int64_t n) {
+            float *dst = (float *)c;
+            c += round256((size_t)n * 4);
+            if (!src) return;
+            if (e == hipSuccess) e = launch_convert(src, kBF16, dst, kF32, n, s);
+            dst_ptr = dst;
+        };
+        widen(pk.trunk.tw, trunk_weight->data, C * pk.K);
+        widen(pk.trunk.tb, trunk_bias_or_null ? trunk_bias_or_null->data : nullptr, C);
+        widen(pk.ow, off_weight->data, (int64_t)GK * C);
+        widen(pk.ob, off_bias_or_null ? off_bias_or_null->data : nullptr, GK);
+        if (pk.mw) {
+            widen(pk.mw, mask_weight_or_null->data, (int64_t)GK * C);
+            widen(pk.mb, mask_bias_or_null ? mask_bias_or_null->data : nullptr, GK);
+        }
+        const size_t n16 = round256((size_t)pk.fwd.B * GK * pk.fwd.L_out * 2);
+        off16 = pk.given_off ? offsets_out_or_null->data : (void *)c;
+        c += n16;
+        if (pk.mw) mask16 = pk.given_mask ? mask_out_or_null->data : (void *)c;
+        if (e != hipSuccess) return DC1D_ERR_LAUNCH;
+    }
     // with a mask: one GEMM for both heads, their weights and biases stacked
     // by the trunk's launch
-    const int GK = pk.G * pk.K;
     float *wcat = pk.mw ? (float *)cat : nullptr;
     float *bcat = pk.mw ? (float *)(cat + round256((size_t)2 * GK * pk.fwd.C_in * 4)) : nullptr;
     pk.trunk.ow = pk.ow;
@@ -762,6 +896,14 @@ int packed_forward_impl(const dc1d_tensor *x, const dc1d_tensor *trunk_weight,
         e = launch_gemm_f32(head_gemm(pk, pk.ow, pk.ob, off, nullptr, shared), brow, bbatch, 1, dev.num_cus, s);
     }
     if (e != hipSuccess) return DC1D_ERR_LAUNCH;
+    if (bf16) {  // the generated offsets (and mask) rounded once into bf16 for the bf16 forward
+        const int64_t n = (int64_t)pk.fwd.B * GK * pk.fwd.L_out;
+        e = launch_convert(off, kF32, off16, kBF16, n, s);
+        if (e == hipSuccess && pk.mw) e = launch_convert(mask, kF32, mask16, kBF16, n, s);
+        if (e != hipSuccess) return DC1D_ERR_LAUNCH;
+        off = off16;
+        mask = mask16;
+    }
     Params p = pk.fwd;
     p.off = off;
     p.mask = mask;

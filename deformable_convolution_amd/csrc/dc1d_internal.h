@@ -131,6 +131,10 @@ hipError_t launch_positions(const void *off, int dtype, int64_t n, int L_out, in
                             int padding, int dilation, int L_in, int32_t *i0, float *frac,
                             uint8_t *valid, hipStream_t stream);
 
+// dst[i] = src[i] converted between storage dtypes (kBF16 -> kF32 exactly,
+// kF32 -> kBF16 rounded to nearest even), i < n.
+hipError_t launch_convert(const void *src, int src_dtype, void *dst, int dst_dtype, int64_t n, hipStream_t stream);
+
 // Generic one-thread-per-output kernel: any groups / offset groups / mask.
 hipError_t launch_direct(const Params &p, hipStream_t stream);
 

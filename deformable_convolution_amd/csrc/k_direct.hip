@@ -35,6 +35,29 @@ __global__ void __launch_bounds__(256) k_positions(const typename D::T *__restri
     }
 }
 
+// Elementwise storage conversion: bf16 -> fp32 is exact; fp32 -> bf16 rounds
+// to nearest even (the conversion instruction).  Grid-stride.
+template <class S, class D>
+__global__ void __launch_bounds__(256) k_convert(const typename S::T *__restrict__ src,
+                                                 typename D::T *__restrict__ dst, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        D::st(dst, i, S::ld(src, i));
+}
+
+hipError_t launch_convert(const void *src, int src_dtype, void *dst, int dst_dtype, int64_t n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    const dim3 grid((unsigned)blocks);
+    if (src_dtype == kBF16 && dst_dtype == kF32)
+        hipLaunchKernelGGL((k_convert<BF16, F32>), grid, dim3(256), 0, stream, (const uint16_t *)src, (float *)dst, n);
+    else if (src_dtype == kF32 && dst_dtype == kBF16)
+        hipLaunchKernelGGL((k_convert<F32, BF16>), grid, dim3(256), 0, stream, (const float *)src, (uint16_t *)dst, n);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 hipError_t launch_positions(const void *off, int dtype, int64_t n, int L_out, int K, int stride,
                             int padding, int dilation, int L_in, int32_t *i0, float *frac,
                             uint8_t *valid, hipStream_t stream) {

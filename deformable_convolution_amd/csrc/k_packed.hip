@@ -103,11 +103,16 @@ hipError_t launch_trunk(const TrunkArgs &a, hipStream_t stream) {
     const int tiles_l = (a.L_out + kTrLT - 1) / kTrLT;
     const int64_t blocks = (int64_t)a.B * a.C * tiles_l;
     if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-    if (a.dtype != kF32) return hipErrorInvalidValue;
     const int64_t span = (int64_t)(kTrLT - 1) * a.stride + (int64_t)(a.K - 1) * a.dilation + 1;
     const int win_cap = span <= kTrWinMax ? (int)span : 0;
-    hipLaunchKernelGGL((k_trunk<F32>), dim3((unsigned)blocks), dim3(kTrThreads), (size_t)win_cap * 4, stream, a,
-                       tiles_l, win_cap);
+    if (a.dtype == kF32)
+        hipLaunchKernelGGL((k_trunk<F32>), dim3((unsigned)blocks), dim3(kTrThreads), (size_t)win_cap * 4, stream, a,
+                           tiles_l, win_cap);
+    else if (a.dtype == kBF16)
+        hipLaunchKernelGGL((k_trunk<BF16>), dim3((unsigned)blocks), dim3(kTrThreads), (size_t)win_cap * 4, stream,
+                           a, tiles_l, win_cap);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

@@ -296,11 +296,13 @@ def forward(x, offsets, weight, bias=None, mask=None, stride=1, padding=0, dilat
 
 def backward(x, offsets, weight, grad_out, mask=None, stride=1, padding=0, dilation=1, groups=1,
              need=("x", "offsets", "mask", "weight", "bias"), workspace=None, constrained=False):
-    """Gradients of sum(grad_out * forward(...)) on the GPU (fp32 tensors).
-    Returns a dict with the requested keys among x, offsets, mask (only with
-    a mask), weight, bias; tensors are allocated here, the arithmetic runs in
-    the library's kernels on torch's current stream.  constrained=True: the
-    backward of the constrained forward."""
+    """Gradients of sum(grad_out * forward(...)) on the GPU (float32 or
+    bfloat16 tensors, all of one dtype; the gradients have it too, bf16 ones
+    computed in fp32 and rounded once).  Returns a dict with the requested
+    keys among x, offsets, mask (only with a mask), weight, bias; tensors are
+    allocated here, the arithmetic runs in the library's kernels on torch's
+    current stream.  constrained=True: the backward of the constrained
+    forward."""
     lib = load_library()
     x, offsets, weight, grad_out, mask = (_contig(t, n) for t, n in ((x, "x"), (offsets, "offsets"),
                                                                       (weight, "weight"),

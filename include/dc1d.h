@@ -219,7 +219,8 @@ int dc1d_forward_constrained(const dc1d_tensor *x, const dc1d_tensor *offsets,
                              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Backward (fp32 storage only; DC1D_ERR_BAD_DTYPE otherwise).  For
+ * Backward (fp32 or bf16 storage; every gradient has its input's dtype, and
+ * grad_out the inputs' dtype).  For
  * grad_out = dL/d(out) [B, C_out, L_out], writes the gradients of
  * L = sum(grad_out * out) with respect to the inputs of dc1d_forward, each
  * into a caller buffer shaped like that input (NULL: not computed):
@@ -245,8 +246,16 @@ int dc1d_forward_constrained(const dc1d_tensor *x, const dc1d_tensor *offsets,
  * a mask.  Gradients must not overlap the inputs, each other or the
  * workspace.
  *
+ * bf16 storage: the inputs are widened exactly into fp32 copies in the
+ * workspace, the fp32 kernels compute every gradient there (fp32
+ * arithmetic, as above), and each requested gradient is rounded once, to
+ * nearest even, into its bf16 buffer (the dc1d page trains the layer with
+ * torch.autograd, whose gradients keep the input dtype; intro and section
+ * Demo notebook).
+ *
  * workspace: at least dc1d_backward_workspace_bytes() bytes, 256-byte
- * aligned, when that is not 0 (it holds dS = the gradient of the samples,
+ * aligned, when that is not 0 (for bf16 it first holds the fp32 copies of
+ * the inputs and the fp32 gradients; then dS = the gradient of the samples,
  * the transposed weight and the samples for the weight gradient, split
  * partial sums, and the grad_x gather's flag, depending on the shape;
  * depthwise shapes need only the flag, or nothing); no initialisation;
@@ -267,8 +276,8 @@ int dc1d_backward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_t
                   size_t workspace_bytes, void *stream);
 
 /*
- * The packed layer (fp32 storage only; DC1D_ERR_BAD_DTYPE otherwise): the
- * layer computes its own offsets, and optionally its mask, from its input,
+ * The packed layer (fp32 or bf16 storage, one dtype for every tensor of the
+ * call): the layer computes its own offsets, and optionally its mask, from its input,
  * then runs the forward above with them (dc1d page, section
  * PackedDeformConv1d: offsets from a depthwise-separable convolutional
  * block; section Modulation (DCNv2): a second pointwise branch off the same
@@ -294,9 +303,17 @@ int dc1d_backward(const dc1d_tensor *x, const dc1d_tensor *offsets, const dc1d_t
  * must not overlap the inputs, each other or the workspace.
  * B * L_out must be below 2^31.
  *
+ * bf16 storage: the generator (trunk and heads) runs in fp32 on the input
+ * and on its parameters widened exactly; the offsets and mask it produces
+ * are rounded once (to nearest even) to bf16, and the bf16 forward reads
+ * those, as a layer computing in its input dtype does (conv1d operator
+ * page: the computation stays in the input dtype).
+ *
  * workspace: at least dc1d_packed_workspace_bytes() bytes, 256-byte
  * aligned, when that is not 0 (the trunk [B, C_in, L_out], the offsets and
- * mask, and the forward's own workspace); no initialisation; nothing kept.
+ * mask in fp32, for bf16 also the widened parameters and the bf16 offsets
+ * and mask, and the forward's own workspace); no initialisation; nothing
+ * kept.
  */
 int dc1d_packed_workspace_bytes(const dc1d_tensor *x, const dc1d_tensor *trunk_weight,
                                 const dc1d_tensor *off_weight, const dc1d_tensor *mask_weight_or_null,

@@ -24,7 +24,6 @@ def test_more_than_one_gpu_exits_with_a_message():
     (["--workload", "packed", "--constrained"], "1D forward"),
     (["--workload", "dcn2d", "--constrained"], "1D forward"),
     (["--workload", "depthwise", "--backward", "--constrained"], "times the forward"),
-    (["--workload", "long_seq_bf16", "--backward"], "fp32"),
 ])
 def test_refused_combinations(argv, text):
     rc, out = bench(*argv)

@@ -221,12 +221,15 @@ def test_backward_validation(lib):
     if not _device_visible():
         assert bcall(lib, x, off, mask, w, gout, gx, goff, gmask, gw, gb) == dc1d.ERR_DEVICE
     assert bcall(lib, x, off, mask, w, None, gx) == dc1d.ERR_NULL_PTR
-    # fp32 only
+    # every gradient in the inputs' dtype (bf16 inputs with an fp32 gradient, and the reverse)
     xb = T([2, 8, 20], dtype=1, addr=x.data)
     ob = T([2, 2, 18, 3], dtype=1, addr=off.data)
     wb = T([6, 8, 3], dtype=1, addr=w.data)
     gb16 = T([2, 6, 18], dtype=1, addr=gout.data)
-    assert bcall(lib, xb, ob, None, wb, gb16) == dc1d.ERR_BAD_DTYPE
+    assert bcall(lib, xb, ob, None, wb, gb16, gx=gx) == dc1d.ERR_BAD_DTYPE
+    assert bcall(lib, x, off, mask, w, gout, gx=T([2, 8, 20], dtype=1, addr=gx.data)) == dc1d.ERR_BAD_DTYPE
+    # grad_out in the inputs' dtype
+    assert bcall(lib, x, off, mask, w, gb16, gx=gx) == dc1d.ERR_BAD_DTYPE
     # a mask gradient needs a mask
     assert bcall(lib, x, off, None, w, gout, gmask=gmask) == dc1d.ERR_BAD_ARG
     # gradient shapes follow their inputs

@@ -1,11 +1,15 @@
-"""GPU parity of the backward (fp32): libdc1d's dc1d_backward through the C
-ABI against the oracle's backward (itself pinned in test_oracle_backward.py).
+"""GPU parity of the backward: libdc1d's dc1d_backward through the C ABI
+against the oracle's backward (itself pinned in test_oracle_backward.py).
 
 Tolerance, per gradient, elementwise:
-    |gpu - oracle| <= 1e-5 * sqrt(n) * rms(oracle) + 1e-6
-with n the number of products summed into one element (fp32 accumulation;
-the oracle is double): grad_x: (C_out/groups) * K * 2; grad_offsets and
-grad_mask: (C_in/G) * (C_out/groups); grad_weight and grad_bias: B * L_out.
+  * fp32: |gpu - oracle| <= 1e-5 * sqrt(n) * rms(oracle) + 1e-6
+    with n the number of products summed into one element (fp32
+    accumulation; the oracle is double): grad_x: (C_out/groups) * K * 2;
+    grad_offsets and grad_mask: (C_in/G) * (C_out/groups); grad_weight and
+    grad_bias: B * L_out.
+  * bf16 (bf16 storage, fp32 arithmetic, each gradient rounded once):
+    |gpu - oracle| <= 2e-2 * max(|oracle|, rms(oracle)), the forward's bf16
+    bound.
 """
 import math
 
@@ -33,6 +37,8 @@ def run_backward(w, seed=0):
     t = inputs.make_inputs(w, seed=seed)
     gen = torch.Generator().manual_seed(seed + 1000)
     dout = torch.randn((w.B, w.C_out, w.L_out), generator=gen, dtype=torch.float32)
+    if w.dtype == "bf16":
+        dout = dout.to(torch.bfloat16)
     g = {k: (v.to(DEV) if v is not None else None) for k, v in t.items()}
     got = dc1d.backward(g["x"], g["offsets"], g["weight"], dout.to(DEV), g["mask"], stride=w.stride,
                         padding=w.padding, dilation=w.dilation, groups=w.groups)
@@ -50,9 +56,14 @@ def run_backward(w, seed=0):
         if r.size == 0:
             continue
         rms = math.sqrt(float(np.mean(r ** 2)))
-        tol = 1e-5 * math.sqrt(n[k]) * rms + 1e-6
-        err = float(np.abs(a - r).max())
-        assert err <= tol, "%s grad_%s: max|err| %.3g > %.3g" % (w.name, k, err, tol)
+        if w.dtype == "f32":
+            tol = 1e-5 * math.sqrt(n[k]) * rms + 1e-6
+            err = float(np.abs(a - r).max())
+            assert err <= tol, "%s grad_%s: max|err| %.3g > %.3g" % (w.name, k, err, tol)
+        else:
+            assert got[k].dtype == torch.bfloat16, k
+            bad = np.abs(a - r) > 2e-2 * np.maximum(np.abs(r), rms)
+            assert not bad.any(), "%s grad_%s: %d elements beyond the bf16 bound" % (w.name, k, int(bad.sum()))
     return got, ref
 
 
@@ -128,3 +139,33 @@ def test_backward_subset_of_gradients_and_empty_batch():
     g0 = dc1d.backward(t0["x"], t0["offsets"], t0["weight"], torch.zeros((0, 8, 28), device=DEV))
     torch.cuda.synchronize()
     assert torch.count_nonzero(g0["weight"]) == 0 and torch.count_nonzero(g0["bias"]) == 0
+
+
+def bf16_shapes():
+    cases = []
+    # (B, C_in, C_out, L_in, K, s, p, d, groups, G, mask, off_scale)
+    spec = [
+        (2, 64, 96, 77, 3, 1, 1, 1, 1, 2, True, 3.0),        # dense, masked
+        (1, 40, 36, 300, 7, 3, 5, 1, 1, 8, False, 30.0),     # dense, strided, wide offsets
+        (2, 12, 18, 50, 3, 1, 1, 2, 3, 4, True, 4.0),        # grouped
+        (2, 16, 16, 300, 3, 2, 1, 1, 16, 16, True, 3.0),     # depthwise, strided (gathered grad_x)
+        (1, 8, 8, 700, 9, 1, 4, 24, 8, 8, False, 5.0),       # depthwise, wide dilation (scattered grad_x)
+        (1, 4, 4, 1500, 5, 1, 2, 2, 4, 4, True, 20.0),       # depthwise, samples moved > 16 (fix pass)
+    ]
+    for i, (B, C_in, C_out, L_in, K, s, p, d, groups, G, mask, sc) in enumerate(spec):
+        L_out = oracle.output_length(L_in, K, s, p, d)
+        cases.append(inputs.custom("bwd_bf16_%d" % i, B=B, C_in=C_in, C_out=C_out, L_in=L_in, K=K, stride=s,
+                                   padding=p, dilation=d, groups=groups, G=G, L_out=L_out, dtype="bf16",
+                                   off_dist=("uniform", -sc, sc),
+                                   mask_dist=("sigmoid_normal", 0.0, 1.0) if mask else None))
+    return cases
+
+
+@pytest.mark.parametrize("w", bf16_shapes(), ids=lambda w: w.name)
+def test_backward_bf16_ragged_shapes(w):
+    run_backward(w, seed=6)
+
+
+@pytest.mark.parametrize("name", ["long_seq_bf16", "dcnv2_bf16"])
+def test_backward_bf16_workloads_reduced_batch(name):
+    run_backward(inputs.WORKLOADS[name].with_batch(1), seed=2)

@@ -183,3 +183,54 @@ def test_packed_argument_errors():
     y = dc1d.packed_forward(x0, *base[1:], **kw)
     torch.cuda.synchronize()
     assert y.shape == (0, w.C_out, w.L_out)
+
+
+# ---- bf16 storage --------------------------------------------------------------
+#
+# Every tensor of the call in bf16: the generator runs in fp32 on the widened
+# parameters, its offsets (and mask) are rounded once to bf16, and the bf16
+# forward reads those.  Checked in two parts, each against the oracle with
+# the bf16 bound |gpu - oracle| <= 2e-2 * max(|oracle|, rms(oracle))
+# elementwise: the generated offsets and mask against the oracle's
+# generator, and the output against the oracle's forward of the GPU's own
+# bf16 offsets and mask (so that the forward's check does not depend on how
+# an offset's rounding moves a sample).
+
+def _bf16_bound(a, r, what):
+    rms_r = rms(r)
+    bad = np.abs(a - r) > 2e-2 * np.maximum(np.abs(r), rms_r)
+    assert not bad.any(), "%s: %d elements beyond the bf16 bound" % (what, int(bad.sum()))
+
+
+def run_packed_bf16(w, seed=0):
+    print("packed bf16 case", w, "seed", seed, flush=True)
+    t32 = inputs.make_packed_inputs(w, seed=seed)
+    t = {k: (v.to(torch.bfloat16) if v is not None else None) for k, v in t32.items()}
+    g = {k: (v.to(DEV) if v is not None else None) for k, v in t.items()}
+    kw = dict(stride=w.stride, padding=w.padding, dilation=w.dilation)
+    out, gen = dc1d.packed_forward(g["x"], g["trunk_weight"], g["trunk_bias"], g["off_weight"], g["off_bias"],
+                                   g["weight"], g["bias"], g["mask_weight"], g["mask_bias"], groups=w.groups,
+                                   with_offsets=True, **kw)
+    torch.cuda.synchronize()
+    off, mask = gen if w.modulated else (gen, None)
+    assert out.dtype == torch.bfloat16 and off.dtype == torch.bfloat16
+    r_off, r_mask = oracle.packed_heads(t["x"], t["trunk_weight"], t["trunk_bias"], t["off_weight"], t["off_bias"],
+                                        t["mask_weight"], t["mask_bias"], **kw)
+    _bf16_bound(off.double().cpu().numpy(), r_off, "%s offsets" % w.name)
+    if w.modulated:
+        _bf16_bound(mask.double().cpu().numpy(), r_mask, "%s mask" % w.name)
+    r_out = oracle.forward(t["x"], off.cpu(), t["weight"], t["bias"], mask.cpu() if w.modulated else None,
+                           groups=w.groups, **kw)
+    a_out = out.double().cpu().numpy()
+    assert np.isfinite(a_out).all()
+    _bf16_bound(a_out, r_out, "%s out" % w.name)
+
+
+@pytest.mark.parametrize("name", ["packed_page", "packed_page_modulated"])
+def test_packed_bf16_page_layer(name):
+    run_packed_bf16(inputs.PACKED_WORKLOADS[name], seed=11)
+
+
+@pytest.mark.parametrize("i", [0, 1, 3, 4, 8])
+def test_packed_bf16_ragged_shapes(i):
+    run_packed_bf16(shapes()[i], seed=12)
