@@ -77,7 +77,7 @@ def work(w):
 # header and the C ABI's launch code.
 _COMMON = ["dc1d_internal.h", "api.hip"]
 _MFMA = ["mfma_kernel.h", "k_mfma.hip", "k_mfma_f32.hip", "k_mfma_f32_mask.hip", "k_mfma_bf16.hip",
-         "k_mfma_bf16_mask.hip"]
+         "k_mfma_bf16_mask.hip", "mfma_wide.h", "k_mfma_wide.hip"]
 _FAMILY_SOURCES = [
     ("mfma_", _MFMA),
     ("depthwise", ["k_direct.hip"]),

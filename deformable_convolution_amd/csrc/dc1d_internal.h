@@ -172,6 +172,14 @@ struct MfmaPlan {
     // position-major kernel (k_mfma_cbt), taken when x is 16-byte aligned
     // (0: not planned; `variant` is then, or otherwise, the kernel)
     int tpos;
+    // the one-wave-per-SIMD bf16 kernel (k_mfma_wide, 256 x 256 tiles): its
+    // window capacity (0: not planned), tiles and LDS bytes; taken when x is
+    // 16-byte aligned, the kernel above otherwise (grid `blocks` of the plan
+    // below is then the one reported)
+    int wide, wide_tiles_m, wide_tiles_n, wide_ncb;
+    size_t wide_lds, wide_wb_bytes;
+    int64_t fallback_blocks;
+    int fallback_splits;
 };
 MfmaPlan plan_mfma(const Params &p, int num_cus);
 hipError_t launch_mfma(const Params &p, const MfmaPlan &pl, hipStream_t stream);
@@ -180,6 +188,11 @@ hipError_t launch_mfma_f32(const Params &p, const MfmaPlan &pl, hipStream_t stre
 hipError_t launch_mfma_f32_mask(const Params &p, const MfmaPlan &pl, hipStream_t stream);
 hipError_t launch_mfma_bf16(const Params &p, const MfmaPlan &pl, hipStream_t stream);
 hipError_t launch_mfma_bf16_mask(const Params &p, const MfmaPlan &pl, hipStream_t stream);
+// the one-wave-per-SIMD bf16 kernel (k_mfma_wide.hip); pl.wide must be planned
+hipError_t launch_mfma_wide(const Params &p, const MfmaPlan &pl, hipStream_t stream);
+bool wide_npos_compiled(int npos, int K);
+int wide_npos_option(int i);  // compiled window capacities, ascending; 0 past the last
+size_t wide_lds_bytes(int npos);
 
 // Backward (fp32): gradients of sum(dout * out).  Any gradient pointer may
 // be null (not computed); dS and S point into the workspace (S only when the

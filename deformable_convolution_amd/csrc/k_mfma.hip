@@ -150,6 +150,43 @@ void plan_for(const Params &p, int num_cus, MfmaPlan &pl) {
         }
         plan_splits(tiles, pl.chunks, num_cus, pl);
         pl.ws_bytes = pl.wb_bytes + (pl.splits > 1 ? (size_t)tiles * pl.splits * BM * BN * 4 : 0);
+        // the one-wave-per-SIMD kernel (256 x 256 tiles) when its tiles alone
+        // fill the GPU, a compiled tap count and window fit, and a tile spans
+        // at most three batch segments (L_out >= 128).  With K odd it runs an
+        // even number of blocks: an odd count gets a block of zero weights,
+        // taken only when that adds at most a fifth (five blocks or more).
+        pl.wide = 0;
+        pl.fallback_blocks = pl.blocks;
+        pl.fallback_splits = pl.splits;
+        const int wncb = (p.C_in + 31) / 32;
+        const bool pad = (p.K % 2 == 1) && (wncb % 2 == 1);
+        if (sizeof(T) == 2 && p.cpo % 16 == 0 && vx && p.K >= 2 && p.K <= 4 && p.L_out >= 128 &&
+            (!pad || wncb >= 5)) {
+            const int64_t wtm = (p.C_out + 255) / 256, wtn = (N + 255) / 256;
+            const int64_t segw = (p.L_out % 256 == 0) ? 1 : std::min<int64_t>(4, 255 / p.L_out + 2);
+            const int64_t want_w = (std::min<int64_t>(256, N) - 1) * p.stride +
+                                   segw * ((int64_t)(p.K - 1) * p.dilation + 2 + 32 + 16);
+            if (wtm * wtn >= num_cus && wtm * wtn < ((int64_t)1 << 31)) {
+                for (int i = 0, npos; (npos = wide_npos_option(i)) > 0; ++i) {
+                    const size_t lds = wide_lds_bytes(npos);
+                    if (npos >= want_w + 2 && lds <= lds_cap && wide_npos_compiled(npos, p.K)) {
+                        pl.wide = npos;
+                        pl.wide_tiles_m = (int)wtm;
+                        pl.wide_tiles_n = (int)wtn;
+                        pl.wide_lds = lds;
+                        pl.wide_ncb = wncb + (pad ? 1 : 0);
+                        pl.wide_wb_bytes =
+                            ((size_t)p.K * p.C_out * pl.wide_ncb * BK * sizeof(T) + 255) & ~(size_t)255;
+                        pl.blocks = wtm * wtn;
+                        pl.threads = 256;
+                        pl.splits = 1;
+                        // the rearranged weights, then a byte per tile (gathered tiles)
+                        pl.ws_bytes = std::max(pl.ws_bytes, pl.wide_wb_bytes + (size_t)(wtm * wtn));
+                        break;
+                    }
+                }
+            }
+        }
         return;
     }
 
@@ -208,7 +245,9 @@ MfmaPlan plan_mfma(const Params &p, int num_cus) {
     if (pl.blocked) {
         static const char *const names[2][3] = {{"mfma_f32_cb8", "mfma_f32_cb16", "mfma_f32_cb32"},
                                                 {"mfma_bf16_cb8", "mfma_bf16_cb16", "mfma_bf16_cb32"}};
-        pl.name = pl.tpos ? "mfma_bf16_cb32t" : names[p.dtype == kF32 ? 0 : 1][pl.cb == 8 ? 0 : (pl.cb == 16 ? 1 : 2)];
+        pl.name = pl.wide ? "mfma_bf16_wide"
+                          : (pl.tpos ? "mfma_bf16_cb32t"
+                                     : names[p.dtype == kF32 ? 0 : 1][pl.cb == 8 ? 0 : (pl.cb == 16 ? 1 : 2)]);
     }
     return pl;
 }
@@ -295,6 +334,15 @@ hipError_t launch_gemm_f32(const Params &q, int64_t brow, int64_t bbatch, int ou
 
 hipError_t launch_mfma(const Params &p, const MfmaPlan &pl, hipStream_t stream) {
     if (pl.blocks == 0) return hipSuccess;
+    if (pl.wide && ((uintptr_t)p.x & 15) == 0) return launch_mfma_wide(p, pl, stream);
+    if (pl.wide) {  // x not 16-byte aligned: the channel-block kernel, on its own grid
+        MfmaPlan q = pl;
+        q.wide = 0;
+        q.blocks = pl.fallback_blocks;
+        q.splits = pl.fallback_splits;
+        q.threads = NTT;
+        return p.mask ? launch_mfma_bf16_mask(p, q, stream) : launch_mfma_bf16(p, q, stream);
+    }
     if (p.dtype == kF32) return p.mask ? launch_mfma_f32_mask(p, pl, stream) : launch_mfma_f32(p, pl, stream);
     return p.mask ? launch_mfma_bf16_mask(p, pl, stream) : launch_mfma_bf16(p, pl, stream);
 }

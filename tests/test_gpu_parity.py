@@ -156,6 +156,88 @@ def test_ragged_shapes_reach_every_kernel():
     assert want <= names, sorted(want - names)
 
 
+# ---- the one-wave-per-SIMD bf16 kernel (256 x 256 tiles) -------------------
+#
+# Planned for bf16 blocks of 32 channels when its tiles alone fill the GPU,
+# so these shapes have about 65536 columns and 200 - 256 output channels.
+
+def _wide_cases():
+    # (B, C_in, C_out, L_in, K, s, p, d, G, mask, off_scale)
+    spec = [
+        (4, 160, 256, 16384, 3, 1, 1, 1, 5, False, 3.0),   # K odd, five blocks: a padding block
+        (2, 176, 200, 32768, 3, 1, 1, 2, 11, True, 4.0),   # partial last block, ragged rows, L_out % 4 != 0
+        (300, 64, 256, 256, 2, 1, 0, 1, 2, True, 2.0),     # K = 2, tiles over two or three batches
+        (512, 160, 256, 128, 3, 1, 1, 1, 5, False, 3.0),   # 128 columns per batch, padding block
+        (4, 128, 256, 32768, 4, 2, 1, 1, 4, True, 5.0),    # K = 4, stride 2 (wider window)
+        (2, 64, 256, 32768, 3, 1, 1, 1, 2, False, 300.0),  # offsets too wide for any window: all gathered
+        (520, 32, 256, 136, 2, 1, 0, 1, 1, True, 2.0),     # one block, 135 columns per batch
+    ]
+    cases = []
+    for i, (B, C_in, C_out, L_in, K, s, p, d, G, mask, sc) in enumerate(spec):
+        L_out = oracle.output_length(L_in, K, s, p, d)
+        cases.append(inputs.custom("wide%d" % i, B=B, C_in=C_in, C_out=C_out, L_in=L_in, K=K, stride=s,
+                                   padding=p, dilation=d, G=G, L_out=L_out, dtype="bf16",
+                                   off_dist=("uniform", -sc, sc),
+                                   mask_dist=("sigmoid_normal", 0.0, 1.0) if mask else None))
+    return cases
+
+
+def _plan_of(w, g):
+    return dc1d.plan(g["x"], g["offsets"], g["weight"], g["bias"], g["mask"], stride=w.stride, padding=w.padding,
+                     dilation=w.dilation, groups=w.groups)
+
+
+def _wide_device():
+    return torch.cuda.get_device_properties(DEV).multi_processor_count <= 256
+
+
+@pytest.mark.parametrize("w", _wide_cases(), ids=lambda w: w.name)
+def test_wide_kernel(w):
+    t = inputs.make_inputs(w, seed=9)
+    g = to_dev(t)
+    pl = _plan_of(w, g)
+    print("plan", pl, flush=True)
+    if _wide_device():
+        assert pl["kernel"] == "mfma_bf16_wide" and pl["splits"] == 1, pl
+    got = gpu_forward(w, g)
+    torch.cuda.synchronize()
+    check(w, got, oracle_forward(w, t))
+
+
+def test_wide_kernel_some_tiles_gathered():
+    """A few offsets far out: the tiles holding them are gathered by the
+    second launch, every other tile is windowed; all match the oracle."""
+    w = _wide_cases()[0]
+    t = inputs.make_inputs(w, seed=10)
+    off = t["offsets"].float()
+    for (b, g_, l, k, v) in [(0, 0, 1000, 1, 700.0), (1, 2, 5000, 0, -900.0), (3, 1, 16383, 2, 2000.0),
+                             (2, 0, 0, 0, -3000.0)]:
+        off[b, g_, l, k] = v
+    t["offsets"] = off.to(t["offsets"].dtype)
+    g = to_dev(t)
+    if _wide_device():
+        assert _plan_of(w, g)["kernel"] == "mfma_bf16_wide"
+    got = gpu_forward(w, g)
+    torch.cuda.synchronize()
+    check(w, got, oracle_forward(w, t))
+
+
+def test_wide_kernel_misaligned_x_takes_the_channel_block_kernel():
+    """x not 16-byte aligned: the channel-block kernel runs instead (on its
+    own grid, with its own workspace layout); both match the oracle."""
+    w = _wide_cases()[0]
+    t = inputs.make_inputs(w, seed=12)
+    g = to_dev(t)
+    if _wide_device():
+        assert _plan_of(w, g)["kernel"] == "mfma_bf16_wide"
+    a = gpu_forward(w, g)
+    b = gpu_forward(w, dict(g, x=_misaligned_copy(g["x"])))
+    torch.cuda.synchronize()
+    ref = oracle_forward(w, t)
+    check(w, a, ref, "wide")
+    check(w, b, ref, "channel blocks")
+
+
 def test_weights_read_in_place_or_rearranged():
     """fp32 blocks of 8 channels x 4 taps read the weights in place when they
     are 16-byte aligned and from a rearranged copy otherwise; same results."""
