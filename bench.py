@@ -77,14 +77,16 @@ def work(w):
 # header and the C ABI's launch code.
 _COMMON = ["dc1d_internal.h", "api.hip"]
 _MFMA = ["mfma_kernel.h", "k_mfma.hip", "k_mfma_f32.hip", "k_mfma_f32_mask.hip", "k_mfma_bf16.hip",
-         "k_mfma_bf16_mask.hip", "mfma_wide.h", "k_mfma_wide.hip"]
+         "k_mfma_bf16_mask.hip"]
+_WIDE = ["mfma_wide.h", "k_mfma_wide.hip"]  # the one-wave-per-SIMD bf16 kernel (includes mfma_kernel.h)
 _FAMILY_SOURCES = [
+    ("mfma_bf16_wide", _MFMA + _WIDE),
     ("mfma_", _MFMA),
     ("depthwise", ["k_direct.hip"]),
     ("direct2d", ["k_dc2d.hip"]),
     ("direct", ["k_direct.hip"]),
     ("backward", ["k_backward.hip"] + _MFMA),
-    ("packed", ["k_packed.hip", "k_direct.hip"] + _MFMA),
+    ("packed", ["k_packed.hip", "k_heads.hip", "k_direct.hip"] + _MFMA),
     ("im2col2d", ["k_dc2d.hip"] + _MFMA),
 ]
 

@@ -890,7 +890,22 @@ int packed_forward_impl(const dc1d_tensor *x, const dc1d_tensor *trunk_weight,
     hipError_t e = launch_trunk(pk.trunk, s);
     if (e != hipSuccess) return DC1D_ERR_LAUNCH;
     const int64_t brow = pk.fwd.L_out, bbatch = (int64_t)pk.fwd.C_in * pk.fwd.L_out;
-    if (pk.mw) {
+    const int M = GK * (pk.mw ? 2 : 1);
+    if (heads_fit(pk.fwd.C_in, pk.K, M, pk.fwd.L_out, t, off, mask)) {  // the persistent head kernel
+        HeadArgs h = {};
+        h.t = t;
+        h.w = pk.mw ? wcat : pk.ow;
+        h.bias = pk.mw ? bcat : pk.ob;
+        h.off = (float *)off;
+        h.mask = (float *)mask;
+        h.B = pk.fwd.B;
+        h.C = pk.fwd.C_in;
+        h.L = pk.fwd.L_out;
+        h.G = pk.G;
+        h.K = pk.K;
+        h.M = M;
+        e = launch_heads(h, dev.num_cus, s);
+    } else if (pk.mw) {
         e = launch_gemm_f32(head_gemm(pk, wcat, bcat, off, mask, shared), brow, bbatch, 2, dev.num_cus, s);
     } else {
         e = launch_gemm_f32(head_gemm(pk, pk.ow, pk.ob, off, nullptr, shared), brow, bbatch, 1, dev.num_cus, s);

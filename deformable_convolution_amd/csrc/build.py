@@ -18,7 +18,7 @@ PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
 OUT = os.path.join(PKG, "libdc1d.so")
 SOURCES = ["api.hip", "k_direct.hip", "k_backward.hip", "k_packed.hip", "k_dc2d.hip", "k_mfma.hip", "k_mfma_f32.hip", "k_mfma_f32_mask.hip", "k_mfma_bf16.hip",
-           "k_mfma_bf16_mask.hip", "k_mfma_wide.hip"]
+           "k_mfma_bf16_mask.hip", "k_mfma_wide.hip", "k_heads.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -217,6 +217,22 @@ hipError_t launch_gemm_f32(const Params &q, int64_t brow, int64_t bbatch, int ou
 // accumulation; C stored in bf16, RNE), out_mode 0 only.
 hipError_t launch_gemm_bf16(const Params &q, int64_t brow, int64_t bbatch, int num_cus, hipStream_t stream);
 size_t gemm_bf16_workspace_bytes(const Params &q, int num_cus);
+// The packed layer's generator heads (k_heads.hip): off[b,g,l,k] =
+// bias[g*K + k] + sum_c w[g*K + k][c] t[b,c,l] and, with mask, mask[b,g,l,k]
+// = sigmoid(bias[G*K + g*K + k] + sum_c w[G*K + g*K + k][c] t[b,c,l]); t
+// [B][C][L], w [M][C] (M = G*K, or 2*G*K with the mask head), off and mask
+// [B][G][L][K], all fp32.  heads_fit: the shapes and alignments the kernel
+// serves (K <= 4, C <= 64, M <= 128*K, L a multiple of 32, 16-byte aligned
+// t, off, mask); the general head GEMM (launch_gemm_f32, out_mode 1 or 2)
+// serves the rest.
+struct HeadArgs {
+    const float *t, *w, *bias;  // bias may be null
+    float *off, *mask;          // mask null without the mask head
+    int B, C, L, G, K, M;
+    int slabs, tiles_per_b, tiles;  // set by launch_heads
+};
+bool heads_fit(int C, int K, int M, int L, const void *t, const void *off, const void *mask);
+hipError_t launch_heads(HeadArgs a, int num_cus, hipStream_t stream);
 // The packed layer's trunk (fp32 storage): t[b,c,l] = tb[c] +
 // sum_k tw[c,k] * x~[b,c, l*stride - padding + k*dilation], t [B][C][L_out].
 struct TrunkArgs {

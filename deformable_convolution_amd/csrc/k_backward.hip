@@ -34,7 +34,7 @@
 //                    k_bwd_dxg_fix for samples moved beyond its reach;
 //   weight gradient  dense: k_restride_dout then k_gemm grad_weight =
 //                    dout S^T; other shapes: k_bwd_weight;
-//   k_bwd_bias       one workgroup per (output channel, batch), atomics.
+//   k_bwd_bias       one workgroup per output channel, fixed order, no atomics.
 #include "dc1d_internal.h"
 
 #include <algorithm>
@@ -130,22 +130,31 @@ __global__ void __launch_bounds__(256) k_bwd_weight(BwdParams a) {
     if (threadIdx.x == 0) a.gw[e] = s_red[0];
 }
 
-// One workgroup per (co, b): the row's sum, added to grad_bias[co] (cleared
-// first) with one atomic.
+// One workgroup per output channel co: grad_bias[co] = the sum of its dout
+// rows over the batch, in a fixed order (thread t adds elements t, t + 256,
+// ... of the channel's B * L_out values, b-major; then a tree over the
+// threads) and stored once: no clear, no atomics, the same bits on every
+// run.  (The flat index keeps several independent loads in flight per
+// thread when the rows are short.)
 __global__ void __launch_bounds__(256) k_bwd_bias(BwdParams a) {
     const Params &p = a.p;
     __shared__ float s_red[256];
-    const int co = blockIdx.x % p.C_out, b = blockIdx.x / p.C_out;
-    const float *d = a.dout + ((int64_t)b * p.C_out + co) * p.L_out;
+    const int co = blockIdx.x;
+    const int64_t n = (int64_t)p.B * p.L_out;
+    const float *d = a.dout + (int64_t)co * p.L_out;
     float acc = 0.0f;
-    for (int l = threadIdx.x; l < p.L_out; l += 256) acc += d[l];
+#pragma unroll 4
+    for (int64_t i = threadIdx.x; i < n; i += 256) {
+        const int64_t b = i / p.L_out, l = i - b * p.L_out;
+        acc += d[b * p.C_out * p.L_out + l];
+    }
     s_red[threadIdx.x] = acc;
     __syncthreads();
     for (int h = 128; h > 0; h >>= 1) {
         if ((int)threadIdx.x < h) s_red[threadIdx.x] += s_red[threadIdx.x + h];
         __syncthreads();
     }
-    if (threadIdx.x == 0) unsafeAtomicAdd(a.gb + co, s_red[0]);
+    if (threadIdx.x == 0) a.gb[co] = s_red[0];
 }
 
 // Dense path (groups == 1): dS = W^T dout and grad_weight = dout S^T are
@@ -1091,12 +1100,8 @@ struct BwdLayout {
 
 hipError_t launch_bias(const BwdParams &a, hipStream_t stream) {
     const Params &p = a.p;
-    if (a.gb) {
-        hipLaunchKernelGGL(k_bwd_zero, dim3(grid_for(p.C_out)), dim3(256), 0, stream, a.gb, (int64_t)p.C_out);
-        const int64_t blocks = (int64_t)p.C_out * p.B;
-        if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-        if (blocks > 0) hipLaunchKernelGGL(k_bwd_bias, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-    }
+    if (a.gb && p.C_out > 0)  // (C_out < 2^31 by validation; an empty batch gives zeros)
+        hipLaunchKernelGGL(k_bwd_bias, dim3((unsigned)p.C_out), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -29,8 +29,9 @@
 //     nothing); one barrier per chunk;
 //   * the MFMA takes the samples as its A operand and the weights as B, so
 //     that a lane's accumulators are one output row and four consecutive
-//     columns per register group: the epilogue adds the row's bias and
-//     stores 8-byte words of bf16 straight from the accumulators.
+//     columns per register group: the epilogue adds the row's bias, and
+//     stages each 32-row block through LDS so that eight lanes write one
+//     row's 128 contiguous bytes.
 //
 // Interpolation: a sample is (1 - f) m x[j] + f m x[j+1] (m the mask, 1
 // without one).  The weights w0 = (1 - f) m and w1 = f m are computed in
@@ -87,9 +88,9 @@ constexpr int kWSEG = 4;                      // batch segments a windowed tile 
 constexpr int kWV = kWBM * (BK / 8) / kWT;    // 16-byte weight words per thread per chunk (4)
 constexpr int kWRV = kWT / (BK / 8);          // rows between one thread's weight words (64)
 constexpr size_t kWideWLds = (size_t)2 * kWBM * BK * 2;  // the two weight tiles (bytes)
-// the gathering instantiation's LDS: the weight tiles and the epilogue's
-// staging rows (4 waves x 32 rows x 72 floats)
-constexpr size_t kWideGatherLds = kWideWLds > 4 * 32 * 72 * 4 ? kWideWLds : 4 * 32 * 72 * 4;
+// the gathering instantiation's LDS: the weight tiles (the epilogue's
+// staging rows fit in them)
+constexpr size_t kWideGatherLds = kWideWLds;
 
 struct WideArgs {
     Params p;
@@ -157,7 +158,10 @@ __global__ void __launch_bounds__(kWT, 1) k_mfma_wide(WideArgs a) {
     // ---- the tile
     const int U = a.tiles_m * a.tiles_n;
     const int unit = remap_xcd(blockIdx.x, U);
-    const int tn = unit % a.tiles_n, tm = unit / a.tiles_n;
+    // row tiles fastest: the row tiles of one column block run side by side
+    // on one XCD and share its x windows (and offsets) in that XCD's L2; the
+    // weight slices are far smaller than x
+    const int tm = unit % a.tiles_m, tn = unit / a.tiles_m;
     const int m0 = tm * kWBM;
     const int n0 = tn * kWBN;  // N < 2^31: 32-bit column arithmetic
     const int n_end = (int)min((int64_t)n0 + kWBN, a.N);
@@ -631,6 +635,51 @@ __global__ void __launch_bounds__(kWT, 1) k_mfma_wide(WideArgs a) {
         const T *__restrict__ bias = (const T *)p.bias;
 #pragma unroll
         for (int mb = 0; mb < kWMB; ++mb) bv[mb] = bias ? BF16::ld(bias, min(m0 + 32 * mb + li, M - 1)) : 0.0f;
+    }
+    if (L_out % 8 == 0 && ((uintptr_t)out & 15) == 0) {
+        // Whole 16-byte words of output rows (a word never straddles a batch
+        // nor the end of N: L_out, and so N, is a multiple of 8).  Each
+        // 32-row block of the wave's 256 x 64 piece goes through LDS (the
+        // weight tiles, free after the main loop's last barrier), bf16 with
+        // the bias added: lane li writes its row's 64 columns, then eight
+        // lanes write one row's 128 contiguous bytes, 4 stores per block.
+        // Written straight from the accumulators, a store would cover 16
+        // bytes of each of 32 rows.
+        constexpr int PITCH = 64 + 8;  // staging row (elements): 144 bytes
+        static_assert(4 * 32 * PITCH * 2 <= kWideWLds, "staging fits in the weight tiles");
+        T *stg = (T *)smem + wv * 32 * PITCH;
+        const int rl = lane / 8, cl = (lane % 8) * 8;
+        const int col = n0 + 64 * wv + cl;
+        const bool col_ok = col < n_end;
+        const int b = (int)fdiv((uint32_t)(col_ok ? col : n0), a.fd_Lout);
+        T *ob = out + (int64_t)b * M * L_out + (col - b * L_out);
+        // LDS is shared by the wave's lanes only here; fences order each
+        // lane's accesses around the exchange
+        auto wave_sync = [] {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        };
+#pragma unroll
+        for (int mb = 0; mb < kWMB; ++mb) {
+            wave_sync();  // the previous block's reads are done
+#pragma unroll
+            for (int nb = 0; nb < kWNB; ++nb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *(u2 *)(stg + li * PITCH + 32 * nb + 8 * g + 4 * lh) =
+                        u2{pack_bf16x2(acc[mb][nb][4 * g] + bv[mb], acc[mb][nb][4 * g + 1] + bv[mb]),
+                           pack_bf16x2(acc[mb][nb][4 * g + 2] + bv[mb], acc[mb][nb][4 * g + 3] + bv[mb])};
+            wave_sync();
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int r = 8 * it + rl;
+                const int row = m0 + 32 * mb + r;
+                const u4 word = *(const u4 *)(stg + r * PITCH + cl);
+                if (col_ok && (m_full || row < M)) *(u4 *)(ob + (int64_t)row * L_out) = word;
+            }
+        }
+        return;
     }
     if (L_out % 4 == 0 && ((uintptr_t)out & 7) == 0) {
         int64_t cbase[kWNB][4];

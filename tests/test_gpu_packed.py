@@ -89,6 +89,16 @@ def shapes():
         # ragged tiles; unmodulated
         (3, 16, 16, 777, 5, 2, 3, 2, 16, 16, True),
         (2, 32, 32, 1000, 3, 1, 1, 1, 32, 32, False),
+        # output lengths a multiple of 32: the persistent head kernel.  Four
+        # slabs of 32 groups (the workload's shape, smaller); three slabs
+        # padded to four, C_in padded to 64, K = 4; one slab (each wave one
+        # column block), K = 2, a partial column tile; two slabs, K = 1;
+        # strided, two slabs
+        (2, 64, 64, 1024, 3, 1, 1, 1, 64, 64, True),
+        (3, 40, 40, 99, 4, 1, 0, 1, 40, 40, True),
+        (2, 16, 16, 161, 2, 1, 0, 1, 16, 8, False),
+        (1, 24, 24, 64, 1, 1, 0, 1, 24, 24, True),
+        (2, 32, 32, 255, 3, 2, 1, 1, 32, 32, True),
     ]
     out = []
     for i, (B, C_in, C_out, L_in, K, s, p, d, groups, G, mod) in enumerate(spec):
