@@ -57,6 +57,11 @@ def shapes():
         (1, 8, 8, 15, 15, 3, 3, (1, 1), (1, 1), (2, 2), 8, 8, "f32", False),      # depthwise -> direct
         (2, 32, 64, 13, 11, 3, 3, (1, 1), (1, 1), (1, 1), 1, 2, "bf16", True),    # bf16 dense
         (1, 16, 16, 12, 12, 3, 3, (2, 2), (1, 1), (1, 1), 4, 4, "bf16", True),    # bf16 grouped
+        # one offset group with 1, 4 or 9 taps
+        (2, 32, 64, 13, 11, 3, 3, (1, 1), (1, 1), (1, 1), 1, 1, "bf16", True),    # bf16, ragged tiles
+        (1, 40, 48, 9, 7, 2, 2, (1, 1), (0, 0), (1, 1), 1, 1, "f32", False),     # 2x2 taps, no mask
+        (1, 24, 32, 6, 10, 1, 1, (1, 1), (0, 0), (1, 1), 1, 1, "bf16", True),     # 1x1 taps
+        (2, 33, 40, 14, 10, 3, 3, (2, 1), (1, 2), (1, 2), 1, 1, "f32", True),     # strides, dilations, C_in odd
     ]
     out = []
     for i, (B, C_in, C_out, H, W, kh, kw, s, p, d, groups, G, dt, mod) in enumerate(spec):
