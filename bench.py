@@ -602,7 +602,7 @@ def run2d(w, steps, warmup, check=True, baseline=True):
             a = out[b:b + 1].double().cpu().numpy()
             rms = math.sqrt(float(np.mean(ref ** 2)))
             if w.dtype == "f32":
-                tol = 1e-5 * math.sqrt(w.C_in // w.groups * w.kh * w.kw) * max(rms, 1.0)
+                tol = 1e-5 * math.sqrt(w.C_in // w.groups * w.kh * w.kw)
                 worst = max(worst, float(np.abs(a - ref).max()) / tol)
             else:
                 worst = max(worst, float((np.abs(a - ref) / (2e-2 * np.maximum(np.abs(ref), rms))).max()))

@@ -8,7 +8,7 @@ moved by the window's start (an integer, added in float64, so the split of
 every position is unchanged), one output channel, stride 1, no padding.
 Positions outside the clipped window are never reached, or lie outside
 [0, L_in) in both problems, so the sub-problem's output is the full one's.
-Tolerance as in the parity tests: 1e-5 * sqrt(C_in/groups * K) * max(rms, 1).
+Tolerance as in the parity tests: max|err| <= 1e-5 * sqrt(C_in/groups * K).
 """
 import math
 
@@ -76,8 +76,7 @@ def run(B, C_in, C_out, L_in, K, stride, padding, dilation, groups, G, kernel_pr
     pts = points(B, C_out, L_out, 256, seed)
     got = y[pts[:, 0], pts[:, 1], pts[:, 2]].double().cpu().numpy()
     ref = reference_at(x, off, w, bias, pts, stride, padding, dilation, groups)
-    rms = math.sqrt(float(np.mean(ref ** 2)))
-    tol = 1e-5 * math.sqrt(C_in // groups * K) * max(rms, 1.0)
+    tol = 1e-5 * math.sqrt(C_in // groups * K)
     err = float(np.abs(got - ref).max())
     del x, off, w, bias, y
     torch.cuda.empty_cache()
