@@ -38,8 +38,8 @@ hipError_t launch_wide_t(const Params &p, const MfmaPlan &pl, hipStream_t stream
     a.gather = (uint8_t *)p.ws + pl.wide_wb_bytes;
     // weights -> [K][C_out][ncb][32]: blocks of 32 channels at one tap (a
     // padding block, when there is one, gets zeros)
-    hipLaunchKernelGGL((k_weight_blocks<uint16_t>), weight_blocks_grid(p.C_out, p.K, pl.wide_ncb * BK), dim3(256), 0,
-                       stream, (const uint16_t *)p.w, wb, p.C_out, p.C_in, p.K, 0, pl.wide_ncb, p.K);
+    hipLaunchKernelGGL((k_weight_blocks<uint16_t>), dim3((unsigned)(p.K * p.C_out)), dim3(256), 0, stream,
+                       (const uint16_t *)p.w, wb, p.C_out, p.C_in, p.K, 0, pl.wide_ncb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 grid((unsigned)(pl.wide_tiles_m * pl.wide_tiles_n));

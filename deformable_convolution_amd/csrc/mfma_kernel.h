@@ -1469,36 +1469,20 @@ __global__ void __launch_bounds__(NTT) k_mfma_cb(MfmaArgs a) {
 
 // Weights [C_out][C_in][K] -> chunk rows [nkb][C_out][ncb][32]: element
 // (kb, m, cb, i*TPC + t) = W[m][CB*cb + i][TPC*kb + t], zero past C_in or K.
-// A plain copy of the stored bits.  Workgroup (m, y) writes elements
-// 1024 y .. 1024 y + 1023 of output channel m's nkb destination rows (all
-// from its one contiguous source row), four per thread: the four loads,
-// then the four stores.
+// A plain copy of the stored bits; one workgroup per destination row.
 template <class T>
 __global__ void __launch_bounds__(256) k_weight_blocks(const T *__restrict__ w, T *__restrict__ wb, int C_out,
-                                                       int C_in, int K, int tpc_log2, int ncb, int nkb) {
-    const int m = blockIdx.x;
+                                                       int C_in, int K, int tpc_log2, int ncb) {
+    const int row = blockIdx.x;  // kb * C_out + m
+    const int kb = row / C_out, m = row - kb * C_out;
     const int len = ncb * BK, cbs = BK >> tpc_log2, tmask = (1 << tpc_log2) - 1;
     const T *__restrict__ wm = w + (int64_t)m * C_in * K;
-    T v[4];
-    int64_t d[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int j = blockIdx.y * 1024 + 256 * i + threadIdx.x;
-        const int kb = j / len, jj = j - kb * len;
-        const int r = jj & (BK - 1);
-        const int ci = (jj >> 5) * cbs + (r >> tpc_log2), k = (kb << tpc_log2) + (r & tmask);
-        d[i] = j < nkb * len ? ((int64_t)kb * C_out + m) * len + jj : -1;
-        v[i] = (d[i] >= 0 && ci < C_in && k < K) ? wm[ci * K + k] : (T)0;
+    T *__restrict__ dst = wb + (int64_t)row * len;
+    for (int j = threadIdx.x; j < len; j += 256) {
+        const int r = j & (BK - 1);
+        const int ci = (j >> 5) * cbs + (r >> tpc_log2), k = (kb << tpc_log2) + (r & tmask);
+        dst[j] = (ci < C_in && k < K) ? wm[ci * K + k] : (T)0;
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        if (d[i] >= 0) wb[d[i]] = v[i];
-}
-
-// The grid of k_weight_blocks for output channels C_out and nkb destination
-// rows of len elements each.
-inline dim3 weight_blocks_grid(int C_out, int nkb, int len) {
-    return dim3((unsigned)C_out, (unsigned)((nkb * len + 1023) / 1024));
 }
 
 // ---- plain GEMM (used by the backward) -------------------------------------------
@@ -1741,8 +1725,8 @@ hipError_t launch_for(const Params &p, const MfmaPlan &pl, hipStream_t stream) {
             a.wb = wb;
             int tpc_log2 = 0;
             while ((BK >> tpc_log2) > pl.cb) ++tpc_log2;
-            hipLaunchKernelGGL((k_weight_blocks<T>), weight_blocks_grid(p.C_out, pl.nkb, pl.ncb * BK), dim3(256), 0, stream,
-                               (const T *)p.w, wb, p.C_out, p.C_in, p.K, tpc_log2, pl.ncb, pl.nkb);
+            hipLaunchKernelGGL((k_weight_blocks<T>), dim3((unsigned)(pl.nkb * p.C_out)), dim3(256), 0, stream,
+                               (const T *)p.w, wb, p.C_out, p.C_in, p.K, tpc_log2, pl.ncb);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
