@@ -445,9 +445,11 @@ def main_backward(args, w):
 def work_packed(w):
     """Work of one packed-layer forward: flops of the trunk, the heads and the
     forward's contraction and sampling; the bytes each of its kernels reads
-    and writes once (trunk: x, t; heads: t per head, offsets and mask;
-    forward: x, offsets, mask, out), and the layer's compulsory bytes (x,
-    parameters, out)."""
+    and writes once, and the layer's compulsory bytes (x, parameters, out).
+    Kernels: where the head kernel computes the trunk itself (K <= 4,
+    C_in <= 64, G*K*heads <= 128*K, L_out a multiple of 32) heads: x,
+    offsets and mask; forward: x, offsets, mask, out.  Otherwise trunk: x,
+    t; heads: t per head, offsets and mask; forward as before."""
     GK = w.G * w.K
     heads = 2 if w.modulated else 1
     flops = (2 * w.B * w.C_in * w.L_out * w.K + 2 * w.B * w.L_out * w.C_in * GK * heads
@@ -456,7 +458,11 @@ def work_packed(w):
     x, t, out = w.B * w.C_in * w.L_in, w.B * w.C_in * w.L_out, w.B * w.C_out * w.L_out
     gen = w.B * GK * w.L_out * heads
     params = w.C_in * (w.K + 1) + (GK * w.C_in + GK) * heads + w.C_out * ((w.C_in // w.groups) * w.K + 1)
-    pipeline = 4 * ((x + t) + (t * heads + gen) + (x + gen + out) + params)
+    fused = w.K <= 4 and w.C_in <= 64 and GK * heads <= 128 * w.K and w.L_out % 32 == 0
+    if fused:
+        pipeline = 4 * ((x + gen) + (x + gen + out) + params)
+    else:
+        pipeline = 4 * ((x + t) + (t * heads + gen) + (x + gen + out) + params)
     compulsory = 4 * (x + params + out)
     return flops, pipeline, compulsory
 

@@ -887,15 +887,22 @@ int packed_forward_impl(const dc1d_tensor *x, const dc1d_tensor *trunk_weight,
     pk.trunk.wcat = wcat;
     pk.trunk.bcat = bcat;
     pk.trunk.GK = GK;
-    hipError_t e = launch_trunk(pk.trunk, s);
-    if (e != hipSuccess) return DC1D_ERR_LAUNCH;
     const int64_t brow = pk.fwd.L_out, bbatch = (int64_t)pk.fwd.C_in * pk.fwd.L_out;
     const int M = GK * (pk.mw ? 2 : 1);
-    if (heads_fit(pk.fwd.C_in, pk.K, M, pk.fwd.L_out, t, off, mask)) {  // the persistent head kernel
+    // fp32 storage: the persistent head kernel computes the trunk itself
+    // (no trunk launch, no stacked head weights); bf16: the trunk kernel
+    // first, then the head kernel reads it
+    const bool fused = !bf16 && heads_fit(pk.fwd.C_in, pk.K, M, pk.fwd.L_out, nullptr, off, mask);
+    hipError_t e = hipSuccess;
+    if (!fused) {
+        e = launch_trunk(pk.trunk, s);
+        if (e != hipSuccess) return DC1D_ERR_LAUNCH;
+    }
+    if (fused || heads_fit(pk.fwd.C_in, pk.K, M, pk.fwd.L_out, t, off, mask)) {  // the persistent head kernel
         HeadArgs h = {};
         h.t = t;
-        h.w = pk.mw ? wcat : pk.ow;
-        h.bias = pk.mw ? bcat : pk.ob;
+        h.w = pk.mw && !fused ? wcat : pk.ow;
+        h.bias = pk.mw && !fused ? bcat : pk.ob;
         h.off = (float *)off;
         h.mask = (float *)mask;
         h.B = pk.fwd.B;
@@ -904,6 +911,17 @@ int packed_forward_impl(const dc1d_tensor *x, const dc1d_tensor *trunk_weight,
         h.G = pk.G;
         h.K = pk.K;
         h.M = M;
+        if (fused) {
+            h.x = (const float *)x->data;
+            h.tw = pk.trunk.tw;
+            h.tb = pk.trunk.tb;
+            h.w2 = pk.mw;
+            h.bias2 = pk.mb;
+            h.L_in = pk.fwd.L_in;
+            h.stride = pk.fwd.stride;
+            h.padding = pk.fwd.padding;
+            h.dilation = pk.fwd.dilation;
+        }
         e = launch_heads(h, dev.num_cus, s);
     } else if (pk.mw) {
         e = launch_gemm_f32(head_gemm(pk, wcat, bcat, off, mask, shared), brow, bbatch, 2, dev.num_cus, s);

@@ -224,12 +224,20 @@ size_t gemm_bf16_workspace_bytes(const Params &q, int num_cus);
 // [B][G][L][K], all fp32.  heads_fit: the shapes and alignments the kernel
 // serves (K <= 4, C <= 64, M <= 128*K, L a multiple of 32, 16-byte aligned
 // t, off, mask); the general head GEMM (launch_gemm_f32, out_mode 1 or 2)
-// serves the rest.
+// serves the rest.  With x non-null (fp32 x [B][C][L_in]) the kernel
+// computes the trunk itself, t[b,c,l] = tb[c] + sum_k tw[c,k] *
+// x~[b,c, l*stride - padding + k*dilation] (x~ zero outside [0, L_in)),
+// the same sum in the same order as k_trunk, and t is not read; the head
+// rows are then w (the offset head, G*K rows) and w2 (the mask head), with
+// biases bias and bias2.
 struct HeadArgs {
     const float *t, *w, *bias;  // bias may be null
     float *off, *mask;          // mask null without the mask head
     int B, C, L, G, K, M;
-    int slabs, tiles_per_b, tiles;  // set by launch_heads
+    // the fused trunk (x null: t is read)
+    const float *x, *tw, *tb, *w2, *bias2;  // tb, bias2 may be null; w2 null without the mask head
+    int L_in, stride, padding, dilation;
+    int slabs, tiles_per_b, tiles, xvec;  // set by launch_heads
 };
 bool heads_fit(int C, int K, int M, int L, const void *t, const void *off, const void *mask);
 hipError_t launch_heads(HeadArgs a, int num_cus, hipStream_t stream);

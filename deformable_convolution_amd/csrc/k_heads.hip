@@ -23,7 +23,9 @@
 //     half), zero past M and past C;
 //   * the trunk tile [2*NKP][128] is staged in LDS (rows past C zero); two
 //     workgroups share a CU, so that one's loads, write-out and barriers
-//     overlap the other's MFMAs;
+//     overlap the other's MFMAs.  With fp32 storage the tile is computed
+//     here from x (each thread four consecutive outputs of a channel, its
+//     taps in k_trunk's order), so the trunk never reaches memory;
 //   * per k-pair and column block one LDS read gives the B operand, shared
 //     by the slab's K row blocks (v_mfma_f32_32x32x2_f32, fp32 throughout);
 //   * the write-out stages each 32-column block of the slab through LDS in
@@ -47,7 +49,7 @@ constexpr int kHSBP = kHBN + 32;  // trunk tile pitch (floats): rows 2kk and 2kk
 // the mask head's activation (the reciprocal instruction, within an ulp)
 __device__ __forceinline__ float head_sigmoid(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
-template <int KT, int NKP>
+template <int KT, int NKP, bool TRUNK>
 __global__ void __launch_bounds__(kHT, 2) k_heads(HeadArgs a) {
     constexpr int CP = 2 * NKP;                // trunk rows staged (C padded)
     constexpr int NBV = CP * kHBN / 4 / kHT;   // 16-byte trunk words per thread per tile
@@ -65,18 +67,25 @@ __global__ void __launch_bounds__(kHT, 2) k_heads(HeadArgs a) {
     const int r0 = slab * SROWS;
     const int C = a.C, L = a.L, M = a.M, G = a.G;
 
-    // the slab's weights (A operand) and the biases of every slab
+    // the slab's weights (A operand) and the biases of every slab; with the
+    // fused trunk the mask head's rows (from G*K on) come from w2 and bias2
+    const int GK = G * KT;
     float aw[KT][NKP];
 #pragma unroll
     for (int mb = 0; mb < KT; ++mb) {
         const int row = r0 + 32 * mb + li;
+        const float *wr = (TRUNK && row >= GK) ? a.w2 + (int64_t)(row - GK) * C : a.w + (int64_t)row * C;
 #pragma unroll
         for (int kk = 0; kk < NKP; ++kk) {
             const int c = 2 * kk + lh;
-            aw[mb][kk] = (row < M && c < C) ? a.w[(int64_t)row * C + c] : 0.0f;
+            aw[mb][kk] = (row < M && c < C) ? wr[c] : 0.0f;
         }
     }
-    for (int r = t; r < 4 * SROWS; r += kHT) s_bias[r] = (a.bias && r < M) ? a.bias[r] : 0.0f;
+    for (int r = t; r < 4 * SROWS; r += kHT) {
+        const float *bs = (TRUNK && r >= GK) ? a.bias2 : a.bias;
+        const int rb = (TRUNK && r >= GK) ? r - GK : r;
+        s_bias[r] = (bs && r < M) ? bs[rb] : 0.0f;
+    }
 
     // trunk words of tile T: word v = t + kHT*z is row v / 32, columns 4*(v % 32) .. +3
     hf4 br[NBV];
@@ -87,6 +96,50 @@ __global__ void __launch_bounds__(kHT, 2) k_heads(HeadArgs a) {
             const int v = t + kHT * z, c = v / 32, col = 4 * (v % 32);
             br[z] = (c < C && l0 + col < L) ? *(const hf4 *)(a.t + ((int64_t)b * C + c) * L + l0 + col)
                                             : hf4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+    };
+    // the fused trunk: the tile's words computed from x and written to LDS
+    // one at a time (word z: the four outputs l0 + col .. +3 of channel c,
+    // the taps added in k_trunk's order); the caller's barrier after the
+    // previous tile has freed the tile
+    auto trunk_b = [&](int T) {
+        const int b = T / a.tiles_per_b, l0 = (T - b * a.tiles_per_b) * kHBN;
+#pragma unroll 2
+        for (int z = 0; z < NBV; ++z) {
+            const int v = t + kHT * z, c = v / 32, col = 4 * (v % 32);
+            const int cc = min(c, C - 1);
+            const float *xr = a.x + ((int64_t)b * C + cc) * a.L_in;
+            const float *twc = a.tw + cc * KT;
+            const float tb = a.tb ? a.tb[cc] : 0.0f;
+            float tv[4];
+            if (a.xvec) {
+                // stride 1, padding, dilation and L_in multiples of 4, x
+                // aligned: tap k's four inputs are one 16-byte word, wholly
+                // inside the row or wholly outside
+                float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int k = 0; k < KT; ++k) {
+                    const int pos = l0 + col - a.padding + k * a.dilation;
+                    const hf4 xv = (pos >= 0 && pos < a.L_in) ? *(const hf4 *)(xr + pos) : hf4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[j] += twc[k] * xv[j];
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) tv[j] = (c < C && l0 + col < L) ? acc[j] + tb : 0.0f;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int base = (l0 + col + j) * a.stride - a.padding;
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int k = 0; k < KT; ++k) {
+                        const int pos = base + k * a.dilation;
+                        acc += twc[k] * ((pos >= 0 && pos < a.L_in) ? xr[pos] : 0.0f);
+                    }
+                    tv[j] = (c < C && l0 + col < L) ? acc + tb : 0.0f;
+                }
+            }
+            *(hf4 *)(s_b + c * kHSBP + col) = hf4{tv[0], tv[1], tv[2], tv[3]};
         }
     };
     auto commit_b = [&]() {
@@ -110,8 +163,12 @@ __global__ void __launch_bounds__(kHT, 2) k_heads(HeadArgs a) {
         const int T = a.tiles - 1 - i;
         // this tile's trunk rows (the other workgroup on the CU computes
         // while they load)
-        fetch_b(T);
-        commit_b();
+        if constexpr (TRUNK) {
+            trunk_b(T);
+        } else {
+            fetch_b(T);
+            commit_b();
+        }
         __syncthreads();
         const int b = T / a.tiles_per_b, l0 = (T - b * a.tiles_per_b) * kHBN;
         // one 32-column block at a time: its K accumulators over every
@@ -174,10 +231,17 @@ __global__ void __launch_bounds__(kHT, 2) k_heads(HeadArgs a) {
 
 template <int KT>
 hipError_t launch_kt(const HeadArgs &a, int nkp, dim3 grid, size_t lds, hipStream_t stream) {
-    if (nkp == 16)
-        hipLaunchKernelGGL((k_heads<KT, 16>), grid, dim3(kHT), lds, stream, a);
-    else
-        hipLaunchKernelGGL((k_heads<KT, 32>), grid, dim3(kHT), lds, stream, a);
+    if (a.x) {
+        if (nkp == 16)
+            hipLaunchKernelGGL((k_heads<KT, 16, true>), grid, dim3(kHT), lds, stream, a);
+        else
+            hipLaunchKernelGGL((k_heads<KT, 32, true>), grid, dim3(kHT), lds, stream, a);
+    } else {
+        if (nkp == 16)
+            hipLaunchKernelGGL((k_heads<KT, 16, false>), grid, dim3(kHT), lds, stream, a);
+        else
+            hipLaunchKernelGGL((k_heads<KT, 32, false>), grid, dim3(kHT), lds, stream, a);
+    }
     return hipGetLastError();
 }
 
@@ -191,7 +255,11 @@ bool heads_fit(int C, int K, int M, int L, const void *t, const void *off, const
 }
 
 hipError_t launch_heads(HeadArgs a, int num_cus, hipStream_t stream) {
-    if (!heads_fit(a.C, a.K, a.M, a.L, a.t, a.off, a.mask)) return hipErrorInvalidValue;
+    if (!heads_fit(a.C, a.K, a.M, a.L, a.x ? nullptr : a.t, a.off, a.mask)) return hipErrorInvalidValue;
+    if (a.x && (!a.tw || (a.mask && !a.w2) || a.L_in < 1 || a.stride < 1 || a.dilation < 1))
+        return hipErrorInvalidValue;
+    a.xvec = a.x && a.stride == 1 && a.padding % 4 == 0 && a.dilation % 4 == 0 && a.L_in % 4 == 0 &&
+             ((uintptr_t)a.x & 15) == 0;
     a.slabs = (a.M + 32 * a.K - 1) / (32 * a.K);
     if (a.slabs == 3) a.slabs = 4;  // (three slabs: one wave idle)
     a.tiles_per_b = (a.L + kHBN - 1) / kHBN;
