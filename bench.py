@@ -509,19 +509,26 @@ def run_packed(w, steps, warmup, check=True, baseline=True):
                "cores": min(int(os.environ["OMP_NUM_THREADS"]), cores), "kind": "oracle",
                "sample": "1 full packed-layer forward (generator and forward, all %d outputs), %.1f s, on %s"
                % (w.B * w.C_out * w.L_out, el, cpu_model())}
-        # the forward's tolerance plus the generated inputs' tolerances carried
-        # through the interpolation (Lipschitz in the position, constant
-        # <= 2 max|x|), as in the packed parity tests
+        # the generated offsets and mask against the oracle's generator, and
+        # the output against the oracle's forward on the GPU's own offsets and
+        # mask with the forward's bound, as in the packed parity tests
+        o2, gen = dc1d.packed_forward(*args, with_offsets=True, **kw)
+        torch.cuda.synchronize()
+        g_off, g_mask = gen if w.modulated else (gen, None)
         a = out.double().cpu().numpy()
+        assert np.array_equal(a, o2.double().cpu().numpy()), "packed output differs with the offsets returned"
         rms = lambda v: math.sqrt(float(np.mean(v ** 2)))
-        n = (w.C_in // w.groups) * w.K
+        a_off = g_off.double().cpu().numpy()
+        a_m = g_mask.double().cpu().numpy() if g_mask is not None else None
         tol_o = 1e-5 * math.sqrt(w.C_in) * max(rms(r_off), 1.0)
         tol_m = tol_o / 4 + 2.0 ** -20
-        mmax = float(np.abs(r_mask).max()) if r_mask is not None else 1.0
-        tol = (1e-5 * math.sqrt(n) * max(rms(ref), 1.0)
-               + n * float(t["weight"].abs().max()) * float(t["x"].abs().max()) * (2 * tol_o * mmax + tol_m))
-        err = float(np.abs(a - ref).max())
-        parity = {"elements": int(ref.size), "max_err": err, "tol": tol, "ok": bool(err <= tol)}
+        gen_ok = float(np.abs(a_off - r_off).max()) <= tol_o and (a_m is None or float(np.abs(a_m - r_mask).max()) <= tol_m)
+        g_ref = oracle.forward(t["x"], a_off, t["weight"], t["bias"], a_m, **kw)
+        tol = 1e-5 * math.sqrt((w.C_in // w.groups) * w.K)
+        err = float(np.abs(a - g_ref).max())
+        err_ref = float(np.abs(a - ref).max())
+        parity = {"elements": int(ref.size), "max_err": err, "tol": tol, "generator_ok": gen_ok,
+                  "max_err_vs_oracle_generator": err_ref, "ok": bool(err <= tol and gen_ok)}
         if not parity["ok"]:
             raise SystemExit("packed parity check failed: %r" % parity)
     tm = timed(step, steps, warmup, dev)

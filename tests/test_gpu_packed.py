@@ -10,10 +10,10 @@ Tolerances, elementwise, derived from the arithmetic:
   is off by about (|z| + 2) * 2^-24 relatively, which the sigmoid scales by
   s(1 - s) <= 1/4, plus the final add and the reciprocal instruction,
   within an ulp);
-* out: the forward's tolerance 1e-5 * sqrt(cpg*K) * max(rms(out), 1) plus
-  the effect of the generated inputs' errors through the interpolation,
-  which is Lipschitz in the position with constant |x(i0+1) - x(i0)| <= 2 max|x|:
-  cpg * K * max|w| * max|x| * (2 * tol_o * max|mask| + tol_m).
+* out: against the oracle's forward evaluated on the offsets and mask the
+  GPU generated (checked above against the oracle's generator), with the
+  forward's own bound max|err| <= 1e-5 * sqrt(cpg*K): the generator's
+  errors are held to theirs, the forward's to its.
 """
 import math
 
@@ -62,11 +62,10 @@ def run_packed(w, seed=0, check_out=True, constrained=False):
     if check_out:
         a_out = out.double().cpu().numpy()
         assert a_out.shape == r_out.shape and np.isfinite(a_out).all()
-        n = (w.C_in // w.groups) * w.K
-        mmax = float(np.abs(r_mask).max()) if w.modulated else 1.0
-        tol = (1e-5 * math.sqrt(n) * max(rms(r_out), 1.0)
-               + n * float(t["weight"].abs().max()) * float(t["x"].abs().max()) * (2 * tol_o * mmax + tol_m))
-        err = float(np.abs(a_out - r_out).max())
+        g_out = oracle.forward(t["x"], a_off, t["weight"], t["bias"], mask.double().cpu().numpy() if w.modulated else None,
+                               groups=w.groups, constrained=constrained, **kw)
+        tol = 1e-5 * math.sqrt((w.C_in // w.groups) * w.K)
+        err = float(np.abs(a_out - g_out).max())
         assert err <= tol, "%s out: %.3g > %.3g" % (w.name, err, tol)
     return out
 
