@@ -409,7 +409,7 @@ def run_backward(w, steps, warmup, check=True, baseline=True):
             "graph": tm["graph"], "parity": parity, "cpu": cpu}
 
 
-def main_backward(args, w):
+def main_backward(args, w, stream=None):
     r = run_backward(w, args.steps, args.warmup, baseline=not args.no_cpu_baseline)
     contraction, sampling, nbytes = work_backward(w)
     ms = r["region_ms"] / args.steps
@@ -439,7 +439,7 @@ def main_backward(args, w):
     }
     if r["cpu"] is not None:
         line["cpu_baseline"] = r["cpu"]
-    print(json.dumps(line), flush=True)
+    print(json.dumps(line), file=stream or sys.stdout, flush=True)
 
 
 def work_packed(w):
@@ -536,7 +536,7 @@ def run_packed(w, steps, warmup, check=True, baseline=True):
             "graph": tm["graph"], "parity": parity, "cpu": cpu}
 
 
-def main_packed(args, w):
+def main_packed(args, w, stream=None):
     r = run_packed(w, args.steps, args.warmup, baseline=not args.no_cpu_baseline)
     flops, pipeline, compulsory = work_packed(w)
     ms = r["region_ms"] / args.steps
@@ -559,7 +559,7 @@ def main_packed(args, w):
     }
     if r["cpu"] is not None:
         line["cpu_baseline"] = r["cpu"]
-    print(json.dumps(line), flush=True)
+    print(json.dumps(line), file=stream or sys.stdout, flush=True)
 
 
 def work2d(w):
@@ -631,7 +631,7 @@ def run2d(w, steps, warmup, check=True, baseline=True):
     return {"kernel": kern, "region_ms": tm["region_ms"], "launch_ms": tm["launch_ms"], "parity": parity, "cpu": cpu}
 
 
-def main2d(args, w):
+def main2d(args, w, stream=None):
     r = run2d(w, args.steps, args.warmup, baseline=not args.no_cpu_baseline)
     contraction, sampling, nbytes = work2d(w)
     ms = r["region_ms"] / args.steps
@@ -656,7 +656,7 @@ def main2d(args, w):
     }
     if r["cpu"] is not None:
         line["cpu_baseline"] = r["cpu"]
-    print(json.dumps(line), flush=True)
+    print(json.dumps(line), file=stream or sys.stdout, flush=True)
 
 
 def pct(v):
@@ -791,6 +791,25 @@ def main():
                 continue
             rec = workload_line(inputs.WORKLOADS[name], max(10, args.steps // 2), args.warmup)
             print(json.dumps(rec), file=sys.stderr, flush=True)
+        # then the scope table's other rows, one record each on stderr: the
+        # backward (the layer shape and the depthwise shape), the packed
+        # layer, 2D in bf16 and fp32 -- each with its own parity check and
+        # CPU baseline; one that fails leaves an error record and the
+        # headline is still measured
+        sub = argparse.Namespace(steps=max(10, args.steps // 2), warmup=args.warmup,
+                                 no_cpu_baseline=args.no_cpu_baseline)
+        for mode, name in (("backward", "dc1d_layer"), ("backward", "depthwise"), ("packed", "packed"),
+                           ("2d", "dcn2d_bf16"), ("2d", "dcn2d")):
+            try:
+                if mode == "backward":
+                    main_backward(sub, inputs.WORKLOADS[name], stream=sys.stderr)
+                elif mode == "packed":
+                    main_packed(sub, inputs.PACKED_WORKLOADS[name], stream=sys.stderr)
+                else:
+                    main2d(sub, inputs.WORKLOADS_2D[name], stream=sys.stderr)
+            except (Exception, SystemExit) as e:  # noqa: BLE001 -- reported, the headline still runs
+                print(json.dumps({"workload": name, "pass": mode, "error": repr(e), "ok": False}), file=sys.stderr,
+                      flush=True)
 
     t = inputs.make_inputs(w, seed=0)
     r = run_gpu(w, args.steps, args.warmup, cold_reps=20, constrained=args.constrained, t=t)
