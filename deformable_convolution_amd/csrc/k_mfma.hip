@@ -318,14 +318,25 @@ hipError_t launch_gemm_bf16(const Params &q, int64_t brow, int64_t bbatch, int n
 
 size_t gemm_bf16_workspace_bytes(const Params &q, int num_cus) { return gemm_ws<TrBF16>(q, num_cus); }
 
+// out_mode 0 (the plain product): 256 x 128 tiles, or 128 x 128 ones when
+// those fill the GPU without splitting the reduction and the larger ones
+// would need a split -- the same MFMA work per CU, without the partial
+// tiles' round trip and the reduction kernel.
+bool gemm_f32_half(const Params &q, int num_cus) {
+    return gemm_plan<TrF32>(q, num_cus).splits > 1 && gemm_plan<TrF32H>(q, num_cus).splits == 1;
+}
+
 size_t gemm_workspace_bytes(const Params &q, int out_mode, int num_cus) {
-    return out_mode == 0 ? gemm_ws<TrF32>(q, num_cus) : gemm_ws<TrF32H>(q, num_cus);
+    if (out_mode == 0) return gemm_f32_half(q, num_cus) ? gemm_ws<TrF32H>(q, num_cus) : gemm_ws<TrF32>(q, num_cus);
+    return gemm_ws<TrF32H>(q, num_cus);
 }
 
 hipError_t launch_gemm_f32(const Params &q, int64_t brow, int64_t bbatch, int out_mode, int num_cus,
                            hipStream_t stream) {
     switch (out_mode) {
-    case 0: return launch_gemm_t<TrF32, 0>(q, brow, bbatch, num_cus, stream);
+    case 0:
+        return gemm_f32_half(q, num_cus) ? launch_gemm_t<TrF32H, 0>(q, brow, bbatch, num_cus, stream)
+                                         : launch_gemm_t<TrF32, 0>(q, brow, bbatch, num_cus, stream);
     case 1: return launch_gemm_t<TrF32H, 1>(q, brow, bbatch, num_cus, stream);
     case 2: return launch_gemm_t<TrF32H, 2>(q, brow, bbatch, num_cus, stream);
     default: return hipErrorInvalidValue;
