@@ -199,17 +199,21 @@ __global__ void __launch_bounds__(256) k_bwd_samples_t(BwdParams a, FastDiv fd_K
 // contributions accumulate in an LDS window (LDS atomics) that is added to
 // grad_x once at the end; samples moved outside the window use global
 // atomics directly.  The offset and mask gradients of a pair accumulate in
-// registers over the block's channels and are stored (a block holding the
-// whole offset group) or added atomically (several blocks per group).
+// registers over the block's channels and are stored: straight into the
+// gradients when a block holds the whole offset group, else into the
+// block's slot of the workspace (the group's channel blocks each own one,
+// [nsub][2][B*G*L_out*K]), which k_bwd_om_sum adds in slot order -- no
+// atomics, the same bits on every run.
 constexpr int kBwdMargin = 32;
 
 struct DxPlan {
     int cbx, lt, win, tiles_l, ngrp_blocks;
-    bool atomic_om;  // several channel blocks per offset group
+    bool atomic_om;  // several channel blocks per offset group: their sums go to slots
+    int nsub;        // channel blocks per offset group (slots)
     size_t lds;
 };
 
-__global__ void __launch_bounds__(256) k_bwd_dx(BwdParams a, DxPlan pl) {
+__global__ void __launch_bounds__(256) k_bwd_dx(BwdParams a, DxPlan pl, float *__restrict__ om_slots) {
     const Params &p = a.p;
     extern __shared__ float smem[];
     const int CBX = pl.cbx, LT = pl.lt, W = pl.win;
@@ -286,8 +290,10 @@ __global__ void __launch_bounds__(256) k_bwd_dx(BwdParams a, DxPlan pl) {
         }
         if (!tap_moves(p, off[oi], tap_range(p, k))) ao = 0.0f;  // a clamped tap: its offset has no effect
         if (pl.atomic_om) {
-            if (a.goff) unsafeAtomicAdd(a.goff + oi, ao);
-            if (a.gmask) unsafeAtomicAdd(a.gmask + oi, am);
+            const int64_t no = (int64_t)p.B * p.G * L_out * K;
+            float *slot = om_slots + (int64_t)(cblk % pl.nsub) * 2 * no;
+            if (a.goff) slot[oi] = ao;
+            if (a.gmask) slot[no + oi] = am;
         } else {
             if (a.goff) a.goff[oi] = ao;
             if (a.gmask) a.gmask[oi] = am;
@@ -299,6 +305,22 @@ __global__ void __launch_bounds__(256) k_bwd_dx(BwdParams a, DxPlan pl) {
         const int c = e / W, j = e - c * W, pos = lo + j;
         const float v = gacc[e];
         if (pos >= 0 && pos < L_in && v != 0.0f) unsafeAtomicAdd(gx + (int64_t)c * L_in + pos, v);
+    }
+}
+
+// The offset and mask gradients from k_bwd_dx's slots, added in slot
+// order (the group's channel blocks in channel order).
+__global__ void __launch_bounds__(256) k_bwd_om_sum(BwdParams a, const float *__restrict__ om_slots, int nsub) {
+    const Params &p = a.p;
+    const int64_t no = (int64_t)p.B * p.G * p.L_out * p.K;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < no; i += (int64_t)gridDim.x * 256) {
+        float so = 0.0f, sm = 0.0f;
+        for (int s2 = 0; s2 < nsub; ++s2) {
+            so += om_slots[(int64_t)s2 * 2 * no + i];
+            sm += om_slots[(int64_t)s2 * 2 * no + no + i];
+        }
+        if (a.goff) a.goff[i] = so;
+        if (a.gmask) a.gmask[i] = sm;
     }
 }
 
@@ -325,6 +347,7 @@ DxPlan plan_dx(const Params &p) {
     pl.tiles_l = (p.L_out + lt - 1) / lt;
     pl.ngrp_blocks = p.C_in / cbx;
     pl.atomic_om = cbx < p.cpo;
+    pl.nsub = p.cpo / cbx;
     pl.lds = 2 * (size_t)cbx * win * 4;
     return pl;
 }
@@ -1095,7 +1118,7 @@ Params gemm_dw(const Params &p, const float *A, const float *S, float *gw, void 
 }
 
 struct BwdLayout {
-    size_t dS, wt, S, A, part, flag, total;
+    size_t dS, wt, S, A, part, om, flag, total;
 };
 
 hipError_t launch_bias(const BwdParams &a, hipStream_t stream) {
@@ -1159,6 +1182,11 @@ BwdLayout layout(const Params &p, bool want_weight, int num_cus) {
     } else if (want_weight) {
         L.S = o;
         o += align256(nds);
+    }
+    const DxPlan dx = plan_dx(p);
+    if (dx.atomic_om) {  // k_bwd_dx's slots for the offset and mask gradients
+        L.om = o;
+        o += align256((size_t)dx.nsub * 2 * p.B * p.G * p.L_out * p.K * 4);
     }
     L.flag = o;  // the grad_x gather's flag
     o += 256;
@@ -1256,10 +1284,7 @@ hipError_t launch_backward(BwdParams a, int num_cus, hipStream_t stream) {
     ZeroSet z = {};
     if (!gather_x) z.add(a.gx, (int64_t)p.B * p.C_in * p.L_in);
     const int64_t no = (int64_t)p.B * p.G * p.L_out * p.K;
-    if (dx.atomic_om && n > 0) {  // offset and mask gradients are accumulated
-        z.add(a.goff, no);
-        z.add(a.gmask, no);
-    }
+    float *om_slots = dx.atomic_om ? (float *)(ws + L.om) : nullptr;
     int *flag = (int *)(ws + L.flag);
     if (gather_x && n > 0) z.add((float *)flag, 1);
     if (z.count > 0) hipLaunchKernelGGL(k_bwd_zero_set, dim3(grid_for(z.most)), dim3(256), 0, stream, z);
@@ -1288,7 +1313,10 @@ hipError_t launch_backward(BwdParams a, int num_cus, hipStream_t stream) {
         BwdParams ad = a;  // the offset and mask gradients (and grad_x when not gathered)
         if (gather_x) ad.gx = nullptr;
         if ((ad.gx || ad.goff || ad.gmask) && dx_blocks > 0)
-            hipLaunchKernelGGL(k_bwd_dx, dim3((unsigned)dx_blocks), dim3(256), dx.lds, stream, ad, dx);
+            hipLaunchKernelGGL(k_bwd_dx, dim3((unsigned)dx_blocks), dim3(256), dx.lds, stream, ad, dx, om_slots);
+        if (dx.atomic_om && (ad.goff || ad.gmask) && dx_blocks > 0)
+            hipLaunchKernelGGL(k_bwd_om_sum, dim3(grid_for(no)), dim3(256), 0, stream, ad, (const float *)om_slots,
+                               dx.nsub);
         if (gather_x) {
             const dim3 grid((unsigned)((int64_t)p.B * xg.cblocks * xg.tiles_l));
             if (xg.cpt == 4)

@@ -169,3 +169,21 @@ def test_backward_bf16_ragged_shapes(w):
 @pytest.mark.parametrize("name", ["long_seq_bf16", "dcnv2_bf16"])
 def test_backward_bf16_workloads_reduced_batch(name):
     run_backward(inputs.WORKLOADS[name].with_batch(1), seed=2)
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_dense_backward_repeats_bit_for_bit(G):
+    """The dense path sums every gradient in a fixed order (the offset and
+    mask gradients per channel block into workspace slots added in slot
+    order, the GEMMs unsplit or split-reduced in split order, grad_x
+    gathered, grad_bias per channel): the same call twice gives the same
+    bits.  (Offsets within the gather's reach of 16 positions.)"""
+    w = inputs.custom("bwd_repeat", B=4, C_in=512, C_out=512, L_in=128, K=16, dilation=3, G=G, L_out=83)
+    t = {k: (v.to(DEV) if v is not None else None) for k, v in inputs.make_inputs(w, seed=11).items()}
+    mask = torch.rand(t["offsets"].shape, device=DEV)
+    dout = torch.randn((w.B, w.C_out, w.L_out), device=DEV)
+    a = dc1d.backward(t["x"], t["offsets"], t["weight"], dout, mask, dilation=3)
+    b = dc1d.backward(t["x"], t["offsets"], t["weight"], dout, mask, dilation=3)
+    torch.cuda.synchronize()
+    for k in ("x", "offsets", "mask", "weight", "bias"):
+        assert torch.equal(a[k], b[k]), k
