@@ -572,15 +572,16 @@ __device__ __forceinline__ DwgGeo dwg_geo(const Params &p, int tile, int tiles_l
 
 template <int KT>
 __global__ void __launch_bounds__(kDwgT, 4) k_bwd_dwg(BwdParams a, int WIN, int NHP, int tiles_l, int *flag,
-                                                      bool bias_here) {
+                                                      bool bias_here, float *__restrict__ wslots) {
     const Params &p = a.p;
     extern __shared__ float smem[];
     float *xs = smem;                          // [WIN]
     int *I0 = (int *)(smem + WIN);             // [KT][NHP]
     float *WL = smem + WIN + KT * NHP;         // [KT][NHP]
     float *WR = smem + WIN + 2 * KT * NHP;     // [KT][NHP]
-    __shared__ float wred[KT];
-    __shared__ float s_bsum;  // the block's share of grad_bias (bias_here)
+    // each wave's weight-gradient sums (taps) and grad_bias sum, added in
+    // wave order into the block's workspace slot
+    __shared__ float wpart[kDwgT / 64][KT + 1];
     __shared__ int s_R, s_irr;
     const int L_in = p.L_in, L_out = p.L_out;
     const int tile = blockIdx.x % tiles_l;
@@ -602,8 +603,6 @@ __global__ void __launch_bounds__(kDwgT, 4) k_bwd_dwg(BwdParams a, int WIN, int 
             if (h >= nhl) I0[e] = kIrregular;
         }
     }
-    if (threadIdx.x < KT) wred[threadIdx.x] = 0.0f;
-    if (threadIdx.x == 0) s_bsum = 0.0f;
     if (threadIdx.x == 0) {
         s_R = 0;
         s_irr = 0;
@@ -747,13 +746,13 @@ __global__ void __launch_bounds__(kDwgT, 4) k_bwd_dwg(BwdParams a, int WIN, int 
                 }
         }
     }
-    // weight gradient partials: wave sums, then LDS, then one atomic per tap
+    // weight gradient partials: wave sums (a fixed butterfly), then LDS
     if (a.gw) {
 #pragma unroll
         for (int k = 0; k < KT; ++k) {
             float v = wacc[k];
             for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-            if ((threadIdx.x & 63) == 0) atomicAdd(wred + k, v);
+            if ((threadIdx.x & 63) == 0) wpart[threadIdx.x / 64][k] = v;
         }
     }
     if (bias_here) {  // grad_bias[c]: this block's outputs' dout, summed
@@ -761,7 +760,7 @@ __global__ void __launch_bounds__(kDwgT, 4) k_bwd_dwg(BwdParams a, int WIN, int 
 #pragma unroll
         for (int o = 0; o < kDwgOpt; ++o) v += (o < nvalid) ? dv[o] : 0.0f;
         for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-        if ((threadIdx.x & 63) == 0) atomicAdd(&s_bsum, v);
+        if ((threadIdx.x & 63) == 0) wpart[threadIdx.x / 64][KT] = v;
     }
     for (int o = 32; o > 0; o >>= 1) rmax = max(rmax, __shfl_xor(rmax, o));
     const bool irr_w = __any(irregular);
@@ -770,8 +769,14 @@ __global__ void __launch_bounds__(kDwgT, 4) k_bwd_dwg(BwdParams a, int WIN, int 
         if (irr_w) s_irr = 1;
     }
     __syncthreads();
-    if (a.gw && threadIdx.x < KT) unsafeAtomicAdd(a.gw + (int64_t)c * KT + threadIdx.x, wred[threadIdx.x]);
-    if (bias_here && threadIdx.x == 0) unsafeAtomicAdd(a.gb + c, s_bsum);
+    // the block's sums into its slot [c][b*tiles_l + tile][KT + 1], added
+    // over the row's blocks in order by k_bwd_dw_wsum
+    if ((threadIdx.x < KT && a.gw) || (threadIdx.x == KT && bias_here)) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kDwgT / 64; ++w) sum += wpart[w][threadIdx.x];
+        wslots[((int64_t)c * p.B * tiles_l + (int64_t)b * tiles_l + tile) * (KT + 1) + threadIdx.x] = sum;
+    }
     if (threadIdx.x == 0 && s_irr) atomicOr(flag, 1);
     if (!a.gx) return;
     // ---- phase 2: the owned positions, gathered
@@ -1156,10 +1161,17 @@ DwgPlan plan_dwg(const Params &p) {
     return pl;
 }
 
+// The depthwise gather pass's per-block grad_weight / grad_bias slots
+// ([C_in][B * tiles][K + 1] floats), 256 bytes past its flag.
+size_t dwg_slot_bytes(const Params &p) {
+    const int64_t tiles_g = (p.L_out + kDwgLT - 1) / kDwgLT;
+    return align256((size_t)p.C_in * p.B * tiles_g * (p.K + 1) * 4);
+}
+
 BwdLayout layout(const Params &p, bool want_weight, int num_cus) {
     BwdLayout L = {};
-    if (depthwise_path(p)) {  // nothing materialised; the gather pass's flag
-        L.total = plan_dwg(p).lds > 0 ? 256 : 0;
+    if (depthwise_path(p)) {  // the gather pass's flag and slots
+        L.total = plan_dwg(p).lds > 0 ? 256 + dwg_slot_bytes(p) : 0;
         return L;
     }
     const size_t nds = (size_t)p.B * p.C_in * p.K * p.L_out * 4;
@@ -1200,6 +1212,41 @@ size_t backward_workspace_bytes(const Params &p, bool want_weight, int num_cus) 
     return layout(p, want_weight, num_cus).total;
 }
 
+// grad_weight (and grad_bias) of the depthwise gather pass: one wave per
+// channel adds that channel's per-block slot sums, lane j taking blocks j,
+// j + 64, ... in order and a fixed butterfly combining the lanes, so every
+// call sums in the same order.
+__global__ void __launch_bounds__(256) k_bwd_dw_wsum(BwdParams a, const float *__restrict__ wslots, int nblk,
+                                                     bool bias_here) {
+    const Params &p = a.p;
+    const int c = blockIdx.x * 4 + (int)(threadIdx.x / 64), lane = threadIdx.x & 63;
+    if (c >= p.C_in) return;
+    const int K1 = p.K + 1;
+    const float *sl = wslots + (int64_t)c * nblk * K1;
+    float acc[10];
+#pragma unroll
+    for (int k = 0; k < 10; ++k) acc[k] = 0.0f;
+    for (int j = lane; j < nblk; j += 64) {
+#pragma unroll
+        for (int k = 0; k < 10; ++k)
+            if (k < K1) acc[k] += sl[(int64_t)j * K1 + k];
+    }
+#pragma unroll
+    for (int k = 0; k < 10; ++k) {
+        if (k < K1) {  // uniform over the wave
+            float v = acc[k];
+            for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+            if (lane == 0) {
+                if (k < p.K) {
+                    if (a.gw) a.gw[(int64_t)c * p.K + k] = v;
+                } else if (bias_here) {
+                    a.gb[c] = v;
+                }
+            }
+        }
+    }
+}
+
 hipError_t launch_backward_dw(BwdParams a, int *flag, hipStream_t stream, bool *bias_done) {
     if (bias_done) *bias_done = false;
     const Params &p = a.p;
@@ -1220,20 +1267,20 @@ hipError_t launch_backward_dw(BwdParams a, int *flag, hipStream_t stream, bool *
         z.add(a.goff, no);
         z.add(a.gmask, no);
     }
-    z.add(a.gw, (int64_t)p.C_out * p.K);
+    if (!gather) z.add(a.gw, (int64_t)p.C_out * p.K);  // the scattering pass accumulates grad_weight
     if (gather) z.add((float *)flag, 1);
-    if (bias_here) z.add(a.gb, p.C_out);
     if (z.count > 0) hipLaunchKernelGGL(k_bwd_zero_set, dim3(grid_for(z.most)), dim3(256), 0, stream, z);
     const dim3 grid((unsigned)((int64_t)p.B * p.C_in * tiles_l));
     if (gather) {
         const int tiles_g = (p.L_out + kDwgLT - 1) / kDwgLT;
         const dim3 grid((unsigned)((int64_t)p.B * p.C_in * tiles_g));
+        float *wslots = (float *)((char *)flag + 256);
         if (bias_done) *bias_done = bias_here;
         switch (p.K) {
 #define DC1D_BDWG(KK)                                                                                              \
     case KK:                                                                                                       \
         hipLaunchKernelGGL((k_bwd_dwg<KK>), grid, dim3(kDwgT), g.lds, stream, a, g.win, g.nhp, tiles_g, flag,     \
-                           bias_here);                                                                             \
+                           bias_here, wslots);                                                                     \
         if (a.gx)                                                                                                  \
             hipLaunchKernelGGL((k_bwd_dwg_fix<KK>), dim3(fix_grid((int64_t)p.B * p.C_in * tiles_g)), dim3(256), 0,  \
                                stream, a, tiles_g, (const int *)flag);                                             \
@@ -1248,6 +1295,9 @@ hipError_t launch_backward_dw(BwdParams a, int *flag, hipStream_t stream, bool *
 #undef DC1D_BDWG
             default: return hipErrorInvalidValue;
         }
+        if (a.gw || bias_here)
+            hipLaunchKernelGGL(k_bwd_dw_wsum, dim3((unsigned)((p.C_in + 3) / 4)), dim3(256), 0, stream, a,
+                               (const float *)wslots, p.B * tiles_g, bias_here);
         return hipGetLastError();
     }
     switch (p.K) {

@@ -187,3 +187,22 @@ def test_dense_backward_repeats_bit_for_bit(G):
     torch.cuda.synchronize()
     for k in ("x", "offsets", "mask", "weight", "bias"):
         assert torch.equal(a[k], b[k]), k
+
+
+def test_depthwise_backward_repeats_bit_for_bit():
+    """The depthwise gather pass sums grad_weight and grad_bias per block
+    (waves in order) into workspace slots that a second launch adds in block
+    order; grad_x and the offset and mask gradients are gathered: the same
+    call twice at the measured depthwise size gives the same bits.  (Offsets
+    within the gather pass's reach, so no sample is left to its fix pass.)"""
+    w = inputs.WORKLOADS["depthwise"]
+    t = {k: (v.to(DEV) if v is not None else None) for k, v in inputs.make_inputs(w, seed=12).items()}
+    t["offsets"] = t["offsets"].clamp(-15.0, 15.0)
+    mask = torch.rand(t["offsets"].shape, device=DEV)
+    dout = torch.randn((w.B, w.C_out, w.L_out), device=DEV)
+    kw = dict(stride=w.stride, padding=w.padding, dilation=w.dilation, groups=w.groups)
+    a = dc1d.backward(t["x"], t["offsets"], t["weight"], dout, mask, **kw)
+    b = dc1d.backward(t["x"], t["offsets"], t["weight"], dout, mask, **kw)
+    torch.cuda.synchronize()
+    for k in ("x", "offsets", "mask", "weight", "bias"):
+        assert torch.equal(a[k], b[k]), k
