@@ -17,10 +17,10 @@
 // integer offsets).
 //
 // Kernels, in order on the caller's stream:
-//   k_bwd_zero_set   clears, in one launch, grad_x when it is scattered, the
-//                    offset / mask gradients when they are accumulated over
-//                    several channel blocks, and the gather's flag;
-//   dS               dense shapes (groups == 1): k_transpose W -> W^T, then
+//   k_bwd_zero_set   clears, in one launch, grad_x when it is scattered and
+//                    (other than on dense shapes) the gather's flag;
+//   dS               dense shapes (groups == 1): k_transpose W -> W^T (it
+//                    also clears the gather's flag), then
 //                    k_gemm dS = W^T dout on the MFMA kernel; other shapes:
 //                    k_bwd_samples (a loop over the group's output channels);
 //                    dS is [B][C_in][K][L_out] in the workspace;
@@ -32,9 +32,11 @@
 //                    and grad_x (LDS atomics) when the gather does not fit;
 //   k_bwd_dxg        grad_x gathered from dS (no clear, no atomics), then
 //                    k_bwd_dxg_fix for samples moved beyond its reach;
-//   weight gradient  dense: k_restride_dout then k_gemm grad_weight =
+//   weight gradient  dense: k_restride_bias (dout restrided, and grad_bias
+//                    from the same reads) then k_gemm grad_weight =
 //                    dout S^T; other shapes: k_bwd_weight;
-//   k_bwd_bias       one workgroup per output channel, fixed order, no atomics.
+//   k_bwd_bias       (where k_restride_bias did not run) one workgroup per
+//                    output channel, fixed order, no atomics.
 #include "dc1d_internal.h"
 
 #include <algorithm>
@@ -1051,17 +1053,47 @@ __global__ void __launch_bounds__(256) k_bwd_dwg_fix(BwdParams a, int tiles_l, c
     }
 }
 
-// out[c][r] = in[r][c] for a rows x cols matrix (32 x 32 tiles through LDS).
+// out[c][r] = in[r][c] for a rows x cols matrix (32 x 32 tiles through LDS);
+// also clears *clear (a flag of a later pass) when given.
 __global__ void __launch_bounds__(256) k_transpose(const float *__restrict__ in, float *__restrict__ out, int rows,
-                                                   int cols) {
+                                                   int cols, int *clear) {
     __shared__ float tile[32][33];
     const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
+    if (clear && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *clear = 0;
     const int tx = threadIdx.x % 32, ty = threadIdx.x / 32;  // 32 x 8
     for (int j = ty; j < 32; j += 8)
         if (r0 + j < rows && c0 + tx < cols) tile[j][tx] = in[(int64_t)(r0 + j) * cols + c0 + tx];
     __syncthreads();
     for (int j = ty; j < 32; j += 8)
         if (c0 + j < cols && r0 + tx < rows) out[(int64_t)(c0 + j) * rows + r0 + tx] = tile[tx][j];
+}
+
+// A[co][b*L_out + l] = dout[b][co][l], one workgroup per output channel
+// (its B * L_out values in k_bwd_bias's order), and with a bias gradient
+// wanted grad_bias[co] summed as k_bwd_bias sums it, in the same order.
+__global__ void __launch_bounds__(256) k_restride_bias(BwdParams a, float *__restrict__ A) {
+    const Params &p = a.p;
+    __shared__ float s_red[256];
+    const int co = blockIdx.x;
+    const int64_t n = (int64_t)p.B * p.L_out;
+    const float *d = a.dout + (int64_t)co * p.L_out;
+    float *arow = A + (int64_t)co * n;
+    float acc = 0.0f;
+#pragma unroll 4
+    for (int64_t i = threadIdx.x; i < n; i += 256) {
+        const int64_t b = i / p.L_out, l = i - b * p.L_out;
+        const float v = d[b * p.C_out * p.L_out + l];
+        arow[i] = v;
+        acc += v;
+    }
+    if (!a.gb) return;
+    s_red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if ((int)threadIdx.x < h) s_red[threadIdx.x] += s_red[threadIdx.x + h];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) a.gb[co] = s_red[0];
 }
 
 // A[co][b*L_out + l] = dout[b][co][l]
@@ -1331,12 +1363,15 @@ hipError_t launch_backward(BwdParams a, int num_cus, hipStream_t stream) {
     }
     const DxgPlan xg = plan_dxg(p);
     const bool gather_x = a.gx && xg.lds > 0;  // grad_x gathered (no clear, no atomics) or scattered
+    bool bias_done = false;
     ZeroSet z = {};
     if (!gather_x) z.add(a.gx, (int64_t)p.B * p.C_in * p.L_in);
     const int64_t no = (int64_t)p.B * p.G * p.L_out * p.K;
     float *om_slots = dx.atomic_om ? (float *)(ws + L.om) : nullptr;
     int *flag = (int *)(ws + L.flag);
-    if (gather_x && n > 0) z.add((float *)flag, 1);
+    // the dense path's k_transpose clears the flag; the others clear it here
+    const bool dense_run = n > 0 && (want_dx || a.gw) && dense_path(p);
+    if (gather_x && n > 0 && !dense_run) z.add((float *)flag, 1);
     if (z.count > 0) hipLaunchKernelGGL(k_bwd_zero_set, dim3(grid_for(z.most)), dim3(256), 0, stream, z);
     const int64_t dx_blocks = (int64_t)p.B * dx.ngrp_blocks * dx.tiles_l;
     if (dx_blocks >= ((int64_t)1 << 31) || (int64_t)p.C_out * p.cpg * p.K >= ((int64_t)1 << 31))
@@ -1350,7 +1385,7 @@ hipError_t launch_backward(BwdParams a, int num_cus, hipStream_t stream) {
             float *wt = (float *)(ws + L.wt);
             const int CK = p.C_in * p.K;
             hipLaunchKernelGGL(k_transpose, dim3((unsigned)((CK + 31) / 32), (unsigned)((p.C_out + 31) / 32)),
-                               dim3(256), 0, stream, (const float *)p.w, wt, p.C_out, CK);
+                               dim3(256), 0, stream, (const float *)p.w, wt, p.C_out, CK, gather_x ? flag : nullptr);
             const hipError_t e = launch_gemm_f32(gemm_ds(p, wt, a.dout, a.dS, ws + L.part), p.L_out,
                                                  (int64_t)p.C_out * p.L_out, 0, num_cus, stream);
             if (e != hipSuccess) return e;
@@ -1380,7 +1415,12 @@ hipError_t launch_backward(BwdParams a, int num_cus, hipStream_t stream) {
             if (dense) {
                 float *A = (float *)(ws + L.A);
                 const int64_t nd = (int64_t)p.B * p.C_out * p.L_out;
-                hipLaunchKernelGGL(k_restride_dout, dim3(grid_for(nd)), dim3(256), 0, stream, a, A);
+                if (a.gb && p.C_out < (1 << 20)) {  // grad_bias from the same reads
+                    hipLaunchKernelGGL(k_restride_bias, dim3((unsigned)p.C_out), dim3(256), 0, stream, a, A);
+                    bias_done = true;
+                } else {
+                    hipLaunchKernelGGL(k_restride_dout, dim3(grid_for(nd)), dim3(256), 0, stream, a, A);
+                }
                 const hipError_t e = launch_gemm_f32(gemm_dw(p, A, s.S, a.gw, ws + L.part), p.C_in * p.K, 0,
                                                      0, num_cus, stream);
                 if (e != hipSuccess) return e;
@@ -1393,7 +1433,7 @@ hipError_t launch_backward(BwdParams a, int num_cus, hipStream_t stream) {
         const int64_t nw = (int64_t)p.C_out * p.cpg * p.K;
         hipLaunchKernelGGL(k_bwd_zero, dim3(grid_for(nw)), dim3(256), 0, stream, a.gw, nw);
     }
-    return launch_bias(a, stream);
+    return bias_done ? hipGetLastError() : launch_bias(a, stream);
 }
 
 }  // namespace dc1d
