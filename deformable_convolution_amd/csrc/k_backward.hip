@@ -164,13 +164,23 @@ __global__ void __launch_bounds__(256) k_bwd_bias(BwdParams a) {
 // the weight gradient in the GEMM's layout [(b, l)][ci*K + k]: a workgroup
 // per row (b, l) (grid-stride), (ci, k) fastest, 32-bit index arithmetic
 // inside a row.
+//
+// Workgroups are dealt to the 8 XCDs in turn (id mod 8), each XCD with its
+// own L2; with one workgroup per row the ids are remapped so that each XCD
+// takes a contiguous run of rows -- whole batches, whose x rows it then
+// fetches alone -- instead of every XCD fetching all of x.
 __global__ void __launch_bounds__(256) k_bwd_samples_t(BwdParams a, FastDiv fd_K, FastDiv fd_cpo) {
     const Params &p = a.p;
     const float *__restrict__ off = (const float *)p.off;
     const float *__restrict__ mask = (const float *)p.mask;
     const int K = p.K, CK = p.C_in * K, L_in = p.L_in;
     const int64_t rows = (int64_t)p.B * p.L_out;
-    for (int64_t bl = blockIdx.x; bl < rows; bl += gridDim.x) {
+    int64_t first = blockIdx.x;
+    if ((int64_t)gridDim.x == rows) {  // XCD j takes rows [j*q + min(j, r), ...), q = rows / 8, r = rows % 8
+        const int U = (int)gridDim.x, q = U >> 3, r = U & 7, xcd = (int)blockIdx.x & 7, loc = (int)blockIdx.x >> 3;
+        first = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + loc;
+    }
+    for (int64_t bl = first; bl < rows; bl += gridDim.x) {
         const int b = (int)(bl / p.L_out), l = (int)(bl - (int64_t)b * p.L_out);
         const float *__restrict__ xb = (const float *)p.x + (int64_t)b * p.C_in * L_in;
         const int64_t orow = (int64_t)b * p.G * p.L_out + l;  // offsets row (b, g = 0) at l
