@@ -184,17 +184,34 @@ __global__ void __launch_bounds__(256) k_im2col2d_band(Params2 p, int runs, int 
         const int rr = e / W, col = e - rr * W, r = r_lo + rr;
         boff[u] = (e < nband && r >= 0 && r < p.H) ? r * W + col : -1;
     }
-    float xv[kBandPer];
+    // bf16: the loads are unconditional (entries outside the image or past
+    // the band read the plane's first element, zeroed when put) and the
+    // sample stores below too, so the compiler can count the memory
+    // operations in flight: waiting for the band's loads then waits for them
+    // alone, not for the stores issued after them (the values stay in
+    // storage format until put, so that widening them does not wait either).
+    // Measured on the 64 x 64 workloads: bf16 119 -> 73 us; fp32 116 -> 123
+    // us, so fp32 keeps the conditional loads and stores.
+    constexpr bool kFlat = sizeof(T) == 2;
+    T xv[kBandPer];
     auto fetch = [&](int ci) {
         const T *__restrict__ xp = x + ((int64_t)b * p.C_in + ci) * plane;
 #pragma unroll
-        for (int u = 0; u < kBandPer; ++u) xv[u] = boff[u] >= 0 ? D::ld(xp, boff[u]) : 0.0f;
+        for (int u = 0; u < kBandPer; ++u) {
+            if constexpr (kFlat)
+                xv[u] = xp[max(boff[u], 0)];
+            else
+                xv[u] = boff[u] >= 0 ? xp[boff[u]] : T(0);
+        }
     };
     auto put = [&](float *band) {
+        float v[kBandPer];
+#pragma unroll
+        for (int u = 0; u < kBandPer; ++u) v[u] = boff[u] >= 0 ? D::ld(xv, u) : 0.0f;
 #pragma unroll
         for (int u = 0; u < kBandPer; ++u) {
             const int e = threadIdx.x + 256 * u;
-            if (e < nband) band[e] = xv[u];
+            if (e < nband) band[e] = v[u];
         }
     };
     if (c_lo < c_hi) {
@@ -207,8 +224,10 @@ __global__ void __launch_bounds__(256) k_im2col2d_band(Params2 p, int runs, int 
         const T *__restrict__ xp = x + ((int64_t)b * p.C_in + ci) * plane;
         const bool more = ci + 1 < c_hi;
         if (more) fetch(ci + 1);
-        if (valid) {
-            T *__restrict__ st = (T *)p.ws + ((int64_t)b * p.C_in + ci) * TT * HWo + q;
+        // (bf16: lanes past the end store the last position's sample -- the
+        // same value at the same address)
+        if (kFlat || valid) {
+            T *__restrict__ st = (T *)p.ws + ((int64_t)b * p.C_in + ci) * TT * HWo + qq;
 #pragma unroll
             for (int t = 0; t < TT; ++t) {
                 float v;
