@@ -169,6 +169,7 @@ __global__ void __launch_bounds__(256) k_bwd_bias(BwdParams a) {
 // own L2; with one workgroup per row the ids are remapped so that each XCD
 // takes a contiguous run of rows -- whole batches, whose x rows it then
 // fetches alone -- instead of every XCD fetching all of x.
+constexpr int kSampU = 4;
 __global__ void __launch_bounds__(256) k_bwd_samples_t(BwdParams a, FastDiv fd_K, FastDiv fd_cpo) {
     const Params &p = a.p;
     const float *__restrict__ off = (const float *)p.off;
@@ -186,18 +187,41 @@ __global__ void __launch_bounds__(256) k_bwd_samples_t(BwdParams a, FastDiv fd_K
         const int64_t orow = (int64_t)b * p.G * p.L_out + l;  // offsets row (b, g = 0) at l
         const int base0 = l * p.stride - p.padding;
         float *__restrict__ dst = a.S + bl * CK;
-        for (int r = threadIdx.x; r < CK; r += 256) {
-            const int ci = (int)fdiv((uint32_t)r, fd_K), k = r - ci * K;
-            const int g = (int)fdiv((uint32_t)ci, fd_cpo);
-            const int64_t oi = (orow + (int64_t)g * p.L_out) * K + k;
-            int i0;
-            float f;
-            split_position(off[oi], base0 + k * p.dilation, tap_range(p, k), i0, f);
-            const float m = mask ? mask[oi] : 1.0f;
-            const float *__restrict__ xrow = xb + (int64_t)ci * L_in;
-            const float x0 = (i0 >= 0 && i0 < L_in) ? xrow[i0] : 0.0f;
-            const float x1 = (i0 + 1 >= 0 && i0 + 1 < L_in) ? xrow[i0 + 1] : 0.0f;
-            dst[r] = fmaf(f, x1 - x0, x0) * m;
+        // four elements per thread at a time, every load and store
+        // unconditional (x at clamped positions, zeroed outside [0, L_in);
+        // lanes past the row's end redo its last element, the same value at
+        // the same address), so the loads of the four are in flight together
+        // and waiting for them never waits for the previous stores
+        for (int r0 = threadIdx.x; r0 < CK; r0 += 256 * kSampU) {
+            int rr[kSampU], ci[kSampU], k[kSampU];
+            float o[kSampU], m[kSampU];
+#pragma unroll
+            for (int u = 0; u < kSampU; ++u) {
+                rr[u] = min(r0 + 256 * u, CK - 1);
+                ci[u] = (int)fdiv((uint32_t)rr[u], fd_K);
+                k[u] = rr[u] - ci[u] * K;
+                const int g = (int)fdiv((uint32_t)ci[u], fd_cpo);
+                const int64_t oi = (orow + (int64_t)g * p.L_out) * K + k[u];
+                o[u] = off[oi];
+                m[u] = mask ? mask[oi] : 1.0f;
+            }
+            float x0[kSampU], x1[kSampU], f[kSampU];
+            bool v0[kSampU], v1[kSampU];
+#pragma unroll
+            for (int u = 0; u < kSampU; ++u) {
+                int i0;
+                split_position(o[u], base0 + k[u] * p.dilation, tap_range(p, k[u]), i0, f[u]);
+                v0[u] = i0 >= 0 && i0 < L_in;
+                v1[u] = i0 + 1 >= 0 && i0 + 1 < L_in;
+                const float *__restrict__ xrow = xb + (int64_t)ci[u] * L_in;
+                x0[u] = xrow[min(max(i0, 0), L_in - 1)];
+                x1[u] = xrow[min(max(i0 + 1, 0), L_in - 1)];
+            }
+#pragma unroll
+            for (int u = 0; u < kSampU; ++u) {
+                const float a0 = v0[u] ? x0[u] : 0.0f, a1 = v1[u] ? x1[u] : 0.0f;
+                dst[rr[u]] = fmaf(f[u], a1 - a0, a0) * m[u];
+            }
         }
     }
 }
