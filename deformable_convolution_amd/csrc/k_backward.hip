@@ -580,8 +580,9 @@ constexpr int kDwgOpt = 1;      // outputs per thread
 constexpr int kDwgLT = kDwgT * kDwgOpt;
 constexpr int kDwgR = 16;       // largest |floor(offset)| gathered
 constexpr int kDwgMargin = 24;  // x window margin (>= kDwgR + 2)
-constexpr int kDwgTail = 2 * kDwgR + 4;  // sentinel entries after each tap's filled outputs (phase 2
-                                         // reads up to (2 kDwgR + 2) + 2 candidates from the last one)
+constexpr int kDwgTail = 2 * kDwgR + 6;  // sentinel entries after each tap's filled outputs (phase 2
+                                         // reads up to (2 kDwgR + 3) + 3 candidates from the first one,
+                                         // which may be the last filled output)
 constexpr int kIrregular = INT_MIN / 2;
 
 __device__ __forceinline__ int floor_div(int a, int b) {
@@ -957,9 +958,12 @@ __global__ void __launch_bounds__(256) k_bwd_dxg(BwdParams a, DxgPlan pl, int *f
             const float *__restrict__ mlk = ML + k * NHP + h0, *__restrict__ mrk = MR + k * NHP + h0;
             const float *__restrict__ dsk = dsc + (int64_t)k * L_out + lh0 + h0;
             const int last = nhl - 1 - h0;  // candidates past the filled outputs read the last one's dS
-            for (int m0 = 0; m0 < ncand; m0 += 2) {
+            // four candidates at a time (their 4 * CPT dS loads in flight
+            // together); the up to three past ncand are sentinels or outputs
+            // that cannot reach i or i + 1, so they add exact zeros
+            for (int m0 = 0; m0 < ncand; m0 += 4) {
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
+                for (int u = 0; u < 4; ++u) {
                     const int v = i0k[m0 + u];
                     const float ml = mlk[m0 + u], mr = mrk[m0 + u];
                     // at most one of a position's two terms is nonzero
