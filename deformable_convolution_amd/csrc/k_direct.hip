@@ -146,6 +146,7 @@ hipError_t launch_direct(const Params &p, hipStream_t stream) {
 constexpr int kDwThreads = 256;
 constexpr int kDwOpt = 2;      // outputs per thread (few registers: high occupancy)
 constexpr int kDwMargin = 16;  // window margin per side (input positions)
+constexpr int kDwWinU = 3;     // window positions per thread loaded up front (covers K * dilation <= 40 at stride 1)
 
 // VW consecutive elements (VW = 2 or 4) as floats, in one load.
 template <class D, int VW>
@@ -208,11 +209,24 @@ __global__ void __launch_bounds__(kDwThreads) k_depthwise(Params p, int WIN, int
     const int L_in = p.L_in;
     const int lo = l0 * p.stride - p.padding - kDwMargin;
 
-    // x window (WIN == 0: every sample reads global memory)
-    for (int j = t; j < WIN; j += kDwThreads) {
-        const int i = lo + j;
-        s_x[j] = (i >= 0 && i < L_in) ? D::ld(xrow, i) : 0.0f;
+    // x window (WIN == 0: every sample reads global memory).  Without a
+    // mask the first WU * kDwThreads positions are loaded at clamped
+    // (in-bounds) addresses before the offsets, so all these loads are in
+    // flight together, and written to LDS (zero outside [0, L_in)) after
+    // them, wider windows loading the rest in a loop (depthwise 5-tap layer:
+    // 177 -> 171 us); with a mask that measured slower (packed layer's 3-tap
+    // pass: 102 -> 105 us), so there the window is loaded first, in a loop.
+    constexpr int WU = MASK ? 0 : kDwWinU;
+    float xw[WU > 0 ? WU : 1];
+    if constexpr (WU == 0) {
+        for (int j = t; j < WIN; j += kDwThreads) {
+            const int i = lo + j;
+            s_x[j] = (i >= 0 && i < L_in) ? D::ld(xrow, i) : 0.0f;
+        }
     }
+#pragma unroll
+    for (int u = 0; u < WU; ++u)  // (lanes past the window reread its last position: no extra lines)
+        xw[u] = D::ld(xrow, min(max(lo + min(t + u * kDwThreads, WIN - 1), 0), L_in - 1));
     // this thread's offsets and mask values
     const int lt = l0 + OPT * t;
     const int nvalid = min(OPT, p.L_out - lt);  // may be <= 0
@@ -234,6 +248,17 @@ __global__ void __launch_bounds__(kDwThreads) k_depthwise(Params p, int WIN, int
                 ov[q] = ok ? D::ld(off, e0 + q) : 0.0f;
                 if (MASK) mv[q] = ok ? D::ld(mask, e0 + q) : 0.0f;
             }
+        }
+    }
+    if constexpr (WU > 0) {
+#pragma unroll
+        for (int u = 0; u < WU; ++u) {
+            const int j = t + u * kDwThreads, i = lo + j;
+            if (j < WIN) s_x[j] = (i >= 0 && i < L_in) ? xw[u] : 0.0f;
+        }
+        for (int j = t + WU * kDwThreads; j < WIN; j += kDwThreads) {
+            const int i = lo + j;
+            s_x[j] = (i >= 0 && i < L_in) ? D::ld(xrow, i) : 0.0f;
         }
     }
     __syncthreads();
