@@ -241,6 +241,7 @@ __global__ void __launch_bounds__(256) k_bwd_samples_t(BwdParams a, FastDiv fd_K
 // [nsub][2][B*G*L_out*K]), which k_bwd_om_sum adds in slot order -- no
 // atomics, the same bits on every run.
 constexpr int kBwdMargin = 32;
+constexpr int kFillU = 8;  // window entries per thread loaded together
 
 struct DxPlan {
     int cbx, lt, win, tiles_l, ngrp_blocks;
@@ -265,10 +266,27 @@ __global__ void __launch_bounds__(256) k_bwd_dx(BwdParams a, DxPlan pl, float *_
     const int l0 = tile * LT;
     const int lo = l0 * p.stride - p.padding - kBwdMargin;
     const float *__restrict__ x = (const float *)p.x + ((int64_t)b * p.C_in + ci0) * L_in;
-    for (int e = threadIdx.x; e < CBX * W; e += 256) {
-        const int c = e / W, j = e - c * W, pos = lo + j;
-        xs[e] = (pos >= 0 && pos < L_in) ? x[(int64_t)c * L_in + pos] : 0.0f;
-        gacc[e] = 0.0f;
+    // the windows, kFillU entries per thread at a time: loads at clamped
+    // (in-bounds) entries and positions, all in flight before the LDS
+    // writes (zero outside [0, L_in); lanes past the end write nothing)
+    const int nwin = CBX * W;
+    for (int e0 = threadIdx.x; e0 < nwin; e0 += 256 * kFillU) {
+        float v[kFillU];
+#pragma unroll
+        for (int u = 0; u < kFillU; ++u) {
+            const int e = min(e0 + 256 * u, nwin - 1);
+            const int c = e / W, j = e - c * W;
+            v[u] = x[(int64_t)c * L_in + min(max(lo + j, 0), L_in - 1)];
+        }
+#pragma unroll
+        for (int u = 0; u < kFillU; ++u) {
+            const int e = e0 + 256 * u;
+            if (e < nwin) {
+                const int c = e / W, pos = lo + (e - c * W);
+                xs[e] = (pos >= 0 && pos < L_in) ? v[u] : 0.0f;
+                gacc[e] = 0.0f;
+            }
+        }
     }
     __syncthreads();
     const float *__restrict__ off = (const float *)p.off;
