@@ -598,6 +598,7 @@ constexpr int kDwgOpt = 1;      // outputs per thread
 constexpr int kDwgLT = kDwgT * kDwgOpt;
 constexpr int kDwgR = 16;       // largest |floor(offset)| gathered
 constexpr int kDwgMargin = 24;  // x window margin (>= kDwgR + 2)
+constexpr int kDwgWinU = 2;     // x window positions per thread loaded with the offsets
 constexpr int kDwgTail = 2 * kDwgR + 6;  // sentinel entries after each tap's filled outputs (phase 2
                                          // reads up to (2 kDwgR + 3) + 3 candidates from the first one,
                                          // which may be the last filled output)
@@ -647,10 +648,13 @@ __global__ void __launch_bounds__(kDwgT, 4) k_bwd_dwg(BwdParams a, int WIN, int 
     const int l0 = geo.l0, lh0 = geo.lh0;
     const int lo = l0 * p.stride - p.padding - kDwgMargin;
     const float *__restrict__ xrow = (const float *)p.x + (int64_t)row * L_in;
-    for (int j = threadIdx.x; j < WIN; j += kDwgT) {
-        const int pos = lo + j;
-        xs[j] = (pos >= 0 && pos < L_in) ? xrow[pos] : 0.0f;
-    }
+    // the x window's first kDwgWinU * kDwgT positions: loaded here at
+    // clamped addresses, written to LDS after the offset, mask and dout
+    // loads below are issued, so all of them are in flight together
+    float xw[kDwgWinU];
+#pragma unroll
+    for (int u = 0; u < kDwgWinU; ++u)
+        xw[u] = xrow[min(max(lo + min((int)threadIdx.x + u * kDwgT, WIN - 1), 0), L_in - 1)];
     {  // entries past the filled outputs match no position
         const int nhl = geo.lh1 - lh0;
         for (int e = threadIdx.x; e < KT * NHP; e += kDwgT) {
@@ -662,7 +666,6 @@ __global__ void __launch_bounds__(kDwgT, 4) k_bwd_dwg(BwdParams a, int WIN, int 
         s_R = 0;
         s_irr = 0;
     }
-    __syncthreads();
     const float *__restrict__ off = (const float *)p.off;
     const float *__restrict__ mask = (const float *)p.mask;
     const float *__restrict__ w = (const float *)p.w + (int64_t)c * KT;
@@ -711,6 +714,16 @@ __global__ void __launch_bounds__(kDwgT, 4) k_bwd_dwg(BwdParams a, int WIN, int 
 #pragma unroll
         for (int o = 0; o < kDwgOpt; ++o) dv[o] = o < nvalid ? dout[lt + o] : 0.0f;
     }
+#pragma unroll
+    for (int u = 0; u < kDwgWinU; ++u) {
+        const int jj = threadIdx.x + u * kDwgT, pos = lo + jj;
+        if (jj < WIN) xs[jj] = (pos >= 0 && pos < L_in) ? xw[u] : 0.0f;
+    }
+    for (int jj = threadIdx.x + kDwgWinU * kDwgT; jj < WIN; jj += kDwgT) {
+        const int pos = lo + jj;
+        xs[jj] = (pos >= 0 && pos < L_in) ? xrow[pos] : 0.0f;
+    }
+    __syncthreads();
     float go[NV], gm[NV];
 #pragma unroll
     for (int o = 0; o < kDwgOpt; ++o) {
